@@ -1,0 +1,227 @@
+"""Seeded synthetic decode-attention workloads.
+
+This module only draws inputs: sequence lengths, page permutations, bf16 bit
+patterns for q / K / V, and sparse index sets.  It holds none of the attention
+arithmetic, so both the fp64 oracle and the HIP path can consume the same bits
+without sharing any code of the method.
+
+Workload shapes follow the decode settings the source pages discuss: GQA and
+MLA decode attention over a paged KV cache (MeldKernel summary, "Experiments
+and results"), and index-sparse MLA decode with 2 requests x 8 query tokens,
+KV = 8192 and Top-2048 (GLM-5.2 decode article, "Summary").  The pages hold no
+dataset, so every tensor is drawn here from N(0, 1) and rounded to bf16.
+
+Random streams are keyed, not sequential: every array is filled in chunks of
+2**22 elements, chunk c of array a drawn from
+``PCG64(SeedSequence([seed, a, c]))``.  That keeps the draw independent of the
+thread count used to fill it.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+MODE_GQA = 0
+MODE_MLA = 1
+MODE_MLA_SPARSE = 2
+
+_CHUNK = 1 << 22
+
+# stream ids (the second SeedSequence word)
+_S_SEQLENS, _S_PAGES, _S_Q, _S_K, _S_V, _S_IDX = range(6)
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """One decode workload.  ``seqlen_kind`` picks how lengths are drawn."""
+
+    name: str
+    mode: int
+    batch: int
+    q_tokens: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim_qk: int
+    head_dim_v: int
+    page_size: int
+    softmax_scale: float
+    seqlen_kind: str            # "uniform" | "loguniform" | "skewed" | "fixed"
+    seqlen_lo: int = 0
+    seqlen_hi: int = 0
+    long_len: int = 0           # skewed: the one long sequence
+    short_len: int = 0          # skewed: all the others
+    topk: int = 0               # sparse: distinct indices per query token
+    shuffle_pages: bool = True
+    seed: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+# The five decode workloads.  Seeds are 1000 + position (1-based).
+CONFIGS: list[Config] = [
+    Config("tiny_gqa", MODE_GQA, batch=4, q_tokens=1, num_q_heads=8, num_kv_heads=2,
+           head_dim_qk=64, head_dim_v=64, page_size=512, softmax_scale=1 / math.sqrt(64),
+           seqlen_kind="uniform", seqlen_lo=1, seqlen_hi=512, shuffle_pages=False, seed=1001),
+    Config("llama3_8b_gqa", MODE_GQA, batch=64, q_tokens=1, num_q_heads=32, num_kv_heads=8,
+           head_dim_qk=128, head_dim_v=128, page_size=16, softmax_scale=1 / math.sqrt(128),
+           seqlen_kind="loguniform", seqlen_lo=128, seqlen_hi=32768, seed=1002),
+    Config("skewed_gqa", MODE_GQA, batch=32, q_tokens=1, num_q_heads=32, num_kv_heads=8,
+           head_dim_qk=128, head_dim_v=128, page_size=16, softmax_scale=1 / math.sqrt(128),
+           seqlen_kind="skewed", long_len=131072, short_len=256, seed=1003),
+    Config("deepseek_mla", MODE_MLA, batch=64, q_tokens=1, num_q_heads=128, num_kv_heads=1,
+           head_dim_qk=576, head_dim_v=512, page_size=64, softmax_scale=1 / math.sqrt(192),
+           seqlen_kind="uniform", seqlen_lo=1024, seqlen_hi=16384, seed=1004),
+    Config("sparse_mla", MODE_MLA_SPARSE, batch=2, q_tokens=8, num_q_heads=128, num_kv_heads=1,
+           head_dim_qk=576, head_dim_v=512, page_size=64, softmax_scale=1 / math.sqrt(192),
+           seqlen_kind="fixed", seqlen_lo=8192, topk=2048, seed=1005),
+]
+CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+
+
+@dataclasses.dataclass
+class Workload:
+    """Host arrays of one draw.  bf16 tensors are held as uint16 bit patterns."""
+
+    cfg: Config
+    seqlens: np.ndarray        # int32 [B]
+    block_table: np.ndarray    # int32 [B, max_pages]; unused entries are -1
+    q: np.ndarray              # uint16 [B, Tq, Hq, dk]
+    k_cache: np.ndarray        # uint16 [num_pages, P, Hkv, dk]  (MLA: the latent cache)
+    v_cache: np.ndarray | None  # uint16 [num_pages, P, Hkv, dv]; None for MLA
+    indices: np.ndarray | None  # int32 [B, Tq, topk]; sparse mode only
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_table.shape[1])
+
+    def kv_bytes(self) -> int:
+        """Bytes of K/V the attention must read (each used row once)."""
+        c = self.cfg
+        if c.mode == MODE_GQA:
+            per_tok = c.num_kv_heads * (c.head_dim_qk + c.head_dim_v) * 2
+            return int(self.seqlens.astype(np.int64).sum()) * per_tok
+        per_tok = c.head_dim_qk * 2
+        if c.mode == MODE_MLA:
+            return int(self.seqlens.astype(np.int64).sum()) * per_tok
+        return int(c.batch * c.q_tokens * c.topk) * per_tok
+
+
+def _gen(seed: int, stream: int, chunk: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, chunk])))
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (inputs are finite)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def normal_bf16(seed: int, stream: int, shape: tuple[int, ...]) -> np.ndarray:
+    """N(0,1) drawn in fp32 and rounded to bf16, filled chunk-parallel."""
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.uint16)
+
+    def fill(c: int) -> None:
+        lo = c * _CHUNK
+        hi = min(n, lo + _CHUNK)
+        out[lo:hi] = round_to_bf16_bits(_gen(seed, stream, c).standard_normal(hi - lo, dtype=np.float32))
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def draw_seqlens(cfg: Config) -> np.ndarray:
+    g = _gen(cfg.seed, _S_SEQLENS, 0)
+    b = cfg.batch
+    if cfg.seqlen_kind == "uniform":          # inclusive integer range
+        s = g.integers(cfg.seqlen_lo, cfg.seqlen_hi + 1, size=b)
+    elif cfg.seqlen_kind == "loguniform":     # L = round(exp(u)), u ~ U[ln lo, ln hi]
+        u = g.uniform(math.log(cfg.seqlen_lo), math.log(cfg.seqlen_hi), size=b)
+        s = np.clip(np.rint(np.exp(u)), cfg.seqlen_lo, cfg.seqlen_hi)
+    elif cfg.seqlen_kind == "skewed":         # the long sequence first, then the short ones
+        s = np.full(b, cfg.short_len)
+        s[0] = cfg.long_len
+    elif cfg.seqlen_kind == "fixed":
+        s = np.full(b, cfg.seqlen_lo)
+    else:
+        raise ValueError(cfg.seqlen_kind)
+    return s.astype(np.int32)
+
+
+def page_table(seqlens: np.ndarray, page_size: int, shuffle: bool, seed: int) -> np.ndarray:
+    """Block table over exactly the pages the sequences need.
+
+    Logical page i of sequence b gets a physical page id; with ``shuffle`` the
+    ids are a seeded random permutation of 0..num_pages-1, else they are laid
+    out in sequence order.  Unused entries are -1.
+    """
+    npg = (seqlens.astype(np.int64) + page_size - 1) // page_size
+    total = int(npg.sum())
+    maxp = int(npg.max()) if len(npg) else 0
+    phys = np.arange(total, dtype=np.int32)
+    if shuffle:
+        phys = _gen(seed, _S_PAGES, 0).permutation(total).astype(np.int32)
+    bt = np.full((len(seqlens), max(maxp, 1)), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(npg):
+        bt[b, :n] = phys[off:off + n]
+        off += int(n)
+    return bt
+
+
+def make_workload(cfg: Config, seqlens: np.ndarray | None = None) -> Workload:
+    """Draw one workload.  ``seqlens`` overrides the configured length draw."""
+    if seqlens is None:
+        seqlens = draw_seqlens(cfg)
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    bt = page_table(seqlens, cfg.page_size, cfg.shuffle_pages, cfg.seed)
+    num_pages = int(((seqlens.astype(np.int64) + cfg.page_size - 1) // cfg.page_size).sum())
+    P = cfg.page_size
+    q = normal_bf16(cfg.seed, _S_Q, (cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.head_dim_qk))
+    k = normal_bf16(cfg.seed, _S_K, (num_pages, P, cfg.num_kv_heads, cfg.head_dim_qk))
+    v = None
+    if cfg.mode == MODE_GQA:
+        v = normal_bf16(cfg.seed, _S_V, (num_pages, P, cfg.num_kv_heads, cfg.head_dim_v))
+    idx = None
+    if cfg.mode == MODE_MLA_SPARSE:
+        idx = np.empty((cfg.batch, cfg.q_tokens, cfg.topk), dtype=np.int32)
+        for b in range(cfg.batch):
+            for t in range(cfg.q_tokens):
+                g = _gen(cfg.seed, _S_IDX, b * cfg.q_tokens + t)
+                idx[b, t] = g.choice(int(seqlens[b]), size=cfg.topk, replace=False)
+    return Workload(cfg, seqlens, bt, q, k, v, idx)
+
+
+def small_variant(cfg: Config, batch: int, seqlen_hi: int, seed_offset: int = 0) -> Config:
+    """A reduced copy of ``cfg`` for oracle-sized parity runs (same heads/dims/paging)."""
+    kw = dataclasses.asdict(cfg)
+    kw.update(name=cfg.name + "_small", batch=batch, seed=cfg.seed + 100 + seed_offset)
+    if cfg.mode == MODE_MLA_SPARSE:
+        kw.update(seqlen_kind="fixed", seqlen_lo=seqlen_hi, topk=min(cfg.topk, seqlen_hi))
+    else:
+        kw.update(seqlen_kind="uniform", seqlen_lo=1, seqlen_hi=seqlen_hi)
+    return Config(**kw)

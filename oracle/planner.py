@@ -1,0 +1,197 @@
+"""Reference Stream-K work plan for split-KV decode (TEST INFRASTRUCTURE).
+
+The method (CSDN Q&A on waves and FlashMLA's Stream-K, "Summary"): cut the
+total work into exactly as many equal chunks as there are compute units and
+launch a single wave, so no unit idles behind a slow tail.  The mapping is
+decided at run time from the real sequence lengths and the hardware shape
+(MeldKernel summary, "Core method"), and only this host plan is rebuilt when
+the lengths change (GLM-5.2 decode article, MegaRTP design, point 1).  The
+host emits fixed-size work descriptors per worker (same article: 732 tile
+tasks over 148 worker queues give 140 queues of 5 and 8 of 4).
+
+Readings (the pages fix only "equal, one chunk per compute unit"):
+* cost model: KV tiles of T tokens; a unit of length L has ceil(L / T) tiles.
+* unit: the query heads sharing one K/V stream for one query token,
+  u = ((b * Tq + t) * Hkv + g) * (G / Hu) + hb; units are ordered by u.
+* tiles are laid out unit-major; chunk k takes floor(N / C) tiles, plus one
+  for the first N mod C chunks, contiguously.
+* a piece is a chunk's intersection with one unit; its split index counts the
+  unit's pieces in chunk order; split units get consecutive partial slots.
+* placement: with X locality domains (XCDs) and C divisible by X, logical
+  chunk k runs on worker w = (k mod C/X) * X + k div (C/X), so consecutive
+  chunks (the pieces of one unit) share a domain when the hardware places
+  worker w in domain w mod X.  Otherwise w = k.
+
+The byte layout below is the contract with the C planner; it is written out
+here independently and compared byte for byte.
+"""
+from __future__ import annotations
+
+import struct
+
+import numpy as np
+
+PLAN_MAGIC = 0x4C504343          # "CCPL" little-endian
+PLAN_VERSION = 1
+HEADER_WORDS = 24
+ITEM_WORDS = 4                   # unit, tok_begin, tok_end, split
+
+MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def unit_lengths(mode: int, batch: int, q_tokens: int, num_q_heads: int, num_kv_heads: int,
+                 heads_per_unit: int, seqlens, topk: int) -> list[int]:
+    G = num_q_heads // num_kv_heads
+    hb = G // heads_per_unit
+    lens = []
+    for b in range(batch):
+        L = topk if mode == MODE_MLA_SPARSE else int(seqlens[b])
+        lens.extend([L] * (q_tokens * num_kv_heads * hb))
+    return lens
+
+
+def validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+             max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, heads_per_unit,
+             seqlens, block_table=None) -> None:
+    if mode not in (MODE_GQA, MODE_MLA, MODE_MLA_SPARSE):
+        raise ValueError("mode")
+    if batch < 1 or q_tokens < 1 or num_q_heads < 1 or num_kv_heads < 1:
+        raise ValueError("shape")
+    if mode != MODE_MLA_SPARSE and q_tokens != 1:
+        raise ValueError("dense decode has one query token per sequence")
+    if num_q_heads % num_kv_heads:
+        raise ValueError("heads")
+    G = num_q_heads // num_kv_heads
+    if heads_per_unit < 1 or G % heads_per_unit:
+        raise ValueError("heads_per_unit")
+    if head_dim_qk < 1 or head_dim_v < 1 or page_size < 1 or max_pages_per_seq < 1 or num_pages < 1:
+        raise ValueError("dims")
+    if num_cus < 1 or num_xcds < 1 or tile_tokens < 1:
+        raise ValueError("opts")
+    for b in range(batch):
+        L = int(seqlens[b])
+        if L < 1:
+            raise ValueError("seqlen")
+        if _ceil_div(L, page_size) > max_pages_per_seq:
+            raise ValueError("seqlen beyond block table")
+        if mode == MODE_MLA_SPARSE and (topk < 1 or topk > L):
+            raise ValueError("topk")
+        if block_table is not None:
+            row = np.asarray(block_table)[b, :_ceil_div(L, page_size)]
+            if np.any(row < 0) or np.any(row >= num_pages):
+                raise ValueError("page")
+
+
+def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+         max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, heads_per_unit,
+         seqlens, block_table=None) -> dict:
+    """Build the plan; returns its fields and the serialised ``blob``."""
+    validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+             max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, heads_per_unit,
+             seqlens, block_table)
+    C, X, T = num_cus, num_xcds, tile_tokens
+    lens = unit_lengths(mode, batch, q_tokens, num_q_heads, num_kv_heads, heads_per_unit, seqlens, topk)
+    U = len(lens)
+    ntiles = [_ceil_div(L, T) for L in lens]
+    first_tile = []
+    acc = 0
+    for n in ntiles:
+        first_tile.append(acc)
+        acc += n
+    N = acc
+
+    # equal split of N tiles into C contiguous chunks (+1 for the first N mod C)
+    base, rem = divmod(N, C)
+    chunk_pieces: list[list[tuple[int, int, int]]] = []
+    u = 0
+    for k in range(C):
+        start = k * base + min(k, rem)
+        end = start + base + (1 if k < rem else 0)
+        pieces = []
+        while u < U and first_tile[u] + ntiles[u] <= start:
+            u += 1
+        v = u
+        while end > start and v < U and first_tile[v] < end:
+            tb = max(start, first_tile[v]) - first_tile[v]
+            te = min(end, first_tile[v] + ntiles[v]) - first_tile[v]
+            pieces.append((v, tb * T, min(te * T, lens[v])))
+            if first_tile[v] + ntiles[v] > end:
+                break
+            v += 1
+        chunk_pieces.append(pieces)
+
+    nsplit = [0] * U
+    items_by_chunk = []
+    for pieces in chunk_pieces:
+        its = []
+        for (v, t0, t1) in pieces:
+            its.append((v, t0, t1, nsplit[v]))
+            nsplit[v] += 1
+        items_by_chunk.append(its)
+    pbase = []
+    S = 0
+    for n in nsplit:
+        if n > 1:
+            pbase.append(S)
+            S += n
+        else:
+            pbase.append(-1)
+
+    if X > 1 and C % X == 0:
+        CX = C // X
+        worker_of_chunk = [(k % CX) * X + k // CX for k in range(C)]
+    else:
+        worker_of_chunk = list(range(C))
+    chunk_of_worker = [0] * C
+    for k, w in enumerate(worker_of_chunk):
+        chunk_of_worker[w] = k
+
+    wg_off = [0]
+    items = []
+    for w in range(C):
+        its = items_by_chunk[chunk_of_worker[w]]
+        items.extend(its)
+        wg_off.append(len(items))
+    W = len(items)
+
+    header = [0] * HEADER_WORDS
+    header[:20] = [PLAN_MAGIC, PLAN_VERSION, mode, batch, q_tokens, num_q_heads, num_kv_heads,
+                   head_dim_qk, head_dim_v, page_size, topk, C, X, T, heads_per_unit, U, N, W, S,
+                   max(nsplit) if nsplit else 0]
+    words = header + wg_off + [x for it in items for x in it] + nsplit + pbase
+    for x in words:
+        if not (-2**31 <= x < 2**31):
+            raise ValueError("plan does not fit int32")
+    blob = struct.pack("<%di" % len(words), *words)
+    return dict(blob=blob, num_units=U, num_tiles=N, num_items=W, num_partials=S,
+                wg_off=wg_off, items=items, unit_nsplit=nsplit, unit_pbase=pbase,
+                worker_of_chunk=worker_of_chunk, unit_len=lens, chunk_items=items_by_chunk)
+
+
+def plan_for(wl, num_cus=256, num_xcds=8, tile_tokens=32, heads_per_unit=None) -> dict:
+    """``plan`` for a workload object from the seeded input generator."""
+    c = wl.cfg
+    hu = heads_per_unit if heads_per_unit is not None else c.num_q_heads // c.num_kv_heads
+    return plan(c.mode, c.batch, c.q_tokens, c.num_q_heads, c.num_kv_heads, c.head_dim_qk, c.head_dim_v,
+                c.page_size, wl.max_pages, wl.num_pages, c.topk, num_cus, num_xcds, tile_tokens, hu,
+                wl.seqlens, wl.block_table)
+
+
+def list_schedule(task_times, num_workers: int):
+    """Greedy list scheduling: each task, in order, starts on the earliest-free worker.
+
+    The hardware block scheduler of the tail-effect example (CSDN Q&A on
+    waves, "Scenario examples") behaves this way.  Returns (makespan,
+    per-worker finish times, per-worker assignment).
+    """
+    free = [0.0] * num_workers
+    assign = [[] for _ in range(num_workers)]
+    for i, t in enumerate(task_times):
+        w = min(range(num_workers), key=lambda j: (free[j], j))
+        assign[w].append(i)
+        free[w] += t
+    return max(free), free, assign
