@@ -1,0 +1,238 @@
+"""ctypes binding of libcrosscu.so: argument marshalling only.
+
+Every computation happens in the C library and its HIP kernels.  PyTorch is
+used for device memory and streams: tensors are passed as raw pointers
+(``data_ptr()``) and the current HIP stream as a handle.  If the library is not
+built, every entry point raises; nothing falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcrosscu.so")
+
+CC_OK = 0
+CC_ERR_INVALID, CC_ERR_UNSUPPORTED, CC_ERR_BUFFER, CC_ERR_PLAN = -1, -2, -3, -4
+CC_ERR_PAGE, CC_ERR_HIP, CC_ERR_DEVICE_DATA = -5, -6, -7
+MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
+POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
+REDUCE_FUSED, REDUCE_SPLIT_COMBINE = 0, 1
+
+# every symbol include/crosscu.h declares
+EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_plan_size", "cc_plan",
+           "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
+           "cc_decode_variant"]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("batch", ctypes.c_int32), ("q_tokens", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("topk", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("num_cus", ctypes.c_int32), ("num_xcds", ctypes.c_int32),
+                ("tile_tokens", ctypes.c_int32), ("heads_per_unit", ctypes.c_int32),
+                ("policy", ctypes.c_int32)]
+
+
+class CrossCUError(RuntimeError):
+    def __init__(self, code: int, what: str, detail: str):
+        super().__init__(f"{what}: {detail} (code {code})")
+        self.code = code
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_SZ = ctypes.c_size_t
+
+
+def load() -> ctypes.CDLL:
+    """Loads the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run cross_cu_load_amd.build.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.cc_version.restype = ctypes.c_int
+    lib.cc_version.argtypes = []
+    lib.cc_last_error.restype = ctypes.c_char_p
+    lib.cc_last_error.argtypes = []
+    lib.cc_strerror.restype = ctypes.c_char_p
+    lib.cc_strerror.argtypes = [ctypes.c_int]
+    lib.cc_device_query.argtypes = [ctypes.c_int, _I32P, _I32P]
+    lib.cc_plan_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), _I32P,
+                                 ctypes.POINTER(_SZ)]
+    lib.cc_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), _I32P, _I32P, _P, _SZ]
+    lib.cc_workspace_size.argtypes = [_P, ctypes.POINTER(_SZ)]
+    lib.cc_workspace_init.argtypes = [_P, _SZ, _P]
+    lib.cc_workspace_check.argtypes = [_P, _P, _P, _I32P, _I32P]
+    dec = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.cc_decode.argtypes = dec
+    lib.cc_decode_variant.argtypes = [ctypes.c_int] + dec
+    for f in EXPORTS:
+        if f not in ("cc_last_error", "cc_strerror"):
+            getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != CC_OK:
+        lib = load()
+        raise CrossCUError(rc, what, (lib.cc_last_error() or b"").decode() or
+                           lib.cc_strerror(rc).decode())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr_i32(a: np.ndarray):
+    return a.ctypes.data_as(_I32P)
+
+
+def problem(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+            max_pages_per_seq, num_pages, topk, softmax_scale) -> Problem:
+    return Problem(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+                   max_pages_per_seq, num_pages, topk, softmax_scale)
+
+
+def device_query(device: int = 0) -> tuple[int, int]:
+    lib = load()
+    cus, xcds = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.cc_device_query(device, ctypes.byref(cus), ctypes.byref(xcds)), "cc_device_query")
+    return cus.value, xcds.value
+
+
+def plan(prob: Problem, seqlens, block_table=None, num_cus=256, num_xcds=8, tile_tokens=32,
+         heads_per_unit=None, policy=POLICY_STREAMK) -> np.ndarray:
+    """Host plan blob (uint8 array) from cc_plan_size + cc_plan."""
+    lib = load()
+    if heads_per_unit is None:
+        heads_per_unit = prob.num_q_heads // prob.num_kv_heads
+    opts = PlanOpts(num_cus, num_xcds, tile_tokens, heads_per_unit, policy)
+    sl = _i32(seqlens)
+    if sl.shape != (prob.batch,):
+        raise ValueError("seqlens must have shape [batch]")
+    nbytes = _SZ()
+    _check(lib.cc_plan_size(ctypes.byref(prob), ctypes.byref(opts), _ptr_i32(sl), ctypes.byref(nbytes)),
+           "cc_plan_size")
+    buf = np.zeros(nbytes.value, dtype=np.uint8)
+    btp = None
+    if block_table is not None:
+        bt = _i32(block_table)
+        if bt.shape != (prob.batch, prob.max_pages_per_seq):
+            raise ValueError("block_table must have shape [batch, max_pages_per_seq]")
+        btp = _ptr_i32(bt)
+    _check(lib.cc_plan(ctypes.byref(prob), ctypes.byref(opts), _ptr_i32(sl), btp,
+                       buf.ctypes.data_as(_P), buf.nbytes), "cc_plan")
+    return buf
+
+
+def workspace_size(plan_host: np.ndarray) -> int:
+    lib = load()
+    n = _SZ()
+    _check(lib.cc_workspace_size(plan_host.ctypes.data_as(_P), ctypes.byref(n)), "cc_workspace_size")
+    return n.value
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_init(ws, stream=None) -> None:
+    lib = load()
+    _check(lib.cc_workspace_init(ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "cc_workspace_init")
+
+
+def workspace_check(plan_host: np.ndarray, ws, stream=None) -> tuple[int, int]:
+    """(non-zero counters, device error flags); synchronises the stream."""
+    lib = load()
+    dirty, flags = ctypes.c_int32(), ctypes.c_int32()
+    rc = lib.cc_workspace_check(plan_host.ctypes.data_as(_P), ctypes.c_void_p(ws.data_ptr()),
+                                _stream(stream), ctypes.byref(dirty), ctypes.byref(flags))
+    if rc not in (CC_OK, CC_ERR_DEVICE_DATA):
+        _check(rc, "cc_workspace_check")
+    return dirty.value, flags.value
+
+
+def _dp(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def decode(prob: Problem, plan_host: np.ndarray, plan_dev, q, k_cache, v_cache, block_table, seqlens,
+           indices, out, lse, workspace, reduce: int = REDUCE_FUSED, stream=None) -> None:
+    """cc_decode_variant on device tensors (asynchronous on the stream)."""
+    lib = load()
+    _check(lib.cc_decode_variant(reduce, ctypes.byref(prob), plan_host.ctypes.data_as(_P), _dp(plan_dev),
+                                 _dp(q), _dp(k_cache), _dp(v_cache), _dp(block_table), _dp(seqlens),
+                                 _dp(indices), _dp(out), _dp(lse), _dp(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "cc_decode")
+
+
+@dataclass
+class DeviceSession:
+    """Device-resident inputs, plan and workspace for repeated decode calls.
+
+    Holds torch device tensors only; every step of the decode runs in the
+    library's kernels.
+    """
+
+    prob: Problem
+    plan_host: np.ndarray
+    plan_dev: object
+    q: object
+    k: object
+    v: object
+    block_table: object
+    seqlens: object
+    indices: object
+    out: object
+    lse: object
+    workspace: object
+
+    def run(self, reduce: int = REDUCE_FUSED, stream=None) -> None:
+        decode(self.prob, self.plan_host, self.plan_dev, self.q, self.k, self.v, self.block_table,
+               self.seqlens, self.indices, self.out, self.lse, self.workspace, reduce, stream)
+
+
+def problem_for(wl) -> Problem:
+    c = wl.cfg
+    return problem(c.mode, c.batch, c.q_tokens, c.num_q_heads, c.num_kv_heads, c.head_dim_qk, c.head_dim_v,
+                   c.page_size, wl.max_pages, wl.num_pages, c.topk, c.softmax_scale)
+
+
+def session(wl, plan_host: np.ndarray, device="cuda") -> DeviceSession:
+    """Copies a host workload (from the seeded generator) and its plan to the device."""
+    import torch
+    dev = torch.device(device)
+
+    def t16(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    def t32(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    c = wl.cfg
+    prob = problem_for(wl)
+    ws = torch.empty(workspace_size(plan_host), dtype=torch.uint8, device=dev)
+    workspace_init(ws)
+    out = torch.empty((c.batch, c.q_tokens, c.num_q_heads, c.head_dim_v), dtype=torch.float32, device=dev)
+    lse = torch.empty((c.batch, c.q_tokens, c.num_q_heads), dtype=torch.float32, device=dev)
+    return DeviceSession(prob, plan_host, torch.from_numpy(plan_host).to(dev), t16(wl.q), t16(wl.k_cache),
+                         t16(wl.v_cache), t32(wl.block_table), t32(wl.seqlens), t32(wl.indices), out, lse, ws)

@@ -1,0 +1,233 @@
+// C ABI of the decode library: argument checks, plan/problem consistency,
+// workspace carving and kernel launches.  Everything here runs on the host
+// and touches device memory only through enqueued kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/crosscu.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  cc::set_error("%s: %s", what, hipGetErrorString(e));
+  return CC_ERR_HIP;
+}
+
+// Shapes the GQA kernel implements.
+int check_gqa(const cc_problem& p, const cc::PlanView& v) {
+  const int G = p.num_q_heads / p.num_kv_heads;
+  if (p.head_dim_qk != p.head_dim_v || (p.head_dim_qk != 64 && p.head_dim_qk != 128)) {
+    cc::set_error("GQA kernel: head_dim_qk == head_dim_v in {64, 128} (got %d, %d)",
+                  p.head_dim_qk, p.head_dim_v);
+    return CC_ERR_UNSUPPORTED;
+  }
+  if (G > 16) {
+    cc::set_error("GQA kernel: group size %d > 16", G);
+    return CC_ERR_UNSUPPORTED;
+  }
+  if (v.header[cc::H_HPU] != G) {
+    cc::set_error("GQA kernel: heads_per_unit must equal the group size %d", G);
+    return CC_ERR_UNSUPPORTED;
+  }
+  if (!is_pow2(p.page_size) || p.page_size < 16) {
+    cc::set_error("GQA kernel: page_size must be a power of two >= 16 (got %d)", p.page_size);
+    return CC_ERR_UNSUPPORTED;
+  }
+  if (v.header[cc::H_TILE] % 32) {
+    cc::set_error("GQA kernel: tile_tokens must be a multiple of 32 (got %d)", v.header[cc::H_TILE]);
+    return CC_ERR_UNSUPPORTED;
+  }
+  return CC_OK;
+}
+
+int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const void* plan_dev,
+                const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                const int32_t* seqlens, const int32_t* indices, float* out, float* lse,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!prob || !plan_host || !plan_dev || !q || !k_cache || !block_table || !seqlens || !out ||
+      !lse || !workspace) {
+    cc::set_error("null argument");
+    return CC_ERR_INVALID;
+  }
+  if (reduce != CC_REDUCE_FUSED && reduce != CC_REDUCE_SPLIT_COMBINE) {
+    cc::set_error("unknown reduction %d", reduce);
+    return CC_ERR_INVALID;
+  }
+  cc::PlanView v;
+  int rc = cc::parse_plan(plan_host, &v);
+  if (rc) return rc;
+  rc = cc::plan_matches(v, *prob);
+  if (rc) return rc;
+  const cc::WorkspaceLayout wl = cc::workspace_layout(v);
+  if (workspace_bytes < wl.total) {
+    cc::set_error("workspace holds %zu bytes, the plan needs %zu", workspace_bytes, wl.total);
+    return CC_ERR_BUFFER;
+  }
+  if (!(prob->softmax_scale > 0.f) || !std::isfinite(prob->softmax_scale)) {
+    cc::set_error("softmax_scale must be finite and > 0");
+    return CC_ERR_INVALID;
+  }
+  const cc_problem& p = *prob;
+  if (p.mode == CC_MODE_GQA) {
+    if (!v_cache) {
+      cc::set_error("GQA needs a V cache");
+      return CC_ERR_INVALID;
+    }
+    rc = check_gqa(p, v);
+    if (rc) return rc;
+  } else {
+    cc::set_error("mode %d is not implemented by this build", p.mode);
+    return CC_ERR_UNSUPPORTED;
+  }
+
+  const int32_t* pd = static_cast<const int32_t*>(plan_dev);
+  char* ws = static_cast<char*>(workspace);
+  cc::DecodeArgs a{};
+  a.mode = p.mode;
+  a.batch = p.batch;
+  a.q_tokens = p.q_tokens;
+  a.hq = p.num_q_heads;
+  a.hkv = p.num_kv_heads;
+  a.dqk = p.head_dim_qk;
+  a.dv = p.head_dim_v;
+  a.page_size = p.page_size;
+  a.max_pages = p.max_pages_per_seq;
+  a.num_pages = p.num_pages;
+  a.topk = p.topk;
+  a.scale_log2 = (float)((double)p.softmax_scale * 1.4426950408889634);
+  a.workers = v.workers();
+  a.units = v.units();
+  a.hpu = v.header[cc::H_HPU];
+  a.tile = v.header[cc::H_TILE];
+  a.wg_off = pd + v.off_wg;
+  a.items = reinterpret_cast<const int4*>(pd + v.off_items);
+  a.unit_nsplit = pd + v.off_nsplit;
+  a.unit_pbase = pd + v.off_pbase;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.block_table = block_table;
+  a.seqlens = seqlens;
+  a.indices = indices;
+  a.out = out;
+  a.lse = lse;
+  a.err = reinterpret_cast<int32_t*>(ws);
+  a.counters = reinterpret_cast<int32_t*>(ws + wl.counters_off);
+  a.partials = reinterpret_cast<float*>(ws + wl.partials_off);
+  a.slot_floats = (int)wl.slot_floats;
+  a.reduce = reduce;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = cc::launch_gqa(a, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (reduce == CC_REDUCE_SPLIT_COMBINE && v.partials() > 0) {
+    e = cc::launch_combine(a, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return CC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cc_version(void) { return 100; }
+
+const char* cc_last_error(void) { return cc::last_error(); }
+
+const char* cc_strerror(int code) {
+  switch (code) {
+    case CC_OK: return "ok";
+    case CC_ERR_INVALID: return "invalid argument";
+    case CC_ERR_UNSUPPORTED: return "unsupported problem";
+    case CC_ERR_BUFFER: return "buffer too small";
+    case CC_ERR_PLAN: return "plan malformed or built for another problem";
+    case CC_ERR_PAGE: return "page id outside the cache";
+    case CC_ERR_HIP: return "HIP runtime error";
+    case CC_ERR_DEVICE_DATA: return "device reported bad data";
+    default: return "unknown error code";
+  }
+}
+
+int cc_device_query(int device, int32_t* num_cus, int32_t* num_xcds) {
+  if (!num_cus || !num_xcds) {
+    cc::set_error("null argument");
+    return CC_ERR_INVALID;
+  }
+  int v = 0;
+  hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiProcessorCount)");
+  *num_cus = v;
+  int x = 1;
+  e = hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, device);
+  if (e != hipSuccess || x < 1) x = 1;
+  *num_xcds = x;
+  return CC_OK;
+}
+
+int cc_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace || bytes % 4) {
+    cc::set_error("workspace must be non-null and a multiple of 4 bytes");
+    return CC_ERR_INVALID;
+  }
+  hipError_t e = cc::launch_fill_zero(workspace, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "workspace fill");
+  return CC_OK;
+}
+
+int cc_workspace_check(const void* plan_host, const void* workspace, void* stream,
+                       int32_t* dirty_counters, int32_t* device_flags) {
+  if (!workspace || !dirty_counters || !device_flags) {
+    cc::set_error("null argument");
+    return CC_ERR_INVALID;
+  }
+  cc::PlanView v;
+  int rc = cc::parse_plan(plan_host, &v);
+  if (rc) return rc;
+  const cc::WorkspaceLayout wl = cc::workspace_layout(v);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  std::vector<int32_t> cnt(v.units());
+  int32_t flags = 0;
+  const char* ws = static_cast<const char*>(workspace);
+  e = hipMemcpy(&flags, ws, sizeof flags, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(error word)");
+  e = hipMemcpy(cnt.data(), ws + wl.counters_off, cnt.size() * sizeof(int32_t),
+                hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(counters)");
+  int32_t dirty = 0;
+  for (int32_t c : cnt) dirty += c != 0;
+  *dirty_counters = dirty;
+  *device_flags = flags;
+  if (dirty || flags) {
+    cc::set_error("workspace: %d non-zero counters, device flags 0x%x", dirty, flags);
+    return CC_ERR_DEVICE_DATA;
+  }
+  return CC_OK;
+}
+
+int cc_decode(const cc_problem* prob, const void* plan_host, const void* plan_dev, const void* q,
+              const void* k_cache, const void* v_cache, const int32_t* block_table,
+              const int32_t* seqlens, const int32_t* indices, float* out, float* lse,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(CC_REDUCE_FUSED, prob, plan_host, plan_dev, q, k_cache, v_cache, block_table,
+                     seqlens, indices, out, lse, workspace, workspace_bytes, stream);
+}
+
+int cc_decode_variant(int reduce, const cc_problem* prob, const void* plan_host,
+                      const void* plan_dev, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table, const int32_t* seqlens,
+                      const int32_t* indices, float* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return decode_impl(reduce, prob, plan_host, plan_dev, q, k_cache, v_cache, block_table, seqlens,
+                     indices, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

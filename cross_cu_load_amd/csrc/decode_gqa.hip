@@ -1,0 +1,624 @@
+// Persistent split-KV GQA decode attention for gfx950 (MI355X).
+//
+// One workgroup of 8 wavefronts per compute unit runs the equal chunk of KV
+// tiles the host plan gave it, so the whole batch is one wave with no tail
+// (CSDN Q&A on waves and FlashMLA's Stream-K, "Summary").  Pieces of a
+// sequence that other compute units also work on are merged inside this
+// kernel by whichever piece arrives last (MeldKernel summary, "Core method":
+// just-in-time reduction, no separate reduction kernel).  The softmax is the
+// streaming form that keeps the result exact while fused (fusion tutorial,
+// FlashAttention section).
+//
+// Inside a workgroup the chunk is cut again into 8 equal contiguous runs of
+// 32-token blocks, one per wave.  A wave streams its run through a private
+// LDS slot: the next block's K and V rows go HBM -> LDS with
+// global_load_lds_dwordx4 (no registers held while in flight) while the
+// current block, read back with ds_read_b128, computes:
+//   S^T[token][head] = K[token][:] . Q[head][:]   v_mfma_f32_16x16x32_bf16
+//   O[head][dv]     += P[head][token] . V[token][dv]
+// Each lane fetches exactly the 16 bytes it later needs as an MFMA operand, so
+// LDS reads are conflict-free and need no barrier.  Computing S^T puts each
+// head's 8 scores of a block in one lane in exactly the A-operand layout P
+// needs, so the softmax needs no data movement beyond two cross-lane max
+// steps; V is transposed in registers with bit operations.
+// Items a wave cannot finish alone (shared with another wave, or split across
+// compute units) leave their (m, l, o) in LDS; after one barrier the whole
+// workgroup merges them and runs the arrival-counter protocol.
+//
+// Scores are kept in base 2: s2 = scale * log2(e) * q.k, lse = ln2 * (m2 + log2 l).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/crosscu.h"
+#include "launch.h"
+
+namespace cc {
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBlk = 32;  // tokens per wave step
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// two fp32 -> packed bf16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Marks a value the whole wave agrees on, so it lives in a scalar register and
+// addresses built from it use the scalar-base load forms.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Asynchronous copy global -> LDS: each lane's `bytes` land at lds + lane * bytes.
+__device__ __forceinline__ void lds_dma16(const char* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const char* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Per-head-dim geometry of one 32-token block in a wave's LDS slot.
+template <int D>
+struct Geo;
+template <>
+struct Geo<128> {
+  using vvec = u32x4;                        // 8 bf16 of one V row per lane
+  static constexpr int KS = 4;               // k-steps of 32 dims
+  static constexpr int W = 8;                // dv columns per lane
+  static constexpr int kBytes = 2 * KS * 1024;
+  static constexpr int vDmaBytes = 16;       // bytes per lane per V transfer
+  static constexpr int vDmas = 8;
+  static constexpr int ring = kBytes + vDmas * 64 * vDmaBytes;  // 16 KiB
+};
+template <>
+struct Geo<64> {
+  using vvec = u32x2;                        // 4 bf16
+  static constexpr int KS = 2;
+  static constexpr int W = 4;
+  static constexpr int kBytes = 2 * KS * 1024;
+  static constexpr int vDmaBytes = 4;        // 8-byte LDS transfers do not exist: two of 4
+  static constexpr int vDmas = 16;
+  static constexpr int ring = kBytes + vDmas * 64 * vDmaBytes;  // 8 KiB
+};
+
+template <int D>
+struct BlockRegs {
+  u32x4 k[2][Geo<D>::KS];        // K rows (A operand), two 16-token halves
+  typename Geo<D>::vvec v[8];    // V rows of tokens tau(lane/16, i)
+};
+
+struct Params {
+  int hq, hkv, group, max_pages, num_pages, log2_page;
+  float scale_log2;
+  int slot_floats;   // floats per partial slot in the workspace
+  int region_bytes;  // LDS bytes per wave (stream slot, later its merge slots)
+  int reduce;
+};
+
+// wave-uniform position in the chunk
+struct Cursor {
+  int it;     // item index
+  int j;      // 32-token block inside the item
+  int nb;     // blocks in the item (from the plan)
+  int unit, tb, te, split;
+  int lim;    // min(te, seqlens[b]): tokens at or past it are masked
+};
+
+__device__ __forceinline__ int blocks_of(int tb, int te) { return (te - tb + kBlk - 1) / kBlk; }
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1)
+gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* __restrict__ items,
+                  const int32_t* __restrict__ unit_nsplit, const int32_t* __restrict__ unit_pbase,
+                  const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kc,
+                  const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
+                  const int32_t* __restrict__ seqlens, float* __restrict__ out,
+                  float* __restrict__ lse, int32_t* err, int32_t* counters, float* partials) {
+  using GE = Geo<D>;
+  constexpr int KS = GE::KS;
+  constexpr int W = GE::W;
+  using vvec = typename GE::vvec;
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // kWaves regions
+  __shared__ int slot_item[2 * kWaves];
+  __shared__ int sh_last;
+
+  const int tid = threadIdx.x;
+  const int wave = uni(tid >> 6), lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int G = p.group;
+  const int slot_stride = G * (D + 2);  // floats of one (m, l, o) merge slot
+  const int page_mask = (1 << p.log2_page) - 1;
+  const size_t row_bytes = (size_t)p.hkv * D * sizeof(uint16_t);
+  char* const region = smem + wave * p.region_bytes;
+  auto merge_slot = [&](int sl) -> float* {
+    return reinterpret_cast<float*>(smem + (sl >> 1) * p.region_bytes) + (sl & 1) * slot_stride;
+  };
+
+  const int i0 = uni(wg_off[blockIdx.x]), i1 = uni(wg_off[blockIdx.x + 1]);
+  if (i0 >= i1) return;
+
+  int nblk = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int4 t = items[i];
+    nblk += blocks_of(uni(t.y), uni(t.z));
+  }
+  const int s = (int)(((long long)nblk * wave) / kWaves);
+  const int e = (int)(((long long)nblk * (wave + 1)) / kWaves);
+
+  if (tid < 2 * kWaves) slot_item[tid] = -1;
+  __syncthreads();
+
+  auto load_item = [&](Cursor& c, int it) {
+    const int4 t = items[it];
+    c.it = it;
+    c.unit = uni(t.x);
+    c.tb = uni(t.y);
+    c.te = uni(t.z);
+    c.split = uni(t.w);
+    c.nb = blocks_of(c.tb, c.te);
+    const int L = uni(seqlens[c.unit / p.hkv]);
+    c.lim = c.te;
+    if (c.te > L) {  // plan built for other lengths: mask past the sequence end
+      atomicOr(err, kErrSeqlen);
+      c.lim = L;
+    }
+  };
+
+  auto page_of = [&](const int32_t* row, int tok) {
+    int lp = min(tok >> p.log2_page, p.max_pages - 1);
+    int pg = uni(row[lp]);
+    if ((unsigned)pg >= (unsigned)p.num_pages) {
+      atomicOr(err, kErrPage);
+      pg = pg < 0 ? 0 : p.num_pages - 1;
+    }
+    return pg;
+  };
+
+  // Every 16-token half of a block lies inside one page (blocks start at
+  // multiples of 32 and pages hold a power of two >= 16 tokens), so a lane's
+  // offset from the half's first row never changes: only the two half bases,
+  // wave-uniform, move from block to block.  A half with no valid token
+  // reads half 0 again; rows past the valid length stay inside their page and
+  // are masked (scores) or zeroed (values) in compute.
+  const uint32_t koff = (uint32_t)((size_t)lr * row_bytes + lg * 16);
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    voff[i] = (uint32_t)((size_t)(4 * lg + i) * row_bytes + W * lr * sizeof(uint16_t));
+
+  // Global sources of one block: the K and V rows of its two 16-token halves.
+  struct Src {
+    const char* k0;
+    const char* k1;
+    const char* v0;
+    const char* v1;
+  };
+  auto sources = [&](const Cursor& c) {
+    const int b = c.unit / p.hkv;
+    const int g = c.unit - b * p.hkv;
+    const int32_t* row = bt + (size_t)b * p.max_pages;
+    const int tok0 = c.tb + c.j * kBlk;
+    const int h1 = (tok0 + 16 < c.lim) ? tok0 + 16 : tok0;
+    const size_t r0 = (size_t)page_of(row, tok0) * (1u << p.log2_page) + (tok0 & page_mask);
+    const size_t r1 = (size_t)page_of(row, h1) * (1u << p.log2_page) + (h1 & page_mask);
+    const size_t go = (size_t)g * D * sizeof(uint16_t);
+    Src S;
+    S.k0 = reinterpret_cast<const char*>(kc) + r0 * row_bytes + go;
+    S.k1 = reinterpret_cast<const char*>(kc) + r1 * row_bytes + go;
+    S.v0 = reinterpret_cast<const char*>(vc) + r0 * row_bytes + go;
+    S.v1 = reinterpret_cast<const char*>(vc) + r1 * row_bytes + go;
+    return S;
+  };
+
+  // Stream one block into this wave's LDS slot.
+  auto fetch = [&](const Src& S) {
+    // K: lane takes token lr of each half, dims 32*ks + 8*lg .. +8
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      lds_dma16(S.k0 + koff + ks * 64, region + ks * 1024);
+      lds_dma16(S.k1 + koff + ks * 64, region + (KS + ks) * 1024);
+    }
+    // V: lane takes tokens tau(lg, i) = 4lg+i (i<4), 16+4lg+(i-4) (i>=4), dims W*lr .. +W
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const char* src = (i < 4 ? S.v0 : S.v1) + voff[i & 3];
+      if constexpr (GE::vDmaBytes == 16) {
+        lds_dma16(src, region + GE::kBytes + i * 1024);
+      } else {
+        lds_dma4(src, region + GE::kBytes + (2 * i) * 256);
+        lds_dma4(src + 4, region + GE::kBytes + (2 * i + 1) * 256);
+      }
+    }
+  };
+
+  // The streamed block, back from LDS into operand registers.
+  auto unpack = [&](BlockRegs<D>& r) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        r.k[h][ks] = *reinterpret_cast<const u32x4*>(region + (h * KS + ks) * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (GE::vDmaBytes == 16) {
+        r.v[i] = *reinterpret_cast<const u32x4*>(region + GE::kBytes + i * 1024 + lane * 16);
+      } else {
+        r.v[i] = u32x2{*reinterpret_cast<const uint32_t*>(region + GE::kBytes + (2 * i) * 256 + lane * 4),
+                       *reinterpret_cast<const uint32_t*>(region + GE::kBytes + (2 * i + 1) * 256 +
+                                                          lane * 4)};
+      }
+    }
+  };
+
+  // (m, l, o) of this wave for item `it` into merge slot sl (real heads only).
+  auto put_slot = [&](int sl, int it, float m, float l, const f32x4* o) {
+    float* sb = merge_slot(sl);
+    if (lane < G) {
+      sb[lane] = m;
+      sb[G + lane] = l;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int hh = 4 * lg + rr;
+      if (hh < G) {
+#pragma unroll
+        for (int cc = 0; cc < W; ++cc) sb[2 * G + hh * D + W * lr + cc] = o[cc][rr];
+      }
+    }
+    if (lane == 0) slot_item[sl] = it;
+  };
+
+  if (s < e) {
+    // ------------------------------------------------ the wave's run [s, e)
+    Cursor c;
+    {
+      int it = i0, cum = 0;
+      load_item(c, it);
+      while (cum + c.nb <= s) {
+        cum += c.nb;
+        load_item(c, ++it);
+      }
+      c.j = s - cum;
+    }
+    const int first_it = c.it;
+
+    // Q^T operand of a unit: lane holds head lr, dims 32*ks + 8*lg .. +8 (zero rows past G)
+    auto load_q = [&](int unit, u32x4* qd) {
+      const int b = unit / p.hkv, g = unit - (unit / p.hkv) * p.hkv;
+      const uint16_t* qp = qg + ((size_t)b * p.hq + (size_t)g * G + min(lr, G - 1)) * D + lg * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 t = *reinterpret_cast<const u32x4*>(qp + ks * 32);
+        qd[ks] = lr < G ? t : u32x4{0, 0, 0, 0};
+      }
+    };
+
+    u32x4 qv[KS], qn[KS];
+    load_q(c.unit, qv);
+    fetch(sources(c));
+
+    // the first item's state when it is neither written out nor the last item
+    bool stashed = false;
+    float m_first = 0.f, l_first = 0.f;
+    f32x4 o_first[W];
+
+    int k = s;
+    for (;;) {
+      // -------- item c.it, blocks c.j .. jend-1 of it
+      const int j0 = c.j;
+      const int jend = min(c.nb, c.j + (e - k));
+      float m_run = -INFINITY, l_run = 0.f;
+      f32x4 o[W];
+#pragma unroll
+      for (int cc = 0; cc < W; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Cursor n = c;
+      for (; c.j < jend; ++c.j, ++k) {
+        const bool more = k + 1 < e;
+        Src S{};
+        if (more) {  // next block's sources (scalar loads, hidden under the DMA in flight)
+          if (c.j + 1 < c.nb) {
+            n.j = c.j + 1;
+          } else {  // the next block opens the next item: fetch its q as well
+            load_item(n, c.it + 1);
+            n.j = 0;
+            load_q(n.unit, qn);
+          }
+          S = sources(n);
+        }
+        BlockRegs<D> cur;
+        wait_vmem();  // block k is in the slot (and any q loads landed)
+        unpack(cur);
+        wait_lds();   // slot read: it may be refilled
+        if (more) fetch(S);
+
+        // S^T = K Q^T for the block's two 16-token halves
+        const int tok0 = c.tb + c.j * kBlk;
+        const int nv = min(kBlk, c.lim - tok0);  // valid tokens in the block
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s0 = mfma_bf16(cur.k[0][ks], qv[ks], s0);
+          s1 = mfma_bf16(cur.k[1][ks], qv[ks], s1);
+        }
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = (4 * lg + i < nv) ? s0[i] * p.scale_log2 : -INFINITY;
+          x[4 + i] = (16 + 4 * lg + i < nv) ? s1[i] * p.scale_log2 : -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - mnew);
+        float pr[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pr[i] = fast_exp2(x[i] - mnew);
+          psum += pr[i];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = mnew;
+        const u32x4 pa = {pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]), pack_bf16(pr[4], pr[5]),
+                          pack_bf16(pr[6], pr[7])};
+
+        // O = alpha * O + P V   (rows of O are heads 4*lg + rr)
+        if (nv < kBlk) {  // rows past the end may hold anything: zero them
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int rel = (i < 4) ? 4 * lg + i : 16 + 4 * lg + (i - 4);
+            if (rel >= nv) cur.v[i] = vvec{};
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float a = __shfl(alpha, 4 * lg + rr);
+#pragma unroll
+          for (int cc = 0; cc < W; ++cc) o[cc][rr] *= a;
+        }
+#pragma unroll
+        for (int cc = 0; cc < W; ++cc) {
+          u32x4 vb;
+#pragma unroll
+          for (int pi = 0; pi < 4; ++pi) {
+            const uint32_t a0 = cur.v[2 * pi][cc >> 1];
+            const uint32_t a1 = cur.v[2 * pi + 1][cc >> 1];
+            vb[pi] = (cc & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+          }
+          o[cc] = mfma_bf16(pa, vb, o[cc]);
+        }
+      }
+      --c.j;  // last block of this item run by the wave
+
+      // -------- end of this wave's part of the item
+      float l_tot = l_run + __shfl_xor(l_run, 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      const bool whole = j0 == 0 && c.j == c.nb - 1;
+      if (whole && unit_nsplit[c.unit] == 1) {
+        const int b = c.unit / p.hkv, g = c.unit - (c.unit / p.hkv) * p.hkv;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int hh = 4 * lg + rr;
+          const float inv = 1.f / __shfl(l_tot, hh);
+          if (hh < G) {
+            float* op = out + ((size_t)b * p.hq + (size_t)g * G + hh) * D + W * lr;
+#pragma unroll
+            for (int c4 = 0; c4 < W; c4 += 4) {
+              *reinterpret_cast<f32x4*>(op + c4) = f32x4{o[c4][rr] * inv, o[c4 + 1][rr] * inv,
+                                                         o[c4 + 2][rr] * inv, o[c4 + 3][rr] * inv};
+            }
+          }
+        }
+        if (lane < G) lse[(size_t)b * p.hq + (size_t)g * G + lane] = (m_run + __log2f(l_tot)) * kLn2;
+      } else if (k < e) {
+        // only a wave's first and last items can be shared or split; this is
+        // the first and more follow: keep it until the slot stops streaming
+        stashed = true;
+        m_first = m_run;
+        l_first = l_tot;
+#pragma unroll
+        for (int cc = 0; cc < W; ++cc) o_first[cc] = o[cc];
+      } else {
+        put_slot(2 * wave + (c.it == first_it ? 0 : 1), c.it, m_run, l_tot, o);
+      }
+      if (k >= e) break;
+      c = n;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qv[ks] = qn[ks];
+    }
+    if (stashed) put_slot(2 * wave, first_it, m_first, l_first, o_first);
+  }
+
+  __syncthreads();
+
+  // ------------------------------------------------ workgroup-level merges
+  for (int sl = 0; sl < 2 * kWaves; ++sl) {
+    const int it = slot_item[sl];
+    if (it < 0) continue;
+    bool seen = false;
+    for (int t = 0; t < sl; ++t) seen |= slot_item[t] == it;
+    if (seen) continue;
+
+    const int4 itm = items[it];
+    const int unit = itm.x, split = itm.w;
+    const int ns = unit_nsplit[unit];
+    const int b = unit / p.hkv, g = unit - (unit / p.hkv) * p.hkv;
+    float* pslot = ns > 1 ? partials + (size_t)(unit_pbase[unit] + split) * p.slot_floats : nullptr;
+    for (int el = tid; el < G * D; el += kThreads) {
+      const int hh = el / D, cc = el - (el / D) * D;
+      float M = -INFINITY;
+      for (int t = sl; t < 2 * kWaves; ++t)
+        if (slot_item[t] == it) M = fmaxf(M, merge_slot(t)[hh]);
+      float L = 0.f, O = 0.f;
+      for (int t = sl; t < 2 * kWaves; ++t) {
+        if (slot_item[t] == it) {
+          const float* sb = merge_slot(t);
+          const float f = fast_exp2(sb[hh] - M);
+          L += sb[G + hh] * f;
+          O += sb[2 * G + hh * D + cc] * f;
+        }
+      }
+      const size_t orow = (size_t)b * p.hq + (size_t)g * G + hh;
+      if (ns == 1) {
+        out[orow * D + cc] = O / L;
+        if (cc == 0) lse[orow] = (M + __log2f(L)) * kLn2;
+      } else {
+        if (cc == 0) {
+          pslot[hh] = M;
+          pslot[G + hh] = L;
+        }
+        pslot[2 * G + hh * D + cc] = O;
+      }
+    }
+    if (ns > 1 && p.reduce == CC_REDUCE_FUSED) {
+      __syncthreads();
+      if (tid == 0) {
+        __threadfence();  // release this piece's partial at device scope
+        const int old = atomicAdd(&counters[unit], 1);
+        sh_last = old == ns - 1;
+      }
+      __syncthreads();
+      if (sh_last) {
+        __threadfence();  // acquire the other pieces' partials
+        const float* pb = partials + (size_t)unit_pbase[unit] * p.slot_floats;
+        for (int el = tid; el < G * D; el += kThreads) {
+          const int hh = el / D, cc = el - (el / D) * D;
+          float M = -INFINITY;
+          for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, pb[(size_t)sp * p.slot_floats + hh]);
+          float L = 0.f, O = 0.f;
+          for (int sp = 0; sp < ns; ++sp) {
+            const float* ps = pb + (size_t)sp * p.slot_floats;
+            const float f = fast_exp2(ps[hh] - M);
+            L += ps[G + hh] * f;
+            O += ps[2 * G + hh * D + cc] * f;
+          }
+          const size_t orow = (size_t)b * p.hq + (size_t)g * G + hh;
+          out[orow * D + cc] = O / L;
+          if (cc == 0) lse[orow] = (M + __log2f(L)) * kLn2;
+        }
+        if (tid == 0) __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Merge kernel of the split-then-combine comparison: one workgroup per unit.
+__global__ void __launch_bounds__(256)
+combine_kernel(int hq, int hkv, int group, int hpu, int q_tokens, int dv, int slot_floats,
+               const int32_t* __restrict__ unit_nsplit, const int32_t* __restrict__ unit_pbase,
+               const float* __restrict__ partials, float* __restrict__ out, float* __restrict__ lse) {
+  const int u = blockIdx.x;
+  const int ns = unit_nsplit[u];
+  if (ns <= 1) return;
+  const int hb_per_kv = group / hpu;
+  const int hb = u % hb_per_kv;
+  const int g = (u / hb_per_kv) % hkv;
+  const int bt = u / (hb_per_kv * hkv);  // b * q_tokens + t
+  const float* pb = partials + (size_t)unit_pbase[u] * slot_floats;
+  for (int el = threadIdx.x; el < hpu * dv; el += blockDim.x) {
+    const int hh = el / dv, cc = el - (el / dv) * dv;
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, pb[(size_t)sp * slot_floats + hh]);
+    float L = 0.f, O = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float* ps = pb + (size_t)sp * slot_floats;
+      const float f = fast_exp2(ps[hh] - M);
+      L += ps[hpu + hh] * f;
+      O += ps[2 * hpu + hh * dv + cc] * f;
+    }
+    const size_t orow = (size_t)bt * hq + (size_t)g * group + (size_t)hb * hpu + hh;
+    out[orow * dv + cc] = O / L;
+    if (cc == 0) lse[orow] = (M + __log2f(L)) * kLn2;
+  }
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+int ilog2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+}  // namespace gqa
+
+using namespace gqa;
+
+hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s) {
+  Params p;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.group = a.hq / a.hkv;
+  p.max_pages = a.max_pages;
+  p.num_pages = a.num_pages;
+  p.log2_page = ilog2(a.page_size);
+  p.scale_log2 = a.scale_log2;
+  p.slot_floats = a.slot_floats;
+  p.reduce = a.reduce;
+  const int ring = a.dqk == 128 ? Geo<128>::ring : Geo<64>::ring;
+  const int slots = 2 * p.group * (a.dqk + 2) * (int)sizeof(float);
+  p.region_bytes = ((ring > slots ? ring : slots) + 15) & ~15;
+  const size_t lds = (size_t)kWaves * p.region_bytes;
+  hipError_t e;
+  if (a.dqk == 128) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gqa::gqa_decode_kernel<128>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    gqa::gqa_decode_kernel<128><<<a.workers, kThreads, lds, s>>>(
+        p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
+        a.out, a.lse, a.err, a.counters, a.partials);
+  } else {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gqa::gqa_decode_kernel<64>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    gqa::gqa_decode_kernel<64><<<a.workers, kThreads, lds, s>>>(
+        p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
+        a.out, a.lse, a.err, a.counters, a.partials);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
+  combine_kernel<<<a.units, 256, 0, s>>>(a.hq, a.hkv, a.hq / a.hkv, a.hpu, a.q_tokens, a.dv,
+                                         a.slot_floats, a.unit_nsplit, a.unit_pbase, a.partials,
+                                         a.out, a.lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  fill_zero_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<uint32_t*>(ptr), words);
+  return hipGetLastError();
+}
+
+}  // namespace cc

@@ -1,0 +1,48 @@
+// Kernel launch interface between the C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace cc {
+
+// Everything a decode launch needs, resolved on the host from the problem,
+// the plan header and the workspace layout.
+struct DecodeArgs {
+  // problem
+  int mode, batch, q_tokens, hq, hkv, dqk, dv, page_size, max_pages, num_pages, topk;
+  float scale_log2;  // softmax_scale * log2(e): scores are kept in base 2
+  // plan (device pointers into the plan copy)
+  int workers, units, hpu, tile;
+  const int32_t* wg_off;
+  const int4* items;  // unit, tok_begin, tok_end, split
+  const int32_t* unit_nsplit;
+  const int32_t* unit_pbase;
+  // tensors (device)
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* indices;
+  float* out;
+  float* lse;
+  // workspace (device)
+  int32_t* err;
+  int32_t* counters;
+  float* partials;
+  int slot_floats;
+  int reduce;  // CC_REDUCE_*
+};
+
+// Device error-word bits.
+constexpr int kErrSeqlen = 1;
+constexpr int kErrPage = 2;
+constexpr int kErrIndex = 4;
+
+hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace cc

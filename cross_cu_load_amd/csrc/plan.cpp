@@ -1,0 +1,352 @@
+// Host planner: the Stream-K split of a decode batch into one equal chunk of
+// KV tiles per compute unit, run as a single wave (CSDN Q&A on waves and
+// FlashMLA's Stream-K, "Summary").  The split is computed from the real
+// sequence lengths and the hardware shape at run time (MeldKernel summary,
+// "Core method") and serialised as fixed-size work descriptors per worker
+// (GLM-5.2 decode article, MegaRTP design: host-built per-worker queues).
+//
+// Plain C++17 with no HIP dependency.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "plan.h"
+
+namespace cc {
+
+namespace {
+thread_local std::string g_err;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Inputs {
+  const cc_problem* p;
+  const cc_plan_opts* o;
+  const int32_t* seqlens;
+  const int32_t* block_table;
+};
+
+int validate(const Inputs& in) {
+  const cc_problem& p = *in.p;
+  const cc_plan_opts& o = *in.o;
+  if (p.mode < CC_MODE_GQA || p.mode > CC_MODE_MLA_SPARSE) {
+    set_error("unknown mode %d", p.mode);
+    return CC_ERR_INVALID;
+  }
+  if (o.policy != CC_POLICY_STREAMK && o.policy != CC_POLICY_PER_UNIT) {
+    set_error("unknown policy %d", o.policy);
+    return CC_ERR_INVALID;
+  }
+  if (p.batch < 1 || p.q_tokens < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1) {
+    set_error("batch, q_tokens and head counts must be >= 1");
+    return CC_ERR_INVALID;
+  }
+  if (p.mode != CC_MODE_MLA_SPARSE && p.q_tokens != 1) {
+    set_error("dense decode takes one query token per sequence (q_tokens=%d)", p.q_tokens);
+    return CC_ERR_INVALID;
+  }
+  if (p.num_q_heads % p.num_kv_heads) {
+    set_error("num_q_heads %d not a multiple of num_kv_heads %d", p.num_q_heads, p.num_kv_heads);
+    return CC_ERR_INVALID;
+  }
+  const int32_t G = p.num_q_heads / p.num_kv_heads;
+  if (o.heads_per_unit < 1 || G % o.heads_per_unit) {
+    set_error("heads_per_unit %d must divide the group size %d", o.heads_per_unit, G);
+    return CC_ERR_INVALID;
+  }
+  if (p.head_dim_qk < 1 || p.head_dim_v < 1 || p.page_size < 1 || p.max_pages_per_seq < 1 ||
+      p.num_pages < 1) {
+    set_error("head dims, page_size, max_pages_per_seq and num_pages must be >= 1");
+    return CC_ERR_INVALID;
+  }
+  if (o.num_cus < 1 || o.num_xcds < 1 || o.tile_tokens < 1) {
+    set_error("num_cus, num_xcds and tile_tokens must be >= 1");
+    return CC_ERR_INVALID;
+  }
+  for (int32_t b = 0; b < p.batch; ++b) {
+    const int32_t L = in.seqlens[b];
+    if (L < 1) {
+      set_error("seqlens[%d] = %d; every sequence needs >= 1 token", b, L);
+      return CC_ERR_INVALID;
+    }
+    const int64_t pages = ceil_div(L, p.page_size);
+    if (pages > p.max_pages_per_seq) {
+      set_error("seqlens[%d] = %d needs %lld pages > max_pages_per_seq %d", b, L, (long long)pages,
+                p.max_pages_per_seq);
+      return CC_ERR_INVALID;
+    }
+    if (p.mode == CC_MODE_MLA_SPARSE && (p.topk < 1 || p.topk > L)) {
+      set_error("topk %d outside [1, seqlens[%d] = %d]", p.topk, b, L);
+      return CC_ERR_INVALID;
+    }
+    if (in.block_table) {
+      const int32_t* row = in.block_table + (int64_t)b * p.max_pages_per_seq;
+      for (int64_t i = 0; i < pages; ++i) {
+        if (row[i] < 0 || row[i] >= p.num_pages) {
+          set_error("block_table[%d][%lld] = %d outside [0, %d)", b, (long long)i, row[i],
+                    p.num_pages);
+          return CC_ERR_PAGE;
+        }
+      }
+    }
+  }
+  return CC_OK;
+}
+
+struct Built {
+  std::vector<int32_t> words;
+};
+
+// The whole plan as int32 words.  Returns CC_OK or an error code.
+int build(const Inputs& in, Built* out) {
+  int rc = validate(in);
+  if (rc) return rc;
+  const cc_problem& p = *in.p;
+  const cc_plan_opts& o = *in.o;
+  const int64_t G = p.num_q_heads / p.num_kv_heads;
+  const int64_t blocks_per_kv = G / o.heads_per_unit;
+  const int64_t units_per_seq = (int64_t)p.q_tokens * p.num_kv_heads * blocks_per_kv;
+  const int64_t U = units_per_seq * p.batch;
+  const int64_t T = o.tile_tokens;
+
+  // unit u belongs to sequence u / units_per_seq
+  auto unit_len = [&](int64_t u) -> int64_t {
+    return p.mode == CC_MODE_MLA_SPARSE ? p.topk : in.seqlens[u / units_per_seq];
+  };
+  std::vector<int64_t> first(U + 1, 0);
+  for (int64_t u = 0; u < U; ++u) first[u + 1] = first[u] + ceil_div(unit_len(u), T);
+  const int64_t N = first[U];
+  const int64_t C = o.policy == CC_POLICY_PER_UNIT ? U : o.num_cus;
+
+  // pieces per logical chunk, as (unit, tok_begin, tok_end)
+  struct Piece { int64_t u, t0, t1; };
+  std::vector<std::vector<Piece>> chunks(C);
+  if (o.policy == CC_POLICY_PER_UNIT) {
+    for (int64_t u = 0; u < U; ++u) chunks[u].push_back({u, 0, unit_len(u)});
+  } else {
+    const int64_t q = N / C, r = N % C;
+    int64_t u = 0;
+    for (int64_t k = 0; k < C; ++k) {
+      const int64_t a = k * q + (k < r ? k : r);
+      const int64_t e = a + q + (k < r ? 1 : 0);
+      if (e == a) continue;
+      while (first[u + 1] <= a) ++u;           // first unit that ends after a
+      for (int64_t v = u; v < U && first[v] < e; ++v) {
+        const int64_t tb = (a > first[v] ? a : first[v]) - first[v];
+        const int64_t te = (e < first[v + 1] ? e : first[v + 1]) - first[v];
+        const int64_t L = unit_len(v);
+        chunks[k].push_back({v, tb * T, te * T < L ? te * T : L});
+      }
+    }
+  }
+
+  // split indices in chunk order, partial slots for split units
+  std::vector<int64_t> nsplit(U, 0);
+  struct Item { int64_t u, t0, t1, s; };
+  std::vector<std::vector<Item>> items(C);
+  for (int64_t k = 0; k < C; ++k)
+    for (const Piece& pc : chunks[k]) items[k].push_back({pc.u, pc.t0, pc.t1, nsplit[pc.u]++});
+  std::vector<int64_t> pbase(U, -1);
+  int64_t S = 0, maxsplit = 0;
+  for (int64_t u = 0; u < U; ++u) {
+    if (nsplit[u] > 1) { pbase[u] = S; S += nsplit[u]; }
+    if (nsplit[u] > maxsplit) maxsplit = nsplit[u];
+  }
+
+  // worker of each logical chunk: consecutive chunks share an XCD
+  std::vector<int64_t> chunk_of_worker(C);
+  const int64_t X = o.num_xcds;
+  const bool spread = o.policy == CC_POLICY_STREAMK && X > 1 && C % X == 0;
+  for (int64_t k = 0; k < C; ++k) {
+    const int64_t w = spread ? (k % (C / X)) * X + k / (C / X) : k;
+    chunk_of_worker[w] = k;
+  }
+
+  int64_t W = 0;
+  for (int64_t k = 0; k < C; ++k) W += (int64_t)items[k].size();
+  const int64_t total = kHeaderWords + wg_words(C) + kItemWords * W + 2 * U;
+  for (int64_t x : {N, C, W, U, S, total}) {
+    if (x > INT32_MAX) {
+      set_error("plan too large for int32 fields");
+      return CC_ERR_INVALID;
+    }
+  }
+  std::vector<int32_t>& w = out->words;
+  w.assign(total, 0);
+  int32_t* h = w.data();
+  h[H_MAGIC] = kPlanMagic;
+  h[H_VERSION] = kPlanVersion;
+  h[H_MODE] = p.mode;
+  h[H_BATCH] = p.batch;
+  h[H_QTOKENS] = p.q_tokens;
+  h[H_HQ] = p.num_q_heads;
+  h[H_HKV] = p.num_kv_heads;
+  h[H_DQK] = p.head_dim_qk;
+  h[H_DV] = p.head_dim_v;
+  h[H_PAGE] = p.page_size;
+  h[H_TOPK] = p.topk;
+  h[H_WORKERS] = (int32_t)C;
+  h[H_XCDS] = o.num_xcds;
+  h[H_TILE] = o.tile_tokens;
+  h[H_HPU] = o.heads_per_unit;
+  h[H_UNITS] = (int32_t)U;
+  h[H_TILES] = (int32_t)N;
+  h[H_ITEMS] = (int32_t)W;
+  h[H_PARTIALS] = (int32_t)S;
+  h[H_MAXSPLIT] = (int32_t)maxsplit;
+  h[H_POLICY] = o.policy;
+  h[H_MAXPAGES] = p.max_pages_per_seq;
+  h[H_NUMPAGES] = p.num_pages;
+  int32_t* wg = h + kHeaderWords;
+  int32_t* it = wg + wg_words(C);
+  int64_t n = 0;
+  for (int64_t wk = 0; wk < C; ++wk) {
+    wg[wk] = (int32_t)n;
+    for (const Item& x : items[chunk_of_worker[wk]]) {
+      it[4 * n + 0] = (int32_t)x.u;
+      it[4 * n + 1] = (int32_t)x.t0;
+      it[4 * n + 2] = (int32_t)x.t1;
+      it[4 * n + 3] = (int32_t)x.s;
+      ++n;
+    }
+  }
+  wg[C] = (int32_t)n;
+  int32_t* ns = it + 4 * W;
+  int32_t* pb = ns + U;
+  for (int64_t u = 0; u < U; ++u) {
+    ns[u] = (int32_t)nsplit[u];
+    pb[u] = (int32_t)pbase[u];
+  }
+  return CC_OK;
+}
+
+int check_args(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens) {
+  if (!prob || !opts || !seqlens) {
+    set_error("null argument");
+    return CC_ERR_INVALID;
+  }
+  return CC_OK;
+}
+
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+}
+
+const char* last_error() { return g_err.c_str(); }
+
+int parse_plan(const void* blob, PlanView* v) {
+  if (!blob || !v) {
+    set_error("null plan");
+    return CC_ERR_PLAN;
+  }
+  const int32_t* h = static_cast<const int32_t*>(blob);
+  if (h[H_MAGIC] != kPlanMagic || h[H_VERSION] != kPlanVersion) {
+    set_error("not a plan blob (magic %08x, version %d)", (unsigned)h[H_MAGIC], h[H_VERSION]);
+    return CC_ERR_PLAN;
+  }
+  const int64_t C = h[H_WORKERS], W = h[H_ITEMS], U = h[H_UNITS];
+  if (C < 1 || W < 0 || U < 1) {
+    set_error("corrupt plan header");
+    return CC_ERR_PLAN;
+  }
+  v->header = h;
+  v->off_wg = kHeaderWords;
+  v->off_items = v->off_wg + wg_words(C);
+  v->off_nsplit = v->off_items + kItemWords * W;
+  v->off_pbase = v->off_nsplit + U;
+  v->wg_off = h + v->off_wg;
+  v->items = h + v->off_items;
+  v->unit_nsplit = h + v->off_nsplit;
+  v->unit_pbase = h + v->off_pbase;
+  v->bytes = (v->off_pbase + U) * sizeof(int32_t);
+  if (v->wg_off[0] != 0 || v->wg_off[C] != W) {
+    set_error("corrupt plan offsets");
+    return CC_ERR_PLAN;
+  }
+  return CC_OK;
+}
+
+int plan_matches(const PlanView& v, const cc_problem& p) {
+  const int32_t* h = v.header;
+  if (h[H_MODE] != p.mode || h[H_BATCH] != p.batch || h[H_QTOKENS] != p.q_tokens ||
+      h[H_HQ] != p.num_q_heads || h[H_HKV] != p.num_kv_heads || h[H_DQK] != p.head_dim_qk ||
+      h[H_DV] != p.head_dim_v || h[H_PAGE] != p.page_size || h[H_TOPK] != p.topk ||
+      h[H_MAXPAGES] != p.max_pages_per_seq || h[H_NUMPAGES] != p.num_pages) {
+    set_error("plan was built for another problem shape");
+    return CC_ERR_PLAN;
+  }
+  return CC_OK;
+}
+
+WorkspaceLayout workspace_layout(const PlanView& v) {
+  WorkspaceLayout L;
+  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+  L.counters_off = 256;  // the error word lives at offset 0
+  L.partials_off = align(L.counters_off + sizeof(int32_t) * (size_t)v.units());
+  const size_t hpu = (size_t)v.header[H_HPU];
+  L.slot_floats = (hpu * ((size_t)v.header[H_DV] + 2) + 63) & ~size_t(63);
+  L.total = align(L.partials_off + sizeof(float) * L.slot_floats * (size_t)v.partials());
+  return L;
+}
+
+}  // namespace cc
+
+extern "C" {
+
+int cc_plan_size(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
+                 size_t* bytes) {
+  int rc = cc::check_args(prob, opts, seqlens);
+  if (rc) return rc;
+  if (!bytes) {
+    cc::set_error("null bytes");
+    return CC_ERR_INVALID;
+  }
+  cc::Built b;
+  rc = cc::build({prob, opts, seqlens, nullptr}, &b);
+  if (rc) return rc;
+  *bytes = b.words.size() * sizeof(int32_t);
+  return CC_OK;
+}
+
+int cc_plan(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
+            const int32_t* block_table, void* plan, size_t bytes) {
+  int rc = cc::check_args(prob, opts, seqlens);
+  if (rc) return rc;
+  if (!plan) {
+    cc::set_error("null plan buffer");
+    return CC_ERR_INVALID;
+  }
+  cc::Built b;
+  rc = cc::build({prob, opts, seqlens, block_table}, &b);
+  if (rc) return rc;
+  const size_t need = b.words.size() * sizeof(int32_t);
+  if (bytes < need) {
+    cc::set_error("plan buffer holds %zu bytes, needs %zu", bytes, need);
+    return CC_ERR_BUFFER;
+  }
+  std::memcpy(plan, b.words.data(), need);
+  return CC_OK;
+}
+
+int cc_workspace_size(const void* plan_host, size_t* bytes) {
+  cc::PlanView v;
+  int rc = cc::parse_plan(plan_host, &v);
+  if (rc) return rc;
+  if (!bytes) {
+    cc::set_error("null bytes");
+    return CC_ERR_INVALID;
+  }
+  *bytes = cc::workspace_layout(v).total;
+  return CC_OK;
+}
+
+}  // extern "C"

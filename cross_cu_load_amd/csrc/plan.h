@@ -1,0 +1,70 @@
+// Host-side view of a work-plan blob (shared by the planner and the launcher).
+//
+// Blob layout, int32 little-endian words:
+//   header[24]
+//   wg_off[C + 1]        items of worker w are items[wg_off[w] .. wg_off[w+1]),
+//                        zero-padded to a multiple of 4 words so items[] is
+//                        16-byte aligned
+//   items[W][4]          unit, tok_begin, tok_end, split (index of the piece
+//                        within its unit, in token order)
+//   unit_nsplit[U]       pieces of each unit
+//   unit_pbase[U]        first partial slot of a split unit, -1 if unsplit
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/crosscu.h"
+
+namespace cc {
+
+constexpr int32_t kPlanMagic = 0x4C504343;  // "CCPL"
+constexpr int32_t kPlanVersion = 1;
+constexpr int kHeaderWords = 24;
+constexpr int kItemWords = 4;
+
+enum HeaderField {
+  H_MAGIC = 0, H_VERSION, H_MODE, H_BATCH, H_QTOKENS, H_HQ, H_HKV, H_DQK, H_DV, H_PAGE, H_TOPK,
+  H_WORKERS, H_XCDS, H_TILE, H_HPU, H_UNITS, H_TILES, H_ITEMS, H_PARTIALS, H_MAXSPLIT, H_POLICY,
+  H_MAXPAGES, H_NUMPAGES, H_RESERVED
+};
+
+struct PlanView {
+  const int32_t* header = nullptr;
+  const int32_t* wg_off = nullptr;
+  const int32_t* items = nullptr;
+  const int32_t* unit_nsplit = nullptr;
+  const int32_t* unit_pbase = nullptr;
+  size_t bytes = 0;
+  // word offsets of the arrays inside the blob (valid for a device copy too)
+  size_t off_wg = 0, off_items = 0, off_nsplit = 0, off_pbase = 0;
+
+  int32_t workers() const { return header[H_WORKERS]; }
+  int32_t units() const { return header[H_UNITS]; }
+  int32_t num_items() const { return header[H_ITEMS]; }
+  int32_t partials() const { return header[H_PARTIALS]; }
+};
+
+// Parses and checks a host blob; returns CC_OK or CC_ERR_PLAN (message set).
+int parse_plan(const void* blob, PlanView* v);
+
+// Checks that a parsed plan was built for `prob`.
+int plan_matches(const PlanView& v, const cc_problem& prob);
+
+// Thread-local error text.
+void set_error(const char* fmt, ...);
+const char* last_error();
+
+// Words of wg_off[] including the alignment padding.
+inline int64_t wg_words(int64_t workers) { return (workers + 1 + 3) & ~int64_t(3); }
+
+// Workspace layout of a plan: error word and counters first, then partials.
+struct WorkspaceLayout {
+  size_t counters_off = 0;   // bytes; int32[U]
+  size_t partials_off = 0;   // bytes; float[S][hpu * (dv + 2)]
+  size_t slot_floats = 0;    // floats per partial slot
+  size_t total = 0;
+};
+WorkspaceLayout workspace_layout(const PlanView& v);
+
+}  // namespace cc

@@ -1,0 +1,185 @@
+/*
+ * crosscu — split-KV decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Each decode query token attends over its own sequence's paged KV cache:
+ *   out = softmax(scale * q K^T) V,   lse = log sum exp(scale * q K^T).
+ * The total KV work of a batch is cut Stream-K style into one equal chunk per
+ * compute unit and run as a single persistent wave (CSDN Q&A on waves and
+ * FlashMLA's Stream-K, "Summary").  Pieces of one sequence that land on
+ * different compute units are merged just in time inside the same kernel by
+ * the piece that finishes last (MeldKernel summary, "Core method": just-in-time
+ * reduction instead of an HBM round trip and a separate reduction kernel).
+ * The mapping is chosen at run time from the real sequence lengths and the
+ * hardware shape (same summary, "Core method"; GLM-5.2 decode article, MegaRTP
+ * design: only the host plan is rebuilt when lengths change).
+ *
+ * Conventions for every call below
+ *  - Return value: CC_OK (0) or a negative CC_ERR_* code.  cc_last_error()
+ *    returns a thread-local message for the last failing call of the thread.
+ *  - Ownership: every buffer belongs to the caller.  Nothing is allocated per
+ *    call and no pointer is retained after a call returns.
+ *  - Host vs device: arguments documented "host" are read on the CPU during
+ *    the call; "device" pointers must be device memory of the current HIP
+ *    device and are only read/written by work enqueued on `stream`.
+ *  - Streams: `stream` is a hipStream_t (NULL = the default stream).  Device
+ *    work is enqueued asynchronously; no call synchronises unless stated.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef CROSSCU_H
+#define CROSSCU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ codes */
+enum {
+  CC_OK = 0,
+  CC_ERR_INVALID = -1,      /* null pointer, bad size or shape                  */
+  CC_ERR_UNSUPPORTED = -2,  /* valid problem the kernels do not implement        */
+  CC_ERR_BUFFER = -3,       /* caller buffer too small                           */
+  CC_ERR_PLAN = -4,         /* plan blob malformed or built for another problem  */
+  CC_ERR_PAGE = -5,         /* block_table entry outside [0, num_pages)          */
+  CC_ERR_HIP = -6,          /* a HIP runtime call failed                         */
+  CC_ERR_DEVICE_DATA = -7   /* cc_workspace_check: the device saw bad data       */
+};
+
+/* Attention forms.
+ *  GQA:        separate K and V caches, Hkv heads, G = Hq / Hkv query heads
+ *              per KV head; query head h reads KV head h / G; one query token.
+ *  MLA:        one latent cache row of head_dim_qk columns per token serves as
+ *              K; its first head_dim_v columns are V; Hkv = 1; one query token.
+ *  MLA_SPARSE: as MLA, but query token t of request b attends only to the
+ *              topk cache positions indices[b][t][0..topk).                    */
+enum { CC_MODE_GQA = 0, CC_MODE_MLA = 1, CC_MODE_MLA_SPARSE = 2 };
+
+/* How a plan divides the work.
+ *  STREAMK:  the total tile count is cut into num_cus equal contiguous chunks
+ *            (one per compute unit, one wave); a sequence may be split.
+ *  PER_UNIT: one worker per unit (query heads sharing one K/V stream), no
+ *            split — the classic one-workgroup-per-(sequence, head) launch.  */
+enum { CC_POLICY_STREAMK = 0, CC_POLICY_PER_UNIT = 1 };
+
+/* Reduction of split units inside cc_decode_variant.
+ *  FUSED:          the last piece of a unit to finish merges the partials in
+ *                  the same kernel (a per-unit arrival counter decides).
+ *  SPLIT_COMBINE:  every piece writes its partial; a second kernel merges.  */
+enum { CC_REDUCE_FUSED = 0, CC_REDUCE_SPLIT_COMBINE = 1 };
+
+/* Problem shape.  Layouts (row-major, innermost last):
+ *   q            bf16  [batch][q_tokens][num_q_heads][head_dim_qk]
+ *   k_cache      bf16  [num_pages][page_size][num_kv_heads][head_dim_qk]
+ *   v_cache      bf16  [num_pages][page_size][num_kv_heads][head_dim_v] (GQA)
+ *   block_table  int32 [batch][max_pages_per_seq]; token j of sequence b lives
+ *                in page block_table[b][j / page_size], slot j % page_size
+ *   seqlens      int32 [batch], each >= 1
+ *   indices      int32 [batch][q_tokens][topk] (MLA_SPARSE), distinct
+ *                positions in [0, seqlens[b])
+ *   out          fp32  [batch][q_tokens][num_q_heads][head_dim_v]
+ *   lse          fp32  [batch][q_tokens][num_q_heads], natural log           */
+typedef struct cc_problem {
+  int32_t mode;
+  int32_t batch;
+  int32_t q_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim_qk;
+  int32_t head_dim_v;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+  int32_t topk;             /* MLA_SPARSE only, else 0 */
+  float softmax_scale;
+} cc_problem;
+
+/* Plan knobs.  num_cus / num_xcds: compute units and XCDs to plan for (see
+ * cc_device_query).  tile_tokens: the cost unit of the equal split (any
+ * value >= 1 plans; cc_decode needs a multiple of 32).  heads_per_unit: query
+ * heads processed together on one K/V stream (divides Hq / Hkv; cc_decode's
+ * GQA kernel needs Hq / Hkv).  policy: CC_POLICY_*.                          */
+typedef struct cc_plan_opts {
+  int32_t num_cus;
+  int32_t num_xcds;
+  int32_t tile_tokens;
+  int32_t heads_per_unit;
+  int32_t policy;
+} cc_plan_opts;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int cc_version(void);
+
+/* Message of the last failing call on this thread ("" if none).  The string
+ * stays valid until the next call on the same thread. */
+const char* cc_last_error(void);
+
+/* Static text for a CC_* code. */
+const char* cc_strerror(int code);
+
+/* Compute units (num_cus) and XCDs (num_xcds) of HIP device `device`. */
+int cc_device_query(int device, int32_t* num_cus, int32_t* num_xcds);
+
+/* Bytes of the plan blob cc_plan would write for these inputs.
+ * seqlens: host int32[batch]. */
+int cc_plan_size(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
+                 size_t* bytes);
+
+/* Build the work plan on the host (pure, deterministic, thread-safe).
+ * seqlens: host int32[batch].  block_table: host int32[batch][max_pages_per_seq]
+ * or NULL; when given, every page a sequence uses is checked to lie in
+ * [0, num_pages) (CC_ERR_PAGE otherwise).  plan: host buffer of `bytes` bytes
+ * (>= cc_plan_size).  The blob is self-describing (header + arrays, int32
+ * little-endian); copy it verbatim to device memory for cc_decode.          */
+int cc_plan(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
+            const int32_t* block_table, void* plan, size_t bytes);
+
+/* Device workspace bytes a plan needs: an error word, one arrival counter per
+ * unit and one partial (m, l, o) slot per piece of a split unit. */
+int cc_workspace_size(const void* plan_host, size_t* bytes);
+
+/* Zero a workspace (device, `bytes` long) on `stream` with a fill kernel.
+ * Needed once after allocation; every cc_decode leaves the counters zero, so
+ * calls ordered on one stream can share a workspace.  Calls that may run
+ * concurrently need separate workspaces. */
+int cc_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Synchronous debug check of a workspace after the work on `stream`:
+ * *dirty_counters = number of non-zero arrival counters, *device_flags = the
+ * device error word (bit 0: a plan item ran past seqlens[b]; bit 1: a page id
+ * outside [0, num_pages); bit 2: a sparse index outside [0, seqlens[b])).
+ * Returns CC_ERR_DEVICE_DATA if either is non-zero. */
+int cc_workspace_check(const void* plan_host, const void* workspace, void* stream,
+                       int32_t* dirty_counters, int32_t* device_flags);
+
+/* Decode attention with the in-kernel just-in-time merge.
+ * plan_host: the blob from cc_plan (host); plan_dev: the same bytes in device
+ * memory.  q, k_cache, v_cache (NULL for MLA modes), block_table, seqlens,
+ * indices (MLA_SPARSE, else NULL): device, layouts as in cc_problem.
+ * out, lse: device outputs.  workspace: device, >= cc_workspace_size bytes,
+ * initialised once with cc_workspace_init.  Asynchronous on `stream`.
+ * Host-side checks (before any launch): null pointers, plan header vs `prob`,
+ * supported shapes, workspace size.  Device data is not validated on the
+ * host; out-of-range page ids, indices or plan/seqlens mismatches are clamped
+ * on the device so no access leaves its buffer, the affected outputs are
+ * unspecified, and cc_workspace_check reports them. */
+int cc_decode(const cc_problem* prob, const void* plan_host, const void* plan_dev, const void* q,
+              const void* k_cache, const void* v_cache, const int32_t* block_table,
+              const int32_t* seqlens, const int32_t* indices, float* out, float* lse,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* cc_decode with an explicit reduction (CC_REDUCE_*): CC_REDUCE_FUSED is
+ * cc_decode; CC_REDUCE_SPLIT_COMBINE writes all partials to the workspace and
+ * merges them in a second kernel.  With a CC_POLICY_PER_UNIT plan nothing is
+ * split and both reductions are the per-(sequence, head) launch. */
+int cc_decode_variant(int reduce, const cc_problem* prob, const void* plan_host,
+                      const void* plan_dev, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table, const int32_t* seqlens,
+                      const int32_t* indices, float* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CROSSCU_H */

@@ -37,6 +37,7 @@ HEADER_WORDS = 24
 ITEM_WORDS = 4                   # unit, tok_begin, tok_end, split
 
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
+POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -56,9 +57,11 @@ def unit_lengths(mode: int, batch: int, q_tokens: int, num_q_heads: int, num_kv_
 
 def validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
              max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, heads_per_unit,
-             seqlens, block_table=None) -> None:
+             seqlens, block_table=None, policy=POLICY_STREAMK) -> None:
     if mode not in (MODE_GQA, MODE_MLA, MODE_MLA_SPARSE):
         raise ValueError("mode")
+    if policy not in (POLICY_STREAMK, POLICY_PER_UNIT):
+        raise ValueError("policy")
     if batch < 1 or q_tokens < 1 or num_q_heads < 1 or num_kv_heads < 1:
         raise ValueError("shape")
     if mode != MODE_MLA_SPARSE and q_tokens != 1:
@@ -88,14 +91,20 @@ def validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head
 
 def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
          max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, heads_per_unit,
-         seqlens, block_table=None) -> dict:
-    """Build the plan; returns its fields and the serialised ``blob``."""
+         seqlens, block_table=None, policy=POLICY_STREAMK) -> dict:
+    """Build the plan; returns its fields and the serialised ``blob``.
+
+    ``policy`` POLICY_PER_UNIT is the comparison launch with one worker per
+    unit and no split (num_cus is then ignored and the worker count is U).
+    """
     validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
              max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, heads_per_unit,
-             seqlens, block_table)
+             seqlens, block_table, policy)
     C, X, T = num_cus, num_xcds, tile_tokens
     lens = unit_lengths(mode, batch, q_tokens, num_q_heads, num_kv_heads, heads_per_unit, seqlens, topk)
     U = len(lens)
+    if policy == POLICY_PER_UNIT:
+        C = U
     ntiles = [_ceil_div(L, T) for L in lens]
     first_tile = []
     acc = 0
@@ -109,6 +118,9 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
     chunk_pieces: list[list[tuple[int, int, int]]] = []
     u = 0
     for k in range(C):
+        if policy == POLICY_PER_UNIT:
+            chunk_pieces.append([(k, 0, lens[k])])
+            continue
         start = k * base + min(k, rem)
         end = start + base + (1 if k < rem else 0)
         pieces = []
@@ -141,7 +153,7 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
         else:
             pbase.append(-1)
 
-    if X > 1 and C % X == 0:
+    if policy == POLICY_STREAMK and X > 1 and C % X == 0:
         CX = C // X
         worker_of_chunk = [(k % CX) * X + k // CX for k in range(C)]
     else:
@@ -159,10 +171,11 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
     W = len(items)
 
     header = [0] * HEADER_WORDS
-    header[:20] = [PLAN_MAGIC, PLAN_VERSION, mode, batch, q_tokens, num_q_heads, num_kv_heads,
+    header[:23] = [PLAN_MAGIC, PLAN_VERSION, mode, batch, q_tokens, num_q_heads, num_kv_heads,
                    head_dim_qk, head_dim_v, page_size, topk, C, X, T, heads_per_unit, U, N, W, S,
-                   max(nsplit) if nsplit else 0]
-    words = header + wg_off + [x for it in items for x in it] + nsplit + pbase
+                   max(nsplit) if nsplit else 0, policy, max_pages_per_seq, num_pages]
+    pad = (-(C + 1)) % 4                 # keeps the item array 16-byte aligned
+    words = header + wg_off + [0] * pad + [x for it in items for x in it] + nsplit + pbase
     for x in words:
         if not (-2**31 <= x < 2**31):
             raise ValueError("plan does not fit int32")
@@ -172,13 +185,14 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
                 worker_of_chunk=worker_of_chunk, unit_len=lens, chunk_items=items_by_chunk)
 
 
-def plan_for(wl, num_cus=256, num_xcds=8, tile_tokens=32, heads_per_unit=None) -> dict:
+def plan_for(wl, num_cus=256, num_xcds=8, tile_tokens=32, heads_per_unit=None,
+             policy=POLICY_STREAMK) -> dict:
     """``plan`` for a workload object from the seeded input generator."""
     c = wl.cfg
     hu = heads_per_unit if heads_per_unit is not None else c.num_q_heads // c.num_kv_heads
     return plan(c.mode, c.batch, c.q_tokens, c.num_q_heads, c.num_kv_heads, c.head_dim_qk, c.head_dim_v,
                 c.page_size, wl.max_pages, wl.num_pages, c.topk, num_cus, num_xcds, tile_tokens, hu,
-                wl.seqlens, wl.block_table)
+                wl.seqlens, wl.block_table, policy)
 
 
 def list_schedule(task_times, num_workers: int):

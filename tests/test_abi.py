@@ -1,0 +1,176 @@
+"""The C-ABI library on the CPU: exports, plan bytes, validation (no GPU compute).
+
+cc_plan must be byte-identical to the reference planner in the oracle on the
+workload lengths and on random inputs; invalid inputs must come back as the
+documented error codes before anything touches a device.
+"""
+import ctypes
+import re
+import os
+
+import numpy as np
+import pytest
+
+from cross_cu_load_amd import binding as B
+from cross_cu_load_amd import workloads as W
+from oracle import planner as PL
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "crosscu.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cc_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == sorted(B.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.cc_version() >= 100
+    assert lib.cc_strerror(B.CC_ERR_PLAN)
+
+
+def _prob(cfg, sl):
+    P = cfg.page_size
+    maxp = int(max((int(L) + P - 1) // P for L in sl))
+    npages = int(sum((int(L) + P - 1) // P for L in sl))
+    return B.problem(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
+                     cfg.head_dim_v, P, maxp, npages, cfg.topk, cfg.softmax_scale), maxp, npages
+
+
+@pytest.mark.parametrize("name", [c.name for c in W.CONFIGS])
+@pytest.mark.parametrize("C,X,T", [(256, 8, 32), (256, 8, 64), (304, 8, 32), (148, 1, 32), (8, 8, 32)])
+@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_PER_UNIT])
+def test_plan_bytes_match_reference_on_workload_lengths(lib, name, C, X, T, policy):
+    cfg = W.CONFIG_BY_NAME[name]
+    sl = W.draw_seqlens(cfg)
+    prob, maxp, npages = _prob(cfg, sl)
+    hu = cfg.group if cfg.mode == W.MODE_GQA else 128
+    blob = B.plan(prob, sl, None, num_cus=C, num_xcds=X, tile_tokens=T, heads_per_unit=hu, policy=policy)
+    ref = PL.plan(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
+                  cfg.head_dim_v, cfg.page_size, maxp, npages, cfg.topk, C, X, T, hu, sl, None, policy)
+    assert blob.tobytes() == ref["blob"]
+    # workspace: 256 B error word area, counters, 256-aligned partial slots of hu*(dv+2) floats
+    slot = -(-hu * (cfg.head_dim_v + 2) // 64) * 64
+    cnt_end = 256 + 4 * ref["num_units"]
+    part = -(-cnt_end // 256) * 256
+    want = -(-(part + 4 * slot * ref["num_partials"]) // 256) * 256
+    assert B.workspace_size(blob) == want
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_plan_bytes_match_reference_fuzz(lib, seed):
+    rng = np.random.default_rng(1000 + seed)
+    mode = int(rng.choice([0, 1, 2]))
+    B_ = int(rng.integers(1, 9))
+    Tq = 1 if mode != 2 else int(rng.integers(1, 5))
+    Hkv = int(rng.choice([1, 2, 8])) if mode == 0 else 1
+    G = int(rng.choice([1, 4, 8]))
+    Hq = Hkv * G
+    hu = int(rng.choice([d for d in (1, 2, 4, 8) if G % d == 0]))
+    P = int(rng.choice([1, 16, 64]))
+    sl = rng.integers(1, 3000, size=B_).astype(np.int32)
+    topk = int(rng.integers(1, int(sl.min()) + 1)) if mode == 2 else 0
+    maxp = int(max((int(L) + P - 1) // P for L in sl))
+    npages = int(sum((int(L) + P - 1) // P for L in sl))
+    bt = W.page_table(sl, P, True, seed)
+    C = int(rng.choice([1, 3, 8, 100, 256, 1000]))
+    X = int(rng.choice([1, 4, 8]))
+    T = int(rng.choice([1, 7, 32, 64]))
+    policy = int(rng.integers(0, 2))
+    prob = B.problem(mode, B_, Tq, Hq, Hkv, 64, 64, P, maxp, npages, topk, 0.125)
+    blob = B.plan(prob, sl, bt, num_cus=C, num_xcds=X, tile_tokens=T, heads_per_unit=hu, policy=policy)
+    ref = PL.plan(mode, B_, Tq, Hq, Hkv, 64, 64, P, maxp, npages, topk, C, X, T, hu, sl, bt, policy)
+    assert blob.tobytes() == ref["blob"]
+
+
+def _base():
+    return dict(mode=0, batch=2, q_tokens=1, num_q_heads=8, num_kv_heads=2, head_dim_qk=64, head_dim_v=64,
+                page_size=16, max_pages_per_seq=2, num_pages=4, topk=0, softmax_scale=0.125)
+
+
+@pytest.mark.parametrize("bad,code", [
+    ("seqlen0", B.CC_ERR_INVALID), ("heads", B.CC_ERR_INVALID), ("hu", B.CC_ERR_INVALID),
+    ("page", B.CC_ERR_PAGE), ("tq", B.CC_ERR_INVALID), ("bt_short", B.CC_ERR_INVALID),
+    ("topk", B.CC_ERR_INVALID), ("mode", B.CC_ERR_INVALID), ("cus0", B.CC_ERR_INVALID)])
+def test_plan_rejects_invalid_inputs(lib, bad, code):
+    kw = _base()
+    sl = np.array([10, 20], np.int32)
+    bt = np.array([[0, -1], [1, 2]], np.int32)
+    hu, cus = 4, 8
+    if bad == "seqlen0":
+        sl = np.array([0, 20], np.int32)
+    elif bad == "heads":
+        kw["num_q_heads"] = 7
+    elif bad == "hu":
+        hu = 3
+    elif bad == "page":
+        bt = np.array([[0, -1], [1, 4]], np.int32)
+    elif bad == "tq":
+        kw["q_tokens"] = 2
+    elif bad == "bt_short":
+        sl = np.array([10, 40], np.int32)
+    elif bad == "topk":
+        kw.update(mode=2, topk=11, num_q_heads=2, num_kv_heads=1)
+        hu = 2
+    elif bad == "mode":
+        kw["mode"] = 7
+    elif bad == "cus0":
+        cus = 0
+    prob = B.problem(**kw)
+    with pytest.raises(B.CrossCUError) as ei:
+        B.plan(prob, sl, bt, num_cus=cus, num_xcds=1, tile_tokens=32, heads_per_unit=hu)
+    assert ei.value.code == code
+    # the Python reference rejects the same inputs
+    with pytest.raises(ValueError):
+        PL.plan(kw["mode"], kw["batch"], kw["q_tokens"], kw["num_q_heads"], kw["num_kv_heads"], 64, 64, 16, 2,
+                4, kw["topk"], cus, 1, 32, hu, sl, bt)
+
+
+def test_plan_buffer_too_small_and_bad_blobs(lib):
+    prob = B.problem(**_base())
+    sl = np.array([10, 20], np.int32)
+    opts = B.PlanOpts(8, 1, 32, 4, 0)
+    n = ctypes.c_size_t()
+    assert lib.cc_plan_size(ctypes.byref(prob), ctypes.byref(opts), sl.ctypes.data_as(B._I32P),
+                            ctypes.byref(n)) == 0
+    small = np.zeros(n.value - 4, np.uint8)
+    rc = lib.cc_plan(ctypes.byref(prob), ctypes.byref(opts), sl.ctypes.data_as(B._I32P), None,
+                     small.ctypes.data_as(ctypes.c_void_p), small.nbytes)
+    assert rc == B.CC_ERR_BUFFER
+    junk = np.zeros(256, np.uint8)
+    sz = ctypes.c_size_t()
+    assert lib.cc_workspace_size(junk.ctypes.data_as(ctypes.c_void_p), ctypes.byref(sz)) == B.CC_ERR_PLAN
+
+
+def test_decode_rejects_before_any_launch(lib):
+    """Host-side checks of cc_decode return codes without touching a device."""
+    kw = _base()
+    prob = B.problem(**kw)
+    sl = np.array([10, 20], np.int32)
+    blob = B.plan(prob, sl, None, num_cus=8, num_xcds=1, tile_tokens=32, heads_per_unit=4)
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails a host check first
+    hp = blob.ctypes.data_as(ctypes.c_void_p)
+    ws_need = B.workspace_size(blob)
+
+    def call(p, plan=hp, ws_bytes=ws_need, v=fake, reduce=0):
+        return lib.cc_decode_variant(reduce, ctypes.byref(p), plan, fake, fake, fake, v, fake, fake, None, fake,
+                                     fake, fake, ws_bytes, None)
+
+    assert call(prob, ws_bytes=ws_need - 1) == B.CC_ERR_BUFFER
+    other = B.problem(**{**kw, "num_pages": 5})
+    assert call(other) == B.CC_ERR_PLAN
+    assert call(prob, v=None) == B.CC_ERR_INVALID
+    assert call(prob, reduce=9) == B.CC_ERR_INVALID
+    junk = np.zeros_like(blob)
+    assert call(prob, plan=junk.ctypes.data_as(ctypes.c_void_p)) == B.CC_ERR_PLAN
+    bad_scale = B.problem(**{**kw, "softmax_scale": 0.0})
+    assert call(bad_scale) == B.CC_ERR_INVALID
+    # unsupported shapes (head dim 96) are refused before launch
+    odd = B.problem(**{**kw, "head_dim_qk": 96, "head_dim_v": 96})
+    blob2 = B.plan(odd, sl, None, num_cus=8, num_xcds=1, tile_tokens=32, heads_per_unit=4)
+    assert lib.cc_decode(ctypes.byref(odd), blob2.ctypes.data_as(ctypes.c_void_p), fake, fake, fake, fake, fake,
+                         fake, None, fake, fake, fake, B.workspace_size(blob2), None) == B.CC_ERR_UNSUPPORTED

@@ -1,0 +1,189 @@
+"""GPU parity of the GQA decode path against the fp64 oracle (through the C ABI).
+
+Bars: max|out - oracle| <= 1e-2 and max|lse - oracle| <= 1e-3 (absolute), no
+NaN/Inf, for bf16 inputs with fp32 accumulation.  Full-size workloads run in
+the launch configuration the benchmark times (one chunk per compute unit,
+32-token tiles, the device's XCD count); the oracle checks every output where
+it finishes in seconds and a sample of units (always including split ones)
+otherwise.
+"""
+import numpy as np
+import pytest
+
+from cross_cu_load_amd import binding as B
+from cross_cu_load_amd import workloads as W
+from oracle import attention as A
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_OUT, TOL_LSE = 1e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def dev(lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    torch.cuda.set_device(0)
+    return B.device_query(0)
+
+
+def run(wl, cus, xcds, tile=32, policy=B.POLICY_STREAMK, reduce=B.REDUCE_FUSED, tag=""):
+    print(f"[gpu] {tag} cfg={wl.cfg.name} B={wl.cfg.batch} C={cus} X={xcds} T={tile} policy={policy} "
+          f"reduce={reduce}", flush=True)
+    plan = B.plan(B.problem_for(wl), wl.seqlens, wl.block_table, num_cus=cus, num_xcds=xcds,
+                  tile_tokens=tile, policy=policy)
+    s = B.session(wl, plan)
+    s.run(reduce)
+    torch.cuda.synchronize()
+    return s, plan
+
+
+def compare(s, wl, only=None):
+    ref_o, ref_l = A.decode_attention_wl(wl, only=only)
+    out = s.out.cpu().numpy().astype(np.float64)
+    lse = s.lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    if only is not None:
+        G = wl.cfg.group
+        mask = np.zeros(lse.shape, bool)
+        for (b, t, g) in only:
+            mask[b, t, g * G:(g + 1) * G] = True
+        out, ref_o = out[mask], ref_o[mask]
+        lse, ref_l = lse[mask], ref_l[mask]
+    do = float(np.max(np.abs(out - ref_o)))
+    dl = float(np.max(np.abs(lse - ref_l)))
+    print(f"       max|dout|={do:.3e} max|dlse|={dl:.3e}", flush=True)
+    assert do <= TOL_OUT and dl <= TOL_LSE
+    return do, dl
+
+
+def clean(s, plan):
+    dirty, flags = B.workspace_check(plan, s.workspace)
+    assert dirty == 0 and flags == 0
+
+
+def test_tiny_gqa_config(dev):
+    wl = W.make_workload(W.CONFIG_BY_NAME["tiny_gqa"])
+    s, plan = run(wl, *dev, tag="tiny")
+    compare(s, wl)
+    clean(s, plan)
+
+
+@pytest.mark.parametrize("name,batch,hi", [("llama3_8b_gqa", 8, 3000), ("skewed_gqa", 6, 5000),
+                                           ("tiny_gqa", 3, 100)])
+def test_small_workloads_all_outputs(dev, name, batch, hi):
+    cfg = W.small_variant(W.CONFIG_BY_NAME[name], batch=batch, seqlen_hi=hi)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, tag="small")
+    compare(s, wl)
+    clean(s, plan)
+
+
+def test_ragged_and_single_token_sequences(dev):
+    cfg = W.CONFIG_BY_NAME["skewed_gqa"]
+    sl = np.array([1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 1, 4097, 1, 999, 1], np.int32)
+    cfg = W.small_variant(cfg, batch=len(sl), seqlen_hi=5000)
+    wl = W.make_workload(cfg, seqlens=sl)
+    s, plan = run(wl, *dev, tag="ragged")
+    compare(s, wl)
+    clean(s, plan)
+    # a one-token sequence returns its V row: p = 1, l = 1, bf16 -> fp32 is exact
+    out = s.out.cpu().numpy()
+    G, P = cfg.group, cfg.page_size
+    for b in np.nonzero(sl == 1)[0]:
+        page = wl.block_table[b, 0]
+        for h in range(cfg.num_q_heads):
+            v = A.bf16_to_f64(wl.v_cache[page, 0, h // G]).astype(np.float32)
+            assert np.array_equal(out[b, 0, h], v)
+
+
+def test_skewed_full_size_all_outputs(dev):
+    wl = W.make_workload(W.CONFIG_BY_NAME["skewed_gqa"])
+    s, plan = run(wl, *dev, tag="skewed-full")
+    compare(s, wl)
+    clean(s, plan)
+
+
+def test_llama_full_size_sampled(dev):
+    cfg = W.CONFIG_BY_NAME["llama3_8b_gqa"]
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, tag="llama-full")
+    from oracle import planner as PL
+    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1])
+    split_units = [u for u, n in enumerate(ref["unit_nsplit"]) if n > 1]
+    rng = np.random.default_rng(5)
+    pick = set(split_units[:24]) | set(int(u) for u in rng.choice(len(ref["unit_nsplit"]), 24, replace=False))
+    longest = int(np.argmax(wl.seqlens))
+    pick |= {longest * cfg.num_kv_heads + g for g in range(cfg.num_kv_heads)}
+    only = [(u // cfg.num_kv_heads, 0, u % cfg.num_kv_heads) for u in sorted(pick)]
+    compare(s, wl, only=only)
+    clean(s, plan)
+
+
+@pytest.mark.parametrize("policy,reduce", [(B.POLICY_PER_UNIT, B.REDUCE_FUSED),
+                                           (B.POLICY_STREAMK, B.REDUCE_SPLIT_COMBINE)])
+@pytest.mark.parametrize("name", ["tiny_gqa", "skewed_gqa"])
+def test_comparison_variants(dev, policy, reduce, name):
+    cfg = W.CONFIG_BY_NAME[name]
+    if name == "skewed_gqa":
+        cfg = W.small_variant(cfg, batch=6, seqlen_hi=5000)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, policy=policy, reduce=reduce, tag="variant")
+    compare(s, wl)
+    clean(s, plan)
+
+
+@pytest.mark.parametrize("cus", [1, 8, 64, 255, 256, 1024])
+def test_split_points_move_with_cu_count(dev, cus):
+    cfg = W.small_variant(W.CONFIG_BY_NAME["skewed_gqa"], batch=5, seqlen_hi=4000, seed_offset=cus)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, cus, dev[1], tag="cus")
+    compare(s, wl)
+    clean(s, plan)
+
+
+def test_repeat_runs_bitwise_identical_and_counters_reset(dev):
+    cfg = W.small_variant(W.CONFIG_BY_NAME["skewed_gqa"], batch=8, seqlen_hi=20000)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, tag="repeat")
+    o0, l0 = s.out.clone(), s.lse.clone()
+    for i in range(20):
+        s.out.fill_(float("nan"))
+        s.run()
+    torch.cuda.synchronize()
+    assert torch.equal(s.out, o0) and torch.equal(s.lse, l0)
+    clean(s, plan)
+
+
+def test_stale_partials_do_not_leak(dev):
+    """Partial slots pre-filled with NaN: every slot a merge reads is written first."""
+    cfg = W.small_variant(W.CONFIG_BY_NAME["skewed_gqa"], batch=6, seqlen_hi=8000)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, tag="nan-poison")
+    o0, l0 = s.out.clone(), s.lse.clone()
+    units = int(plan.view(np.int32)[15])
+    partials_off = -(-(256 + 4 * units) // 256) * 256
+    assert int(plan.view(np.int32)[18]) > 0, "the case must split some unit"
+    s.workspace[partials_off:].view(torch.float32).fill_(float("nan"))
+    s.run()
+    torch.cuda.synchronize()
+    assert torch.equal(s.out, o0) and torch.equal(s.lse, l0)
+    clean(s, plan)
+
+
+def test_page_placement_is_bitwise_irrelevant(dev):
+    cfg = W.small_variant(W.CONFIG_BY_NAME["llama3_8b_gqa"], batch=6, seqlen_hi=4000)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, tag="placement-a")
+    o_a = s.out.clone()
+    # re-place every page at a different physical slot, same logical content
+    perm = np.random.default_rng(3).permutation(wl.num_pages)
+    k2 = np.empty_like(wl.k_cache)
+    v2 = np.empty_like(wl.v_cache)
+    k2[perm] = wl.k_cache
+    v2[perm] = wl.v_cache
+    bt2 = np.where(wl.block_table >= 0, perm[np.maximum(wl.block_table, 0)], -1).astype(np.int32)
+    wl2 = W.Workload(wl.cfg, wl.seqlens, bt2, wl.q, k2, v2, None)
+    s2, _ = run(wl2, *dev, tag="placement-b")
+    assert torch.equal(s2.out, o_a) and torch.equal(s2.lse, s.lse)
