@@ -6,9 +6,12 @@ paged KV with 16-token pages and a shuffled block table).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload skewed_gqa]
 
 One step = one call of the decode (plan already on the device, inputs resident
-in HBM).  Before every timed step a 1 GiB scratch write evicts the 256 MB
-last-level cache, so each step reads its KV from HBM; the write is outside the
-timed region.  Each step is timed with HIP events recorded on the stream the
+in HBM).  Before every timed step a 1 GiB scratch buffer is read through, which
+evicts the KV from the 256 MB last-level cache without leaving dirty lines
+behind (a write-based flush would leave write-back traffic running into the
+timed step), so each step reads its KV from HBM; the flush is outside the
+timed region.  The same box's plain streaming-read ceiling (1 GiB, the
+library's read probe, same flush) is reported beside the result.  Each step is timed with HIP events recorded on the stream the
 kernels run on.  The two comparison launches of the same computation (one
 workgroup per (sequence, KV head); split + separate combine kernel) are timed
 the same way beside it, and the fp64 CPU oracle is timed on the host cores.
@@ -18,6 +21,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -37,6 +41,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="skewed_gqa")
+    ap.add_argument("--layout", choices=["nhd", "hnd"], default="nhd",
+                    help="page layout of the GQA K/V caches: token-major [P][Hkv][d] or head-major [Hkv][P][d]")
     ap.add_argument("--variant-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
@@ -71,6 +77,33 @@ def time_steps(torch, run, steps, warmup, flush=None):
 def stats(ms):
     return dict(mean_us=float(ms.mean() * 1e3), median_us=float(np.median(ms) * 1e3),
                 p10_us=float(np.percentile(ms, 10) * 1e3), p90_us=float(np.percentile(ms, 90) * 1e3))
+
+
+def timeline_pass(torch, B, s, workers, xcds, flush):
+    """One cold decode with the in-kernel timeline on: CU busy fraction and XCD placement."""
+    buf = torch.zeros(8 * workers, dtype=torch.int64, device="cuda")
+    B.debug_timeline(buf)
+    flush()
+    s.run()
+    torch.cuda.synchronize()
+    B.debug_timeline(None)
+    t = buf.view(workers, 8).cpu().numpy().astype(np.int64)
+    start, stream_end, merged, arrived, end, xcc = t[:, 0], t[:, 1], t[:, 2], t[:, 3], t[:, 4], t[:, 5]
+    t0 = start.min()
+    span = float(end.max() - t0)                      # 100 MHz ticks
+    busy = float((end - start).sum()) / (workers * span) if span > 0 else 0.0
+    to_us = 1e-2
+    return {"makespan_us": span * to_us, "cu_busy_frac": busy,
+            "start_spread_us": float(start.max() - t0) * to_us,
+            "stream_end_us": [float(np.percentile(stream_end - t0, q)) * to_us for q in (0, 50, 100)],
+            "end_us": [float(np.percentile(end - t0, q)) * to_us for q in (0, 50, 100)],
+            "post_stream_us_median_max": [float(np.median(end - stream_end)) * to_us,
+                                          float((end - stream_end).max()) * to_us],
+            "piece_merge_us_median": float(np.median(merged - stream_end)) * to_us,
+            "arrival_us_median": float(np.median(arrived - merged)) * to_us,
+            "unit_merge_us_max": float((end - arrived).max()) * to_us,
+            "xcd_is_w_mod_x": bool(np.all(xcc == np.arange(workers) % xcds)),
+            "xcd_ids_seen": sorted(set(int(x) for x in xcc))}
 
 
 def cpu_baseline(wl, args):
@@ -108,6 +141,8 @@ def main():
     torch.cuda.set_device(0)
     cus, xcds = B.device_query(0)
     cfg = W.CONFIG_BY_NAME[args.workload]
+    if cfg.mode == W.MODE_GQA:
+        cfg = dataclasses.replace(cfg, kv_layout=W.KV_HND if args.layout == "hnd" else W.KV_NHD)
     wl = W.make_workload(cfg)
     kv = wl.kv_bytes()
     prob = B.problem_for(wl)
@@ -120,10 +155,18 @@ def main():
         plan = B.plan(prob, wl.seqlens, wl.block_table, num_cus=cus, num_xcds=xcds)
     plan_us = (time.perf_counter() - t0) / 20 * 1e6
     s = B.session(wl, plan)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    scratch = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1024 * 512, dtype=torch.int32, device="cuda")
 
     def flush():
-        scratch.fill_(1)
+        B.probe_read(scratch, 0, 1024, sink)
+
+    # practical ceiling: a plain 1 GiB streaming read, same flush
+    probe_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    probe_ms = time_steps(torch, lambda: B.probe_read(probe_buf, 0, 1024, sink), 20, 3, flush)
+    probe_gbs = (1 << 30) / (float(np.median(probe_ms)) * 1e-3) / 1e9
+    del probe_buf
+    log(args, f"read probe ceiling: {probe_gbs:.0f} GB/s")
 
     ms = time_steps(torch, s.run, args.steps, args.warmup, flush)
     warm = time_steps(torch, s.run, args.steps, args.warmup)
@@ -131,6 +174,8 @@ def main():
     dirty, flags = B.workspace_check(plan, s.workspace)
     assert dirty == 0 and flags == 0, "workspace left dirty"
     log(args, f"stream-k fused: {st}")
+    tline = timeline_pass(torch, B, s, cus, xcds, flush)
+    log(args, f"timeline: {tline}")
 
     variants = {}
     if not args.no_variants:
@@ -164,16 +209,20 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "seqlens_sum": int(wl.seqlens.sum()),
                    "seqlen_max": int(wl.seqlens.max()), "num_q_heads": cfg.num_q_heads,
                    "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim_qk, "page_size": cfg.page_size,
-                   "num_cus": cus, "num_xcds": xcds, "tile_tokens": 32, "kv_bytes": kv},
+                   "num_cus": cus, "num_xcds": xcds, "tile_tokens": 32, "kv_bytes": kv,
+                   "kv_layout": args.layout if cfg.mode == W.MODE_GQA else "latent"},
         "us_per_batch": st["mean_us"],
         "us_per_batch_median": st["median_us"],
         "us_p10_p90": [st["p10_us"], st["p90_us"]],
         "warm_us_median": stats(warm)["median_us"],
         "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+        "read_probe_ceiling_gbs": probe_gbs,
+        "frac_of_read_probe": gbs / probe_gbs,
         "plan_host_us": plan_us,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
         "variants": variants,
+        "timeline": tline,
     }
     if variants:
         result["speedup_vs_variants"] = {k: v["mean_us"] / st["mean_us"] for k, v in variants.items()}

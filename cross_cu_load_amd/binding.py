@@ -21,12 +21,13 @@ CC_ERR_INVALID, CC_ERR_UNSUPPORTED, CC_ERR_BUFFER, CC_ERR_PLAN = -1, -2, -3, -4
 CC_ERR_PAGE, CC_ERR_HIP, CC_ERR_DEVICE_DATA = -5, -6, -7
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
 POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
+KV_NHD, KV_HND = 0, 1
 REDUCE_FUSED, REDUCE_SPLIT_COMBINE = 0, 1
 
-# every symbol include/crosscu.h declares
+# every symbol include/*.h declares
 EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_plan_size", "cc_plan",
            "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
-           "cc_decode_variant"]
+           "cc_decode_variant", "cc_debug_timeline", "cc_probe_read"]
 
 
 class Problem(ctypes.Structure):
@@ -34,7 +35,8 @@ class Problem(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32), ("topk", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("num_pages", ctypes.c_int32), ("topk", ctypes.c_int32), ("kv_layout", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
 
 
 class PlanOpts(ctypes.Structure):
@@ -79,6 +81,9 @@ def load() -> ctypes.CDLL:
     dec = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.cc_decode.argtypes = dec
     lib.cc_decode_variant.argtypes = [ctypes.c_int] + dec
+    lib.cc_debug_timeline.argtypes = [_P, _SZ]
+    lib.cc_probe_read.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, _P, _P]
     for f in EXPORTS:
         if f not in ("cc_last_error", "cc_strerror"):
             getattr(lib, f).restype = ctypes.c_int
@@ -102,9 +107,9 @@ def _ptr_i32(a: np.ndarray):
 
 
 def problem(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
-            max_pages_per_seq, num_pages, topk, softmax_scale) -> Problem:
+            max_pages_per_seq, num_pages, topk, softmax_scale, kv_layout=KV_NHD) -> Problem:
     return Problem(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
-                   max_pages_per_seq, num_pages, topk, softmax_scale)
+                   max_pages_per_seq, num_pages, topk, kv_layout, softmax_scale)
 
 
 def device_query(device: int = 0) -> tuple[int, int]:
@@ -170,6 +175,26 @@ def workspace_check(plan_host: np.ndarray, ws, stream=None) -> tuple[int, int]:
     return dirty.value, flags.value
 
 
+def debug_timeline(buf) -> None:
+    """Sets (a uint64 device tensor of 4 words per worker) or clears (None) the timeline."""
+    lib = load()
+    if buf is None:
+        _check(lib.cc_debug_timeline(None, 0), "cc_debug_timeline")
+    else:
+        _check(lib.cc_debug_timeline(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()),
+               "cc_debug_timeline")
+
+
+def probe_read(buf, method: int, workgroups: int, sink, pages=None, page_bytes: int = 0,
+               stream=None) -> None:
+    """cc_probe_read on a device tensor (asynchronous)."""
+    lib = load()
+    npages = 0 if pages is None else pages.numel()
+    _check(lib.cc_probe_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(), method,
+                             _dp(pages), page_bytes, npages, workgroups, _dp(sink), _stream(stream)),
+           "cc_probe_read")
+
+
 def _dp(t):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -214,7 +239,7 @@ class DeviceSession:
 def problem_for(wl) -> Problem:
     c = wl.cfg
     return problem(c.mode, c.batch, c.q_tokens, c.num_q_heads, c.num_kv_heads, c.head_dim_qk, c.head_dim_v,
-                   c.page_size, wl.max_pages, wl.num_pages, c.topk, c.softmax_scale)
+                   c.page_size, wl.max_pages, wl.num_pages, c.topk, c.softmax_scale, wl.kv_layout)
 
 
 def session(wl, plan_host: np.ndarray, device="cuda") -> DeviceSession:

@@ -8,10 +8,15 @@
 #include <vector>
 
 #include "../../include/crosscu.h"
+#include "../../include/crosscu_debug.h"
 #include "launch.h"
 #include "plan.h"
 
 namespace {
+
+// debug timeline buffer (process-wide; set by cc_debug_timeline)
+void* g_timeline = nullptr;
+size_t g_timeline_bytes = 0;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -70,6 +75,10 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
     cc::set_error("workspace holds %zu bytes, the plan needs %zu", workspace_bytes, wl.total);
     return CC_ERR_BUFFER;
   }
+  if (prob->kv_layout != CC_KV_NHD && prob->kv_layout != CC_KV_HND) {
+    cc::set_error("unknown kv_layout %d", prob->kv_layout);
+    return CC_ERR_INVALID;
+  }
   if (!(prob->softmax_scale > 0.f) || !std::isfinite(prob->softmax_scale)) {
     cc::set_error("softmax_scale must be finite and > 0");
     return CC_ERR_INVALID;
@@ -101,6 +110,7 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
   a.max_pages = p.max_pages_per_seq;
   a.num_pages = p.num_pages;
   a.topk = p.topk;
+  a.kv_layout = p.kv_layout;
   a.scale_log2 = (float)((double)p.softmax_scale * 1.4426950408889634);
   a.workers = v.workers();
   a.units = v.units();
@@ -123,6 +133,9 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
   a.partials = reinterpret_cast<float*>(ws + wl.partials_off);
   a.slot_floats = (int)wl.slot_floats;
   a.reduce = reduce;
+  a.timeline = (g_timeline && g_timeline_bytes >= (size_t)v.workers() * 8 * cc::kTimelineWords)
+                   ? static_cast<unsigned long long*>(g_timeline)
+                   : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = cc::launch_gqa(a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -138,6 +151,12 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
 extern "C" {
 
 int cc_version(void) { return 100; }
+
+int cc_debug_timeline(void* buf, size_t bytes) {
+  g_timeline = buf;
+  g_timeline_bytes = buf ? bytes : 0;
+  return CC_OK;
+}
 
 const char* cc_last_error(void) { return cc::last_error(); }
 

@@ -32,6 +32,7 @@
 
 #include "../../include/crosscu.h"
 #include "launch.h"
+#include "merge.h"
 
 namespace cc {
 namespace gqa {
@@ -74,6 +75,13 @@ __device__ __forceinline__ void lds_dma4(const char* src, char* lds) {
   __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds, 4, 0, 0);
 }
 
+// Id of the XCD this wave runs on (hardware register XCC_ID, low 4 bits).
+__device__ __forceinline__ unsigned xcc_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -109,6 +117,10 @@ struct BlockRegs {
 
 struct Params {
   int hq, hkv, group, max_pages, num_pages, log2_page;
+  // byte strides of the paged cache: a page, a KV head inside a page, and one
+  // token of one head inside a page (token-major or head-major page layout)
+  long long page_bytes;
+  int head_bytes, token_bytes;
   float scale_log2;
   int slot_floats;   // floats per partial slot in the workspace
   int region_bytes;  // LDS bytes per wave (stream slot, later its merge slots)
@@ -122,6 +134,8 @@ struct Cursor {
   int nb;     // blocks in the item (from the plan)
   int unit, tb, te, split;
   int lim;    // min(te, seqlens[b]): tokens at or past it are masked
+  int nsplit; // pieces of the unit across the grid
+  int pbase;  // first partial slot of the unit (split units)
 };
 
 __device__ __forceinline__ int blocks_of(int tb, int te) { return (te - tb + kBlk - 1) / kBlk; }
@@ -133,14 +147,17 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
                   const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kc,
                   const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
                   const int32_t* __restrict__ seqlens, float* __restrict__ out,
-                  float* __restrict__ lse, int32_t* err, int32_t* counters, float* partials) {
+                  float* __restrict__ lse, int32_t* err, int32_t* counters, float* partials,
+                  unsigned long long* timeline) {
   using GE = Geo<D>;
   constexpr int KS = GE::KS;
   constexpr int W = GE::W;
   using vvec = typename GE::vvec;
   extern __shared__ __attribute__((aligned(16))) char smem[];  // kWaves regions
   __shared__ int slot_item[2 * kWaves];
-  __shared__ int sh_last;
+  __shared__ int slot_meta[2 * kWaves][4];  // unit, split, nsplit, pbase of the slot's item
+  __shared__ int last_of[2 * kWaves];       // per first-slot: this workgroup merges the unit
+  __shared__ __attribute__((aligned(16))) float merge_lds[merge_lds_floats(kThreads, 16)];
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63;
@@ -148,14 +165,21 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   const int G = p.group;
   const int slot_stride = G * (D + 2);  // floats of one (m, l, o) merge slot
   const int page_mask = (1 << p.log2_page) - 1;
-  const size_t row_bytes = (size_t)p.hkv * D * sizeof(uint16_t);
   char* const region = smem + wave * p.region_bytes;
   auto merge_slot = [&](int sl) -> float* {
     return reinterpret_cast<float*>(smem + (sl >> 1) * p.region_bytes) + (sl & 1) * slot_stride;
   };
 
+  unsigned long long* tl = timeline ? timeline + kTimelineWords * blockIdx.x : nullptr;
+  if (tl && tid == 0) {
+    tl[0] = __builtin_amdgcn_s_memrealtime();
+    tl[5] = xcc_id();
+  }
   const int i0 = uni(wg_off[blockIdx.x]), i1 = uni(wg_off[blockIdx.x + 1]);
-  if (i0 >= i1) return;
+  if (i0 >= i1) {
+    if (tl && tid == 0) tl[1] = tl[2] = tl[3] = tl[4] = tl[0];
+    return;
+  }
 
   int nblk = 0;
   for (int i = i0; i < i1; ++i) {
@@ -176,6 +200,8 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     c.te = uni(t.z);
     c.split = uni(t.w);
     c.nb = blocks_of(c.tb, c.te);
+    c.nsplit = uni(unit_nsplit[c.unit]);
+    c.pbase = uni(unit_pbase[c.unit]);
     const int L = uni(seqlens[c.unit / p.hkv]);
     c.lim = c.te;
     if (c.te > L) {  // plan built for other lengths: mask past the sequence end
@@ -200,11 +226,11 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   // wave-uniform, move from block to block.  A half with no valid token
   // reads half 0 again; rows past the valid length stay inside their page and
   // are masked (scores) or zeroed (values) in compute.
-  const uint32_t koff = (uint32_t)((size_t)lr * row_bytes + lg * 16);
+  const uint32_t tstride = (uint32_t)p.token_bytes;
+  const uint32_t koff = lr * tstride + lg * 16;
   uint32_t voff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    voff[i] = (uint32_t)((size_t)(4 * lg + i) * row_bytes + W * lr * sizeof(uint16_t));
+  for (int i = 0; i < 4; ++i) voff[i] = (4 * lg + i) * tstride + W * lr * (uint32_t)sizeof(uint16_t);
 
   // Global sources of one block: the K and V rows of its two 16-token halves.
   struct Src {
@@ -219,14 +245,14 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     const int32_t* row = bt + (size_t)b * p.max_pages;
     const int tok0 = c.tb + c.j * kBlk;
     const int h1 = (tok0 + 16 < c.lim) ? tok0 + 16 : tok0;
-    const size_t r0 = (size_t)page_of(row, tok0) * (1u << p.log2_page) + (tok0 & page_mask);
-    const size_t r1 = (size_t)page_of(row, h1) * (1u << p.log2_page) + (h1 & page_mask);
-    const size_t go = (size_t)g * D * sizeof(uint16_t);
+    const size_t go = (size_t)g * p.head_bytes;
+    const size_t o0 = (size_t)page_of(row, tok0) * p.page_bytes + go + (size_t)(tok0 & page_mask) * tstride;
+    const size_t o1 = (size_t)page_of(row, h1) * p.page_bytes + go + (size_t)(h1 & page_mask) * tstride;
     Src S;
-    S.k0 = reinterpret_cast<const char*>(kc) + r0 * row_bytes + go;
-    S.k1 = reinterpret_cast<const char*>(kc) + r1 * row_bytes + go;
-    S.v0 = reinterpret_cast<const char*>(vc) + r0 * row_bytes + go;
-    S.v1 = reinterpret_cast<const char*>(vc) + r1 * row_bytes + go;
+    S.k0 = reinterpret_cast<const char*>(kc) + o0;
+    S.k1 = reinterpret_cast<const char*>(kc) + o1;
+    S.v0 = reinterpret_cast<const char*>(vc) + o0;
+    S.v1 = reinterpret_cast<const char*>(vc) + o1;
     return S;
   };
 
@@ -271,7 +297,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   };
 
   // (m, l, o) of this wave for item `it` into merge slot sl (real heads only).
-  auto put_slot = [&](int sl, int it, float m, float l, const f32x4* o) {
+  auto put_slot = [&](int sl, const Cursor& cu, float m, float l, const f32x4* o) {
     float* sb = merge_slot(sl);
     if (lane < G) {
       sb[lane] = m;
@@ -285,7 +311,13 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
         for (int cc = 0; cc < W; ++cc) sb[2 * G + hh * D + W * lr + cc] = o[cc][rr];
       }
     }
-    if (lane == 0) slot_item[sl] = it;
+    if (lane == 0) {
+      slot_item[sl] = cu.it;
+      slot_meta[sl][0] = cu.unit;
+      slot_meta[sl][1] = cu.split;
+      slot_meta[sl][2] = cu.nsplit;
+      slot_meta[sl][3] = cu.pbase;
+    }
   };
 
   if (s < e) {
@@ -319,6 +351,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
 
     // the first item's state when it is neither written out nor the last item
     bool stashed = false;
+    Cursor c_first = c;
     float m_first = 0.f, l_first = 0.f;
     f32x4 o_first[W];
 
@@ -416,7 +449,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       float l_tot = l_run + __shfl_xor(l_run, 16);
       l_tot += __shfl_xor(l_tot, 32);
       const bool whole = j0 == 0 && c.j == c.nb - 1;
-      if (whole && unit_nsplit[c.unit] == 1) {
+      if (whole && c.nsplit == 1) {
         const int b = c.unit / p.hkv, g = c.unit - (c.unit / p.hkv) * p.hkv;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -436,49 +469,62 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
         // only a wave's first and last items can be shared or split; this is
         // the first and more follow: keep it until the slot stops streaming
         stashed = true;
+        c_first = c;
         m_first = m_run;
         l_first = l_tot;
 #pragma unroll
         for (int cc = 0; cc < W; ++cc) o_first[cc] = o[cc];
       } else {
-        put_slot(2 * wave + (c.it == first_it ? 0 : 1), c.it, m_run, l_tot, o);
+        put_slot(2 * wave + (c.it == first_it ? 0 : 1), c, m_run, l_tot, o);
       }
       if (k >= e) break;
       c = n;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qv[ks] = qn[ks];
     }
-    if (stashed) put_slot(2 * wave, first_it, m_first, l_first, o_first);
+    if (stashed) put_slot(2 * wave, c_first, m_first, l_first, o_first);
   }
 
   __syncthreads();
+  if (tl && tid == 0) tl[1] = __builtin_amdgcn_s_memrealtime();
 
   // ------------------------------------------------ workgroup-level merges
+  // Phase 1: every item the waves left in LDS is merged over its waves and
+  // written out (whole unit) or handed on as this piece's partial.
+  if (tid < 2 * kWaves) last_of[tid] = 0;
+  int sit[2 * kWaves];  // slot -> item, held in registers for the whole phase
+#pragma unroll
+  for (int t = 0; t < 2 * kWaves; ++t) sit[t] = uni(slot_item[t]);
   for (int sl = 0; sl < 2 * kWaves; ++sl) {
-    const int it = slot_item[sl];
+    const int it = sit[sl];
     if (it < 0) continue;
-    bool seen = false;
-    for (int t = 0; t < sl; ++t) seen |= slot_item[t] == it;
-    if (seen) continue;
-
-    const int4 itm = items[it];
-    const int unit = itm.x, split = itm.w;
-    const int ns = unit_nsplit[unit];
+    unsigned mask = 0;  // slots holding this item (the first is sl)
+#pragma unroll
+    for (int t = 0; t < 2 * kWaves; ++t) mask |= (unsigned)(sit[t] == it) << t;
+    if (mask & ((1u << sl) - 1)) continue;  // merged at its first slot
+    const int unit = uni(slot_meta[sl][0]), split = uni(slot_meta[sl][1]), ns = uni(slot_meta[sl][2]);
     const int b = unit / p.hkv, g = unit - (unit / p.hkv) * p.hkv;
-    float* pslot = ns > 1 ? partials + (size_t)(unit_pbase[unit] + split) * p.slot_floats : nullptr;
+    float* pslot = ns > 1 ? partials + (size_t)(uni(slot_meta[sl][3]) + split) * p.slot_floats : nullptr;
     for (int el = tid; el < G * D; el += kThreads) {
       const int hh = el / D, cc = el - (el / D) * D;
+      float mt[2 * kWaves], lt[2 * kWaves], ot[2 * kWaves];
+#pragma unroll
+      for (int t = 0; t < 2 * kWaves; ++t) {  // every load issued before any is used
+        const float* sb = merge_slot(t);
+        const bool on = (mask >> t) & 1;
+        mt[t] = on ? sb[hh] : -INFINITY;
+        lt[t] = on ? sb[G + hh] : 0.f;
+        ot[t] = on ? sb[2 * G + hh * D + cc] : 0.f;
+      }
       float M = -INFINITY;
-      for (int t = sl; t < 2 * kWaves; ++t)
-        if (slot_item[t] == it) M = fmaxf(M, merge_slot(t)[hh]);
+#pragma unroll
+      for (int t = 0; t < 2 * kWaves; ++t) M = fmaxf(M, mt[t]);
       float L = 0.f, O = 0.f;
-      for (int t = sl; t < 2 * kWaves; ++t) {
-        if (slot_item[t] == it) {
-          const float* sb = merge_slot(t);
-          const float f = fast_exp2(sb[hh] - M);
-          L += sb[G + hh] * f;
-          O += sb[2 * G + hh * D + cc] * f;
-        }
+#pragma unroll
+      for (int t = 0; t < 2 * kWaves; ++t) {  // slot order = token order
+        const float f = fast_exp2(mt[t] - M);
+        L += lt[t] * f;
+        O += ot[t] * f;
       }
       const size_t orow = (size_t)b * p.hq + (size_t)g * G + hh;
       if (ns == 1) {
@@ -489,47 +535,60 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
           pslot[hh] = M;
           pslot[G + hh] = L;
         }
-        pslot[2 * G + hh * D + cc] = O;
+        pslot[partial_o_offset(G) + hh * D + cc] = O;
       }
     }
-    if (ns > 1 && p.reduce == CC_REDUCE_FUSED) {
-      __syncthreads();
-      if (tid == 0) {
-        __threadfence();  // release this piece's partial at device scope
-        const int old = atomicAdd(&counters[unit], 1);
-        sh_last = old == ns - 1;
-      }
-      __syncthreads();
-      if (sh_last) {
-        __threadfence();  // acquire the other pieces' partials
-        const float* pb = partials + (size_t)unit_pbase[unit] * p.slot_floats;
-        for (int el = tid; el < G * D; el += kThreads) {
-          const int hh = el / D, cc = el - (el / D) * D;
-          float M = -INFINITY;
-          for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, pb[(size_t)sp * p.slot_floats + hh]);
-          float L = 0.f, O = 0.f;
-          for (int sp = 0; sp < ns; ++sp) {
-            const float* ps = pb + (size_t)sp * p.slot_floats;
-            const float f = fast_exp2(ps[hh] - M);
-            L += ps[G + hh] * f;
-            O += ps[2 * G + hh * D + cc] * f;
-          }
-          const size_t orow = (size_t)b * p.hq + (size_t)g * G + hh;
-          out[orow * D + cc] = O / L;
-          if (cc == 0) lse[orow] = (M + __log2f(L)) * kLn2;
+  }
+  if (tl && tid == 0) tl[2] = __builtin_amdgcn_s_memrealtime();
+  if (p.reduce == CC_REDUCE_FUSED) {
+    // Phase 2: one release for all of this workgroup's partials, then one
+    // arrival per split item; the piece that completes a unit merges it.
+    __syncthreads();
+    if (tid == 0) {
+      bool any_split = false;
+      for (int sl = 0; sl < 2 * kWaves; ++sl) any_split |= slot_item[sl] >= 0 && slot_meta[sl][2] > 1;
+      if (any_split) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // publish the partials device-wide
+        bool any_last = false;
+        for (int sl = 0; sl < 2 * kWaves; ++sl) {
+          const int it = slot_item[sl];
+          if (it < 0 || slot_meta[sl][2] <= 1) continue;
+          bool seen = false;
+          for (int t = 0; t < sl; ++t) seen |= slot_item[t] == it;
+          if (seen) continue;
+          const int old = atomicAdd(&counters[slot_meta[sl][0]], 1);
+          last_of[sl] = old == slot_meta[sl][2] - 1;
+          any_last |= last_of[sl] != 0;
         }
-        if (tid == 0) __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (any_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other pieces' partials
       }
-      __syncthreads();
     }
+    __syncthreads();
+    if (tl && tid == 0) tl[3] = __builtin_amdgcn_s_memrealtime();
+    // Phase 3: merges of the units this workgroup completed
+    for (int sl = 0; sl < 2 * kWaves; ++sl) {
+      if (!uni(last_of[sl])) continue;
+      const int unit = uni(slot_meta[sl][0]), ns = uni(slot_meta[sl][2]);
+      const int b = unit / p.hkv, g = unit - (unit / p.hkv) * p.hkv;
+      const size_t orow = (size_t)b * p.hq + (size_t)g * G;
+      merge_splits<kThreads>(partials + (size_t)uni(slot_meta[sl][3]) * p.slot_floats, ns, p.slot_floats, G, D,
+                             out + orow * D, lse + orow, merge_lds);
+      if (tid == 0) __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (tl && tid == 0) {
+    if (p.reduce != CC_REDUCE_FUSED) tl[3] = tl[2];
+    tl[4] = __builtin_amdgcn_s_memrealtime();
   }
 }
 
 // Merge kernel of the split-then-combine comparison: one workgroup per unit.
-__global__ void __launch_bounds__(256)
-combine_kernel(int hq, int hkv, int group, int hpu, int q_tokens, int dv, int slot_floats,
+constexpr int kCombineThreads = 256;
+__global__ void __launch_bounds__(kCombineThreads)
+combine_kernel(int hq, int hkv, int group, int hpu, int dv, int slot_floats,
                const int32_t* __restrict__ unit_nsplit, const int32_t* __restrict__ unit_pbase,
                const float* __restrict__ partials, float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) float lds[merge_lds_floats(kCombineThreads, 128)];
   const int u = blockIdx.x;
   const int ns = unit_nsplit[u];
   if (ns <= 1) return;
@@ -537,22 +596,9 @@ combine_kernel(int hq, int hkv, int group, int hpu, int q_tokens, int dv, int sl
   const int hb = u % hb_per_kv;
   const int g = (u / hb_per_kv) % hkv;
   const int bt = u / (hb_per_kv * hkv);  // b * q_tokens + t
-  const float* pb = partials + (size_t)unit_pbase[u] * slot_floats;
-  for (int el = threadIdx.x; el < hpu * dv; el += blockDim.x) {
-    const int hh = el / dv, cc = el - (el / dv) * dv;
-    float M = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, pb[(size_t)sp * slot_floats + hh]);
-    float L = 0.f, O = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float* ps = pb + (size_t)sp * slot_floats;
-      const float f = fast_exp2(ps[hh] - M);
-      L += ps[hpu + hh] * f;
-      O += ps[2 * hpu + hh * dv + cc] * f;
-    }
-    const size_t orow = (size_t)bt * hq + (size_t)g * group + (size_t)hb * hpu + hh;
-    out[orow * dv + cc] = O / L;
-    if (cc == 0) lse[orow] = (M + __log2f(L)) * kLn2;
-  }
+  const size_t orow = (size_t)bt * hq + (size_t)g * group + (size_t)hb * hpu;
+  merge_splits<kCombineThreads>(partials + (size_t)unit_pbase[u] * slot_floats, ns, slot_floats, hpu, dv,
+                                out + orow * dv, lse + orow, lds);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t words) {
@@ -579,6 +625,15 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s) {
   p.max_pages = a.max_pages;
   p.num_pages = a.num_pages;
   p.log2_page = ilog2(a.page_size);
+  const long long head_row = (long long)a.dqk * sizeof(uint16_t);
+  p.page_bytes = (long long)a.page_size * a.hkv * head_row;
+  if (a.kv_layout == CC_KV_HND) {  // [page][head][token][dim]
+    p.head_bytes = (int)(a.page_size * head_row);
+    p.token_bytes = (int)head_row;
+  } else {                         // [page][token][head][dim]
+    p.head_bytes = (int)head_row;
+    p.token_bytes = (int)(a.hkv * head_row);
+  }
   p.scale_log2 = a.scale_log2;
   p.slot_floats = a.slot_floats;
   p.reduce = a.reduce;
@@ -593,22 +648,22 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     gqa::gqa_decode_kernel<128><<<a.workers, kThreads, lds, s>>>(
         p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
-        a.out, a.lse, a.err, a.counters, a.partials);
+        a.out, a.lse, a.err, a.counters, a.partials, a.timeline);
   } else {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gqa::gqa_decode_kernel<64>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     gqa::gqa_decode_kernel<64><<<a.workers, kThreads, lds, s>>>(
         p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
-        a.out, a.lse, a.err, a.counters, a.partials);
+        a.out, a.lse, a.err, a.counters, a.partials, a.timeline);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
-  combine_kernel<<<a.units, 256, 0, s>>>(a.hq, a.hkv, a.hq / a.hkv, a.hpu, a.q_tokens, a.dv,
-                                         a.slot_floats, a.unit_nsplit, a.unit_pbase, a.partials,
-                                         a.out, a.lse);
+  combine_kernel<<<a.units, kCombineThreads, 0, s>>>(a.hq, a.hkv, a.hq / a.hkv, a.hpu, a.dv,
+                                                     a.slot_floats, a.unit_nsplit, a.unit_pbase,
+                                                     a.partials, a.out, a.lse);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ namespace cc {
 // the plan header and the workspace layout.
 struct DecodeArgs {
   // problem
-  int mode, batch, q_tokens, hq, hkv, dqk, dv, page_size, max_pages, num_pages, topk;
+  int mode, batch, q_tokens, hq, hkv, dqk, dv, page_size, max_pages, num_pages, topk, kv_layout;
   float scale_log2;  // softmax_scale * log2(e): scores are kept in base 2
   // plan (device pointers into the plan copy)
   int workers, units, hpu, tile;
@@ -34,7 +34,12 @@ struct DecodeArgs {
   float* partials;
   int slot_floats;
   int reduce;  // CC_REDUCE_*
+  // optional in-kernel timeline (kTimelineWords x uint64 per workgroup), null when off
+  unsigned long long* timeline;
 };
+
+// uint64 words per workgroup in the debug timeline
+constexpr int kTimelineWords = 8;
 
 // Device error-word bits.
 constexpr int kErrSeqlen = 1;

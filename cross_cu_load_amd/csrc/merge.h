@@ -1,0 +1,160 @@
+// Log-sum-exp merge of a unit's split partials, run by one whole workgroup.
+//
+// Each split piece s of a unit left (m_s, l_s, o_s) per head: the running max
+// of its scores (base 2), the sum of exp2(score - m_s) and the un-normalised
+// output.  The exact result over the union of the pieces is
+//   M = max_s m_s,  c_s = exp2(m_s - M) / sum_s l_s exp2(m_s - M),
+//   out = sum_s c_s o_s,  lse = ln2 * (M + log2 sum_s l_s exp2(m_s - M)).
+// This is the reduction a split-KV decode hands its partial outputs to
+// (MeldKernel summary, "Core method": partial outputs feed the reduction).
+//
+// The merge sits on the critical path of the last piece to arrive, so every
+// load is issued independently: one wave per head for (M, L), then float4
+// reads of o_s with several splits in flight per thread and, when the unit is
+// small, the splits spread over thread groups and summed through LDS.
+// Splits are combined in index order with fixed groupings: the result does not
+// depend on which piece arrived last.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace cc {
+
+constexpr int kMergeCoef = 2048;  // split coefficients held in LDS per pass
+constexpr int kMergeInflight = 8; // o_s loads in flight per thread
+
+// Offset (floats) of o inside a partial slot.
+__host__ __device__ constexpr int partial_o_offset(int hpu) { return (2 * hpu + 3) & ~3; }
+
+// LDS floats merge_splits needs for NT threads and hpu heads.
+__host__ __device__ constexpr int merge_lds_floats(int nt, int hpu) {
+  return ((2 * hpu + kMergeCoef + 3) & ~3) + 4 * nt;
+}
+
+// partials: slot s at pb + s * slot_floats holds m[hpu] at 0, l[hpu] at hpu and
+// o[hpu][dv] at partial_o_offset(hpu) (16-byte aligned).
+// out: head hh of the unit at out + hh * dv; lse: lse[hh].  dv % 4 == 0.
+template <int NT>
+__device__ void merge_splits(const float* pb, int ns, int slot_floats, int hpu, int dv, float* out,
+                             float* lse, float* lds) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  constexpr int kWavesM = NT / 64;
+  float* ml = lds;                         // M[hpu], 1/L[hpu]
+  float* coef = lds + 2 * hpu;             // [split in pass][hpu]
+  f4* red = reinterpret_cast<f4*>(lds + ((2 * hpu + kMergeCoef + 3) & ~3));
+  constexpr float kLn2 = 0.69314718055994531f;
+
+  // (M, L) per head: one wave per head, lanes over splits.  With at most 64
+  // splits whose coefficients all fit in LDS (the common case) each lane keeps
+  // its split's (m, l) in registers and writes c_s right away, so the whole
+  // merge is two rounds of loads: (m, l), then o.
+  const bool one_pass = ns <= 64 && ns * hpu <= kMergeCoef;
+  for (int hh = wave; hh < hpu; hh += kWavesM) {
+    if (one_pass) {
+      const bool on = lane < ns;
+      const float* ps = pb + (size_t)(on ? lane : 0) * slot_floats;
+      const float m = on ? ps[hh] : -INFINITY;
+      const float l = on ? ps[hpu + hh] : 0.f;
+      float mx = m;
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float w = on ? __builtin_amdgcn_exp2f(m - mx) : 0.f;
+      float L = l * w;
+      for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+      if (on) coef[lane * hpu + hh] = w / L;
+      if (lane == 0) lse[hh] = (mx + __log2f(L)) * kLn2;
+      continue;
+    }
+    float mx = -INFINITY;
+    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, pb[(size_t)s * slot_floats + hh]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float L = 0.f;
+    for (int s = lane; s < ns; s += 64) {
+      const float* ps = pb + (size_t)s * slot_floats;
+      L += ps[hpu + hh] * __builtin_amdgcn_exp2f(ps[hh] - mx);
+    }
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    if (lane == 0) {
+      ml[hh] = mx;
+      ml[hpu + hh] = 1.f / L;
+      lse[hh] = (mx + __log2f(L)) * kLn2;
+    }
+  }
+  __syncthreads();
+
+  const int EG = hpu * dv / 4;  // float4 groups of the output
+  const int chunk = kMergeCoef / hpu > 0 ? kMergeCoef / hpu : 1;
+  // small units: split the splits over TG thread groups and add through LDS
+  int TG = NT / EG;
+  TG = TG < 1 ? 1 : (TG > 8 ? 8 : TG);
+  const int EPT = NT / TG;      // threads per split group
+  const int q = tid / EPT, e = tid - (tid / EPT) * EPT;
+  f4 acc_small = {0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < ns; c0 += chunk) {
+    const int c1 = min(ns, c0 + chunk);
+    if (!one_pass) {
+      for (int i = tid; i < (c1 - c0) * hpu; i += NT) {
+        const int s = c0 + i / hpu, hh = i - (i / hpu) * hpu;
+        coef[i] = __builtin_amdgcn_exp2f(pb[(size_t)s * slot_floats + hh] - ml[hh]) * ml[hpu + hh];
+      }
+      __syncthreads();
+    }
+    if (TG > 1) {
+      if (q < TG && e < EG) {
+        const int hh = (4 * e) / dv, col = 4 * e - hh * dv;
+        const float* base = pb + partial_o_offset(hpu) + hh * dv + col;
+        for (int s = c0 + q; s < c1; s += kMergeInflight * TG) {
+          f4 v[kMergeInflight];
+          float cf[kMergeInflight];
+#pragma unroll
+          for (int u = 0; u < kMergeInflight; ++u) {
+            const int ss = s + u * TG;
+            const bool ok = ss < c1;
+            v[u] = ok ? *reinterpret_cast<const f4*>(base + (size_t)ss * slot_floats) : f4{0.f, 0.f, 0.f, 0.f};
+            cf[u] = ok ? coef[(ss - c0) * hpu + hh] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < kMergeInflight; ++u) acc_small += cf[u] * v[u];
+        }
+      }
+    } else {
+      for (int eg = tid; eg < EG; eg += NT) {
+        const int hh = (4 * eg) / dv, col = 4 * eg - hh * dv;
+        const float* base = pb + partial_o_offset(hpu) + hh * dv + col;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = c0; s < c1; s += kMergeInflight) {
+          f4 v[kMergeInflight];
+          float cf[kMergeInflight];
+#pragma unroll
+          for (int u = 0; u < kMergeInflight; ++u) {
+            const int ss = s + u;
+            const bool ok = ss < c1;
+            v[u] = ok ? *reinterpret_cast<const f4*>(base + (size_t)ss * slot_floats) : f4{0.f, 0.f, 0.f, 0.f};
+            cf[u] = ok ? coef[(ss - c0) * hpu + hh] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < kMergeInflight; ++u) acc += cf[u] * v[u];
+        }
+        f4* dst = reinterpret_cast<f4*>(out + hh * dv + col);
+        if (c0 > 0) acc += *dst;
+        *dst = acc;
+      }
+    }
+    __syncthreads();  // coefficients of this pass consumed
+  }
+  if (TG > 1) {
+    if (q < TG && e < EG) red[q * EPT + e] = acc_small;
+    __syncthreads();
+    if (q == 0 && e < EG) {
+      f4 acc = red[e];
+      for (int g = 1; g < TG; ++g) acc += red[g * EPT + e];
+      const int hh = (4 * e) / dv, col = 4 * e - hh * dv;
+      *reinterpret_cast<f4*>(out + hh * dv + col) = acc;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace cc

@@ -293,7 +293,8 @@ WorkspaceLayout workspace_layout(const PlanView& v) {
   L.counters_off = 256;  // the error word lives at offset 0
   L.partials_off = align(L.counters_off + sizeof(int32_t) * (size_t)v.units());
   const size_t hpu = (size_t)v.header[H_HPU];
-  L.slot_floats = (hpu * ((size_t)v.header[H_DV] + 2) + 63) & ~size_t(63);
+  const size_t o_off = (2 * hpu + 3) & ~size_t(3);  // o starts 16-byte aligned
+  L.slot_floats = (o_off + hpu * (size_t)v.header[H_DV] + 63) & ~size_t(63);
   L.total = align(L.partials_off + sizeof(float) * L.slot_floats * (size_t)v.partials());
   return L;
 }

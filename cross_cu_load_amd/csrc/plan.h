@@ -61,7 +61,7 @@ inline int64_t wg_words(int64_t workers) { return (workers + 1 + 3) & ~int64_t(3
 // Workspace layout of a plan: error word and counters first, then partials.
 struct WorkspaceLayout {
   size_t counters_off = 0;   // bytes; int32[U]
-  size_t partials_off = 0;   // bytes; float[S][hpu * (dv + 2)]
+  size_t partials_off = 0;   // bytes; S slots {m[hpu], l[hpu], pad to 4, o[hpu][dv]}
   size_t slot_floats = 0;    // floats per partial slot
   size_t total = 0;
 };

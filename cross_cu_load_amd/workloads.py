@@ -28,6 +28,8 @@ import numpy as np
 MODE_GQA = 0
 MODE_MLA = 1
 MODE_MLA_SPARSE = 2
+KV_NHD = 0   # pages [P][Hkv][d]: token-major
+KV_HND = 1   # pages [Hkv][P][d]: head-major
 
 _CHUNK = 1 << 22
 
@@ -57,6 +59,7 @@ class Config:
     topk: int = 0               # sparse: distinct indices per query token
     shuffle_pages: bool = True
     seed: int = 0
+    kv_layout: int = KV_NHD
 
     @property
     def group(self) -> int:
@@ -92,9 +95,13 @@ class Workload:
     seqlens: np.ndarray        # int32 [B]
     block_table: np.ndarray    # int32 [B, max_pages]; unused entries are -1
     q: np.ndarray              # uint16 [B, Tq, Hq, dk]
-    k_cache: np.ndarray        # uint16 [num_pages, P, Hkv, dk]  (MLA: the latent cache)
-    v_cache: np.ndarray | None  # uint16 [num_pages, P, Hkv, dv]; None for MLA
+    k_cache: np.ndarray        # uint16 [num_pages, P, Hkv, dk] (NHD) or [num_pages, Hkv, P, dk] (HND)
+    v_cache: np.ndarray | None  # uint16, as k_cache with dv; None for MLA
     indices: np.ndarray | None  # int32 [B, Tq, topk]; sparse mode only
+
+    @property
+    def kv_layout(self) -> int:
+        return self.cfg.kv_layout
 
     @property
     def num_pages(self) -> int:
@@ -206,6 +213,9 @@ def make_workload(cfg: Config, seqlens: np.ndarray | None = None) -> Workload:
     v = None
     if cfg.mode == MODE_GQA:
         v = normal_bf16(cfg.seed, _S_V, (num_pages, P, cfg.num_kv_heads, cfg.head_dim_v))
+    if cfg.kv_layout == KV_HND:   # same logical content, head-major pages
+        k = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+        v = None if v is None else np.ascontiguousarray(v.transpose(0, 2, 1, 3))
     idx = None
     if cfg.mode == MODE_MLA_SPARSE:
         idx = np.empty((cfg.batch, cfg.q_tokens, cfg.topk), dtype=np.int32)

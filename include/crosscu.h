@@ -56,6 +56,12 @@ enum {
  *              topk cache positions indices[b][t][0..topk).                    */
 enum { CC_MODE_GQA = 0, CC_MODE_MLA = 1, CC_MODE_MLA_SPARSE = 2 };
 
+/* Page layouts of the GQA K and V caches (MLA caches have one head: both are
+ * [num_pages][page_size][head_dim_qk]).
+ *  NHD: [num_pages][page_size][num_kv_heads][head_dim]  token-major pages
+ *  HND: [num_pages][num_kv_heads][page_size][head_dim]  head-major pages     */
+enum { CC_KV_NHD = 0, CC_KV_HND = 1 };
+
 /* How a plan divides the work.
  *  STREAMK:  the total tile count is cut into num_cus equal contiguous chunks
  *            (one per compute unit, one wave); a sequence may be split.
@@ -71,8 +77,9 @@ enum { CC_REDUCE_FUSED = 0, CC_REDUCE_SPLIT_COMBINE = 1 };
 
 /* Problem shape.  Layouts (row-major, innermost last):
  *   q            bf16  [batch][q_tokens][num_q_heads][head_dim_qk]
- *   k_cache      bf16  [num_pages][page_size][num_kv_heads][head_dim_qk]
- *   v_cache      bf16  [num_pages][page_size][num_kv_heads][head_dim_v] (GQA)
+ *   k_cache      bf16  [num_pages][page_size][num_kv_heads][head_dim_qk] (NHD)
+ *                   or [num_pages][num_kv_heads][page_size][head_dim_qk] (HND)
+ *   v_cache      bf16  as k_cache with head_dim_v (GQA only)
  *   block_table  int32 [batch][max_pages_per_seq]; token j of sequence b lives
  *                in page block_table[b][j / page_size], slot j % page_size
  *   seqlens      int32 [batch], each >= 1
@@ -92,6 +99,7 @@ typedef struct cc_problem {
   int32_t max_pages_per_seq;
   int32_t num_pages;
   int32_t topk;             /* MLA_SPARSE only, else 0 */
+  int32_t kv_layout;        /* CC_KV_NHD or CC_KV_HND */
   float softmax_scale;
 } cc_problem;
 

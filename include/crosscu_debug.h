@@ -1,0 +1,57 @@
+/*
+ * crosscu debug hooks: an in-kernel timeline of the persistent decode launch.
+ *
+ * With a timeline buffer set, every workgroup of a later cc_decode /
+ * cc_decode_variant launch on any stream records eight uint64 words at
+ * buf[8 * w .. 8 * w + 7], times on the constant 100 MHz clock
+ * (s_memrealtime):
+ *   [0] start,
+ *   [1] all its waves have finished streaming KV,
+ *   [2] its items shared by waves or split across workgroups are merged and
+ *       written (outputs, or partials for split units),
+ *   [3] its arrival counters are updated (equal to [2] without the in-kernel
+ *       merge),
+ *   [4] exit, after merging the units it completed,
+ *   [5] the id of the XCD (accelerator complex die) it ran on,
+ *   [6], [7] unused (0).
+ * Workgroups with no work record [0] == [1] == ... == [4].  From these the caller
+ * computes the busy fraction of the compute units over the launch and checks
+ * the workgroup-to-XCD placement the planner assumes (workgroup w on XCD
+ * w mod num_xcds).
+ */
+#ifndef CROSSCU_DEBUG_H
+#define CROSSCU_DEBUG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Sets (buf != NULL) or clears (buf == NULL) the timeline buffer for this
+ * process.  buf: device memory of `bytes` bytes; launches whose worker count
+ * exceeds bytes / 64 record nothing.  The library only writes to it from
+ * kernels; the caller owns it and must keep it alive while set.  Returns
+ * CC_OK. */
+int cc_debug_timeline(void* buf, size_t bytes);
+
+/* Streaming-read probe: reads `bytes` (a multiple of 16 KiB, >= 16 KiB) of
+ * device memory `buf` once with `workgroups` persistent workgroups of 512
+ * threads, asynchronously on `stream`, so the caller can time the practical
+ * HBM read ceiling of a load path.
+ *   method 0: 128-bit loads into registers, 8 per lane in flight;
+ *   method 1: 128-bit loads straight into LDS, one 16 KiB slot per wave;
+ *   method 2: the same into two 8 KiB slots per wave, one refilling while
+ *             the other is read.
+ * pages: optional device int32[num_pages], a read order of page_bytes-sized
+ * pages (page_bytes a multiple of 16 KiB); NULL reads contiguously.  sink:
+ * device uint32[workgroups * 512], written.  Returns CC_OK, CC_ERR_INVALID or
+ * CC_ERR_HIP. */
+int cc_probe_read(const void* buf, long long bytes, int method, const int32_t* pages, int page_bytes,
+                  int num_pages, int workgroups, void* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CROSSCU_DEBUG_H */

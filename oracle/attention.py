@@ -17,8 +17,9 @@ Readings of points the pages leave open
   index-sparse mode it sees exactly its own index set.
 * GQA head map: query head h reads KV head h // (Hq / Hkv) (contiguous groups).
 * MLA: one latent KV row of dk columns serves as K; its first dv columns are V.
-* Paged layout: cache[page, slot, kv_head, dim]; token j of sequence b is
-  page block_table[b, j // P], slot j % P.  Sparse indices are token
+* Paged layout: cache[page, slot, kv_head, dim] (token-major, "NHD") or
+  cache[page, kv_head, slot, dim] (head-major, "HND"); token j of sequence b
+  is page block_table[b, j // P], slot j % P.  Sparse indices are token
   positions within the request's cache.
 
 Everything runs in float64; bf16 inputs are widened exactly.  Every function
@@ -94,7 +95,7 @@ def lse_merge(parts) -> tuple[np.ndarray, np.ndarray]:
 def decode_attention(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray | None,
                      block_table: np.ndarray, seqlens: np.ndarray, scale: float,
                      head_dim_v: int | None = None, indices: np.ndarray | None = None,
-                     only: list[tuple[int, int, int]] | None = None):
+                     only: list[tuple[int, int, int]] | None = None, head_major: bool = False):
     """Reference decode attention.
 
     q_bits   uint16 [B, Tq, Hq, dk]
@@ -103,9 +104,13 @@ def decode_attention(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray 
              columns of the K rows (MLA)
     indices  int32 [B, Tq, topk] for index-sparse decode, else None
     only     optional list of (b, t, kv_head) units to compute; others stay NaN
+    head_major  caches are [pages, Hkv, P, d] instead of [pages, P, Hkv, d]
 
     Returns out float64 [B, Tq, Hq, dv] and lse float64 [B, Tq, Hq].
     """
+    if head_major:   # index the same elements through a token-major view
+        k_bits = k_bits.transpose(0, 2, 1, 3)
+        v_bits = None if v_bits is None else v_bits.transpose(0, 2, 1, 3)
     B, Tq, Hq, dk = q_bits.shape
     P, Hkv = k_bits.shape[1], k_bits.shape[2]
     G = Hq // Hkv
@@ -131,4 +136,5 @@ def decode_attention_wl(wl, only=None):
     """``decode_attention`` on a workload object from the seeded input generator."""
     c = wl.cfg
     return decode_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seqlens,
-                            c.softmax_scale, head_dim_v=c.head_dim_v, indices=wl.indices, only=only)
+                            c.softmax_scale, head_dim_v=c.head_dim_v, indices=wl.indices, only=only,
+                            head_major=wl.kv_layout == 1)

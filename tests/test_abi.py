@@ -15,13 +15,16 @@ from cross_cu_load_amd import binding as B
 from cross_cu_load_amd import workloads as W
 from oracle import planner as PL
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "crosscu.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(cc_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in os.listdir(INCLUDE):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(cc_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -53,8 +56,9 @@ def test_plan_bytes_match_reference_on_workload_lengths(lib, name, C, X, T, poli
     ref = PL.plan(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
                   cfg.head_dim_v, cfg.page_size, maxp, npages, cfg.topk, C, X, T, hu, sl, None, policy)
     assert blob.tobytes() == ref["blob"]
-    # workspace: 256 B error word area, counters, 256-aligned partial slots of hu*(dv+2) floats
-    slot = -(-hu * (cfg.head_dim_v + 2) // 64) * 64
+    # workspace: 256 B error word area, counters, 256-aligned partial slots of
+    # {m[hu], l[hu], pad to 4 floats, o[hu][dv]} rounded up to 64 floats
+    slot = -(-(-(-2 * hu // 4) * 4 + hu * cfg.head_dim_v) // 64) * 64
     cnt_end = 256 + 4 * ref["num_units"]
     part = -(-cnt_end // 256) * 256
     want = -(-(part + 4 * slot * ref["num_partials"]) // 256) * 256

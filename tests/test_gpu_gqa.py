@@ -7,6 +7,8 @@ the launch configuration the benchmark times (one chunk per compute unit,
 it finishes in seconds and a sample of units (always including split ones)
 otherwise.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -70,10 +72,12 @@ def test_tiny_gqa_config(dev):
     clean(s, plan)
 
 
+@pytest.mark.parametrize("layout", [W.KV_NHD, W.KV_HND])
 @pytest.mark.parametrize("name,batch,hi", [("llama3_8b_gqa", 8, 3000), ("skewed_gqa", 6, 5000),
                                            ("tiny_gqa", 3, 100)])
-def test_small_workloads_all_outputs(dev, name, batch, hi):
+def test_small_workloads_all_outputs(dev, name, batch, hi, layout):
     cfg = W.small_variant(W.CONFIG_BY_NAME[name], batch=batch, seqlen_hi=hi)
+    cfg = dataclasses.replace(cfg, kv_layout=layout)
     wl = W.make_workload(cfg)
     s, plan = run(wl, *dev, tag="small")
     compare(s, wl)
@@ -98,8 +102,9 @@ def test_ragged_and_single_token_sequences(dev):
             assert np.array_equal(out[b, 0, h], v)
 
 
-def test_skewed_full_size_all_outputs(dev):
-    wl = W.make_workload(W.CONFIG_BY_NAME["skewed_gqa"])
+@pytest.mark.parametrize("layout", [W.KV_NHD, W.KV_HND])
+def test_skewed_full_size_all_outputs(dev, layout):
+    wl = W.make_workload(dataclasses.replace(W.CONFIG_BY_NAME["skewed_gqa"], kv_layout=layout))
     s, plan = run(wl, *dev, tag="skewed-full")
     compare(s, wl)
     clean(s, plan)

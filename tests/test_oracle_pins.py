@@ -219,6 +219,21 @@ def test_page_placement_is_bitwise_irrelevant():
         assert np.array_equal(o, o2) and np.array_equal(s, s2)
 
 
+def test_head_major_pages_index_the_same_elements():
+    rng = np.random.default_rng(61)
+    lens = (29, 3, 64)
+    pr = rand_problem(rng, B=3, Hq=8, Hkv=2, lens=lens, P=16)
+    o, s = run(pr)
+    kh = np.ascontiguousarray(pr["kc"].transpose(0, 2, 1, 3))
+    vh = np.ascontiguousarray(pr["vc"].transpose(0, 2, 1, 3))
+    o2, s2 = A.decode_attention(pr["q"], kh, vh, pr["bt"], pr["lens"], pr["scale"], head_major=True)
+    assert np.array_equal(o, o2) and np.array_equal(s, s2)
+    # and a head-major cache read as token-major gives something else
+    o3, _ = A.decode_attention(pr["q"], kh.reshape(pr["kc"].shape), vh.reshape(pr["vc"].shape), pr["bt"],
+                               pr["lens"], pr["scale"])
+    assert not np.allclose(o3, o)
+
+
 def test_gqa_equals_mha_with_repeated_kv():
     rng = np.random.default_rng(31)
     lens = (12, 5)
