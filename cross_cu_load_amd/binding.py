@@ -119,12 +119,19 @@ def device_query(device: int = 0) -> tuple[int, int]:
     return cus.value, xcds.value
 
 
+def kernel_heads_per_unit(prob: Problem) -> int:
+    """heads_per_unit that cc_decode's kernel for this mode accepts."""
+    if prob.mode == MODE_GQA:
+        return prob.num_q_heads // prob.num_kv_heads
+    return 64
+
+
 def plan(prob: Problem, seqlens, block_table=None, num_cus=256, num_xcds=8, tile_tokens=32,
          heads_per_unit=None, policy=POLICY_STREAMK) -> np.ndarray:
     """Host plan blob (uint8 array) from cc_plan_size + cc_plan."""
     lib = load()
     if heads_per_unit is None:
-        heads_per_unit = prob.num_q_heads // prob.num_kv_heads
+        heads_per_unit = kernel_heads_per_unit(prob)
     opts = PlanOpts(num_cus, num_xcds, tile_tokens, heads_per_unit, policy)
     sl = _i32(seqlens)
     if sl.shape != (prob.batch,):

@@ -52,6 +52,29 @@ int check_gqa(const cc_problem& p, const cc::PlanView& v) {
   return CC_OK;
 }
 
+// Shapes the MLA kernels implement (dense and index-sparse).
+int check_mla(const cc_problem& p, const cc::PlanView& v) {
+  if (p.num_kv_heads != 1 || p.num_q_heads != 128 || p.head_dim_qk != 576 || p.head_dim_v != 512) {
+    cc::set_error("MLA kernel: 128 query heads over one 576-wide latent head with dv 512 "
+                  "(got Hq %d, Hkv %d, dk %d, dv %d)", p.num_q_heads, p.num_kv_heads, p.head_dim_qk,
+                  p.head_dim_v);
+    return CC_ERR_UNSUPPORTED;
+  }
+  if (v.header[cc::H_HPU] != 64) {
+    cc::set_error("MLA kernel: heads_per_unit must be 64 (two head blocks per query token)");
+    return CC_ERR_UNSUPPORTED;
+  }
+  if (!is_pow2(p.page_size) || (p.mode == CC_MODE_MLA && p.page_size < 32)) {
+    cc::set_error("MLA kernel: page_size must be a power of two (>= 32 for dense MLA), got %d", p.page_size);
+    return CC_ERR_UNSUPPORTED;
+  }
+  if (v.header[cc::H_TILE] % 32) {
+    cc::set_error("MLA kernel: tile_tokens must be a multiple of 32 (got %d)", v.header[cc::H_TILE]);
+    return CC_ERR_UNSUPPORTED;
+  }
+  return CC_OK;
+}
+
 int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const void* plan_dev,
                 const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                 const int32_t* seqlens, const int32_t* indices, float* out, float* lse,
@@ -92,8 +115,12 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
     rc = check_gqa(p, v);
     if (rc) return rc;
   } else {
-    cc::set_error("mode %d is not implemented by this build", p.mode);
-    return CC_ERR_UNSUPPORTED;
+    if (p.mode == CC_MODE_MLA_SPARSE && !indices) {
+      cc::set_error("index-sparse MLA needs indices");
+      return CC_ERR_INVALID;
+    }
+    rc = check_mla(p, v);
+    if (rc) return rc;
   }
 
   const int32_t* pd = static_cast<const int32_t*>(plan_dev);
@@ -137,7 +164,7 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
                    ? static_cast<unsigned long long*>(g_timeline)
                    : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = cc::launch_gqa(a, s);
+  hipError_t e = p.mode == CC_MODE_GQA ? cc::launch_gqa(a, s) : cc::launch_mla(a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (reduce == CC_REDUCE_SPLIT_COMBINE && v.partials() > 0) {
     e = cc::launch_combine(a, s);

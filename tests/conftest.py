@@ -20,3 +20,14 @@ def lib():
         import __graft_entry__
         __graft_entry__.build()
     return binding.load()
+
+
+@pytest.fixture(scope="session")
+def dev(lib):
+    """(compute units, XCDs) of cuda:0; skips when no GPU is visible."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    torch.cuda.set_device(0)
+    from cross_cu_load_amd import binding
+    return binding.device_query(0)

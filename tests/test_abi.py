@@ -51,18 +51,18 @@ def test_plan_bytes_match_reference_on_workload_lengths(lib, name, C, X, T, poli
     cfg = W.CONFIG_BY_NAME[name]
     sl = W.draw_seqlens(cfg)
     prob, maxp, npages = _prob(cfg, sl)
-    hu = cfg.group if cfg.mode == W.MODE_GQA else 128
-    blob = B.plan(prob, sl, None, num_cus=C, num_xcds=X, tile_tokens=T, heads_per_unit=hu, policy=policy)
-    ref = PL.plan(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
-                  cfg.head_dim_v, cfg.page_size, maxp, npages, cfg.topk, C, X, T, hu, sl, None, policy)
-    assert blob.tobytes() == ref["blob"]
-    # workspace: 256 B error word area, counters, 256-aligned partial slots of
-    # {m[hu], l[hu], pad to 4 floats, o[hu][dv]} rounded up to 64 floats
-    slot = -(-(-(-2 * hu // 4) * 4 + hu * cfg.head_dim_v) // 64) * 64
-    cnt_end = 256 + 4 * ref["num_units"]
-    part = -(-cnt_end // 256) * 256
-    want = -(-(part + 4 * slot * ref["num_partials"]) // 256) * 256
-    assert B.workspace_size(blob) == want
+    for hu in ([cfg.group] if cfg.mode == W.MODE_GQA else [64, 128]):
+        blob = B.plan(prob, sl, None, num_cus=C, num_xcds=X, tile_tokens=T, heads_per_unit=hu, policy=policy)
+        ref = PL.plan(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
+                      cfg.head_dim_v, cfg.page_size, maxp, npages, cfg.topk, C, X, T, hu, sl, None, policy)
+        assert blob.tobytes() == ref["blob"]
+        # workspace: 256 B error word area, counters, 256-aligned partial slots of
+        # {m[hu], l[hu], pad to 4 floats, o[hu][dv]} rounded up to 64 floats
+        slot = -(-(-(-2 * hu // 4) * 4 + hu * cfg.head_dim_v) // 64) * 64
+        cnt_end = 256 + 4 * ref["num_units"]
+        part = -(-cnt_end // 256) * 256
+        want = -(-(part + 4 * slot * ref["num_partials"]) // 256) * 256
+        assert B.workspace_size(blob) == want
 
 
 @pytest.mark.parametrize("seed", range(40))
@@ -178,3 +178,25 @@ def test_decode_rejects_before_any_launch(lib):
     blob2 = B.plan(odd, sl, None, num_cus=8, num_xcds=1, tile_tokens=32, heads_per_unit=4)
     assert lib.cc_decode(ctypes.byref(odd), blob2.ctypes.data_as(ctypes.c_void_p), fake, fake, fake, fake, fake,
                          fake, None, fake, fake, fake, B.workspace_size(blob2), None) == B.CC_ERR_UNSUPPORTED
+
+
+def test_mla_decode_rejects_before_any_launch(lib):
+    """MLA shape, heads_per_unit, page, tile and indices checks fail on the host."""
+    kw = dict(mode=B.MODE_MLA, batch=2, q_tokens=1, num_q_heads=128, num_kv_heads=1, head_dim_qk=576,
+              head_dim_v=512, page_size=64, max_pages_per_seq=2, num_pages=4, topk=0, softmax_scale=0.07)
+    sl = np.array([100, 20], np.int32)
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails a host check first
+
+    def call(p, hu=64, tile=32, indices=None):
+        blob = B.plan(p, sl, None, num_cus=8, num_xcds=1, tile_tokens=tile, heads_per_unit=hu)
+        return lib.cc_decode(ctypes.byref(p), blob.ctypes.data_as(ctypes.c_void_p), fake, fake, fake, None, fake,
+                             fake, indices, fake, fake, fake, B.workspace_size(blob), None)
+
+    prob = B.problem(**kw)
+    assert call(prob, hu=128) == B.CC_ERR_UNSUPPORTED
+    assert call(prob, tile=48) == B.CC_ERR_UNSUPPORTED
+    assert call(B.problem(**{**kw, "page_size": 16, "max_pages_per_seq": 7, "num_pages": 9})) == B.CC_ERR_UNSUPPORTED
+    assert call(B.problem(**{**kw, "head_dim_v": 448})) == B.CC_ERR_UNSUPPORTED
+    sparse = B.problem(**{**kw, "mode": B.MODE_MLA_SPARSE, "topk": 16})
+    assert call(sparse) == B.CC_ERR_INVALID          # no indices
+    assert B.kernel_heads_per_unit(prob) == 64 and B.kernel_heads_per_unit(sparse) == 64

@@ -16,53 +16,10 @@ from cross_cu_load_amd import binding as B
 from cross_cu_load_amd import workloads as W
 from oracle import attention as A
 
+from gpu_helpers import clean, compare, run
+
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
-
-TOL_OUT, TOL_LSE = 1e-2, 1e-3
-
-
-@pytest.fixture(scope="module")
-def dev(lib):
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU visible")
-    torch.cuda.set_device(0)
-    return B.device_query(0)
-
-
-def run(wl, cus, xcds, tile=32, policy=B.POLICY_STREAMK, reduce=B.REDUCE_FUSED, tag=""):
-    print(f"[gpu] {tag} cfg={wl.cfg.name} B={wl.cfg.batch} C={cus} X={xcds} T={tile} policy={policy} "
-          f"reduce={reduce}", flush=True)
-    plan = B.plan(B.problem_for(wl), wl.seqlens, wl.block_table, num_cus=cus, num_xcds=xcds,
-                  tile_tokens=tile, policy=policy)
-    s = B.session(wl, plan)
-    s.run(reduce)
-    torch.cuda.synchronize()
-    return s, plan
-
-
-def compare(s, wl, only=None):
-    ref_o, ref_l = A.decode_attention_wl(wl, only=only)
-    out = s.out.cpu().numpy().astype(np.float64)
-    lse = s.lse.cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
-    if only is not None:
-        G = wl.cfg.group
-        mask = np.zeros(lse.shape, bool)
-        for (b, t, g) in only:
-            mask[b, t, g * G:(g + 1) * G] = True
-        out, ref_o = out[mask], ref_o[mask]
-        lse, ref_l = lse[mask], ref_l[mask]
-    do = float(np.max(np.abs(out - ref_o)))
-    dl = float(np.max(np.abs(lse - ref_l)))
-    print(f"       max|dout|={do:.3e} max|dlse|={dl:.3e}", flush=True)
-    assert do <= TOL_OUT and dl <= TOL_LSE
-    return do, dl
-
-
-def clean(s, plan):
-    dirty, flags = B.workspace_check(plan, s.workspace)
-    assert dirty == 0 and flags == 0
 
 
 def test_tiny_gqa_config(dev):
