@@ -33,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+METRIC = "decode-attn KV GB/s & fraction of 8 TB/s HBM peak; \u00b5s/batch on skewed varlen"
 
 
 def parse():
@@ -108,23 +110,43 @@ def timeline_pass(torch, B, s, workers, xcds, flush):
             "xcd_ids_seen": sorted(set(int(x) for x in xcc))}
 
 
-def profiled_traffic(workload, layout):
+KERNEL_SOURCES = {"gqa_decode_kernel": ("decode_gqa.hip", "merge.h", "launch.h"),
+                  "mla_decode_kernel": ("decode_mla.hip", "merge.h", "launch.h")}
+
+
+def kernel_name(mode):
+    return "gqa_decode_kernel" if mode == 0 else "mla_decode_kernel"
+
+
+def source_hash(kernel):
+    """sha256[:16] of the sources the decode kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, "cross_cu_load_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel, workload, layout):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if the
     decode kernel's sources are unchanged since it was taken (else None)."""
-    import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", f"gqa_decode_kernel_{workload}_{layout}.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_{layout}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    h = hashlib.sha256()
-    for f in ("decode_gqa.hip", "merge.h", "launch.h"):
-        h.update(open(os.path.join(ROOT, "cross_cu_load_amd", "csrc", f), "rb").read())
     m_src = re.search(r"source_sha256_16: (\w+)", text)
     m_tr = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    if not m_src or not m_tr or m_src.group(1) != h.hexdigest()[:16]:
+    if not m_src or not m_tr or m_src.group(1) != source_hash(kernel):
         return None
     return int(m_tr.group(1))
+
+
+def mfma_flops(wl):
+    """Dense contraction flops of one decode: 2 (dk + dv) per (query head, key)."""
+    c = wl.cfg
+    keys = c.topk * c.q_tokens * c.batch if wl.indices is not None else int(wl.seqlens.sum()) * c.q_tokens
+    return 2.0 * (c.head_dim_qk + c.head_dim_v) * c.num_q_heads * keys
 
 
 def cpu_baseline(wl, args):
@@ -221,8 +243,9 @@ def main():
 
     mean_s = st["mean_us"] * 1e-6
     gbs = kv / mean_s / 1e9
+    layout_name = args.layout if cfg.mode == W.MODE_GQA else "latent"
     result = {
-        "metric": "decode-attn KV GB/s & fraction of 8 TB/s HBM peak; us/batch on skewed varlen",
+        "metric": METRIC,
         "value": gbs,
         "unit": "GB/s",
         "n_gpus": 1,
@@ -238,7 +261,7 @@ def main():
                    "seqlen_max": int(wl.seqlens.max()), "num_q_heads": cfg.num_q_heads,
                    "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim_qk, "page_size": cfg.page_size,
                    "num_cus": cus, "num_xcds": xcds, "tile_tokens": 32, "kv_bytes": kv,
-                   "kv_layout": args.layout if cfg.mode == W.MODE_GQA else "latent"},
+                   "kv_layout": layout_name},
         "us_per_batch": st["mean_us"],
         "us_per_batch_median": st["median_us"],
         "us_p10_p90": [st["p10_us"], st["p90_us"]],
@@ -248,7 +271,10 @@ def main():
         "frac_of_read_probe": gbs / probe_gbs,
         "plan_host_us": plan_us,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": profiled_traffic(cfg.name, args.layout)},
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic(kernel_name(cfg.mode), cfg.name, layout_name)},
+        "mfma_tflops": mfma_flops(wl) / mean_s / 1e12,
+        "mfma_frac_of_bf16_dense_peak": mfma_flops(wl) / mean_s / 1e12 / BF16_DENSE_PEAK_TFLOPS,
         "variants": variants,
         "timeline": tline,
     }
