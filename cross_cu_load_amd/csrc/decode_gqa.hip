@@ -67,12 +67,25 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // addresses built from it use the scalar-base load forms.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Asynchronous copy global -> LDS: each lane's `bytes` land at lds + lane * bytes.
-__device__ __forceinline__ void lds_dma16(const char* src, char* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds, 16, 0, 0);
+// Asynchronous copy global -> LDS: lane i's bytes from sbase + voff land at
+// lds + i * bytes (sbase and lds wave-uniform, voff per lane).  Inline asm on
+// purpose: the compiler's own wait insertion cannot tell the stream slots from
+// the merge slots that reuse them and would put a full vmcnt wait (which also
+// waits for every output store in flight) before each LDS read; the kernel
+// waits for its transfers explicitly.  M0 carries the LDS address (the
+// compiler uses M0 nowhere else in this kernel); one wait state separates its
+// write from the transfer.  The KV cache is read once per decode, so the
+// transfers carry the non-temporal cache policy (nt): on MI355X a streaming
+// read of this kind reaches ~6.7 TB/s with it and ~5.7 TB/s without.
+__device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, char* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_ptr)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_dma4(const char* src, char* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds, 4, 0, 0);
+__device__ __forceinline__ void lds_dma4(const char* sbase, uint32_t voff, char* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_ptr)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 nt"
+               :: "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
 }
 
 // Id of the XCD this wave runs on (hardware register XCC_ID, low 4 bits).
@@ -156,8 +169,15 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   extern __shared__ __attribute__((aligned(16))) char smem[];  // kWaves regions
   __shared__ int slot_item[2 * kWaves];
   __shared__ int slot_meta[2 * kWaves][4];  // unit, split, nsplit, pbase of the slot's item
-  __shared__ int last_of[2 * kWaves];       // per first-slot: this workgroup merges the unit
-  __shared__ __attribute__((aligned(16))) float merge_lds[merge_lds_floats(kThreads, 16)];
+  __shared__ int done_units[2 * kWaves][3];  // units this workgroup completes: {pbase, nsplit, out row}
+  __shared__ float slot_w[2 * kWaves][16];    // phase-1 weight of each merge slot, per head
+  __shared__ float item_L[2 * kWaves][16];    // phase-1 sum L of each item, per head
+  __shared__ int it_slot[2 * kWaves];         // phase-1 items: first slot,
+  __shared__ unsigned it_mask[2 * kWaves];    // the slots holding it,
+  __shared__ int num_items;                   // and how many
+  __shared__ int split_list[2 * kWaves][3];   // split items: unit, nsplit, first partial slot
+  __shared__ int num_split;
+  __shared__ int num_done;
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63;
@@ -261,18 +281,18 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     // K: lane takes token lr of each half, dims 32*ks + 8*lg .. +8
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      lds_dma16(S.k0 + koff + ks * 64, region + ks * 1024);
-      lds_dma16(S.k1 + koff + ks * 64, region + (KS + ks) * 1024);
+      lds_dma16(S.k0 + ks * 64, koff, region + ks * 1024);
+      lds_dma16(S.k1 + ks * 64, koff, region + (KS + ks) * 1024);
     }
     // V: lane takes tokens tau(lg, i) = 4lg+i (i<4), 16+4lg+(i-4) (i>=4), dims W*lr .. +W
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const char* src = (i < 4 ? S.v0 : S.v1) + voff[i & 3];
+      const char* base = i < 4 ? S.v0 : S.v1;
       if constexpr (GE::vDmaBytes == 16) {
-        lds_dma16(src, region + GE::kBytes + i * 1024);
+        lds_dma16(base, voff[i & 3], region + GE::kBytes + i * 1024);
       } else {
-        lds_dma4(src, region + GE::kBytes + (2 * i) * 256);
-        lds_dma4(src + 4, region + GE::kBytes + (2 * i + 1) * 256);
+        lds_dma4(base, voff[i & 3], region + GE::kBytes + (2 * i) * 256);
+        lds_dma4(base + 4, voff[i & 3], region + GE::kBytes + (2 * i + 1) * 256);
       }
     }
   };
@@ -490,91 +510,124 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
 
   // ------------------------------------------------ workgroup-level merges
   // Phase 1: every item the waves left in LDS is merged over its waves and
-  // written out (whole unit) or handed on as this piece's partial.
-  if (tid < 2 * kWaves) last_of[tid] = 0;
-  int sit[2 * kWaves];  // slot -> item, held in registers for the whole phase
+  // written out (whole unit) or handed on as this piece's partial.  All items
+  // at once: (a) one thread per (item, head) takes the max over the item's
+  // slots, the sum L and each slot's weight exp2(m - M); (b) after a barrier a
+  // flat loop over (item, element) adds the weighted outputs in slot (token)
+  // order.  Only the slots that hold an item are read.
+  if (tid == 0) {
+    // distinct items in slot order (first slot, slots holding it), and the
+    // split ones among them (unit, nsplit, first partial slot), from one read
+    // of the slot table into registers
+    int si[2 * kWaves];
 #pragma unroll
-  for (int t = 0; t < 2 * kWaves; ++t) sit[t] = uni(slot_item[t]);
-  for (int sl = 0; sl < 2 * kWaves; ++sl) {
-    const int it = sit[sl];
-    if (it < 0) continue;
-    unsigned mask = 0;  // slots holding this item (the first is sl)
+    for (int t = 0; t < 2 * kWaves; ++t) si[t] = slot_item[t];
+    int n = 0, nsp = 0;
 #pragma unroll
-    for (int t = 0; t < 2 * kWaves; ++t) mask |= (unsigned)(sit[t] == it) << t;
-    if (mask & ((1u << sl) - 1)) continue;  // merged at its first slot
-    const int unit = uni(slot_meta[sl][0]), split = uni(slot_meta[sl][1]), ns = uni(slot_meta[sl][2]);
-    const int b = unit / p.hkv, g = unit - (unit / p.hkv) * p.hkv;
-    float* pslot = ns > 1 ? partials + (size_t)(uni(slot_meta[sl][3]) + split) * p.slot_floats : nullptr;
-    for (int el = tid; el < G * D; el += kThreads) {
-      const int hh = el / D, cc = el - (el / D) * D;
-      float mt[2 * kWaves], lt[2 * kWaves], ot[2 * kWaves];
+    for (int sl = 0; sl < 2 * kWaves; ++sl) {
+      unsigned mask = 0;
+      bool before = false;
 #pragma unroll
-      for (int t = 0; t < 2 * kWaves; ++t) {  // every load issued before any is used
-        const float* sb = merge_slot(t);
-        const bool on = (mask >> t) & 1;
-        mt[t] = on ? sb[hh] : -INFINITY;
-        lt[t] = on ? sb[G + hh] : 0.f;
-        ot[t] = on ? sb[2 * G + hh * D + cc] : 0.f;
+      for (int t = 0; t < 2 * kWaves; ++t) {
+        mask |= (unsigned)(si[t] == si[sl]) << t;
+        before |= t < sl && si[t] == si[sl];
       }
-      float M = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2 * kWaves; ++t) M = fmaxf(M, mt[t]);
-      float L = 0.f, O = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2 * kWaves; ++t) {  // slot order = token order
-        const float f = fast_exp2(mt[t] - M);
-        L += lt[t] * f;
-        O += ot[t] * f;
-      }
-      const size_t orow = (size_t)b * p.hq + (size_t)g * G + hh;
-      if (ns == 1) {
-        out[orow * D + cc] = O / L;
-        if (cc == 0) lse[orow] = (M + __log2f(L)) * kLn2;
-      } else {
-        if (cc == 0) {
-          pslot[hh] = M;
-          pslot[G + hh] = L;
+      if (si[sl] >= 0 && !before) {
+        it_slot[n] = sl;
+        it_mask[n] = mask;
+        ++n;
+        const int ns = slot_meta[sl][2];
+        if (ns > 1) {
+          split_list[nsp][0] = slot_meta[sl][0];
+          split_list[nsp][1] = ns;
+          split_list[nsp][2] = slot_meta[sl][3];
+          ++nsp;
         }
-        pslot[partial_o_offset(G) + hh * D + cc] = O;
       }
+    }
+    num_items = n;
+    num_split = nsp;
+  }
+  __syncthreads();
+  const int nit = uni(num_items);
+  const int GD = G * D;
+  if (tid < nit * G) {
+    const int ii = tid / G, hh = tid - (tid / G) * G;
+    const unsigned mask = it_mask[ii];
+    const int sl0 = it_slot[ii];
+    float M = -INFINITY;
+    for (unsigned mm = mask; mm; mm &= mm - 1) M = fmaxf(M, merge_slot(__builtin_ctz(mm))[hh]);
+    float L = 0.f;
+    for (unsigned mm = mask; mm; mm &= mm - 1) {
+      const int t = __builtin_ctz(mm);
+      const float* sb = merge_slot(t);
+      const float f = fast_exp2(sb[hh] - M);
+      L += sb[G + hh] * f;
+      slot_w[t][hh] = f;
+    }
+    item_L[ii][hh] = L;
+    const int unit = slot_meta[sl0][0], split = slot_meta[sl0][1], ns = slot_meta[sl0][2];
+    if (ns == 1) {
+      lse[(size_t)unit * G + hh] = (M + __log2f(L)) * kLn2;  // row of unit (b, g): b Hq + g G = unit G
+    } else {
+      float* pslot = partials + (size_t)(slot_meta[sl0][3] + split) * p.slot_floats;
+      partial_store(pslot + hh, M);
+      partial_store(pslot + G + hh, L);
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nit * GD; idx += kThreads) {
+    const int ii = uni(idx / GD);  // G * D is a multiple of 64: one item per wave and pass
+    const int e = idx - ii * GD, hh = e / D;
+    const unsigned mask = uni(it_mask[ii]);
+    const int sl0 = uni(it_slot[ii]);
+    float O = 0.f;
+    for (unsigned mm = mask; mm; mm &= mm - 1) {
+      const int t = __builtin_ctz(mm);
+      O += merge_slot(t)[2 * G + e] * slot_w[t][hh];
+    }
+    const int unit = uni(slot_meta[sl0][0]), split = uni(slot_meta[sl0][1]), ns = uni(slot_meta[sl0][2]);
+    if (ns == 1) {
+      out[(size_t)unit * GD + e] = O / item_L[ii][hh];
+    } else {
+      partial_store(partials + (size_t)(uni(slot_meta[sl0][3]) + split) * p.slot_floats + partial_o_offset(G) + e, O);
     }
   }
   if (tl && tid == 0) tl[2] = __builtin_amdgcn_s_memrealtime();
   if (p.reduce == CC_REDUCE_FUSED) {
-    // Phase 2: one release for all of this workgroup's partials, then one
-    // arrival per split item; the piece that completes a unit merges it.
+    // Phase 2: every wave's partial stores are complete (device-coherent, see
+    // partial_store), then one arrival per split item; the piece that
+    // completes a unit merges it and resets its counter (every other piece has
+    // arrived).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
-      bool any_split = false;
-      for (int sl = 0; sl < 2 * kWaves; ++sl) any_split |= slot_item[sl] >= 0 && slot_meta[sl][2] > 1;
-      if (any_split) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // publish the partials device-wide
-        bool any_last = false;
-        for (int sl = 0; sl < 2 * kWaves; ++sl) {
-          const int it = slot_item[sl];
-          if (it < 0 || slot_meta[sl][2] <= 1) continue;
-          bool seen = false;
-          for (int t = 0; t < sl; ++t) seen |= slot_item[t] == it;
-          if (seen) continue;
-          const int old = atomicAdd(&counters[slot_meta[sl][0]], 1);
-          last_of[sl] = old == slot_meta[sl][2] - 1;
-          any_last |= last_of[sl] != 0;
+      const int nsp = num_split;
+      int nd = 0;
+      if (nsp > 0) {
+        int old[2 * kWaves];
+#pragma unroll
+        for (int k = 0; k < 2 * kWaves; ++k)  // all arrivals in flight together
+          old[k] = k < nsp ? atomicAdd(&counters[split_list[k][0]], 1) : 0;
+#pragma unroll
+        for (int k = 0; k < 2 * kWaves; ++k) {
+          if (k < nsp && old[k] == split_list[k][1] - 1) {
+            const int unit = split_list[k][0];
+            __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            done_units[nd][0] = split_list[k][2];
+            done_units[nd][1] = split_list[k][1];
+            done_units[nd][2] = unit * G;  // output row of unit (b, g): b Hq + g G
+            ++nd;
+          }
         }
-        if (any_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other pieces' partials
       }
+      num_done = nd;
     }
     __syncthreads();
     if (tl && tid == 0) tl[3] = __builtin_amdgcn_s_memrealtime();
-    // Phase 3: merges of the units this workgroup completed
-    for (int sl = 0; sl < 2 * kWaves; ++sl) {
-      if (!uni(last_of[sl])) continue;
-      const int unit = uni(slot_meta[sl][0]), ns = uni(slot_meta[sl][2]);
-      const int b = unit / p.hkv, g = unit - (unit / p.hkv) * p.hkv;
-      const size_t orow = (size_t)b * p.hq + (size_t)g * G;
-      merge_splits<kThreads>(partials + (size_t)uni(slot_meta[sl][3]) * p.slot_floats, ns, p.slot_floats, G, D,
-                             out + orow * D, lse + orow, merge_lds);
-      if (tid == 0) __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // Phase 3: the units this workgroup completed, merged together
+    const int nd = uni(num_done);
+    if (nd > 0) merge_units_direct<kThreads>(partials, done_units, nd, p.slot_floats, G, D, out, lse);
   }
   if (tl && tid == 0) {
     if (p.reduce != CC_REDUCE_FUSED) tl[3] = tl[2];

@@ -105,10 +105,12 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // would wait for every transfer in flight before any LDS read; the kernel
 // orders the ring itself with explicit vmcnt waits and barriers.  M0 carries
 // the LDS address (the compiler uses M0 nowhere else in these kernels); one
-// wait state separates its write from the transfer.
+// wait state separates its write from the transfer.  The transfers carry the
+// non-temporal cache policy (nt): a streaming read reaches ~6.7 TB/s with it
+// and ~5.7 TB/s without on MI355X.
 __device__ __forceinline__ void lds_dma16(const char* src, char* lds) {
   const uint32_t m0 = uni((int)(uint32_t)(uintptr_t)(lds_ptr)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :: "v"(src), "s"(m0) : "memory", "m0");
 }
 __device__ __forceinline__ unsigned xcc_id() {

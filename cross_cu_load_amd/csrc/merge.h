@@ -23,6 +23,21 @@ namespace cc {
 constexpr int kMergeCoef = 2048;  // split coefficients held in LDS per pass
 constexpr int kMergeInflight = 8; // o_s loads in flight per thread
 
+// Partials cross compute units (and XCDs, whose L2 caches are not coherent
+// with each other) inside one launch.  They are written and read as relaxed
+// agent-scope atomics: those accesses carry the device-scope cache policy and
+// are coherent across the XCDs by themselves, so neither the writer nor the
+// reader has to write back or invalidate a whole L2 (what an agent-scope
+// release/acquire fence does for ordinary data).  The writer makes the stores
+// complete (s_waitcnt vmcnt(0)) before its arrival on the unit's counter; the
+// reader issues its loads after observing the last arrival.
+__device__ __forceinline__ void partial_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float partial_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Offset (floats) of o inside a partial slot.
 __host__ __device__ constexpr int partial_o_offset(int hpu) { return (2 * hpu + 3) & ~3; }
 
@@ -154,6 +169,60 @@ __device__ void merge_splits(const float* pb, int ns, int slot_floats, int hpu, 
       *reinterpret_cast<f4*>(out + hh * dv + col) = acc;
     }
     __syncthreads();
+  }
+}
+
+// Single-round merge for units whose output fits the workgroup (hpu * dv <=
+// NT elements per unit, nu units at once): thread e owns output element e of
+// every unit it covers and issues the loads of m, l and o of 32 splits at a
+// time before using any of them, combining the chunks online (in split order,
+// so the result does not depend on which piece arrived last).  On the tail of
+// a decode this halves the memory round trips of merge_splits' two-phase form.
+// units[i] = {partial base slot, nsplit, output row}; out/lse rows are
+// dv / 1 floats apart.
+constexpr int kDirectChunk = 32;
+template <int NT>
+__device__ __forceinline__ void merge_units_direct(const float* partials, const int (*units)[3], int nu, int slot_floats, int hpu,
+                                   int dv, float* out, float* lse) {
+  constexpr float kLn2 = 0.69314718055994531f;
+  const int E = hpu * dv;
+  const int o_off = partial_o_offset(hpu);
+  for (int u = 0; u < nu; ++u) {
+    // unit fields are the same for every thread: split bases stay scalar
+    const int ns = __builtin_amdgcn_readfirstlane(units[u][1]);
+    const float* pb = partials + (size_t)__builtin_amdgcn_readfirstlane(units[u][0]) * slot_floats;
+    const size_t row0 = (size_t)__builtin_amdgcn_readfirstlane(units[u][2]);
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int hh = e / dv, col = e - (e / dv) * dv;
+      float M = -INFINITY, L = 0.f, O = 0.f;
+      for (int s0 = 0; s0 < ns; s0 += kDirectChunk) {
+        float mt[kDirectChunk], lt[kDirectChunk], ot[kDirectChunk];
+#pragma unroll
+        for (int i = 0; i < kDirectChunk; ++i) {
+          const bool ok = s0 + i < ns;
+          const float* ps = pb + (size_t)(ok ? s0 + i : 0) * slot_floats;
+          mt[i] = ok ? partial_load(ps + hh) : -INFINITY;
+          lt[i] = ok ? partial_load(ps + hpu + hh) : 0.f;
+          ot[i] = ok ? partial_load(ps + o_off + e) : 0.f;
+        }
+        float Mc = M;
+#pragma unroll
+        for (int i = 0; i < kDirectChunk; ++i) Mc = fmaxf(Mc, mt[i]);
+        const float a = __builtin_amdgcn_exp2f(M - Mc);  // 0 on the first chunk (M = -inf, Mc finite)
+        L *= a;
+        O *= a;
+#pragma unroll
+        for (int i = 0; i < kDirectChunk; ++i) {
+          const float f = __builtin_amdgcn_exp2f(mt[i] - Mc);
+          L += lt[i] * f;
+          O += ot[i] * f;
+        }
+        M = Mc;
+      }
+      const size_t row = row0 + hh;
+      out[row * dv + col] = O / L;
+      if (col == 0) lse[row] = (M + __log2f(L)) * kLn2;
+    }
   }
 }
 

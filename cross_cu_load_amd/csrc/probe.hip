@@ -21,13 +21,20 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kThreads = 512;
 constexpr int kUnroll = 8;  // 16-byte loads in flight per lane (register path)
 
+template <bool NT>
 __device__ __forceinline__ void lds_dma16(const char* src, char* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr)lds, 16, 0, NT ? 2 : 0);  // policy 2: nt
+}
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const char* p) {
+  return NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)) : *reinterpret_cast<const u32x4*>(p);
 }
 
 // method 0: global_load_dwordx4 into registers, kUnroll per lane in flight.
 // method 1: global_load_lds_dwordx4 into one 16 KiB LDS slot per wave.
 // method 2: global_load_lds_dwordx4 into two 8 KiB LDS slots per wave (ping-pong).
+// methods 3 and 4: methods 0 and 2 with the non-temporal cache policy (nt).
+template <bool NT>
 __global__ void __launch_bounds__(kThreads, 1)
 read_probe(const char* __restrict__ buf, long long bytes, int method, const int* __restrict__ pages,
            int page_bytes, int num_pages, uint32_t* __restrict__ sink) {
@@ -56,7 +63,7 @@ read_probe(const char* __restrict__ buf, long long bytes, int method, const int*
       const char* p = src_of(st) + lane * 16;
       u32x4 v[kUnroll * 2];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const u32x4*>(p + u * 1024);
+      for (int u = 0; u < 16; ++u) v[u] = load16<NT>(p + u * 1024);
 #pragma unroll
       for (int u = 0; u < 16; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
@@ -74,7 +81,7 @@ read_probe(const char* __restrict__ buf, long long bytes, int method, const int*
       const long long t = s0 + wave + (kk / sub) * nw;
       const char* p = src_of(t) + (kk % sub) * slot_bytes + lane * 16;
       char* dst = region + (kk % nslots) * slot_bytes;
-      for (int c = 0; c < chunks; ++c) lds_dma16(p + c * 1024, dst + c * 1024);
+      for (int c = 0; c < chunks; ++c) lds_dma16<NT>(p + c * 1024, dst + c * 1024);
     };
     (void)st;
     if (kend > 0) issue(0);
@@ -103,14 +110,19 @@ read_probe(const char* __restrict__ buf, long long bytes, int method, const int*
 extern "C" int cc_probe_read(const void* buf, long long bytes, int method, const int32_t* pages,
                              int page_bytes, int num_pages, int workgroups, void* sink, void* stream) {
   using namespace cc::probe;
-  if (!buf || !sink || bytes < 16384 || method < 0 || method > 2 || workgroups < 1) return CC_ERR_INVALID;
+  if (!buf || !sink || bytes < 16384 || method < 0 || method > 4 || workgroups < 1) return CC_ERR_INVALID;
   if (pages && (page_bytes < 16384 || page_bytes % 16384 || num_pages < 1)) return CC_ERR_INVALID;
-  const size_t lds = method == 0 ? 0 : (size_t)(kThreads / 64) * 16384;
-  if (lds > 65536 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&read_probe), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess)
+  const bool nt = method >= 3;
+  const int m = method == 3 ? 0 : (method == 4 ? 2 : method);
+  const size_t lds = m == 0 ? 0 : (size_t)(kThreads / 64) * 16384;
+  const void* fn = nt ? reinterpret_cast<const void*>(&read_probe<true>) : reinterpret_cast<const void*>(&read_probe<false>);
+  if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return CC_ERR_HIP;
-  read_probe<<<workgroups, kThreads, lds, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const char*>(buf), bytes, method, pages, page_bytes, num_pages, static_cast<uint32_t*>(sink));
+  if (nt)
+    read_probe<true><<<workgroups, kThreads, lds, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const char*>(buf), bytes, m, pages, page_bytes, num_pages, static_cast<uint32_t*>(sink));
+  else
+    read_probe<false><<<workgroups, kThreads, lds, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const char*>(buf), bytes, m, pages, page_bytes, num_pages, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? CC_OK : CC_ERR_HIP;
 }

@@ -43,7 +43,9 @@ int cc_debug_timeline(void* buf, size_t bytes);
  *   method 0: 128-bit loads into registers, 8 per lane in flight;
  *   method 1: 128-bit loads straight into LDS, one 16 KiB slot per wave;
  *   method 2: the same into two 8 KiB slots per wave, one refilling while
- *             the other is read.
+ *             the other is read;
+ *   methods 3, 4: methods 0 and 2 with the non-temporal cache policy (nt),
+ *             the policy the decode kernels read the KV cache with.
  * pages: optional device int32[num_pages], a read order of page_bytes-sized
  * pages (page_bytes a multiple of 16 KiB); NULL reads contiguously.  sink:
  * device uint32[workgroups * 512], written.  Returns CC_OK, CC_ERR_INVALID or
