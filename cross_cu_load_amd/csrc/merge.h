@@ -23,14 +23,17 @@ namespace cc {
 constexpr int kMergeCoef = 2048;  // split coefficients held in LDS per pass
 constexpr int kMergeInflight = 8; // o_s loads in flight per thread
 
-// Partials cross compute units (and XCDs, whose L2 caches are not coherent
-// with each other) inside one launch.  They are written and read as relaxed
-// agent-scope atomics: those accesses carry the device-scope cache policy and
-// are coherent across the XCDs by themselves, so neither the writer nor the
-// reader has to write back or invalidate a whole L2 (what an agent-scope
-// release/acquire fence does for ordinary data).  The writer makes the stores
-// complete (s_waitcnt vmcnt(0)) before its arrival on the unit's counter; the
-// reader issues its loads after observing the last arrival.
+// Small partials (a GQA group: a few KB per piece) cross compute units (and
+// XCDs, whose L2 caches are not coherent with each other) inside one launch
+// as relaxed agent-scope atomics: those accesses carry the device-scope cache
+// policy and are coherent across the XCDs by themselves, so neither the
+// writer nor the reader has to write back or invalidate a whole L2 (what an
+// agent-scope release/acquire fence does for ordinary data).  The writer makes
+// the stores complete (s_waitcnt vmcnt(0)) before its arrival on the unit's
+// counter; the reader issues its loads after observing the last arrival.
+// Large partials (MLA: 128 KB per piece) use ordinary vector stores and the
+// fences instead: per-element device-scope accesses cost more than the fences
+// there.
 __device__ __forceinline__ void partial_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -47,7 +50,9 @@ __host__ __device__ constexpr int merge_lds_floats(int nt, int hpu) {
 }
 
 // partials: slot s at pb + s * slot_floats holds m[hpu] at 0, l[hpu] at hpu and
-// o[hpu][dv] at partial_o_offset(hpu) (16-byte aligned).
+// o[hpu][dv] at partial_o_offset(hpu) (16-byte aligned), written with ordinary
+// stores and published by an agent-scope release (or a kernel boundary); the
+// caller has performed the matching acquire.
 // out: head hh of the unit at out + hh * dv; lse: lse[hh].  dv % 4 == 0.
 template <int NT>
 __device__ void merge_splits(const float* pb, int ns, int slot_floats, int hpu, int dv, float* out,
