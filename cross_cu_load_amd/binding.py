@@ -20,7 +20,7 @@ CC_OK = 0
 CC_ERR_INVALID, CC_ERR_UNSUPPORTED, CC_ERR_BUFFER, CC_ERR_PLAN = -1, -2, -3, -4
 CC_ERR_PAGE, CC_ERR_HIP, CC_ERR_DEVICE_DATA = -5, -6, -7
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
-POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
+POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_COST = 0, 1, 2
 KV_NHD, KV_HND = 0, 1
 REDUCE_FUSED, REDUCE_SPLIT_COMBINE = 0, 1
 
@@ -127,8 +127,12 @@ def kernel_heads_per_unit(prob: Problem) -> int:
 
 
 def plan(prob: Problem, seqlens, block_table=None, num_cus=256, num_xcds=8, tile_tokens=32,
-         heads_per_unit=None, policy=POLICY_STREAMK) -> np.ndarray:
-    """Host plan blob (uint8 array) from cc_plan_size + cc_plan."""
+         heads_per_unit=None, policy=POLICY_STREAMK_COST) -> np.ndarray:
+    """Host plan blob (uint8 array) from cc_plan_size + cc_plan.
+
+    The default policy is the cost-balanced Stream-K split (equal chunks of
+    tile cost plus a fixed cost per unit); POLICY_STREAMK cuts equal tile
+    counts; POLICY_PER_UNIT is one worker per unit."""
     lib = load()
     if heads_per_unit is None:
         heads_per_unit = kernel_heads_per_unit(prob)

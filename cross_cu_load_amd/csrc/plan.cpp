@@ -35,7 +35,7 @@ int validate(const Inputs& in) {
     set_error("unknown mode %d", p.mode);
     return CC_ERR_INVALID;
   }
-  if (o.policy != CC_POLICY_STREAMK && o.policy != CC_POLICY_PER_UNIT) {
+  if (o.policy != CC_POLICY_STREAMK && o.policy != CC_POLICY_PER_UNIT && o.policy != CC_POLICY_STREAMK_COST) {
     set_error("unknown policy %d", o.policy);
     return CC_ERR_INVALID;
   }
@@ -125,6 +125,26 @@ int build(const Inputs& in, Built* out) {
   std::vector<std::vector<Piece>> chunks(C);
   if (o.policy == CC_POLICY_PER_UNIT) {
     for (int64_t u = 0; u < U; ++u) chunks[u].push_back({u, 0, unit_len(u)});
+  } else if (o.policy == CC_POLICY_STREAMK_COST) {
+    // equal split of the cost: kCostPerTile per tile plus kUnitCost per unit,
+    // the unit's overhead first; a tile goes to the chunk whose cost range
+    // holds its starting position
+    const int64_t total = kUnitCost * U + kCostPerTile * N;
+    const int64_t q = total / C, r = total % C;
+    auto bound = [&](int64_t k) { return k * q + (k < r ? k : r); };  // chunk k: [bound(k), bound(k+1))
+    int64_t cs = 0, k = 0;
+    for (int64_t u = 0; u < U; ++u) {
+      const int64_t n = first[u + 1] - first[u], L = unit_len(u);
+      for (int64_t i = 0; i < n;) {
+        const int64_t start = cs + kUnitCost + kCostPerTile * i;
+        while (bound(k + 1) <= start) ++k;
+        int64_t last = ceil_div(bound(k + 1) - cs - kUnitCost, kCostPerTile);
+        if (last > n) last = n;
+        chunks[k].push_back({u, i * T, last * T < L ? last * T : L});
+        i = last;
+      }
+      cs += kUnitCost + kCostPerTile * n;
+    }
   } else {
     const int64_t q = N / C, r = N % C;
     int64_t u = 0;
@@ -158,7 +178,7 @@ int build(const Inputs& in, Built* out) {
   // worker of each logical chunk: consecutive chunks share an XCD
   std::vector<int64_t> chunk_of_worker(C);
   const int64_t X = o.num_xcds;
-  const bool spread = o.policy == CC_POLICY_STREAMK && X > 1 && C % X == 0;
+  const bool spread = o.policy != CC_POLICY_PER_UNIT && X > 1 && C % X == 0;
   for (int64_t k = 0; k < C; ++k) {
     const int64_t w = spread ? (k % (C / X)) * X + k / (C / X) : k;
     chunk_of_worker[w] = k;
@@ -199,6 +219,7 @@ int build(const Inputs& in, Built* out) {
   h[H_POLICY] = o.policy;
   h[H_MAXPAGES] = p.max_pages_per_seq;
   h[H_NUMPAGES] = p.num_pages;
+  h[H_RESERVED] = o.policy == CC_POLICY_STREAMK_COST ? (int32_t)kUnitCost : 0;
   int32_t* wg = h + kHeaderWords;
   int32_t* it = wg + wg_words(C);
   int64_t n = 0;

@@ -58,6 +58,11 @@ const char* last_error();
 // Words of wg_off[] including the alignment padding.
 inline int64_t wg_words(int64_t workers) { return (workers + 1 + 3) & ~int64_t(3); }
 
+// Cost model of CC_POLICY_STREAMK_COST: one tile costs kCostPerTile, and each
+// unit adds kUnitCost (the plan header's last word records it).
+constexpr int64_t kCostPerTile = 16;
+constexpr int64_t kUnitCost = 16;
+
 // Workspace layout of a plan: error word and counters first, then partials.
 struct WorkspaceLayout {
   size_t counters_off = 0;   // bytes; int32[U]

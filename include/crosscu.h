@@ -63,11 +63,19 @@ enum { CC_MODE_GQA = 0, CC_MODE_MLA = 1, CC_MODE_MLA_SPARSE = 2 };
 enum { CC_KV_NHD = 0, CC_KV_HND = 1 };
 
 /* How a plan divides the work.
- *  STREAMK:  the total tile count is cut into num_cus equal contiguous chunks
- *            (one per compute unit, one wave); a sequence may be split.
- *  PER_UNIT: one worker per unit (query heads sharing one K/V stream), no
- *            split — the classic one-workgroup-per-(sequence, head) launch.  */
-enum { CC_POLICY_STREAMK = 0, CC_POLICY_PER_UNIT = 1 };
+ *  STREAMK:      the total tile count is cut into num_cus equal contiguous
+ *                chunks (one per compute unit, one wave); a sequence may be
+ *                split.
+ *  PER_UNIT:     one worker per unit (query heads sharing one K/V stream), no
+ *                split — the classic one-workgroup-per-(sequence, head) launch.
+ *  STREAMK_COST: as STREAMK, but what is cut into equal chunks is the cost of
+ *                the work: one tile costs 16, and every unit adds 16 more for
+ *                the fixed work of finishing it (merging its pieces inside a
+ *                compute unit, writing its output), so compute units holding
+ *                many short sequences get fewer tiles.  Units are laid out in
+ *                order, each unit's overhead before its tiles, and a tile goes
+ *                to the chunk whose cost range holds its starting position.  */
+enum { CC_POLICY_STREAMK = 0, CC_POLICY_PER_UNIT = 1, CC_POLICY_STREAMK_COST = 2 };
 
 /* Reduction of split units inside cc_decode_variant.
  *  FUSED:          the last piece of a unit to finish merges the partials in

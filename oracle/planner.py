@@ -15,6 +15,13 @@ Readings (the pages fix only "equal, one chunk per compute unit"):
   u = ((b * Tq + t) * Hkv + g) * (G / Hu) + hb; units are ordered by u.
 * tiles are laid out unit-major; chunk k takes floor(N / C) tiles, plus one
   for the first N mod C chunks, contiguously.
+* POLICY_STREAMK_COST (a refinement of the same equal split): what is split
+  evenly is the cost of the work, COST_PER_TILE per tile plus UNIT_COST per
+  unit, for the fixed work of finishing a unit (merging its pieces inside a
+  compute unit, writing its output); a unit occupies a contiguous cost range
+  with its overhead first, and a tile belongs to the chunk whose cost range
+  holds the tile's starting position.  Chunk k's range is
+  [k * q + min(k, r), (k+1) * q + min(k+1, r)) for total cost = q C + r.
 * a piece is a chunk's intersection with one unit; its split index counts the
   unit's pieces in chunk order; split units get consecutive partial slots.
 * placement: with X locality domains (XCDs) and C divisible by X, logical
@@ -37,7 +44,9 @@ HEADER_WORDS = 24
 ITEM_WORDS = 4                   # unit, tok_begin, tok_end, split
 
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
-POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
+POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_COST = 0, 1, 2
+COST_PER_TILE = 16                # cost units of one tile (POLICY_STREAMK_COST)
+UNIT_COST = 16                    # cost units charged once per unit (= one tile)
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -60,7 +69,7 @@ def validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head
              seqlens, block_table=None, policy=POLICY_STREAMK) -> None:
     if mode not in (MODE_GQA, MODE_MLA, MODE_MLA_SPARSE):
         raise ValueError("mode")
-    if policy not in (POLICY_STREAMK, POLICY_PER_UNIT):
+    if policy not in (POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_COST):
         raise ValueError("policy")
     if batch < 1 or q_tokens < 1 or num_q_heads < 1 or num_kv_heads < 1:
         raise ValueError("shape")
@@ -113,11 +122,13 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
         acc += n
     N = acc
 
+    chunk_pieces: list[list[tuple[int, int, int]]] = []
+    if policy == POLICY_STREAMK_COST:
+        chunk_pieces = _cost_split(ntiles, lens, C, T)
     # equal split of N tiles into C contiguous chunks (+1 for the first N mod C)
     base, rem = divmod(N, C)
-    chunk_pieces: list[list[tuple[int, int, int]]] = []
     u = 0
-    for k in range(C):
+    for k in range(C if policy != POLICY_STREAMK_COST else 0):
         if policy == POLICY_PER_UNIT:
             chunk_pieces.append([(k, 0, lens[k])])
             continue
@@ -153,7 +164,7 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
         else:
             pbase.append(-1)
 
-    if policy == POLICY_STREAMK and X > 1 and C % X == 0:
+    if policy != POLICY_PER_UNIT and X > 1 and C % X == 0:
         CX = C // X
         worker_of_chunk = [(k % CX) * X + k // CX for k in range(C)]
     else:
@@ -174,6 +185,7 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
     header[:23] = [PLAN_MAGIC, PLAN_VERSION, mode, batch, q_tokens, num_q_heads, num_kv_heads,
                    head_dim_qk, head_dim_v, page_size, topk, C, X, T, heads_per_unit, U, N, W, S,
                    max(nsplit) if nsplit else 0, policy, max_pages_per_seq, num_pages]
+    header[23] = UNIT_COST if policy == POLICY_STREAMK_COST else 0
     pad = (-(C + 1)) % 4                 # keeps the item array 16-byte aligned
     words = header + wg_off + [0] * pad + [x for it in items for x in it] + nsplit + pbase
     for x in words:
@@ -183,6 +195,32 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
     return dict(blob=blob, num_units=U, num_tiles=N, num_items=W, num_partials=S,
                 wg_off=wg_off, items=items, unit_nsplit=nsplit, unit_pbase=pbase,
                 worker_of_chunk=worker_of_chunk, unit_len=lens, chunk_items=items_by_chunk)
+
+
+def _cost_split(ntiles, lens, C: int, T: int):
+    """Chunks of POLICY_STREAMK_COST: pieces (unit, tok_begin, tok_end) per chunk.
+
+    Unit u's cost range starts at cs[u] = sum over earlier units of
+    (UNIT_COST + COST_PER_TILE * n); its tile i starts at cs[u] + UNIT_COST +
+    COST_PER_TILE * i and belongs to the chunk whose range holds that position.
+    """
+    total = sum(UNIT_COST + COST_PER_TILE * n for n in ntiles)
+    q, r = divmod(total, C)
+    bound = [k * q + min(k, r) for k in range(C + 1)]   # chunk k: [bound[k], bound[k+1])
+    pieces: list[list[tuple[int, int, int]]] = [[] for _ in range(C)]
+    cs, k = 0, 0
+    for u, n in enumerate(ntiles):
+        i = 0
+        while i < n:
+            start = cs + UNIT_COST + COST_PER_TILE * i
+            while bound[k + 1] <= start:
+                k += 1
+            # tiles of u whose start lies before the end of chunk k
+            last = min(n, _ceil_div(bound[k + 1] - cs - UNIT_COST, COST_PER_TILE))
+            pieces[k].append((u, i * T, min(last * T, lens[u])))
+            i = last
+        cs += UNIT_COST + COST_PER_TILE * n
+    return pieces
 
 
 def plan_for(wl, num_cus=256, num_xcds=8, tile_tokens=32, heads_per_unit=None,

@@ -12,7 +12,7 @@ from oracle import attention as A
 TOL_OUT, TOL_LSE = 1e-2, 1e-3
 
 
-def run(wl, cus, xcds, tile=32, policy=B.POLICY_STREAMK, reduce=B.REDUCE_FUSED, tag=""):
+def run(wl, cus, xcds, tile=32, policy=B.POLICY_STREAMK_COST, reduce=B.REDUCE_FUSED, tag=""):
     import torch
     print(f"[gpu] {tag} cfg={wl.cfg.name} B={wl.cfg.batch} C={cus} X={xcds} T={tile} policy={policy} "
           f"reduce={reduce}", flush=True)

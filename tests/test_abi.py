@@ -46,7 +46,7 @@ def _prob(cfg, sl):
 
 @pytest.mark.parametrize("name", [c.name for c in W.CONFIGS])
 @pytest.mark.parametrize("C,X,T", [(256, 8, 32), (256, 8, 64), (304, 8, 32), (148, 1, 32), (8, 8, 32)])
-@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_PER_UNIT])
+@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_PER_UNIT, B.POLICY_STREAMK_COST])
 def test_plan_bytes_match_reference_on_workload_lengths(lib, name, C, X, T, policy):
     cfg = W.CONFIG_BY_NAME[name]
     sl = W.draw_seqlens(cfg)
@@ -84,7 +84,7 @@ def test_plan_bytes_match_reference_fuzz(lib, seed):
     C = int(rng.choice([1, 3, 8, 100, 256, 1000]))
     X = int(rng.choice([1, 4, 8]))
     T = int(rng.choice([1, 7, 32, 64]))
-    policy = int(rng.integers(0, 2))
+    policy = int(rng.integers(0, 3))
     prob = B.problem(mode, B_, Tq, Hq, Hkv, 64, 64, P, maxp, npages, topk, 0.125)
     blob = B.plan(prob, sl, bt, num_cus=C, num_xcds=X, tile_tokens=T, heads_per_unit=hu, policy=policy)
     ref = PL.plan(mode, B_, Tq, Hq, Hkv, 64, 64, P, maxp, npages, topk, C, X, T, hu, sl, bt, policy)

@@ -59,10 +59,11 @@ def test_ragged_and_single_token_sequences(dev):
             assert np.array_equal(out[b, 0, h], v)
 
 
+@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_STREAMK_COST])
 @pytest.mark.parametrize("layout", [W.KV_NHD, W.KV_HND])
-def test_skewed_full_size_all_outputs(dev, layout):
+def test_skewed_full_size_all_outputs(dev, layout, policy):
     wl = W.make_workload(dataclasses.replace(W.CONFIG_BY_NAME["skewed_gqa"], kv_layout=layout))
-    s, plan = run(wl, *dev, tag="skewed-full")
+    s, plan = run(wl, *dev, policy=policy, tag="skewed-full")
     compare(s, wl)
     clean(s, plan)
 
@@ -72,7 +73,7 @@ def test_llama_full_size_sampled(dev):
     wl = W.make_workload(cfg)
     s, plan = run(wl, *dev, tag="llama-full")
     from oracle import planner as PL
-    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1])
+    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1], policy=PL.POLICY_STREAMK_COST)
     split_units = [u for u, n in enumerate(ref["unit_nsplit"]) if n > 1]
     rng = np.random.default_rng(5)
     pick = set(split_units[:24]) | set(int(u) for u in rng.choice(len(ref["unit_nsplit"]), 24, replace=False))
@@ -84,7 +85,7 @@ def test_llama_full_size_sampled(dev):
 
 
 @pytest.mark.parametrize("policy,reduce", [(B.POLICY_PER_UNIT, B.REDUCE_FUSED),
-                                           (B.POLICY_STREAMK, B.REDUCE_SPLIT_COMBINE)])
+                                           (B.POLICY_STREAMK_COST, B.REDUCE_SPLIT_COMBINE)])
 @pytest.mark.parametrize("name", ["tiny_gqa", "skewed_gqa"])
 def test_comparison_variants(dev, policy, reduce, name):
     cfg = W.CONFIG_BY_NAME[name]
@@ -96,11 +97,12 @@ def test_comparison_variants(dev, policy, reduce, name):
     clean(s, plan)
 
 
+@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_STREAMK_COST])
 @pytest.mark.parametrize("cus", [1, 8, 64, 255, 256, 1024])
-def test_split_points_move_with_cu_count(dev, cus):
+def test_split_points_move_with_cu_count(dev, cus, policy):
     cfg = W.small_variant(W.CONFIG_BY_NAME["skewed_gqa"], batch=5, seqlen_hi=4000, seed_offset=cus)
     wl = W.make_workload(cfg)
-    s, plan = run(wl, cus, dev[1], tag="cus")
+    s, plan = run(wl, cus, dev[1], policy=policy, tag="cus")
     compare(s, wl)
     clean(s, plan)
 

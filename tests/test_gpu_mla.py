@@ -60,7 +60,7 @@ def test_mla_ragged_and_single_token(dev):
 def test_mla_full_size_sampled(dev):
     wl = W.make_workload(MLA)
     s, plan = run(wl, *dev, tag="mla-full")
-    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1], heads_per_unit=64)
+    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1], heads_per_unit=64, policy=PL.POLICY_STREAMK_COST)
     assert plan.tobytes() == ref["blob"]
     split_tok = sorted({u // 2 for u, n in enumerate(ref["unit_nsplit"]) if n > 1})
     rng = np.random.default_rng(7)
@@ -108,7 +108,7 @@ def test_sparse_index_order_irrelevant(dev):
 
 
 @pytest.mark.parametrize("policy,reduce", [(B.POLICY_PER_UNIT, B.REDUCE_FUSED),
-                                           (B.POLICY_STREAMK, B.REDUCE_SPLIT_COMBINE)])
+                                           (B.POLICY_STREAMK_COST, B.REDUCE_SPLIT_COMBINE)])
 @pytest.mark.parametrize("name", ["deepseek_mla", "sparse_mla"])
 def test_mla_comparison_variants(dev, policy, reduce, name):
     cfg = W.CONFIG_BY_NAME[name]
@@ -119,11 +119,12 @@ def test_mla_comparison_variants(dev, policy, reduce, name):
     clean(s, plan)
 
 
+@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_STREAMK_COST])
 @pytest.mark.parametrize("cus", [1, 7, 64, 256, 1024])
-def test_mla_split_points_move_with_cu_count(dev, cus):
+def test_mla_split_points_move_with_cu_count(dev, cus, policy):
     cfg = W.small_variant(MLA, batch=3, seqlen_hi=4000, seed_offset=cus)
     wl = W.make_workload(cfg)
-    s, plan = run(wl, cus, dev[1], tag="mla-cus")
+    s, plan = run(wl, cus, dev[1], policy=policy, tag="mla-cus")
     compare(s, wl)
     clean(s, plan)
 

@@ -19,12 +19,12 @@ from oracle import planner as PL
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _plan(lens, C=8, X=1, T=4, G=1, Hkv=1, mode=PL.MODE_GQA, Tq=1, topk=0, hu=None):
+def _plan(lens, C=8, X=1, T=4, G=1, Hkv=1, mode=PL.MODE_GQA, Tq=1, topk=0, hu=None, policy=PL.POLICY_STREAMK):
     lens = np.asarray(lens, np.int32)
     P = 16
     maxp = int(max((int(L) + P - 1) // P for L in lens))
     return PL.plan(mode, len(lens), Tq, G * Hkv, Hkv, 64, 64, P, maxp, 1 << 20, topk, C, X, T,
-                   hu if hu is not None else G, lens)
+                   hu if hu is not None else G, lens, None, policy)
 
 
 def test_golden_732_tasks_over_148_workers():
@@ -56,16 +56,25 @@ def test_golden_tail_effect_and_equal_split():
     assert chunk.max() == total / g["num_sms"] == 155
 
 
-def _check_invariants(p, lens, C, X, T):
+def _check_invariants(p, lens, C, X, T, policy=PL.POLICY_STREAMK):
     U = len(lens)
     ntiles = [-(-L // T) for L in lens]
     N = sum(ntiles)
     assert p["num_tiles"] == N and p["num_units"] == U
     # chunk sizes: floor(N/C), +1 on the first N mod C logical chunks
-    base, rem = divmod(N, C)
-    for k, its in enumerate(p["chunk_items"]):
-        tiles = sum(-(-(t1 - t0) // T) for (_, t0, t1, _) in its)
-        assert tiles == base + (k < rem)
+    if policy == PL.POLICY_STREAMK:
+        base, rem = divmod(N, C)
+        for k, its in enumerate(p["chunk_items"]):
+            tiles = sum(-(-(t1 - t0) // T) for (_, t0, t1, _) in its)
+            assert tiles == base + (k < rem)
+    else:
+        # cost of a chunk (16 per tile, 16 per unit it starts) is within one
+        # tile plus one unit of its share of the total cost
+        K, O = PL.COST_PER_TILE, PL.UNIT_COST
+        q, r = divmod(K * N + O * U, C)
+        for k, its in enumerate(p["chunk_items"]):
+            cost = sum(K * -(-(t1 - t0) // T) + (O if t0 == 0 else 0) for (_, t0, t1, _) in its)
+            assert abs(cost - (q + (k < r))) <= K + O
     # every token of every unit covered exactly once, in order
     cover = [[] for _ in range(U)]
     for its in p["chunk_items"]:
@@ -122,24 +131,64 @@ def _brute_force(lens, C, T):
     return [[tuple(x) for x in c] for c in chunks]
 
 
+def _brute_force_cost(lens, C, T):
+    """Cost policy, tile by tile: a tile's cost position is the cost of all
+    earlier units (16 + 16 per tile each), 16 for its own unit and 16 per
+    earlier tile of it; the tile goes to the chunk whose range holds it,
+    found by scanning the ranges."""
+    K, O = PL.COST_PER_TILE, PL.UNIT_COST
+    ntiles = [-(-L // T) for L in lens]
+    total = sum(O + K * n for n in ntiles)
+    ranges = [(k * (total // C) + min(k, total % C), (k + 1) * (total // C) + min(k + 1, total % C))
+              for k in range(C)]
+    chunks = [[] for _ in range(C)]
+    before = 0
+    for u, n in enumerate(ntiles):
+        for j in range(n):
+            pos = before + O + K * j
+            k = next(k for k, (a, b) in enumerate(ranges) if a <= pos < b)
+            if chunks[k] and chunks[k][-1][0] == u:
+                chunks[k][-1][2] = min((j + 1) * T, lens[u])
+            else:
+                chunks[k].append([u, j * T, min((j + 1) * T, lens[u])])
+        before += O + K * n
+    return [[tuple(x) for x in c] for c in chunks]
+
+
+@pytest.mark.parametrize("policy", [PL.POLICY_STREAMK, PL.POLICY_STREAMK_COST])
 @pytest.mark.parametrize("seed", range(30))
-def test_brute_force_and_invariants_small(seed):
+def test_brute_force_and_invariants_small(seed, policy):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 5))
     lens = [int(x) for x in rng.integers(1, 60, size=B)]
     C = int(rng.choice([1, 2, 3, 5, 8, 16]))
     X = int(rng.choice([1, 2, 4, 8]))
     T = int(rng.choice([1, 4, 16, 32]))
-    p = _plan(lens, C=C, X=X, T=T)
-    _check_invariants(p, lens, C, X, T)
-    bf = _brute_force(lens, C, T)
+    p = _plan(lens, C=C, X=X, T=T, policy=policy)
+    _check_invariants(p, lens, C, X, T, policy)
+    bf = _brute_force(lens, C, T) if policy == PL.POLICY_STREAMK else _brute_force_cost(lens, C, T)
     got = [[(u, t0, t1) for (u, t0, t1, _) in its] for its in p["chunk_items"]]
     assert got == bf
 
 
+def test_cost_policy_gives_short_units_fewer_tiles():
+    # one long unit and many short ones: the chunks made of short units carry
+    # a unit cost each, so they get fewer tiles than the equal-tile split gives
+    lens = [4096] + [64] * 60
+    C, T = 16, 32
+    eq = _plan(lens, C=C, T=T)
+    co = _plan(lens, C=C, T=T, policy=PL.POLICY_STREAMK_COST)
+    tiles = lambda p, k: sum(-(-(t1 - t0) // T) for (_, t0, t1, _) in p["chunk_items"][k])
+    assert tiles(co, C - 1) < tiles(eq, C - 1)          # the last chunk holds only short units
+    assert tiles(co, 0) >= tiles(eq, 0)                 # the first holds only the long one
+    assert co["blob"][80:84] != b"\x00\x00\x00\x00"      # header word 20: policy
+    assert np.frombuffer(co["blob"][:96], np.int32)[23] == PL.UNIT_COST
+
+
+@pytest.mark.parametrize("policy", [PL.POLICY_STREAMK, PL.POLICY_STREAMK_COST])
 @pytest.mark.parametrize("C", [1, 3, 8, 148, 256, 304, 1000])
 @pytest.mark.parametrize("T", [16, 32, 64])
-def test_invariants_on_the_workload_lengths(C, T):
+def test_invariants_on_the_workload_lengths(C, T, policy):
     for cfg in W.CONFIGS:
         lens_b = W.draw_seqlens(cfg)
         hu = cfg.group if cfg.mode == W.MODE_GQA else min(cfg.num_q_heads, 128)
@@ -149,8 +198,8 @@ def test_invariants_on_the_workload_lengths(C, T):
         P = cfg.page_size
         maxp = int(max((int(L) + P - 1) // P for L in lens_b))
         p = PL.plan(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
-                    cfg.head_dim_v, P, maxp, 1 << 20, cfg.topk, C, 8, T, hu, lens_b)
-        _check_invariants(p, lens, C, 8, T)
+                    cfg.head_dim_v, P, maxp, 1 << 20, cfg.topk, C, 8, T, hu, lens_b, None, policy)
+        _check_invariants(p, lens, C, 8, T, policy)
 
 
 def test_skewed_workload_split_shape():
