@@ -43,8 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="skewed_gqa")
-    ap.add_argument("--layout", choices=["nhd", "hnd"], default="nhd",
-                    help="page layout of the GQA K/V caches: token-major [P][Hkv][d] or head-major [Hkv][P][d]")
+    ap.add_argument("--layout", choices=["nhd", "hnd"], default="hnd",
+                    help="page layout of the GQA K/V caches: head-major [Hkv][P][d] (default) or token-major [P][Hkv][d]")
     ap.add_argument("--variant-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")

@@ -172,6 +172,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   __shared__ int done_units[2 * kWaves][3];  // units this workgroup completes: {pbase, nsplit, out row}
   __shared__ float slot_w[2 * kWaves][16];    // phase-1 weight of each merge slot, per head
   __shared__ float item_L[2 * kWaves][16];    // phase-1 sum L of each item, per head
+  __shared__ float item_M[2 * kWaves][16];    // phase-1 max M of each item, per head
   __shared__ int it_slot[2 * kWaves];         // phase-1 items: first slot,
   __shared__ unsigned it_mask[2 * kWaves];    // the slots holding it,
   __shared__ int num_items;                   // and how many
@@ -552,28 +553,29 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   const int nit = uni(num_items);
   const int GD = G * D;
   if (tid < nit * G) {
+    // (item, head): all slots' (m, l) loaded together (only the item's count)
     const int ii = tid / G, hh = tid - (tid / G) * G;
     const unsigned mask = it_mask[ii];
-    const int sl0 = it_slot[ii];
-    float M = -INFINITY;
-    for (unsigned mm = mask; mm; mm &= mm - 1) M = fmaxf(M, merge_slot(__builtin_ctz(mm))[hh]);
-    float L = 0.f;
-    for (unsigned mm = mask; mm; mm &= mm - 1) {
-      const int t = __builtin_ctz(mm);
+    float mt[2 * kWaves], lt[2 * kWaves];
+#pragma unroll
+    for (int t = 0; t < 2 * kWaves; ++t) {
+      const bool on = (mask >> t) & 1;
       const float* sb = merge_slot(t);
-      const float f = fast_exp2(sb[hh] - M);
-      L += sb[G + hh] * f;
-      slot_w[t][hh] = f;
+      mt[t] = on ? sb[hh] : -INFINITY;
+      lt[t] = on ? sb[G + hh] : 0.f;
     }
+    float M = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2 * kWaves; ++t) M = fmaxf(M, mt[t]);
+    float L = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2 * kWaves; ++t) {  // slot (= token) order
+      const float f = fast_exp2(mt[t] - M);  // 0 for slots of other items
+      L += lt[t] * f;
+      if ((mask >> t) & 1) slot_w[t][hh] = f;
+    }
+    item_M[ii][hh] = M;
     item_L[ii][hh] = L;
-    const int unit = slot_meta[sl0][0], split = slot_meta[sl0][1], ns = slot_meta[sl0][2];
-    if (ns == 1) {
-      lse[(size_t)unit * G + hh] = (M + __log2f(L)) * kLn2;  // row of unit (b, g): b Hq + g G = unit G
-    } else {
-      float* pslot = partials + (size_t)(slot_meta[sl0][3] + split) * p.slot_floats;
-      partial_store(pslot + hh, M);
-      partial_store(pslot + G + hh, L);
-    }
   }
   __syncthreads();
   for (int idx = tid; idx < nit * GD; idx += kThreads) {
@@ -587,10 +589,17 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       O += merge_slot(t)[2 * G + e] * slot_w[t][hh];
     }
     const int unit = uni(slot_meta[sl0][0]), split = uni(slot_meta[sl0][1]), ns = uni(slot_meta[sl0][2]);
+    const bool head_lane = e - hh * D == 0;
     if (ns == 1) {
-      out[(size_t)unit * GD + e] = O / item_L[ii][hh];
+      out[(size_t)unit * GD + e] = O / item_L[ii][hh];  // row of unit (b, g): b Hq + g G = unit G
+      if (head_lane) lse[(size_t)unit * G + hh] = (item_M[ii][hh] + __log2f(item_L[ii][hh])) * kLn2;
     } else {
-      partial_store(partials + (size_t)(uni(slot_meta[sl0][3]) + split) * p.slot_floats + partial_o_offset(G) + e, O);
+      float* pslot = partials + (size_t)(uni(slot_meta[sl0][3]) + split) * p.slot_floats;
+      partial_store(pslot + partial_o_offset(G) + e, O);
+      if (head_lane) {
+        partial_store(pslot + hh, item_M[ii][hh]);
+        partial_store(pslot + G + hh, item_L[ii][hh]);
+      }
     }
   }
   if (tl && tid == 0) tl[2] = __builtin_amdgcn_s_memrealtime();
