@@ -123,7 +123,7 @@ def kernel_heads_per_unit(prob: Problem) -> int:
     """heads_per_unit that cc_decode's kernel for this mode accepts."""
     if prob.mode == MODE_GQA:
         return prob.num_q_heads // prob.num_kv_heads
-    return 64
+    return 128
 
 
 def plan(prob: Problem, seqlens, block_table=None, num_cus=256, num_xcds=8, tile_tokens=32,

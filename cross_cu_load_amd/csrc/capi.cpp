@@ -60,8 +60,8 @@ int check_mla(const cc_problem& p, const cc::PlanView& v) {
                   p.head_dim_v);
     return CC_ERR_UNSUPPORTED;
   }
-  if (v.header[cc::H_HPU] != 64) {
-    cc::set_error("MLA kernel: heads_per_unit must be 64 (two head blocks per query token)");
+  if (v.header[cc::H_HPU] != 128) {
+    cc::set_error("MLA kernel: heads_per_unit must be 128 (one unit per query token)");
     return CC_ERR_UNSUPPORTED;
   }
   if (!is_pow2(p.page_size) || (p.mode == CC_MODE_MLA && p.page_size < 32)) {

@@ -2,40 +2,37 @@
 // index-sparse.
 //
 // MLA shape: 128 query heads share one latent KV row of 576 bf16 per token;
-// the whole row is K, its first 512 columns are V.  One workgroup of 8 waves
+// the whole row is K, its first 512 columns are V.  One workgroup of 4 waves
 // per compute unit runs the equal chunk of KV tiles the host plan gave it
 // (CSDN Q&A on waves and FlashMLA's Stream-K, "Summary"); sequences split
 // across compute units are merged inside this kernel by the piece that
 // arrives last (MeldKernel summary, "Core method").
 //
-// A unit is one query token's block of 64 heads (the two head blocks of a
-// token are adjacent units, so their chunks stream the same tokens at the
-// same time and the second read is served by the memory-side cache).  Each
-// pair of waves owns 16 heads and every wave sees every KV token of the tile.
-// The two waves of a pair split the work of the two dense contractions
-// (v_mfma_f32_16x16x32_bf16 tiles):
-//   S^T[32 tokens][16 heads] = K[32][576] . Q^T[576][16]: wave h of the pair
-//     sums k-steps 9h .. 9h+8 (dims 288h .. 288h+287) and the pair adds the
-//     two partials through LDS, in the same order in both waves, so both hold
-//     bitwise the same scores and run the same softmax;
-//   O[16 heads][512] += P[16][32] . V[32][512]: wave h accumulates dv columns
-//     256h .. 256h+255.
-// Per wave that is 9 k-steps of Q^T (36 registers) and 64 accumulators, which
-// leaves the register file room for the operand pipeline.  S^T leaves each
-// head's scores in the layout P needs as an A operand; V is transposed in
-// registers with one byte permute per word.
+// A unit is one query token with all 128 heads, so every KV row is read from
+// HBM once per query token.  Wave w owns heads 32w .. 32w+31 and runs both
+// dense contractions on v_mfma_f32_32x32x16_bf16 tiles, one wave per SIMD with
+// the whole register file:
+//   S^T[32 tokens][32 heads] = K[32][576] . Q^T[576][32]   (36 k-steps; Q^T in
+//     144 VGPRs for the whole item),
+//   O^T[512][32 heads]      += V^T[512][32] . P^T[32][32]  (16 column blocks of
+//     32 dv x 32 heads: 256 accumulators, held in AGPRs).
+// S^T leaves lane (n, g) with head n's scores of tokens 8j + 4g + i, which is
+// exactly the P^T operand of the two 16-token k-blocks of O^T once the tokens
+// of a k-block are ordered {16b + 4g + i, 16b + 8 + 4g + i}.  Each lane of O^T
+// belongs to one head, so softmax rescales are lane-local.  V^T operands come
+// straight from gfx950's transposing LDS read (ds_read_b64_tr_b16): two reads
+// give a lane 8 tokens of one dv column.
 //
-// A 32-token tile (36 KiB) streams HBM -> LDS with global_load_lds_dwordx4
+// A 32-token tile (36.5 KiB) streams HBM -> LDS with global_load_lds_dwordx4
 // through a 3-stage ring, so two tiles are in flight while one computes.  Wave
-// w moves tokens w, w+8, w+16, w+24: each token's first 512 columns are one
-// transfer into an LDS row padded to 1040 bytes (rows 260 dwords apart fall in
-// different banks, so the MFMA operand reads are conflict free and every
-// lane's address is one base register plus an immediate), and the 64 rope
-// columns of its 4 tokens are one half-wave transfer into the wave's own
-// 512-byte region, 16-byte chunks in [token][chunk] order with the chunk index
-// XOR-ed by bit 0 of the token slot; regions 544 bytes apart keep the rope
-// operand reads conflict free too.  The fetch needs no per-lane loads, so it
-// never waits behind the transfers in flight.
+// w moves tokens 8w .. 8w+7: each token's first 512 columns are one transfer
+// into an LDS row placed so that both the K operand reads and the transposed
+// V reads are bank-conflict free (every lane's address is one base register
+// plus an immediate), and the 64 rope columns of
+// its 8 tokens are one transfer into a [token][chunk] area whose 16-byte chunk
+// c of token t sits at slot c ^ ((t >> 1) & 7), which keeps the rope operand
+// reads conflict free.  The fetch needs no per-lane loads, so it never waits
+// behind the transfers in flight.
 //
 // The running max is only moved when a head's block max exceeds it by more
 // than 2^8 (in base 2): probabilities stay below 256, and the rescale of the
@@ -54,45 +51,148 @@ namespace mla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kHeads = 64;                  // heads per unit (= per workgroup)
-constexpr int kHG = 16;                     // heads per wave pair
+constexpr int kHeads = 128;                 // heads per unit (= per workgroup)
+constexpr int kHW = 32;                     // heads per wave
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kRowBytes = kDqk * 2;         // 1152
 constexpr int kBlk = 32;                    // tokens per tile
-constexpr int kKHalf = 9;                   // 32-dim k-steps of q.k per wave of a pair
-constexpr int kRowPad = 1040;               // LDS bytes per token row (1024 + 16 pad)
-constexpr int kRopeOff = kBlk * kRowPad;
-constexpr int kRopeWave = 544;              // LDS bytes between the waves' rope regions (512 + 32)
-constexpr int kStageBytes = kRopeOff + (kWaves - 1) * kRopeWave + 512;   // 37600
-constexpr int kRowsPerWave = kBlk / kWaves;                              // 4
-constexpr int kDmaPerWave = kRowsPerWave + 1;                            // + 1 rope transfer
+constexpr int kKSteps = kDqk / 16;          // 36 k-steps of q.k
+constexpr int kLatentSteps = 32;            // k-steps inside the first 512 columns
+// LDS row of token t (its first 512 columns): 1088 t + 16 ((t / 4) % 4).  Row
+// starts fall on 16-byte bank slot 4 (t % 4) + (t / 4) % 4 modulo 256 bytes, so
+// 16 consecutive tokens hit 16 different slots (K operand reads) and 4
+// consecutive tokens start 64 bytes apart (transposed V reads): both conflict free.
+__host__ __device__ constexpr int row_lds(int t) { return 1088 * t + 16 * ((t >> 2) & 3); }
+constexpr int kRopeOff = 34816;             // >= row_lds(31) + 1024, 256-aligned
+constexpr int kStageBytes = kRopeOff + kBlk * 128;   // 38912
+static_assert(row_lds(kBlk - 1) + 1024 <= kRopeOff, "rows overlap the rope area");
+constexpr int kRowsPerWave = kBlk / kWaves;          // 8
+constexpr int kDmaPerWave = kRowsPerWave + 1;        // + 1 rope transfer
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLazy = 8.f;                // log2 headroom before the max is moved
+constexpr int kPreS = 6;                    // K operand reads in flight ahead of the score MFMAs
+constexpr int kPreV = 4;                    // V^T operands in flight ahead of the output MFMAs
 
-// The three ring stages and the exchange buffer of the score partials.
-__shared__ __attribute__((aligned(16))) char ring0[kStageBytes];
-__shared__ __attribute__((aligned(16))) char ring1[kStageBytes];
-__shared__ __attribute__((aligned(16))) char ring2[kStageBytes];
-__shared__ __attribute__((aligned(16))) f32x4 xch[kWaves][2][64];
+__shared__ __attribute__((aligned(16))) char ring[3][kStageBytes];
+__shared__ __attribute__((aligned(16))) char qrope[kWaves][(kKSteps - kLatentSteps) * 1024];
 
-template <int S>
-__device__ __forceinline__ char* stage() {
-  return S == 0 ? ring0 : (S == 1 ? ring1 : ring2);
+
+
+// ---- The output accumulators: a0 .. a255, owned by inline asm.
+// O^T block d (32 dv rows x 32 heads, 16 registers per lane) lives in
+// a[16 d .. 16 d + 15] for the whole kernel.  Every instruction that touches
+// them is inline asm below: the compiler itself never allocates an AGPR in this
+// kernel (its values fit the 256 VGPRs; a test checks the generated code), and
+// its register allocator cannot keep 256 accumulators in place once VALU code
+// (the rescale, the reset) touches them.  Because the compiler does not see
+// these registers, the asm carries the wait states CDNA3/4 require around an
+// XDL (MFMA) result: 18 independent cycles before a VALU, memory or
+// v_accvgpr_read access to it, 2 after a VALU write (v_accvgpr_write) before
+// an MFMA reads it.  Back-to-back accumulation into the same block needs none.
+template <class F, int... I>
+__device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
 }
-template <int S>
-using IC = std::integral_constant<int, S>;
-
-__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                 c, 0, 0, 0);
+template <int N, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
+// Declares a0 .. a255 used, so the launch reserves them (the asm statements
+// below name them only in their text).
+__device__ __forceinline__ void acc_reserve() {
+  asm volatile("" :::
+    "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15",
+    "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31",
+    "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47",
+    "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63",
+    "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", "a76", "a77", "a78", "a79",
+    "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", "a91", "a92", "a93", "a94", "a95",
+    "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104", "a105", "a106", "a107", "a108", "a109", "a110", "a111",
+    "a112", "a113", "a114", "a115", "a116", "a117", "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127",
+    "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143",
+    "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156", "a157", "a158", "a159",
+    "a160", "a161", "a162", "a163", "a164", "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175",
+    "a176", "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188", "a189", "a190", "a191",
+    "a192", "a193", "a194", "a195", "a196", "a197", "a198", "a199", "a200", "a201", "a202", "a203", "a204", "a205", "a206", "a207",
+    "a208", "a209", "a210", "a211", "a212", "a213", "a214", "a215", "a216", "a217", "a218", "a219", "a220", "a221", "a222", "a223",
+    "a224", "a225", "a226", "a227", "a228", "a229", "a230", "a231", "a232", "a233", "a234", "a235", "a236", "a237", "a238", "a239",
+    "a240", "a241", "a242", "a243", "a244", "a245", "a246", "a247", "a248", "a249", "a250", "a251", "a252", "a253", "a254", "a255");
+}
+__device__ __forceinline__ void wait_xdl_result() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
+__device__ __forceinline__ void wait_valu_to_xdl() { asm volatile("s_nop 1" ::: "memory"); }
+template <int D>
+__device__ __forceinline__ void acc_zero1(const u32x4& z) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[%c1:%c2], %0, %0, 0" ::"v"(z), "n"(16 * D), "n"(16 * D + 15));
+}
+template <int... D>
+__device__ __forceinline__ void acc_zero_all(const u32x4& z, std::integer_sequence<int, D...>) {
+  (acc_zero1<D>(z), ...);
+}
+// 16 MFMAs with zero operands and a zero accumulator write zeros to a0 .. a255.
+__device__ __forceinline__ void acc_zero() {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  wait_xdl_result();
+  acc_zero_all(z, std::make_integer_sequence<int, 16>{});
+}
+template <int R>
+__device__ __forceinline__ void acc_scale1(float s) {
+  float t;
+  asm volatile("v_accvgpr_read_b32 %0, a%c2\n\tv_mul_f32 %0, %0, %1\n\tv_accvgpr_write_b32 a%c2, %0"
+               : "=&v"(t)
+               : "v"(s), "n"(R));
+}
+template <int... R>
+__device__ __forceinline__ void acc_scale_all(float s, std::integer_sequence<int, R...>) {
+  (acc_scale1<R>(s), ...);
+}
+__device__ __forceinline__ void acc_scale(float s) {
+  wait_xdl_result();
+  acc_scale_all(s, std::make_integer_sequence<int, 256>{});
+  wait_valu_to_xdl();
+}
+template <int R>
+__device__ __forceinline__ float acc_read() {
+  float x;
+  asm volatile("v_accvgpr_read_b32 %0, a%c1" : "=v"(x) : "n"(R));
+  return x;
+}
+// O^T block d (dv 32 d .. 32 d + 31) += V^T P^T.  P^T is written by VALU code
+// the compiler may place right before this statement, so the statement starts
+// with the 2 wait states an MFMA operand needs after a VALU write.
+template <int D>
+__device__ __forceinline__ void pv1(const u32x4& v, const u32x4& p) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[%c2:%c3], %0, %1, a[%c2:%c3]" ::"v"(v), "v"(p),
+               "n"(16 * D), "n"(16 * D + 15));
+}
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+// lane i receives element i % 4 of the chunks supplied by lanes i / 4 + 4 e.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16* lp;
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds_ptr)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+// The score chain keeps its accumulator in VGPRs (the AGPRs hold the output
+// accumulators): written as inline asm with VGPR operands.  Back-to-back
+// accumulation into the same registers needs no wait states; before VALU reads
+// the result, mfma32_v_drain provides the 18 independent cycles a 32x32 XDL
+// result needs on CDNA3/4.
+__device__ __forceinline__ void mfma32_v_first(f32x16& d, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_v(f32x16& d, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_v_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2 f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
@@ -112,6 +212,24 @@ __device__ __forceinline__ void lds_dma16(const char* src, char* lds) {
   const uint32_t m0 = uni((int)(uint32_t)(uintptr_t)(lds_ptr)lds);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :: "v"(src), "s"(m0) : "memory", "m0");
+}
+// The same transfer with a scalar base and a per-lane offset.
+__device__ __forceinline__ void lds_dma16s(const char* sbase, uint32_t voff, char* lds) {
+  const uint32_t m0 = uni((int)(uint32_t)(uintptr_t)(lds_ptr)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
+}
+// A dword load the compiler does not track: the kernel's own vmcnt waits make
+// it complete before the value is read with take_dword (both are ordered asm).
+__device__ __forceinline__ uint32_t load_dword_async(const int32_t* ptr) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(ptr) : "memory");
+  return v;
+}
+__device__ __forceinline__ int take_dword(uint32_t v) {
+  int s;
+  asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(s) : "v"(v) : "memory");
+  return s;
 }
 __device__ __forceinline__ unsigned xcc_id() {
   unsigned v;
@@ -140,28 +258,86 @@ struct Item {
   int unit, tb, te, split, nsplit, pbase;
 };
 
-// K^T operand reads of wave half H for both 16-token halves of the tile:
-// k-step ks < 16 is latent dims 32 ks .. from the padded rows, ks >= 16 rope.
-template <int H>
-__device__ __forceinline__ void scores_half(const char* tile, uint32_t kbase, uint32_t rbase,
-                                            const u32x4 (&qv)[kKHalf], f32x4& s0, f32x4& s1) {
+// Merge of a 128-head unit's split partials by the whole workgroup, run after
+// the stream (the ring's LDS is free).  Threads 0..127, one per head, load
+// every split's (m, l) of their head (16 splits in flight), form (M, L) and the
+// lse, and stage the split weights c_s = exp2(m_s - M) / L for up to
+// kMergeChunk splits in LDS.  Then all threads stream the output as float4
+// columns, consecutive threads on consecutive columns (coalesced), 8 columns
+// x 4 splits = 32 loads in flight per thread, so the merge takes a handful of
+// memory round trips.  Splits are combined in index order, so the result does
+// not depend on which piece arrived last.  The partials were published with an
+// agent-scope release; the caller has performed the matching acquire.
+constexpr int kMergeChunk = 64;  // split weights staged per pass: 64 x 128 floats
+constexpr int kMergeCols = 8;    // float4 columns per thread per round
+constexpr int kMergeSplits = 4;  // splits per round
+__device__ __forceinline__ void merge_unit(const float* pb, int ns, int slot_floats, float* out, float* lse,
+                                           float* lds) {
+  float* ml = lds;                 // M[128], 1/L[128]
+  float* coef = lds + 2 * kHeads;  // [split in pass][head]
+  const int tid = threadIdx.x;
+  __syncthreads();  // the LDS is free: every wave is past its last tile (or the previous merge)
+  if (tid < kHeads) {
+    float M = -INFINITY, L = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 16) {
+      float mt[16], lt[16];
 #pragma unroll
-  for (int jb = 0; jb < kKHalf; jb += 3) {
-    u32x4 ka[3], kb[3];
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = s0 + i < ns;
+        const float* ps = pb + (size_t)(ok ? s0 + i : 0) * slot_floats;
+        mt[i] = ok ? ps[tid] : -INFINITY;
+        lt[i] = ok ? ps[kHeads + tid] : 0.f;
+      }
+      float Mc = M;
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int ks = H * kKHalf + jb + u;
-      const uint32_t off0 = ks < 16 ? kbase + 64 * ks : rbase + 64 * (ks - 16);
-      const uint32_t off1 = ks < 16 ? kbase + 16 * kRowPad + 64 * ks : rbase + 256 + 64 * (ks - 16);
-      ka[u] = *reinterpret_cast<const u32x4*>(tile + off0);
-      kb[u] = *reinterpret_cast<const u32x4*>(tile + off1);
+      for (int i = 0; i < 16; ++i) Mc = fmaxf(Mc, mt[i]);
+      L *= fast_exp2(M - Mc);  // 0 on the first chunk
+#pragma unroll
+      for (int i = 0; i < 16; ++i) L += lt[i] * fast_exp2(mt[i] - Mc);
+      M = Mc;
     }
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      s0 = mfma16(ka[u], qv[jb + u], s0);
-      s1 = mfma16(kb[u], qv[jb + u], s1);
+    ml[tid] = M;
+    ml[kHeads + tid] = 1.f / L;
+    lse[tid] = (M + __log2f(L)) * kLn2;
+  }
+  const f32x4* o4 = reinterpret_cast<const f32x4*>(pb + partial_o_offset(kHeads));
+  f32x4* out4 = reinterpret_cast<f32x4*>(out);
+  const int slot4 = slot_floats / 4;
+  constexpr int kCols4 = kHeads * kDv / 4;  // 16384 float4 per unit
+  for (int c0 = 0; c0 < ns; c0 += kMergeChunk) {
+    const int nc = min(kMergeChunk, ns - c0);
+    __syncthreads();  // (M, 1/L) visible; the previous pass's weights consumed
+    for (int i = tid; i < nc * kHeads; i += kThreads) {
+      const int sp = i >> 7, h = i & (kHeads - 1);
+      coef[i] = fast_exp2(pb[(size_t)(c0 + sp) * slot_floats + h] - ml[h]) * ml[kHeads + h];
     }
-    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    for (int e0 = tid; e0 < kCols4; e0 += kThreads * kMergeCols) {
+      f32x4 acc[kMergeCols];
+#pragma unroll
+      for (int u = 0; u < kMergeCols; ++u) acc[u] = c0 == 0 ? f32x4{} : out4[e0 + kThreads * u];
+      for (int s0 = 0; s0 < nc; s0 += kMergeSplits) {
+        f32x4 v[kMergeCols][kMergeSplits];
+#pragma unroll
+        for (int u = 0; u < kMergeCols; ++u)
+#pragma unroll
+          for (int t = 0; t < kMergeSplits; ++t) {
+            const bool ok = s0 + t < nc;
+            v[u][t] = ok ? o4[(size_t)(c0 + s0 + t) * slot4 + e0 + kThreads * u] : f32x4{};
+          }
+#pragma unroll
+        for (int u = 0; u < kMergeCols; ++u) {
+          const int h = (e0 + kThreads * u) >> 7;  // 128 float4 per head row
+#pragma unroll
+          for (int t = 0; t < kMergeSplits; ++t) {
+            const float c = s0 + t < nc ? coef[(s0 + t) * kHeads + h] : 0.f;
+            acc[u] += c * v[u][t];
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeCols; ++u) out4[e0 + kThreads * u] = acc[u];
+    }
   }
 }
 
@@ -173,13 +349,11 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
                   const int32_t* __restrict__ bt, const int32_t* __restrict__ seqlens,
                   const int32_t* __restrict__ indices, float* __restrict__ out, float* __restrict__ lse,
                   int32_t* err, int32_t* counters, float* partials, unsigned long long* timeline) {
-  __shared__ __attribute__((aligned(16))) float merge_lds[merge_lds_floats(kThreads, kHeads)];
   __shared__ int sh_last;
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63;
-  const int hg = wave >> 1, half = wave & 1;  // head group of the pair, half of the pair
-  const int lr = lane & 15, lg = lane >> 4;   // MFMA row/column, lane group
+  const int n = lane & 31, g = lane >> 5;  // MFMA row/column, lane group
 
   unsigned long long* tl = timeline ? timeline + kTimelineWords * blockIdx.x : nullptr;
   if (tl && tid == 0) {
@@ -208,8 +382,7 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     nblk += (uni(t.z) - uni(t.y) + kBlk - 1) / kBlk;
   }
 
-  // unit = (b * Tq + t) * 2 + head block; q token row (b * Tq + t)
-  const int hblocks = p.hq / kHeads;
+  // unit = b * Tq + t (one unit per query token)
   const int page_mask = (1 << p.log2_page) - 1;
   auto row_of = [&](int b, int tok) -> long long {  // cache row of token `tok` of sequence b
     int lp = min(tok >> p.log2_page, p.max_pages - 1);
@@ -221,68 +394,98 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     return (long long)pg * (1 << p.log2_page) + (tok & page_mask);
   };
 
+  // block-table entry of block j of item I (dense)
+  auto bt_entry = [&](const Item& I, int j) -> const int32_t* {
+    const int lp = min((I.tb + j * kBlk) >> p.log2_page, p.max_pages - 1);
+    return bt + (size_t)(I.unit / p.q_tokens) * p.max_pages + lp;
+  };
+
   // ---- issue the tile of block (item I, block j) into the stage at dst
-  // row transfer q < 4: token j2 = wave + 8q, its first 1024 bytes -> LDS row j2 (1040 apart)
-  // rope transfer (lanes 0..31): lane l takes token wave + 8(l/8), chunk (l%8) ^ ((l/8)%2)
-  const int rq = (lane >> 3) & 3;  // token slot of this lane's rope chunk
-  const int rchunk = (lane & 7) ^ (rq & 1);
-  auto fetch = [&](const Item& I, int j, char* dst) {
-    const int b = I.unit / hblocks / p.q_tokens;
+  // row transfer q < 8: token 8 wave + q, its first 1024 bytes -> LDS row row_lds(t)
+  // rope transfer: lane l takes token rt = 8 wave + l / 8, LDS slot l % 8 holds chunk (l % 8) ^ ((rt / 2) % 8)
+  const int rslot = lane >> 3;
+  const int rt = kRowsPerWave * wave + rslot;
+  const int rchunk = (lane & 7) ^ ((rt >> 1) & 7);
+  // dense: a 32-token block lies inside one page (pages hold >= 32 tokens), so
+  // its rows are contiguous; rows past the item end re-read the last valid row.
+  struct DenseFetch {
+    const char* base;
+    int nvalid;
+  };
+  auto dense_prep = [&](const Item& I, int j, int pg) -> DenseFetch {
     const int tok0 = I.tb + j * kBlk;
-    const int tl_last = min(tok0 + kBlk, I.te) - 1;  // rows past the item end re-read the last valid row
-    char* rope_dst = dst + kRopeOff + wave * kRopeWave;
-    if constexpr (!SPARSE) {
-      // a 32-token block lies inside one page (pages hold >= 32 tokens): rows are contiguous
-      const char* base = reinterpret_cast<const char*>(kc) + row_of(b, tok0) * kRowBytes;
-      const int nvalid = tl_last - tok0 + 1;
-#pragma unroll
-      for (int q = 0; q < kRowsPerWave; ++q) {
-        const int j2 = wave + kWaves * q;
-        lds_dma16(base + (size_t)min(j2, nvalid - 1) * kRowBytes + 16 * lane, dst + j2 * kRowPad);
-      }
-      const int t = min(wave + kWaves * rq, nvalid - 1);
-      if (lane < 32) lds_dma16(base + (size_t)t * kRowBytes + 1024 + 16 * rchunk, rope_dst);
-    } else {
-      const int32_t* idx = indices + (size_t)(I.unit / hblocks) * p.topk;
-      const int L = uni(seqlens[b]);
-      const char* rope_src = nullptr;
-#pragma unroll
-      for (int q = 0; q < kRowsPerWave; ++q) {
-        const int j2 = wave + kWaves * q;
-        int tok = uni(idx[min(tok0 + j2, tl_last)]);
-        if ((unsigned)tok >= (unsigned)L) {
-          atomicOr(err, kErrIndex);
-          tok = 0;
-        }
-        const char* row = reinterpret_cast<const char*>(kc) + row_of(b, tok) * kRowBytes;
-        lds_dma16(row + 16 * lane, dst + j2 * kRowPad);
-        if (rq == q) rope_src = row;
-      }
-      if (lane < 32) lds_dma16(rope_src + 1024 + 16 * rchunk, rope_dst);
+    if ((unsigned)pg >= (unsigned)p.num_pages) {
+      atomicOr(err, kErrPage);
+      pg = pg < 0 ? 0 : p.num_pages - 1;
     }
+    DenseFetch F;
+    F.base = reinterpret_cast<const char*>(kc) + ((long long)pg * (1 << p.log2_page) + (tok0 & page_mask)) * kRowBytes;
+    F.nvalid = min(kBlk, I.te - tok0);
+    return F;
+  };
+  auto dense_piece = [&](const DenseFetch& F, int q, char* dst) __attribute__((always_inline)) {
+    if (q < kRowsPerWave) {
+      const int t = kRowsPerWave * wave + q;
+      lds_dma16s(F.base + (size_t)min(t, F.nvalid - 1) * kRowBytes, 16 * lane, dst + row_lds(t));
+    } else {
+      lds_dma16s(F.base, min(rt, F.nvalid - 1) * kRowBytes + 1024 + 16 * rchunk, dst + kRopeOff + 1024 * wave);
+    }
+  };
+  // index-sparse: rows gathered through the index list
+  auto sparse_fetch = [&](const Item& I, int j, char* dst) {
+    const int b = I.unit / p.q_tokens;
+    const int tok0 = I.tb + j * kBlk;
+    const int tl_last = min(tok0 + kBlk, I.te) - 1;
+    const int32_t* idx = indices + (size_t)I.unit * p.topk;
+    const int L = uni(seqlens[b]);
+    const char* rope_src = nullptr;
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) {
+      const int t = kRowsPerWave * wave + q;
+      int tok = uni(idx[min(tok0 + t, tl_last)]);
+      if ((unsigned)tok >= (unsigned)L) {
+        atomicOr(err, kErrIndex);
+        tok = 0;
+      }
+      const char* row = reinterpret_cast<const char*>(kc) + row_of(b, tok) * kRowBytes;
+      lds_dma16(row + 16 * lane, dst + row_lds(t));
+      if (rslot == q) rope_src = row;
+    }
+    lds_dma16(rope_src + 1024 + 16 * rchunk, dst + kRopeOff + 1024 * wave);
   };
 
   // LDS read addresses of the MFMA operands: one base per operand, the rest immediate
-  //   K, half hh, k-step ks < 16: token 16hh + lr, dims 32ks + 8lg -> lr*1040 + 16lg + hh*16*1040 + 64ks
-  //   rope, half hh, k-step 16 + r: token t = 16hh + lr, chunk 4r + lg, stored by wave t%8 at slot t/8
-  //     -> rope + (lr%8)*544 + (lr/8)*128 + 16 (lg ^ lr/8) + hh*256 + r*64
-  //   V, dv group g4, slot i: token tau(lg, i) = 4lg + i (i < 4), 16 + 4lg + i-4 (i >= 4),
-  //     chunk 16 g4 + lr -> (4lg*1040 + 16lr) + (i<4 ? i : 12 + i)*1040 + 256 g4
-  const uint32_t kbase = lr * kRowPad + 16 * lg;
-  const uint32_t rbase = kRopeOff + (lr & 7) * kRopeWave + 128 * (lr >> 3) + 16 * (lg ^ (lr >> 3));
-  const uint32_t vbase = 4 * lg * kRowPad + 16 * lr + 512 * half;  // this wave's dv half
-
-  // Q^T operand: lane holds head 16 hg + lr, dims 288 half + 32 j + 8 lg .. +8.
-  // The q loads are followed by kDmaPerWave stores of zero into the unused
-  // words 4, 8, .., 20 of the workspace header: the compiler counts those (it
-  // does not see the asm transfers), so it waits for q with vmcnt(kDmaPerWave),
-  // which leaves exactly the next tile's transfers in flight, instead of vmcnt(0).
-  u32x4 qv[kKHalf];
-  auto load_q = [&](int unit) {
-    const size_t row = (size_t)(unit / hblocks) * p.hq + (size_t)(unit % hblocks) * kHeads + hg * kHG + lr;
-    const uint16_t* qp = qg + row * kDqk + 8 * lg + 32 * kKHalf * half;
+  //   K, k-step ks < 32: token n, dims 16 ks + 8 g -> row_lds(n) + 16 g + 32 ks
+  //   rope, k-step 32 + r: token n, chunk c = 2 r + g at slot c ^ ((n / 2) % 8)
+  //   V^T (transposed reads, 16-lane groups G = lane / 16, j = lane % 16): block d
+  //     of 32 dv, k-block b, half c: lane supplies token 16 b + 8 c + 4 g + j / 4,
+  //     dv 32 d + 16 (G % 2) + 4 (j % 4) .. +3, and receives row dv 32 d + (lane % 32)
+  //     at tokens 16 b + 8 c + 4 g + e; row_lds of those tokens is lane-constant
+  //     apart: + 17408 b + 8736 c (the 4-token groups keep their slot pattern)
+  const uint32_t kbase = row_lds(n) + 16 * g;
+  uint32_t rope_off[4];
 #pragma unroll
-    for (int j = 0; j < kKHalf; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qp + 32 * j);
+  for (int r = 0; r < 4; ++r) rope_off[r] = kRopeOff + 128 * n + 16 * ((2 * r + g) ^ ((n >> 1) & 7));
+  const uint32_t vbase = row_lds(4 * g + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+
+  // Q^T operand: lane holds head 32 wave + n, dims 16 ks + 8 g .. +8.  The 32
+  // latent k-steps stay in registers (128 VGPRs) for the whole item; the 4 rope
+  // k-steps go to the wave's own LDS area in the same lane order (one transfer
+  // per k-step, read back conflict free).  The q loads are followed by
+  // kDmaPerWave stores of zero into unused words of the workspace header: the
+  // compiler counts those (it does not see the asm transfers), so it waits for
+  // q with vmcnt(kDmaPerWave), which leaves exactly the next tile's transfers
+  // in flight, instead of vmcnt(0).
+  u32x4 qv[kLatentSteps];
+  char* qrope_w = qrope[wave];
+  auto load_q = [&](int unit) {
+    const size_t row = (size_t)unit * p.hq + kHW * wave + n;
+    const uint16_t* qp = qg + row * kDqk + 8 * g;
+#pragma unroll
+    for (int j = 0; j < kLatentSteps; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qp + 16 * j);
+#pragma unroll
+    for (int r = 0; r < kKSteps - kLatentSteps; ++r)
+      lds_dma16(reinterpret_cast<const char*>(qp + 16 * (kLatentSteps + r)), qrope_w + 1024 * r);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) err[4 * (i + 1)] = 0;  // every lane, same word: no branch
@@ -310,70 +513,138 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       }
     }
   };
+  // The page of the tile after the one being fetched is loaded asynchronously
+  // (into pg_pref) before that fetch's transfers, so the wait at the top of
+  // the next iteration covers it and the fetch never waits on the block table.
+  auto page_now = [&](const Item& I, int j) { return SPARSE ? 0 : uni(*bt_entry(I, j)); };
+  uint32_t pg_pref = 0;
   load_q(cur.unit);
-  fetch(pI, p_j, stage<0>());
+  auto fetch_now = [&](const Item& I, int j, char* dst, int pg) {
+    if constexpr (SPARSE) {
+      sparse_fetch(I, j, dst);
+    } else {
+      const DenseFetch F = dense_prep(I, j, pg);
+#pragma unroll
+      for (int q = 0; q < kDmaPerWave; ++q) dense_piece(F, q, dst);
+    }
+  };
+  fetch_now(pI, p_j, ring[0], page_now(pI, p_j));
   advance(pI, p_it, p_j, p_nb);
   if (nblk > 1) {
-    fetch(pI, p_j, stage<1>());
-    advance(pI, p_it, p_j, p_nb);
+    const int pg1 = page_now(pI, p_j);
+    Item nI = pI;
+    int n_it = p_it, n_j = p_j, n_nb = p_nb;
+    advance(nI, n_it, n_j, n_nb);
+    if constexpr (!SPARSE) pg_pref = load_dword_async(nblk > 2 ? bt_entry(nI, n_j) : bt);
+    fetch_now(pI, p_j, ring[1], pg1);
+    pI = nI;
+    p_it = n_it;
+    p_j = n_j;
+    p_nb = n_nb;
   } else {
-    fetch(cur, 0, stage<1>());
+    fetch_now(cur, 0, ring[1], 0);
   }
 
-  float m_run = -INFINITY, l_run = 0.f;  // per lane: head lr of the pair (four lanes per head)
-  f32x4 o[2][8];                          // dv group 2 half + gg, column c: dv = 128 g4 + 8 lr + c; rows heads 4lg+r
-#pragma unroll
-  for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) o[gg][c] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;  // head n of the wave (lanes n and n + 32 agree on m_run)
+  // O^T block d: rows dv 32 d + row, columns heads (in a[16 d .. 16 d + 15])
+  acc_reserve();
+  acc_zero();
   bool fresh = true;  // no block of the current item seen yet
+  int pend0 = 0, pend1 = 0, npend = 0;  // units to merge after the stream
 
-  // one block: tile k in stage ST; the fetch two blocks ahead goes to stage (ST + 2) % 3
-  auto step = [&](auto stage_c, int k) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage_c)::value;
+  // one block: tile k in stage st = k % 3; the fetch two blocks ahead goes to stage (k + 2) % 3
+  int st = 0, st2 = 2;
+  auto step = [&](int k) __attribute__((always_inline)) {
     // tile k (and any q loads, issued before tile k+1's transfers) has landed
-    // for every wave; tile k-1's stage and the exchange buffer are free
+    // for every wave; every wave is done with tile k-1's stage
     wait_vmcnt<kDmaPerWave>();
     wait_lds();
     barrier();
-    const char* tile = stage<ST>();
+    const char* tile = ring[st];
     const int tok0 = cur.tb + cur_j * kBlk;
     const int nv = min(kBlk, cur.te - tok0);
 
-    // partial S^T of this wave's dims half, then the pair's sum
-    f32x4 s0 = {}, s1 = {};
-    if (half == 0)
-      scores_half<0>(tile, kbase, rbase, qv, s0, s1);
-    else
-      scores_half<1>(tile, kbase, rbase, qv, s0, s1);
-    xch[wave][0][lane] = s0;
-    xch[wave][1][lane] = s1;
+    // The fetch of the tile two blocks ahead (a filler past the end): its
+    // transfers go between the score MFMAs, unless this tile ends an item and
+    // the next item's q loads have to be issued before them (the vmcnt waits
+    // count on that order), or the rows are gathered through indices.
     const bool item_ends = cur_j == cur_nb - 1;
-    if (item_ends && k + 1 < nblk) {
+    const bool q_next = item_ends && k + 1 < nblk;
+    const Item fI = k + 2 < nblk ? pI : cur;
+    const int fj = k + 2 < nblk ? p_j : cur_j;
+    int fpg = 0;  // page of the fetched block (dense; the filler reads page 0, never used)
+    if (k + 2 < nblk) {
+      if constexpr (!SPARSE) fpg = take_dword(pg_pref);
+      Item nI = pI;
+      int n_it = p_it, n_j = p_j, n_nb = p_nb;
+      advance(nI, n_it, n_j, n_nb);
+      if constexpr (!SPARSE) pg_pref = load_dword_async(k + 3 < nblk ? bt_entry(nI, n_j) : bt);
+      pI = nI;
+      p_it = n_it;
+      p_j = n_j;
+      p_nb = n_nb;
+    }
+    DenseFetch F = {nullptr, 0};
+    if constexpr (!SPARSE) F = dense_prep(fI, fj, fpg);
+    char* fdst = ring[st2];
+
+    // S^T = K Q^T, 36 k-steps, operands read kPreS k-steps ahead
+    f32x16 s;
+    auto scores = [&](auto inter_c) __attribute__((always_inline)) {
+      constexpr bool kInter = decltype(inter_c)::value;
+      u32x4 qr[kKSteps - kLatentSteps];  // rope part of Q^T, read at the start of the chain
+#pragma unroll
+      for (int r = 0; r < kKSteps - kLatentSteps; ++r)
+        qr[r] = *reinterpret_cast<const u32x4*>(qrope_w + 1024 * r + 16 * lane);
+      u32x4 kop[kKSteps];
+      auto kload = [&](int ks) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(tile + (ks < kLatentSteps ? kbase + 32 * ks : rope_off[ks - kLatentSteps]));
+      };
+#pragma unroll
+      for (int ks = 0; ks < kPreS; ++ks) kop[ks] = kload(ks);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        if (ks + kPreS < kKSteps) kop[ks + kPreS] = kload(ks + kPreS);
+        if (ks == 0)
+          mfma32_v_first(s, kop[0], qv[0]);
+        else if (ks < kLatentSteps)
+          mfma32_v(s, kop[ks], qv[ks]);
+        else
+          mfma32_v(s, kop[ks], qr[ks - kLatentSteps]);
+        if constexpr (kInter)
+          if ((ks & 3) == 2) dense_piece(F, ks >> 2, fdst);
+      }
+    };
+    if (!SPARSE && !q_next)
+      scores(std::true_type{});
+    else
+      scores(std::false_type{});
+    mfma32_v_drain();
+    if (q_next) {
       // q of the next item replaces this one as soon as the scores no longer need it
       load_q(uni(items[cur_it + 1].x));
     }
-    if (k + 2 < nblk) {
-      fetch(pI, p_j, stage<(ST + 2) % 3>());
-      advance(pI, p_it, p_j, p_nb);
-    } else {
-      fetch(cur, cur_j, stage<(ST + 2) % 3>());
-    }
-    wait_lds();
-    barrier();
-    s0 += xch[wave ^ 1][0][lane];  // IEEE addition commutes: both waves of the pair get the same sum
-    s1 += xch[wave ^ 1][1][lane];
-
-    // scores (base 2), masked past the item end; x[i] is token tau(lg, i)
-    float x[8];
+    if (SPARSE || q_next) {
+      if constexpr (SPARSE) {
+        sparse_fetch(fI, fj, fdst);
+      } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (4 * lg + i < nv) ? s0[i] * p.scale_log2 : -INFINITY;
-      x[4 + i] = (16 + 4 * lg + i < nv) ? s1[i] * p.scale_log2 : -INFINITY;
+        for (int q = 0; q < kDmaPerWave; ++q) dense_piece(F, q, fdst);
+      }
     }
-    float bmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+
+    // scores (base 2), masked past the item end; register r is token 8 (r / 4) + 4 g + r % 4
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (8 * (r >> 2) + 4 * g + (r & 3) < nv) ? s[r] * p.scale_log2 : -INFINITY;
+    float bmax = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, x[r]);
+    {  // max with the other half of the wave (lanes n and n + 32 hold the same head)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, bmax),
+                                                      __builtin_bit_cast(uint32_t, bmax), false, false);
+      bmax = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+    }
     // move the reference max only when some head needs it
     const bool need = bmax > m_run + kLazy;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -381,89 +652,72 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       const float alpha = fast_exp2(m_run - mnew);
       l_run *= alpha;
       m_run = mnew;
-      if (!fresh) {  // O rows of register r are heads 4 lg + r
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float a = __shfl(alpha, 4 * lg + rr);
-#pragma unroll
-          for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) o[gg][c][rr] *= a;
-        }
-      }
+      if (!fresh) acc_scale(alpha);  // every accumulator of this lane belongs to head n
     }
     fresh = false;
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[i] = fast_exp2(x[i] - m_run);
-      psum += x[i];
+    for (int r = 0; r < 16; ++r) {
+      x[r] = fast_exp2(x[r] - m_run);
+      psum += x[r];
     }
     l_run += psum;
-    const u32x4 pa = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+    // P^T operand of k-block b: tokens {16 b + 4 g + i, 16 b + 8 + 4 g + i} = registers 8 b .. 8 b + 7
+    u32x4 pb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      pb[b] = u32x4{pack_bf16(x[8 * b], x[8 * b + 1]), pack_bf16(x[8 * b + 2], x[8 * b + 3]),
+                    pack_bf16(x[8 * b + 4], x[8 * b + 5]), pack_bf16(x[8 * b + 6], x[8 * b + 7])};
 
-    // O += P V over this wave's dv half.  Rows past the item end hold a copy of
-    // the last valid row (finite) and their probabilities are exactly 0, so
-    // they add nothing.
-    u32x4 vr[2][8];
+    // O^T += V^T P^T.  Rows past the item end hold a copy of the last valid row
+    // (finite) and their probabilities are exactly 0, so they add nothing.
+    // 32 MFMAs m = 16 b + d (k-block b, dv block d), V^T operands read kPreV ahead
+    {
+      u32x4 vop[32];
+      auto vload = [&](int m) -> u32x4 {
+        const char* a = tile + vbase + 64 * (m & 15) + 17408 * (m >> 4);
+        const u32x2 lo = lds_read_tr16(a), hi = lds_read_tr16(a + 8736);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
 #pragma unroll
-    for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        vr[gg][i] = *reinterpret_cast<const u32x4*>(tile + vbase + (i < 4 ? i : 12 + i) * kRowPad + 256 * gg);
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        // B operand of column 8 lr + c: element i = V[tau(lg, i)][col], two per word
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 vb;
-#pragma unroll
-        for (int pi = 0; pi < 4; ++pi)
-          vb[pi] = __builtin_amdgcn_perm(vr[gg][2 * pi + 1][c >> 1], vr[gg][2 * pi][c >> 1], sel);
-        o[gg][c] = mfma16(pa, vb, o[gg][c]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int m = 0; m < kPreV; ++m) vop[m] = vload(m);
+      unroll<32>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m + kPreV < 32) vop[m + kPreV] = vload(m + kPreV);
+        pv1<m & 15>(vop[m], pb[m >> 4]);
+      });
     }
 
     if (item_ends) {
       // -------- finish the item: this workgroup holds the whole piece
-      float l_tot = l_run + __shfl_xor(l_run, 16);
-      l_tot += __shfl_xor(l_tot, 32);
-      const size_t qrow = (size_t)cur.unit * kHeads;  // first head of the unit: (b Tq + t) Hq + 64 hb
-      const int h0 = hg * kHG;                        // pair's first head in the unit
-      if (cur.nsplit == 1) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int hh = 4 * lg + rr;
-          const float inv = 1.f / __shfl(l_tot, hh);
-          float* orow = out + (qrow + h0 + hh) * kDv + 256 * half + 8 * lr;
-#pragma unroll
-          for (int gg = 0; gg < 2; ++gg) {
-            *reinterpret_cast<f32x4*>(orow + 128 * gg) =
-                f32x4{o[gg][0][rr] * inv, o[gg][1][rr] * inv, o[gg][2][rr] * inv, o[gg][3][rr] * inv};
-            *reinterpret_cast<f32x4*>(orow + 128 * gg + 4) =
-                f32x4{o[gg][4][rr] * inv, o[gg][5][rr] * inv, o[gg][6][rr] * inv, o[gg][7][rr] * inv};
-          }
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const size_t qrow = (size_t)cur.unit * kHeads;  // first head of the unit: (b Tq + t) Hq
+      const int hh = kHW * wave + n;                  // this lane's head in the unit
+      // register 4 jj + i of block d is dv 32 d + 8 jj + 4 g + i
+      const bool whole = cur.nsplit == 1;
+      float* ps = partials + (size_t)(cur.pbase + cur.split) * p.slot_floats;
+      const float scale = whole ? 1.f / l_tot : 1.f;
+      float* orow = whole ? out + (qrow + hh) * kDv + 4 * g : ps + partial_o_offset(kHeads) + (size_t)hh * kDv + 4 * g;
+      if (g == 0) {
+        if (whole) {
+          lse[qrow + hh] = (m_run + __log2f(l_tot)) * kLn2;
+        } else {
+          ps[hh] = m_run;
+          ps[kHeads + hh] = l_tot;
         }
-        if (half == 0 && lane < 16) lse[qrow + h0 + lane] = (m_run + __log2f(l_tot)) * kLn2;
-      } else {
-        float* ps = partials + (size_t)(cur.pbase + cur.split) * p.slot_floats;
-        if (half == 0 && lane < 16) {
-          ps[h0 + lane] = m_run;
-          ps[kHeads + h0 + lane] = l_tot;
-        }
-        float* po = ps + partial_o_offset(kHeads) + (size_t)h0 * kDv + 256 * half;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int hh = 4 * lg + rr;
-          float* orow = po + (size_t)hh * kDv + 8 * lr;
-#pragma unroll
-          for (int gg = 0; gg < 2; ++gg) {
-            *reinterpret_cast<f32x4*>(orow + 128 * gg) = f32x4{o[gg][0][rr], o[gg][1][rr], o[gg][2][rr], o[gg][3][rr]};
-            *reinterpret_cast<f32x4*>(orow + 128 * gg + 4) = f32x4{o[gg][4][rr], o[gg][5][rr], o[gg][6][rr], o[gg][7][rr]};
-          }
-        }
+      }
+      wait_xdl_result();
+      unroll<16>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        unroll<4>([&](auto jc) {
+          constexpr int jj = decltype(jc)::value;
+          *reinterpret_cast<f32x4*>(orow + 32 * d + 8 * jj) =
+              f32x4{acc_read<16 * d + 4 * jj>(), acc_read<16 * d + 4 * jj + 1>(), acc_read<16 * d + 4 * jj + 2>(),
+                    acc_read<16 * d + 4 * jj + 3>()} *
+              scale;
+        });
+      });
+      if (!whole) {
         if (p.reduce == CC_REDUCE_FUSED) {
           __syncthreads();  // every wave's share of the partial is written
           if (tid == 0) {
@@ -475,9 +729,13 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
           }
           __syncthreads();
           if (uni(sh_last)) {
-            merge_splits<kThreads>(partials + (size_t)cur.pbase * p.slot_floats, cur.nsplit, p.slot_floats,
-                                   kHeads, kDv, out + qrow * kDv, lse + qrow, merge_lds);
-            if (tid == 0) __hip_atomic_store(&counters[cur.unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // merged after the stream: only a chunk's first and last items can be split
+            if (npend == 0) {
+              pend0 = cur.unit;
+            } else {
+              pend1 = cur.unit;
+            }
+            ++npend;
           }
         }
       }
@@ -488,22 +746,27 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
         cur_nb = (cur.te - cur.tb + kBlk - 1) / kBlk;
         m_run = -INFINITY;
         l_run = 0.f;
-#pragma unroll
-        for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) o[gg][c] = f32x4{};
+        acc_zero();
         fresh = true;
       }
     } else {
       ++cur_j;
     }
   };
-  for (int k = 0; k < nblk; k += 3) {
-    step(IC<0>{}, k);
-    if (k + 1 < nblk) step(IC<1>{}, k + 1);
-    if (k + 2 < nblk) step(IC<2>{}, k + 2);
+  for (int k = 0; k < nblk; ++k) {
+    step(k);
+    st = st == 2 ? 0 : st + 1;
+    st2 = st2 == 2 ? 0 : st2 + 1;
   }
-  if (tl && tid == 0) tl[1] = tl[2] = tl[3] = tl[4] = __builtin_amdgcn_s_memrealtime();
+  if (tl && tid == 0) tl[1] = tl[2] = __builtin_amdgcn_s_memrealtime();
+  // units this workgroup completed last: merge their partials (no q or accumulators live here)
+  for (int i = 0; i < npend; ++i) {
+    const int unit = uni(i == 0 ? pend0 : pend1);
+    merge_unit(partials + (size_t)uni(unit_pbase[unit]) * p.slot_floats, uni(unit_nsplit[unit]), p.slot_floats,
+               out + (size_t)unit * kHeads * kDv, lse + (size_t)unit * kHeads, reinterpret_cast<float*>(ring[0]));
+    if (tid == 0) __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tl && tid == 0) tl[3] = tl[4] = __builtin_amdgcn_s_memrealtime();
 }
 
 int ilog2(int x) {

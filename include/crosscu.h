@@ -115,8 +115,9 @@ typedef struct cc_problem {
  * cc_device_query).  tile_tokens: the cost unit of the equal split (any
  * value >= 1 plans; cc_decode needs a multiple of 32).  heads_per_unit: query
  * heads processed together on one K/V stream (divides Hq / Hkv; cc_decode's
- * GQA kernel needs Hq / Hkv, its MLA kernels need 64, so the two head blocks
- * of a query token are adjacent units).  policy: CC_POLICY_*.               */
+ * GQA kernel needs Hq / Hkv, its MLA kernels need 128: all heads of a query
+ * token form one unit, so each latent row is read once per query token).
+ * policy: CC_POLICY_*.                                                      */
 typedef struct cc_plan_opts {
   int32_t num_cus;
   int32_t num_xcds;

@@ -187,16 +187,16 @@ def test_mla_decode_rejects_before_any_launch(lib):
     sl = np.array([100, 20], np.int32)
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails a host check first
 
-    def call(p, hu=64, tile=32, indices=None):
+    def call(p, hu=128, tile=32, indices=None):
         blob = B.plan(p, sl, None, num_cus=8, num_xcds=1, tile_tokens=tile, heads_per_unit=hu)
         return lib.cc_decode(ctypes.byref(p), blob.ctypes.data_as(ctypes.c_void_p), fake, fake, fake, None, fake,
                              fake, indices, fake, fake, fake, B.workspace_size(blob), None)
 
     prob = B.problem(**kw)
-    assert call(prob, hu=128) == B.CC_ERR_UNSUPPORTED
+    assert call(prob, hu=64) == B.CC_ERR_UNSUPPORTED
     assert call(prob, tile=48) == B.CC_ERR_UNSUPPORTED
     assert call(B.problem(**{**kw, "page_size": 16, "max_pages_per_seq": 7, "num_pages": 9})) == B.CC_ERR_UNSUPPORTED
     assert call(B.problem(**{**kw, "head_dim_v": 448})) == B.CC_ERR_UNSUPPORTED
     sparse = B.problem(**{**kw, "mode": B.MODE_MLA_SPARSE, "topk": 16})
     assert call(sparse) == B.CC_ERR_INVALID          # no indices
-    assert B.kernel_heads_per_unit(prob) == 64 and B.kernel_heads_per_unit(sparse) == 64
+    assert B.kernel_heads_per_unit(prob) == 128 and B.kernel_heads_per_unit(sparse) == 128

@@ -60,7 +60,7 @@ def test_mla_ragged_and_single_token(dev):
 def test_mla_full_size_sampled(dev):
     wl = W.make_workload(MLA)
     s, plan = run(wl, *dev, tag="mla-full")
-    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1], heads_per_unit=64, policy=PL.POLICY_STREAMK_COST)
+    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1], heads_per_unit=128, policy=PL.POLICY_STREAMK_COST)
     assert plan.tobytes() == ref["blob"]
     split_tok = sorted({u // 2 for u, n in enumerate(ref["unit_nsplit"]) if n > 1})
     rng = np.random.default_rng(7)
