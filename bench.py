@@ -60,7 +60,20 @@ def log(args, *a):
 
 
 def time_steps(torch, run, steps, warmup, flush=None):
-    """Per-step event timings (ms) of run(); flush() runs untimed before each step."""
+    """Per-step event timings (ms) of run(); flush() runs untimed before each step.
+
+    Python's garbage collector is paused while steps are enqueued: a collection
+    between a step's two events would show up as GPU idle time inside it."""
+    import gc
+    gc.collect()
+    gc.disable()
+    try:
+        return _time_steps(torch, run, steps, warmup, flush)
+    finally:
+        gc.enable()
+
+
+def _time_steps(torch, run, steps, warmup, flush):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         if flush:
@@ -228,7 +241,8 @@ def main():
     dirty, flags = B.workspace_check(plan, s.workspace)
     assert dirty == 0 and flags == 0, "workspace left dirty"
     log(args, f"stream-k fused: {st}")
-    tline = timeline_pass(torch, B, s, cus, xcds, flush)
+    workers = int(plan.view(np.int32)[11])  # plan header: worker (chunk) count
+    tline = timeline_pass(torch, B, s, workers, xcds, flush)
     log(args, f"timeline: {tline}")
 
     variants = {}

@@ -723,6 +723,7 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
+  if (a.mode != CC_MODE_GQA) return launch_mla_combine(a, s);  // MLA partials hold fp16 rows
   combine_kernel<<<a.units, kCombineThreads, 0, s>>>(a.hq, a.hkv, a.hq / a.hkv, a.hpu, a.dv,
                                                      a.slot_floats, a.unit_nsplit, a.unit_pbase,
                                                      a.partials, a.out, a.lse);

@@ -13,7 +13,7 @@
 // dense contractions on v_mfma_f32_32x32x16_bf16 tiles, one wave per SIMD with
 // the whole register file:
 //   S^T[32 tokens][32 heads] = K[32][576] . Q^T[576][32]   (36 k-steps; Q^T in
-//     144 VGPRs for the whole item),
+//     112 VGPRs and 8 KiB of LDS per wave for the whole item),
 //   O^T[512][32 heads]      += V^T[512][32] . P^T[32][32]  (16 column blocks of
 //     32 dv x 32 heads: 256 accumulators, held in AGPRs).
 // S^T leaves lane (n, g) with head n's scores of tokens 8j + 4g + i, which is
@@ -67,6 +67,7 @@ constexpr int kRowBytes = kDqk * 2;         // 1152
 constexpr int kBlk = 32;                    // tokens per tile
 constexpr int kKSteps = kDqk / 16;          // 36 k-steps of q.k
 constexpr int kLatentSteps = 32;            // k-steps inside the first 512 columns
+constexpr int kQReg = 28;                   // k-steps of Q^T held in registers (the rest in LDS)
 // LDS row of token t (its first 512 columns): 1088 t + 16 ((t / 4) % 4).  Row
 // starts fall on 16-byte bank slot 4 (t % 4) + (t / 4) % 4 modulo 256 bytes, so
 // 16 consecutive tokens hit 16 different slots (K operand reads) and 4
@@ -79,11 +80,11 @@ constexpr int kRowsPerWave = kBlk / kWaves;          // 8
 constexpr int kDmaPerWave = kRowsPerWave + 1;        // + 1 rope transfer
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLazy = 8.f;                // log2 headroom before the max is moved
-constexpr int kPreS = 6;                    // K operand reads in flight ahead of the score MFMAs
+constexpr int kPreS = 4;                    // K operand reads in flight ahead of the score MFMAs
 constexpr int kPreV = 4;                    // V^T operands in flight ahead of the output MFMAs
 
 __shared__ __attribute__((aligned(16))) char ring[3][kStageBytes];
-__shared__ __attribute__((aligned(16))) char qrope[kWaves][(kKSteps - kLatentSteps) * 1024];
+__shared__ __attribute__((aligned(16))) char qlds[kWaves][(kKSteps - kQReg) * 1024];
 
 
 
@@ -159,6 +160,19 @@ __device__ __forceinline__ void acc_scale(float s) {
   acc_scale_all(s, std::make_integer_sequence<int, 256>{});
   wait_valu_to_xdl();
 }
+// max |a_i| over a0 .. a255 (one register read at a time).
+template <int R>
+__device__ __forceinline__ void acc_absmax1(float& m) {
+  float t;
+  asm volatile("v_accvgpr_read_b32 %1, a%c2\n\tv_max_f32 %0, %0, |%1|" : "+v"(m), "=&v"(t) : "n"(R));
+}
+template <int... R>
+__device__ __forceinline__ float acc_absmax_all(std::integer_sequence<int, R...>) {
+  float m = 0.f;
+  (acc_absmax1<R>(m), ...);
+  return m;
+}
+__device__ __forceinline__ float acc_absmax() { return acc_absmax_all(std::make_integer_sequence<int, 256>{}); }
 template <int R>
 __device__ __forceinline__ float acc_read() {
   float x;
@@ -258,26 +272,40 @@ struct Item {
   int unit, tb, te, split, nsplit, pbase;
 };
 
-// Merge of a 128-head unit's split partials by the whole workgroup, run after
-// the stream (the ring's LDS is free).  Threads 0..127, one per head, load
-// every split's (m, l) of their head (16 splits in flight), form (M, L) and the
-// lse, and stage the split weights c_s = exp2(m_s - M) / L for up to
-// kMergeChunk splits in LDS.  Then all threads stream the output as float4
-// columns, consecutive threads on consecutive columns (coalesced), 8 columns
-// x 4 splits = 32 loads in flight per thread, so the merge takes a handful of
-// memory round trips.  Splits are combined in index order, so the result does
-// not depend on which piece arrived last.  The partials were published with an
-// agent-scope release; the caller has performed the matching acquire.
-constexpr int kMergeChunk = 64;  // split weights staged per pass: 64 x 128 floats
-constexpr int kMergeCols = 8;    // float4 columns per thread per round
-constexpr int kMergeSplits = 4;  // splits per round
+// A split piece's partial (one workspace slot): m[128] at float 0, l[128] at
+// 128, r[128] at 256, then o[128][512] in fp16 at float 384, each head row o
+// divided by its own r = max |o| (fp32), so the halves hold values in [-1, 1]
+// and the rounding error of the merged output stays below max |v| 2^-12.
+// Half the bytes of an fp32 partial: the piece writes 128 KiB, the merger
+// reads 128 KiB per piece.
+constexpr int kPartL = kHeads, kPartR = 2 * kHeads, kPartO = 3 * kHeads;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// Merge of heads h0 .. h0 + nh - 1 of a unit's split partials by one
+// workgroup.  Threads 0 .. nh - 1, one per head, load every split's (m, l) of
+// their head (16 splits in flight), form (M, L) and the lse, and stage the
+// split weights c_s = exp2(m_s - M) r_s / L for up to kMergeChunk splits in
+// LDS.  Then all threads stream the output in 16-byte columns (8 halves),
+// consecutive threads on consecutive columns, kMergeCols columns x
+// kMergeSplits splits = 32 loads in flight per thread.  Splits are combined in
+// index order, so the result does not depend on which piece arrived last.
+// The partials were published with an agent-scope release (or a kernel
+// boundary); the caller has performed the matching acquire.
+constexpr int kMergeChunk = 64;  // split weights staged per pass
+constexpr int kMergeCols = 4;    // 16-byte columns per thread per round
+static_assert((16 * (512 / 8)) % (256 * 4) == 0, "merged head ranges are whole rounds");
+constexpr int kMergeSplits = 8;  // splits per round
+__host__ __device__ constexpr int merge_lds_floats_mla(int nh) { return 2 * nh + kMergeChunk * nh; }
 __device__ __forceinline__ void merge_unit(const float* pb, int ns, int slot_floats, float* out, float* lse,
-                                           float* lds) {
-  float* ml = lds;                 // M[128], 1/L[128]
-  float* coef = lds + 2 * kHeads;  // [split in pass][head]
+                                           float* lds, int h0, int nh) {
+  float* ml = lds;            // M[nh], 1/L[nh]
+  float* coef = lds + 2 * nh;  // [split in pass][head]
   const int tid = threadIdx.x;
   __syncthreads();  // the LDS is free: every wave is past its last tile (or the previous merge)
-  if (tid < kHeads) {
+  if (tid < nh) {
+    const int h = h0 + tid;
     float M = -INFINITY, L = 0.f;
     for (int s0 = 0; s0 < ns; s0 += 16) {
       float mt[16], lt[16];
@@ -285,8 +313,8 @@ __device__ __forceinline__ void merge_unit(const float* pb, int ns, int slot_flo
       for (int i = 0; i < 16; ++i) {
         const bool ok = s0 + i < ns;
         const float* ps = pb + (size_t)(ok ? s0 + i : 0) * slot_floats;
-        mt[i] = ok ? ps[tid] : -INFINITY;
-        lt[i] = ok ? ps[kHeads + tid] : 0.f;
+        mt[i] = ok ? ps[h] : -INFINITY;
+        lt[i] = ok ? ps[kPartL + h] : 0.f;
       }
       float Mc = M;
 #pragma unroll
@@ -297,46 +325,64 @@ __device__ __forceinline__ void merge_unit(const float* pb, int ns, int slot_flo
       M = Mc;
     }
     ml[tid] = M;
-    ml[kHeads + tid] = 1.f / L;
-    lse[tid] = (M + __log2f(L)) * kLn2;
+    ml[nh + tid] = 1.f / L;
+    lse[h] = (M + __log2f(L)) * kLn2;
   }
-  const f32x4* o4 = reinterpret_cast<const f32x4*>(pb + partial_o_offset(kHeads));
-  f32x4* out4 = reinterpret_cast<f32x4*>(out);
-  const int slot4 = slot_floats / 4;
-  constexpr int kCols4 = kHeads * kDv / 4;  // 16384 float4 per unit
+  typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+  const int slot16 = slot_floats / 4;                    // 16-byte words per slot
+  const u32x4_* o16 = reinterpret_cast<const u32x4_*>(pb + kPartO) + (size_t)h0 * (kDv / 8);
+  f32x4* out4 = reinterpret_cast<f32x4*>(out) + (size_t)h0 * (kDv / 4);
+  const int ncols = nh * (kDv / 8);                      // 16-byte columns of the head range
   for (int c0 = 0; c0 < ns; c0 += kMergeChunk) {
     const int nc = min(kMergeChunk, ns - c0);
     __syncthreads();  // (M, 1/L) visible; the previous pass's weights consumed
-    for (int i = tid; i < nc * kHeads; i += kThreads) {
-      const int sp = i >> 7, h = i & (kHeads - 1);
-      coef[i] = fast_exp2(pb[(size_t)(c0 + sp) * slot_floats + h] - ml[h]) * ml[kHeads + h];
+    for (int i = tid; i < nc * nh; i += kThreads) {
+      const int sp = i / nh, hl = i - (i / nh) * nh;
+      const float* ps = pb + (size_t)(c0 + sp) * slot_floats;
+      coef[i] = fast_exp2(ps[h0 + hl] - ml[hl]) * ps[kPartR + h0 + hl] * ml[nh + hl];
     }
     __syncthreads();
-    for (int e0 = tid; e0 < kCols4; e0 += kThreads * kMergeCols) {
-      f32x4 acc[kMergeCols];
+    // ncols is a multiple of kThreads * kMergeCols (128 or 16 heads of 64
+    // columns), so no column is out of range; a round past the last split
+    // re-reads the last one with weight 0
+    for (int e0 = tid; e0 < ncols; e0 += kThreads * kMergeCols) {
+      f32x8 acc[kMergeCols];
 #pragma unroll
-      for (int u = 0; u < kMergeCols; ++u) acc[u] = c0 == 0 ? f32x4{} : out4[e0 + kThreads * u];
-      for (int s0 = 0; s0 < nc; s0 += kMergeSplits) {
-        f32x4 v[kMergeCols][kMergeSplits];
-#pragma unroll
-        for (int u = 0; u < kMergeCols; ++u)
-#pragma unroll
-          for (int t = 0; t < kMergeSplits; ++t) {
-            const bool ok = s0 + t < nc;
-            v[u][t] = ok ? o4[(size_t)(c0 + s0 + t) * slot4 + e0 + kThreads * u] : f32x4{};
-          }
-#pragma unroll
-        for (int u = 0; u < kMergeCols; ++u) {
-          const int h = (e0 + kThreads * u) >> 7;  // 128 float4 per head row
-#pragma unroll
-          for (int t = 0; t < kMergeSplits; ++t) {
-            const float c = s0 + t < nc ? coef[(s0 + t) * kHeads + h] : 0.f;
-            acc[u] += c * v[u][t];
-          }
+      for (int u = 0; u < kMergeCols; ++u) {
+        const int e = e0 + kThreads * u;
+        if (c0 == 0) {
+          acc[u] = f32x8{};
+        } else {
+          const f32x4 a = out4[2 * e], b = out4[2 * e + 1];
+          acc[u] = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         }
       }
+      for (int s0 = 0; s0 < nc; s0 += kMergeSplits) {
+        u32x4_ v[kMergeCols][kMergeSplits];
 #pragma unroll
-      for (int u = 0; u < kMergeCols; ++u) out4[e0 + kThreads * u] = acc[u];
+        for (int t = 0; t < kMergeSplits; ++t) {
+          const u32x4_* src = o16 + (size_t)(c0 + min(s0 + t, nc - 1)) * slot16;  // wave-uniform base
+#pragma unroll
+          for (int u = 0; u < kMergeCols; ++u) v[u][t] = src[e0 + kThreads * u];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one round of loads live at a time
+#pragma unroll
+        for (int u = 0; u < kMergeCols; ++u) {
+          const int hl = (e0 + kThreads * u) / (kDv / 8);
+#pragma unroll
+          for (int t = 0; t < kMergeSplits; ++t) {
+            const float c = s0 + t < nc ? coef[(s0 + t) * nh + hl] : 0.f;
+            acc[u] += c * __builtin_convertvector(__builtin_bit_cast(f16x8, v[u][t]), f32x8);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeCols; ++u) {
+        const int e = e0 + kThreads * u;
+        out4[2 * e] = f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
+        out4[2 * e + 1] = f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]};
+      }
     }
   }
 }
@@ -384,15 +430,6 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
 
   // unit = b * Tq + t (one unit per query token)
   const int page_mask = (1 << p.log2_page) - 1;
-  auto row_of = [&](int b, int tok) -> long long {  // cache row of token `tok` of sequence b
-    int lp = min(tok >> p.log2_page, p.max_pages - 1);
-    int pg = uni(bt[(size_t)b * p.max_pages + lp]);
-    if ((unsigned)pg >= (unsigned)p.num_pages) {
-      atomicOr(err, kErrPage);
-      pg = pg < 0 ? 0 : p.num_pages - 1;
-    }
-    return (long long)pg * (1 << p.log2_page) + (tok & page_mask);
-  };
 
   // block-table entry of block j of item I (dense)
   auto bt_entry = [&](const Item& I, int j) -> const int32_t* {
@@ -431,24 +468,47 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       lds_dma16s(F.base, min(rt, F.nvalid - 1) * kRowBytes + 1024 + 16 * rchunk, dst + kRopeOff + 1024 * wave);
     }
   };
-  // index-sparse: rows gathered through the index list
+  // index-sparse: rows gathered through the index list.  All 8 row ids of the
+  // wave are loaded first, then all 8 block-table entries, and only then
+  // checked, so the gather costs two memory round trips rather than sixteen.
   auto sparse_fetch = [&](const Item& I, int j, char* dst) {
     const int b = I.unit / p.q_tokens;
     const int tok0 = I.tb + j * kBlk;
     const int tl_last = min(tok0 + kBlk, I.te) - 1;
     const int32_t* idx = indices + (size_t)I.unit * p.topk;
     const int L = uni(seqlens[b]);
+    int tok[kRowsPerWave], pg[kRowsPerWave];
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) tok[q] = uni(idx[min(tok0 + kRowsPerWave * wave + q, tl_last)]);
+    const int32_t* btb = bt + (size_t)b * p.max_pages;
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q)
+      pg[q] = uni(btb[min(max(tok[q], 0) >> p.log2_page, p.max_pages - 1)]);
+    bool bad_tok = false, bad_pg = false;
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) {
+      const bool bt_ = (unsigned)tok[q] >= (unsigned)L;
+      bad_tok |= bt_;
+      bad_pg |= !bt_ && (unsigned)pg[q] >= (unsigned)p.num_pages;
+    }
+    if (bad_tok || bad_pg) {
+      atomicOr(err, (bad_tok ? kErrIndex : 0) | (bad_pg ? kErrPage : 0));
+#pragma unroll
+      for (int q = 0; q < kRowsPerWave; ++q) {
+        if ((unsigned)tok[q] >= (unsigned)L) {  // an invalid id reads token 0 instead
+          tok[q] = 0;
+          pg[q] = uni(btb[0]);
+          if ((unsigned)pg[q] >= (unsigned)p.num_pages) atomicOr(err, kErrPage);
+        }
+        if ((unsigned)pg[q] >= (unsigned)p.num_pages) pg[q] = pg[q] < 0 ? 0 : p.num_pages - 1;
+      }
+    }
     const char* rope_src = nullptr;
 #pragma unroll
     for (int q = 0; q < kRowsPerWave; ++q) {
-      const int t = kRowsPerWave * wave + q;
-      int tok = uni(idx[min(tok0 + t, tl_last)]);
-      if ((unsigned)tok >= (unsigned)L) {
-        atomicOr(err, kErrIndex);
-        tok = 0;
-      }
-      const char* row = reinterpret_cast<const char*>(kc) + row_of(b, tok) * kRowBytes;
-      lds_dma16(row + 16 * lane, dst + row_lds(t));
+      const char* row = reinterpret_cast<const char*>(kc) +
+                        ((long long)pg[q] * (1 << p.log2_page) + (tok[q] & page_mask)) * kRowBytes;
+      lds_dma16(row + 16 * lane, dst + row_lds(kRowsPerWave * wave + q));
       if (rslot == q) rope_src = row;
     }
     lds_dma16(rope_src + 1024 + 16 * rchunk, dst + kRopeOff + 1024 * wave);
@@ -468,24 +528,25 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   for (int r = 0; r < 4; ++r) rope_off[r] = kRopeOff + 128 * n + 16 * ((2 * r + g) ^ ((n >> 1) & 7));
   const uint32_t vbase = row_lds(4 * g + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
-  // Q^T operand: lane holds head 32 wave + n, dims 16 ks + 8 g .. +8.  The 32
-  // latent k-steps stay in registers (128 VGPRs) for the whole item; the 4 rope
-  // k-steps go to the wave's own LDS area in the same lane order (one transfer
-  // per k-step, read back conflict free).  The q loads are followed by
+  // Q^T operand: lane holds head 32 wave + n, dims 16 ks + 8 g .. +8.  The
+  // first kQReg k-steps stay in registers (112 VGPRs) for the whole item; the
+  // other 8 go to the wave's own LDS area in the same lane order (one transfer
+  // per k-step, read back conflict free), which leaves the register file room
+  // for the operand pipeline.  The q loads are followed by
   // kDmaPerWave stores of zero into unused words of the workspace header: the
   // compiler counts those (it does not see the asm transfers), so it waits for
   // q with vmcnt(kDmaPerWave), which leaves exactly the next tile's transfers
   // in flight, instead of vmcnt(0).
-  u32x4 qv[kLatentSteps];
-  char* qrope_w = qrope[wave];
+  u32x4 qv[kQReg];
+  char* qlds_w = qlds[wave];
   auto load_q = [&](int unit) {
     const size_t row = (size_t)unit * p.hq + kHW * wave + n;
     const uint16_t* qp = qg + row * kDqk + 8 * g;
 #pragma unroll
-    for (int j = 0; j < kLatentSteps; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qp + 16 * j);
+    for (int j = 0; j < kQReg; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qp + 16 * j);
 #pragma unroll
-    for (int r = 0; r < kKSteps - kLatentSteps; ++r)
-      lds_dma16(reinterpret_cast<const char*>(qp + 16 * (kLatentSteps + r)), qrope_w + 1024 * r);
+    for (int r = 0; r < kKSteps - kQReg; ++r)
+      lds_dma16(reinterpret_cast<const char*>(qp + 16 * (kQReg + r)), qlds_w + 1024 * r);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) err[4 * (i + 1)] = 0;  // every lane, same word: no branch
@@ -592,25 +653,22 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     f32x16 s;
     auto scores = [&](auto inter_c) __attribute__((always_inline)) {
       constexpr bool kInter = decltype(inter_c)::value;
-      u32x4 qr[kKSteps - kLatentSteps];  // rope part of Q^T, read at the start of the chain
-#pragma unroll
-      for (int r = 0; r < kKSteps - kLatentSteps; ++r)
-        qr[r] = *reinterpret_cast<const u32x4*>(qrope_w + 1024 * r + 16 * lane);
-      u32x4 kop[kKSteps];
-      auto kload = [&](int ks) -> u32x4 {
-        return *reinterpret_cast<const u32x4*>(tile + (ks < kLatentSteps ? kbase + 32 * ks : rope_off[ks - kLatentSteps]));
+      u32x4 kop[kKSteps], qop[kKSteps];  // K^T operands; Q^T operands of the LDS k-steps
+      auto kload = [&](int ks) {
+        kop[ks] = *reinterpret_cast<const u32x4*>(tile + (ks < kLatentSteps ? kbase + 32 * ks : rope_off[ks - kLatentSteps]));
+        if (ks >= kQReg) qop[ks] = *reinterpret_cast<const u32x4*>(qlds_w + 1024 * (ks - kQReg) + 16 * lane);
       };
 #pragma unroll
-      for (int ks = 0; ks < kPreS; ++ks) kop[ks] = kload(ks);
+      for (int ks = 0; ks < kPreS; ++ks) kload(ks);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        if (ks + kPreS < kKSteps) kop[ks + kPreS] = kload(ks + kPreS);
+        if (ks + kPreS < kKSteps) kload(ks + kPreS);
         if (ks == 0)
           mfma32_v_first(s, kop[0], qv[0]);
-        else if (ks < kLatentSteps)
+        else if (ks < kQReg)
           mfma32_v(s, kop[ks], qv[ks]);
         else
-          mfma32_v(s, kop[ks], qr[ks - kLatentSteps]);
+          mfma32_v(s, kop[ks], qop[ks]);
         if constexpr (kInter)
           if ((ks & 3) == 2) dense_piece(F, ks >> 2, fdst);
       }
@@ -697,26 +755,49 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       const bool whole = cur.nsplit == 1;
       float* ps = partials + (size_t)(cur.pbase + cur.split) * p.slot_floats;
       const float scale = whole ? 1.f / l_tot : 1.f;
-      float* orow = whole ? out + (qrow + hh) * kDv + 4 * g : ps + partial_o_offset(kHeads) + (size_t)hh * kDv + 4 * g;
-      if (g == 0) {
-        if (whole) {
-          lse[qrow + hh] = (m_run + __log2f(l_tot)) * kLn2;
-        } else {
-          ps[hh] = m_run;
-          ps[kHeads + hh] = l_tot;
-        }
-      }
+      float* orow = out + (qrow + hh) * kDv + 4 * g;
       wait_xdl_result();
-      unroll<16>([&](auto dc) {
-        constexpr int d = decltype(dc)::value;
-        unroll<4>([&](auto jc) {
-          constexpr int jj = decltype(jc)::value;
-          *reinterpret_cast<f32x4*>(orow + 32 * d + 8 * jj) =
-              f32x4{acc_read<16 * d + 4 * jj>(), acc_read<16 * d + 4 * jj + 1>(), acc_read<16 * d + 4 * jj + 2>(),
-                    acc_read<16 * d + 4 * jj + 3>()} *
-              scale;
+      if (whole) {
+        if (g == 0) lse[qrow + hh] = (m_run + __log2f(l_tot)) * kLn2;
+        unroll<16>([&](auto dc) {
+          constexpr int d = decltype(dc)::value;
+          unroll<4>([&](auto jc) {
+            constexpr int jj = decltype(jc)::value;
+            *reinterpret_cast<f32x4*>(orow + 32 * d + 8 * jj) =
+                f32x4{acc_read<16 * d + 4 * jj>(), acc_read<16 * d + 4 * jj + 1>(), acc_read<16 * d + 4 * jj + 2>(),
+                      acc_read<16 * d + 4 * jj + 3>()} *
+                scale;
+          });
         });
-      });
+      } else {
+        // row scale r = max |o| over the head's 512 columns (this lane holds
+        // 256 of them, lane n ^ 32 the rest), then o / r in fp16
+        float r = acc_absmax();
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, r),
+                                                          __builtin_bit_cast(uint32_t, r), false, false);
+          r = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+        }
+        const float rinv = r > 0.f ? 1.f / r : 0.f;
+        if (g == 0) {
+          ps[hh] = m_run;
+          ps[kPartL + hh] = l_tot;
+          ps[kPartR + hh] = r;
+        }
+        _Float16* orow16 = reinterpret_cast<_Float16*>(ps + kPartO) + (size_t)hh * kDv + 4 * g;
+        unroll<16>([&](auto dc) {
+          constexpr int d = decltype(dc)::value;
+          unroll<4>([&](auto jc) {
+            constexpr int jj = decltype(jc)::value;
+            const f16x2 lo = __builtin_convertvector(
+                f32x2{acc_read<16 * d + 4 * jj>() * rinv, acc_read<16 * d + 4 * jj + 1>() * rinv}, f16x2);
+            const f16x2 hi = __builtin_convertvector(
+                f32x2{acc_read<16 * d + 4 * jj + 2>() * rinv, acc_read<16 * d + 4 * jj + 3>() * rinv}, f16x2);
+            *reinterpret_cast<u32x2*>(orow16 + 32 * d + 8 * jj) =
+                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          });
+        });
+      }
       if (!whole) {
         if (p.reduce == CC_REDUCE_FUSED) {
           __syncthreads();  // every wave's share of the partial is written
@@ -763,10 +844,26 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   for (int i = 0; i < npend; ++i) {
     const int unit = uni(i == 0 ? pend0 : pend1);
     merge_unit(partials + (size_t)uni(unit_pbase[unit]) * p.slot_floats, uni(unit_nsplit[unit]), p.slot_floats,
-               out + (size_t)unit * kHeads * kDv, lse + (size_t)unit * kHeads, reinterpret_cast<float*>(ring[0]));
+               out + (size_t)unit * kHeads * kDv, lse + (size_t)unit * kHeads, reinterpret_cast<float*>(ring[0]), 0,
+               kHeads);
     if (tid == 0) __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (tl && tid == 0) tl[3] = tl[4] = __builtin_amdgcn_s_memrealtime();
+}
+
+// Split-then-combine comparison launch: the decode kernel only writes the
+// pieces' partials; this kernel merges them, one workgroup per (unit, group
+// of kCombineHeads heads), with the same merge as the fused path.
+constexpr int kCombineHeads = 16;
+__global__ void __launch_bounds__(kThreads)
+mla_combine_kernel(int slot_floats, const int32_t* __restrict__ unit_nsplit, const int32_t* __restrict__ unit_pbase,
+                   const float* __restrict__ partials, float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) float lds[merge_lds_floats_mla(kCombineHeads)];
+  const int u = blockIdx.x;
+  const int ns = unit_nsplit[u];
+  if (ns <= 1) return;
+  merge_unit(partials + (size_t)unit_pbase[u] * slot_floats, ns, slot_floats, out + (size_t)u * kHeads * kDv,
+             lse + (size_t)u * kHeads, lds, blockIdx.y * kCombineHeads, kCombineHeads);
 }
 
 int ilog2(int x) {
@@ -776,6 +873,12 @@ int ilog2(int x) {
 }
 
 }  // namespace mla
+
+hipError_t launch_mla_combine(const DecodeArgs& a, hipStream_t s) {
+  mla::mla_combine_kernel<<<dim3(a.units, mla::kHeads / mla::kCombineHeads), mla::kThreads, 0, s>>>(
+      a.slot_floats, a.unit_nsplit, a.unit_pbase, a.partials, a.out, a.lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_mla(const DecodeArgs& a, hipStream_t s) {
   mla::Params p;

@@ -49,6 +49,7 @@ constexpr int kErrIndex = 4;
 hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_mla(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_mla_combine(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace cc

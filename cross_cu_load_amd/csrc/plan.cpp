@@ -129,6 +129,7 @@ int build(const Inputs& in, Built* out) {
     // equal split of the cost: kCostPerTile per tile plus kUnitCost per unit,
     // the unit's overhead first; a tile goes to the chunk whose cost range
     // holds its starting position
+    const int64_t kUnitCost = unit_cost(p.mode);
     const int64_t total = kUnitCost * U + kCostPerTile * N;
     const int64_t q = total / C, r = total % C;
     auto bound = [&](int64_t k) { return k * q + (k < r ? k : r); };  // chunk k: [bound(k), bound(k+1))
@@ -219,7 +220,7 @@ int build(const Inputs& in, Built* out) {
   h[H_POLICY] = o.policy;
   h[H_MAXPAGES] = p.max_pages_per_seq;
   h[H_NUMPAGES] = p.num_pages;
-  h[H_RESERVED] = o.policy == CC_POLICY_STREAMK_COST ? (int32_t)kUnitCost : 0;
+  h[H_RESERVED] = o.policy == CC_POLICY_STREAMK_COST ? (int32_t)unit_cost(p.mode) : 0;
   int32_t* wg = h + kHeaderWords;
   int32_t* it = wg + wg_words(C);
   int64_t n = 0;

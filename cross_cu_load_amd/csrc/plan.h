@@ -59,9 +59,13 @@ const char* last_error();
 inline int64_t wg_words(int64_t workers) { return (workers + 1 + 3) & ~int64_t(3); }
 
 // Cost model of CC_POLICY_STREAMK_COST: one tile costs kCostPerTile, and each
-// unit adds kUnitCost (the plan header's last word records it).
+// unit adds unit_cost(mode) (the plan header's last word records it).  A GQA
+// unit's start and finish cost about one tile; an MLA unit's (the 128-head
+// partial written and published, the next query token's q loaded) about six.
 constexpr int64_t kCostPerTile = 16;
-constexpr int64_t kUnitCost = 16;
+constexpr int64_t kUnitCostGqa = 16;
+constexpr int64_t kUnitCostMla = 96;
+inline int64_t unit_cost(int mode) { return mode == CC_MODE_GQA ? kUnitCostGqa : kUnitCostMla; }
 
 // Workspace layout of a plan: error word and counters first, then partials.
 struct WorkspaceLayout {

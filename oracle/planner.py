@@ -16,9 +16,10 @@ Readings (the pages fix only "equal, one chunk per compute unit"):
 * tiles are laid out unit-major; chunk k takes floor(N / C) tiles, plus one
   for the first N mod C chunks, contiguously.
 * POLICY_STREAMK_COST (a refinement of the same equal split): what is split
-  evenly is the cost of the work, COST_PER_TILE per tile plus UNIT_COST per
-  unit, for the fixed work of finishing a unit (merging its pieces inside a
-  compute unit, writing its output); a unit occupies a contiguous cost range
+  evenly is the cost of the work, COST_PER_TILE per tile plus unit_cost(mode)
+  per unit, for the fixed work of starting and finishing a unit (loading its
+  queries, publishing or writing its output; six tiles' worth for a 128-head
+  MLA unit, one for a GQA group); a unit occupies a contiguous cost range
   with its overhead first, and a tile belongs to the chunk whose cost range
   holds the tile's starting position.  Chunk k's range is
   [k * q + min(k, r), (k+1) * q + min(k+1, r)) for total cost = q C + r.
@@ -46,7 +47,13 @@ ITEM_WORDS = 4                   # unit, tok_begin, tok_end, split
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
 POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_COST = 0, 1, 2
 COST_PER_TILE = 16                # cost units of one tile (POLICY_STREAMK_COST)
-UNIT_COST = 16                    # cost units charged once per unit (= one tile)
+UNIT_COST = 16                    # cost units charged once per GQA unit (= one tile)
+UNIT_COST_MLA = 96                # ... per MLA unit (= six tiles)
+
+
+def unit_cost(mode: int) -> int:
+    """Cost units charged once per unit of POLICY_STREAMK_COST in this mode."""
+    return UNIT_COST if mode == MODE_GQA else UNIT_COST_MLA
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -124,7 +131,7 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
 
     chunk_pieces: list[list[tuple[int, int, int]]] = []
     if policy == POLICY_STREAMK_COST:
-        chunk_pieces = _cost_split(ntiles, lens, C, T)
+        chunk_pieces = _cost_split(ntiles, lens, C, T, unit_cost(mode))
     # equal split of N tiles into C contiguous chunks (+1 for the first N mod C)
     base, rem = divmod(N, C)
     u = 0
@@ -185,7 +192,7 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
     header[:23] = [PLAN_MAGIC, PLAN_VERSION, mode, batch, q_tokens, num_q_heads, num_kv_heads,
                    head_dim_qk, head_dim_v, page_size, topk, C, X, T, heads_per_unit, U, N, W, S,
                    max(nsplit) if nsplit else 0, policy, max_pages_per_seq, num_pages]
-    header[23] = UNIT_COST if policy == POLICY_STREAMK_COST else 0
+    header[23] = unit_cost(mode) if policy == POLICY_STREAMK_COST else 0
     pad = (-(C + 1)) % 4                 # keeps the item array 16-byte aligned
     words = header + wg_off + [0] * pad + [x for it in items for x in it] + nsplit + pbase
     for x in words:
@@ -197,14 +204,14 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
                 worker_of_chunk=worker_of_chunk, unit_len=lens, chunk_items=items_by_chunk)
 
 
-def _cost_split(ntiles, lens, C: int, T: int):
+def _cost_split(ntiles, lens, C: int, T: int, O: int = UNIT_COST):
     """Chunks of POLICY_STREAMK_COST: pieces (unit, tok_begin, tok_end) per chunk.
 
     Unit u's cost range starts at cs[u] = sum over earlier units of
-    (UNIT_COST + COST_PER_TILE * n); its tile i starts at cs[u] + UNIT_COST +
+    (O + COST_PER_TILE * n), O the unit cost; its tile i starts at cs[u] + O +
     COST_PER_TILE * i and belongs to the chunk whose range holds that position.
     """
-    total = sum(UNIT_COST + COST_PER_TILE * n for n in ntiles)
+    total = sum(O + COST_PER_TILE * n for n in ntiles)
     q, r = divmod(total, C)
     bound = [k * q + min(k, r) for k in range(C + 1)]   # chunk k: [bound[k], bound[k+1])
     pieces: list[list[tuple[int, int, int]]] = [[] for _ in range(C)]
@@ -212,14 +219,14 @@ def _cost_split(ntiles, lens, C: int, T: int):
     for u, n in enumerate(ntiles):
         i = 0
         while i < n:
-            start = cs + UNIT_COST + COST_PER_TILE * i
+            start = cs + O + COST_PER_TILE * i
             while bound[k + 1] <= start:
                 k += 1
             # tiles of u whose start lies before the end of chunk k
-            last = min(n, _ceil_div(bound[k + 1] - cs - UNIT_COST, COST_PER_TILE))
+            last = min(n, _ceil_div(bound[k + 1] - cs - O, COST_PER_TILE))
             pieces[k].append((u, i * T, min(last * T, lens[u])))
             i = last
-        cs += UNIT_COST + COST_PER_TILE * n
+        cs += O + COST_PER_TILE * n
     return pieces
 
 

@@ -1,0 +1,76 @@
+"""Register contract of the MLA kernel, checked on the generated gfx950 code.
+
+The MLA kernel keeps its 256 output accumulators in a0 .. a255 and touches
+them only from inline asm; the compiler does not know those registers hold
+live values.  If its own register allocation ever placed a value in an AGPR
+(it does so when VGPR pressure passes 256), that value and the accumulators
+would overwrite each other.  This compiles the kernel (hipcc cross-compiles
+for gfx950 without a GPU) and checks that every AGPR access in the decode
+kernels sits inside an inline-asm block, and that nothing spills to scratch.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "cross_cu_load_amd", "csrc", "decode_mla.hip")
+AGPR = re.compile(r"\bv_accvgpr_|\ba\[\d+|\ba\d+\b")
+
+
+def _hipcc():
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+@pytest.fixture(scope="module")
+def mla_asm(tmp_path_factory):
+    hipcc = _hipcc()
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "decode_mla.s"
+    cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", str(out), SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def _kernel_body(asm, sparse):
+    name = f"_ZN2cc3mla17mla_decode_kernelILb{1 if sparse else 0}EE"
+    start = asm.index("\n" + name) + 1
+    end = asm.index("s_endpgm", start)
+    return asm[start:end]
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_agprs_touched_only_by_inline_asm(mla_asm, sparse):
+    body = _kernel_body(mla_asm, sparse)
+    inside, outside = False, []
+    for line in body.splitlines():
+        if ";;#ASMSTART" in line:
+            inside = True
+            continue
+        if ";;#ASMEND" in line:
+            inside = False
+            continue
+        code = line.split(";")[0]
+        if not inside and AGPR.search(code):
+            outside.append(line.strip())
+    assert not outside, f"{len(outside)} compiler-generated AGPR accesses, e.g. {outside[:3]}"
+
+
+def test_no_scratch_and_full_agpr_reservation(mla_asm):
+    for sparse in (False, True):
+        name = f"_ZN2cc3mla17mla_decode_kernelILb{1 if sparse else 0}EE"
+        meta = mla_asm[mla_asm.index(".name:           " + name):]
+        meta = meta[:meta.index(".wavefront_size")] if ".wavefront_size" in meta else meta[:4000]
+        pre = mla_asm[:mla_asm.index(".name:           " + name)]
+        block = pre[pre.rindex("- .agpr_count"):]
+        assert re.search(r"\.agpr_count:\s+256", block), "the kernel must reserve a0..a255"
+        assert re.search(r"\.private_segment_fixed_size:\s+0\b", block + meta), "scratch spills"
+        assert re.search(r"\.vgpr_spill_count:\s+0\b", block + meta), "VGPR spills"

@@ -56,7 +56,7 @@ def test_golden_tail_effect_and_equal_split():
     assert chunk.max() == total / g["num_sms"] == 155
 
 
-def _check_invariants(p, lens, C, X, T, policy=PL.POLICY_STREAMK):
+def _check_invariants(p, lens, C, X, T, policy=PL.POLICY_STREAMK, mode=PL.MODE_GQA):
     U = len(lens)
     ntiles = [-(-L // T) for L in lens]
     N = sum(ntiles)
@@ -68,9 +68,9 @@ def _check_invariants(p, lens, C, X, T, policy=PL.POLICY_STREAMK):
             tiles = sum(-(-(t1 - t0) // T) for (_, t0, t1, _) in its)
             assert tiles == base + (k < rem)
     else:
-        # cost of a chunk (16 per tile, 16 per unit it starts) is within one
-        # tile plus one unit of its share of the total cost
-        K, O = PL.COST_PER_TILE, PL.UNIT_COST
+        # cost of a chunk (16 per tile, the mode's unit cost per unit it
+        # starts) is within one tile plus one unit of its share of the total
+        K, O = PL.COST_PER_TILE, PL.unit_cost(mode)
         q, r = divmod(K * N + O * U, C)
         for k, its in enumerate(p["chunk_items"]):
             cost = sum(K * -(-(t1 - t0) // T) + (O if t0 == 0 else 0) for (_, t0, t1, _) in its)
@@ -199,7 +199,7 @@ def test_invariants_on_the_workload_lengths(C, T, policy):
         maxp = int(max((int(L) + P - 1) // P for L in lens_b))
         p = PL.plan(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
                     cfg.head_dim_v, P, maxp, 1 << 20, cfg.topk, C, 8, T, hu, lens_b, None, policy)
-        _check_invariants(p, lens, C, 8, T, policy)
+        _check_invariants(p, lens, C, 8, T, policy, cfg.mode)
 
 
 def test_skewed_workload_split_shape():
@@ -235,3 +235,12 @@ def test_invalid_inputs_rejected(bad):
         kw["seqlens"] = np.array([10, 40], np.int32)
     with pytest.raises(ValueError):
         PL.plan(**kw)
+
+
+def test_cost_policy_unit_cost_follows_mode():
+    """An MLA unit is charged six tiles, a GQA unit one, and the header says which."""
+    lens = [300, 70, 1000]
+    for mode, hu, O in ((PL.MODE_GQA, 1, 16), (PL.MODE_MLA, 1, 96)):
+        p = _plan(lens, C=4, T=32, mode=mode, hu=hu, policy=PL.POLICY_STREAMK_COST)
+        assert np.frombuffer(p["blob"][:96], np.int32)[23] == O == PL.unit_cost(mode)
+        _check_invariants(p, lens, 4, 1, 32, PL.POLICY_STREAMK_COST, mode)
