@@ -198,7 +198,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   }
   const int i0 = uni(wg_off[blockIdx.x]), i1 = uni(wg_off[blockIdx.x + 1]);
   if (i0 >= i1) {
-    if (tl && tid == 0) tl[1] = tl[2] = tl[3] = tl[4] = tl[0];
+    if (tl && tid == 0) tl[1] = tl[2] = tl[3] = tl[4] = tl[6] = tl[7] = tl[0];
     return;
   }
 
@@ -516,40 +516,42 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   // slots, the sum L and each slot's weight exp2(m - M); (b) after a barrier a
   // flat loop over (item, element) adds the weighted outputs in slot (token)
   // order.  Only the slots that hold an item are read.
-  if (tid == 0) {
+  if (tid < 64) {
     // distinct items in slot order (first slot, slots holding it), and the
-    // split ones among them (unit, nsplit, first partial slot), from one read
-    // of the slot table into registers
-    int si[2 * kWaves];
+    // split ones among them (unit, nsplit, first partial slot): one lane per
+    // merge slot, compacted with ballots so the list stays in slot order
+    const int me = lane < 2 * kWaves ? slot_item[lane] : -1;
+    unsigned mask = 0;
+    bool before = false;
 #pragma unroll
-    for (int t = 0; t < 2 * kWaves; ++t) si[t] = slot_item[t];
-    int n = 0, nsp = 0;
-#pragma unroll
-    for (int sl = 0; sl < 2 * kWaves; ++sl) {
-      unsigned mask = 0;
-      bool before = false;
-#pragma unroll
-      for (int t = 0; t < 2 * kWaves; ++t) {
-        mask |= (unsigned)(si[t] == si[sl]) << t;
-        before |= t < sl && si[t] == si[sl];
-      }
-      if (si[sl] >= 0 && !before) {
-        it_slot[n] = sl;
-        it_mask[n] = mask;
-        ++n;
-        const int ns = slot_meta[sl][2];
-        if (ns > 1) {
-          split_list[nsp][0] = slot_meta[sl][0];
-          split_list[nsp][1] = ns;
-          split_list[nsp][2] = slot_meta[sl][3];
-          ++nsp;
-        }
-      }
+    for (int t = 0; t < 2 * kWaves; ++t) {
+      const bool same = __builtin_amdgcn_readlane(me, t) == me;
+      mask |= (unsigned)same << t;
+      before |= same && t < lane;
     }
-    num_items = n;
-    num_split = nsp;
+    const bool first = lane < 2 * kWaves && me >= 0 && !before;
+    const int ns = first ? slot_meta[lane][2] : 0;
+    const bool split = ns > 1;
+    const unsigned long long fb = __ballot(first), sb = __ballot(split);
+    const unsigned long long below = (1ull << lane) - 1;
+    if (first) {
+      const int n = __popcll(fb & below);
+      it_slot[n] = lane;
+      it_mask[n] = mask;
+    }
+    if (split) {
+      const int k = __popcll(sb & below);
+      split_list[k][0] = slot_meta[lane][0];
+      split_list[k][1] = ns;
+      split_list[k][2] = slot_meta[lane][3];
+    }
+    if (lane == 0) {
+      num_items = __popcll(fb);
+      num_split = __popcll(sb);
+    }
   }
   __syncthreads();
+  if (tl && tid == 0) tl[6] = __builtin_amdgcn_s_memrealtime();
   const int nit = uni(num_items);
   const int GD = G * D;
   if (tid < nit * G) {
@@ -578,6 +580,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     item_L[ii][hh] = L;
   }
   __syncthreads();
+  if (tl && tid == 0) tl[7] = __builtin_amdgcn_s_memrealtime();
   for (int idx = tid; idx < nit * GD; idx += kThreads) {
     const int ii = uni(idx / GD);  // G * D is a multiple of 64: one item per wave and pass
     const int e = idx - ii * GD, hh = e / D;
@@ -610,27 +613,26 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     // arrived).
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) {
-      const int nsp = num_split;
-      int nd = 0;
-      if (nsp > 0) {
-        int old[2 * kWaves];
-#pragma unroll
-        for (int k = 0; k < 2 * kWaves; ++k)  // all arrivals in flight together
-          old[k] = k < nsp ? atomicAdd(&counters[split_list[k][0]], 1) : 0;
-#pragma unroll
-        for (int k = 0; k < 2 * kWaves; ++k) {
-          if (k < nsp && old[k] == split_list[k][1] - 1) {
-            const int unit = split_list[k][0];
-            __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            done_units[nd][0] = split_list[k][2];
-            done_units[nd][1] = split_list[k][1];
-            done_units[nd][2] = unit * G;  // output row of unit (b, g): b Hq + g G
-            ++nd;
-          }
-        }
+    if (tid < 64) {
+      // one lane per split item: all arrivals in one atomic instruction; the
+      // lanes that completed their unit are compacted in split-list order
+      const bool on = lane < num_split;
+      int unit = 0, ns = 0, old = -1;
+      if (on) {
+        unit = split_list[lane][0];
+        ns = split_list[lane][1];
+        old = atomicAdd(&counters[unit], 1);
       }
-      num_done = nd;
+      const bool done = on && old == ns - 1;
+      const unsigned long long db = __ballot(done);
+      if (done) {
+        __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int d = __popcll(db & ((1ull << lane) - 1));
+        done_units[d][0] = split_list[lane][2];
+        done_units[d][1] = ns;
+        done_units[d][2] = unit * G;  // output row of unit (b, g): b Hq + g G
+      }
+      if (lane == 0) num_done = __popcll(db);
     }
     __syncthreads();
     if (tl && tid == 0) tl[3] = __builtin_amdgcn_s_memrealtime();

@@ -245,6 +245,22 @@ __device__ __forceinline__ int take_dword(uint32_t v) {
   asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(s) : "v"(v) : "memory");
   return s;
 }
+// 16-byte store with the device-coherent policy (sc1): it writes through this
+// XCD's L2, so once vmcnt clears the bytes are visible to every XCD.  Asm, so
+// the compiler does not count it: the kernel waits for it explicitly.  A store
+// of more than 8 bytes needs one wait state before a VALU instruction may
+// overwrite its data registers; the compiler inserts that only for stores it
+// can see, so the statement ends with it.
+__device__ __forceinline__ void store16_coherent(char* p, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
+}
+// A VGPR written by load_dword_async, read only after the wait that covers
+// the load (ordered asm, so nothing that uses the value moves above it).
+__device__ __forceinline__ uint32_t take_vgpr(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v) : "memory");
+  return r;
+}
 __device__ __forceinline__ unsigned xcc_id() {
   unsigned v;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
@@ -270,6 +286,7 @@ struct Params {
 
 struct Item {
   int unit, tb, te, split, nsplit, pbase;
+  int L;  // index-sparse: length of the unit's sequence (valid row ids are < L)
 };
 
 // A split piece's partial (one workspace slot): m[128] at float 0, l[128] at
@@ -279,6 +296,8 @@ struct Item {
 // Half the bytes of an fp32 partial: the piece writes 128 KiB, the merger
 // reads 128 KiB per piece.
 constexpr int kPartL = kHeads, kPartR = 2 * kHeads, kPartO = 3 * kHeads;
+constexpr int kPartRowLds = 272;  // LDS bytes per head row of a transposed partial quarter (256 + pad)
+static_assert(kPartRowLds * kHW * kWaves <= kStageBytes, "partial transpose fits one stage");
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -420,6 +439,7 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     I.split = uni(t.w);
     I.nsplit = uni(unit_nsplit[I.unit]);
     I.pbase = uni(unit_pbase[I.unit]);
+    I.L = SPARSE ? uni(seqlens[I.unit / p.q_tokens]) : 0;
     return I;
   };
   int nblk = 0;
@@ -468,50 +488,43 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       lds_dma16s(F.base, min(rt, F.nvalid - 1) * kRowBytes + 1024 + 16 * rchunk, dst + kRopeOff + 1024 * wave);
     }
   };
-  // index-sparse: rows gathered through the index list.  All 8 row ids of the
-  // wave are loaded first, then all 8 block-table entries, and only then
-  // checked, so the gather costs two memory round trips rather than sixteen.
-  auto sparse_fetch = [&](const Item& I, int j, char* dst) {
-    const int b = I.unit / p.q_tokens;
+  // index-sparse: lane l of wave w stands for row rt = 8 w + l / 8 of a tile
+  // (the row its rope transfer takes).  The row ids of a tile are loaded two
+  // steps before its transfers and the block-table entries of those rows one
+  // step before, as untracked dword loads issued ahead of that step's
+  // transfers: the wait at the top of the next step covers them, so no step
+  // waits on the index or block-table round trips.  Rows past the item end
+  // repeat its last row (a cursor past the last item repeats the last row of
+  // the chunk: its transfers fill a stage that is never read).
+  auto sid_ptr = [&](const Item& I, int j) -> const int32_t* {
     const int tok0 = I.tb + j * kBlk;
     const int tl_last = min(tok0 + kBlk, I.te) - 1;
-    const int32_t* idx = indices + (size_t)I.unit * p.topk;
-    const int L = uni(seqlens[b]);
-    int tok[kRowsPerWave], pg[kRowsPerWave];
-#pragma unroll
-    for (int q = 0; q < kRowsPerWave; ++q) tok[q] = uni(idx[min(tok0 + kRowsPerWave * wave + q, tl_last)]);
-    const int32_t* btb = bt + (size_t)b * p.max_pages;
-#pragma unroll
-    for (int q = 0; q < kRowsPerWave; ++q)
-      pg[q] = uni(btb[min(max(tok[q], 0) >> p.log2_page, p.max_pages - 1)]);
-    bool bad_tok = false, bad_pg = false;
-#pragma unroll
-    for (int q = 0; q < kRowsPerWave; ++q) {
-      const bool bt_ = (unsigned)tok[q] >= (unsigned)L;
-      bad_tok |= bt_;
-      bad_pg |= !bt_ && (unsigned)pg[q] >= (unsigned)p.num_pages;
+    return indices + (size_t)I.unit * p.topk + min(tok0 + rt, tl_last);
+  };
+  auto sid_check = [&](const Item& I, uint32_t sid) -> uint32_t {
+    const bool bad = sid >= (uint32_t)I.L;  // an invalid id reads token 0 instead
+    if (bad) atomicOr(err, kErrIndex);
+    return bad ? 0u : sid;
+  };
+  auto spg_ptr = [&](const Item& I, uint32_t sid) -> const int32_t* {
+    return bt + (size_t)(I.unit / p.q_tokens) * p.max_pages + min((int)(sid >> p.log2_page), p.max_pages - 1);
+  };
+  auto spg_check = [&](uint32_t pg) -> uint32_t {
+    const bool bad = pg >= (uint32_t)p.num_pages;
+    if (bad) atomicOr(err, kErrPage);
+    return bad ? ((int)pg < 0 ? 0u : (uint32_t)(p.num_pages - 1)) : pg;
+  };
+  auto srow = [&](uint32_t sid, uint32_t pg) -> const char* {
+    return reinterpret_cast<const char*>(kc) + ((long long)pg * (1 << p.log2_page) + (sid & page_mask)) * kRowBytes;
+  };
+  // transfer q of a tile whose checked row ids and pages are sid, spg (per lane)
+  auto sparse_piece = [&](uint32_t sid, uint32_t spg, int q, char* dst) __attribute__((always_inline)) {
+    if (q < kRowsPerWave) {
+      const uint32_t id = __builtin_amdgcn_readlane(sid, 8 * q), pg = __builtin_amdgcn_readlane(spg, 8 * q);
+      lds_dma16s(srow(id, pg), 16 * lane, dst + row_lds(kRowsPerWave * wave + q));
+    } else {
+      lds_dma16(srow(sid, spg) + 1024 + 16 * rchunk, dst + kRopeOff + 1024 * wave);
     }
-    if (bad_tok || bad_pg) {
-      atomicOr(err, (bad_tok ? kErrIndex : 0) | (bad_pg ? kErrPage : 0));
-#pragma unroll
-      for (int q = 0; q < kRowsPerWave; ++q) {
-        if ((unsigned)tok[q] >= (unsigned)L) {  // an invalid id reads token 0 instead
-          tok[q] = 0;
-          pg[q] = uni(btb[0]);
-          if ((unsigned)pg[q] >= (unsigned)p.num_pages) atomicOr(err, kErrPage);
-        }
-        if ((unsigned)pg[q] >= (unsigned)p.num_pages) pg[q] = pg[q] < 0 ? 0 : p.num_pages - 1;
-      }
-    }
-    const char* rope_src = nullptr;
-#pragma unroll
-    for (int q = 0; q < kRowsPerWave; ++q) {
-      const char* row = reinterpret_cast<const char*>(kc) +
-                        ((long long)pg[q] * (1 << p.log2_page) + (tok[q] & page_mask)) * kRowBytes;
-      lds_dma16(row + 16 * lane, dst + row_lds(kRowsPerWave * wave + q));
-      if (rslot == q) rope_src = row;
-    }
-    lds_dma16(rope_src + 1024 + 16 * rchunk, dst + kRopeOff + 1024 * wave);
   };
 
   // LDS read addresses of the MFMA operands: one base per operand, the rest immediate
@@ -555,10 +568,12 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
 
   // ------------------------------------------------ the block stream
   // Every iteration issues exactly one tile fetch (kDmaPerWave transfers per
-  // wave), after the score products and after the next item's q loads, so the
-  // loads outstanding at the top of iteration k are, oldest first: tile k,
-  // [the q loads of iteration k-1], tile k+1.  Past the last block the fetch
-  // re-reads the current block into the free stage (never read again).
+  // wave) as its last memory operations: among the score products, or after
+  // the next item's q loads when the item ends.  So the loads outstanding at
+  // the top of iteration k are, oldest first: tile k, [the page / row-id
+  // prefetches and q loads of iteration k-1], tile k+1.  Past the last block
+  // the fetch re-reads a block of the chunk into the free stage (never read
+  // again).
   Item cur = load_item(i0);
   int cur_it = i0, cur_j = 0, cur_nb = (cur.te - cur.tb + kBlk - 1) / kBlk;
   // producer cursor (two tiles ahead)
@@ -577,33 +592,63 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   // The page of the tile after the one being fetched is loaded asynchronously
   // (into pg_pref) before that fetch's transfers, so the wait at the top of
   // the next iteration covers it and the fetch never waits on the block table.
-  auto page_now = [&](const Item& I, int j) { return SPARSE ? 0 : uni(*bt_entry(I, j)); };
+  auto page_now = [&](const Item& I, int j) { return uni(*bt_entry(I, j)); };
   uint32_t pg_pref = 0;
-  load_q(cur.unit);
-  auto fetch_now = [&](const Item& I, int j, char* dst, int pg) {
-    if constexpr (SPARSE) {
-      sparse_fetch(I, j, dst);
-    } else {
+  // index-sparse pipeline: at the top of step k, sid2 holds the checked row
+  // ids of tile k+2; in flight (landed once the top wait is passed) are the
+  // row ids of tile k+3 (sid_fl) and the block-table entries of tile k+2
+  // (spg_fl); c3, c4 are the cursors of tiles k+3, k+4
+  struct Cursor {
+    Item I;
+    int it, j, nb;
+  };
+  auto adv = [&](Cursor& c) { advance(c.I, c.it, c.j, c.nb); };
+  Cursor c3{cur, i0, 0, cur_nb}, c4 = c3;
+  uint32_t sid2 = 0, sid_fl = 0, spg_fl = 0;
+  if constexpr (SPARSE) {
+    // tiles 0 and 1 and the state of step 0 with ordinary loads (once)
+    Cursor c = c3;
+    const uint32_t s0 = sid_check(c.I, (uint32_t)*sid_ptr(c.I, c.j));
+    const uint32_t p0 = spg_check((uint32_t)*spg_ptr(c.I, s0));
+    adv(c);
+    const uint32_t s1 = sid_check(c.I, (uint32_t)*sid_ptr(c.I, c.j));
+    const uint32_t p1 = spg_check((uint32_t)*spg_ptr(c.I, s1));
+    adv(c);
+    sid2 = sid_check(c.I, (uint32_t)*sid_ptr(c.I, c.j));
+    spg_fl = (uint32_t)*spg_ptr(c.I, sid2);
+    adv(c);
+    c3 = c;
+    sid_fl = (uint32_t)*sid_ptr(c3.I, c3.j);
+    c4 = c3;
+    adv(c4);
+    load_q(cur.unit);
+#pragma unroll
+    for (int q = 0; q < kDmaPerWave; ++q) sparse_piece(s0, p0, q, ring[0]);
+#pragma unroll
+    for (int q = 0; q < kDmaPerWave; ++q) sparse_piece(s1, p1, q, ring[1]);
+  } else {
+    load_q(cur.unit);
+    auto fetch_now = [&](const Item& I, int j, char* dst, int pg) {
       const DenseFetch F = dense_prep(I, j, pg);
 #pragma unroll
       for (int q = 0; q < kDmaPerWave; ++q) dense_piece(F, q, dst);
+    };
+    fetch_now(pI, p_j, ring[0], page_now(pI, p_j));
+    advance(pI, p_it, p_j, p_nb);
+    if (nblk > 1) {
+      const int pg1 = page_now(pI, p_j);
+      Item nI = pI;
+      int n_it = p_it, n_j = p_j, n_nb = p_nb;
+      advance(nI, n_it, n_j, n_nb);
+      pg_pref = load_dword_async(nblk > 2 ? bt_entry(nI, n_j) : bt);
+      fetch_now(pI, p_j, ring[1], pg1);
+      pI = nI;
+      p_it = n_it;
+      p_j = n_j;
+      p_nb = n_nb;
+    } else {
+      fetch_now(cur, 0, ring[1], 0);
     }
-  };
-  fetch_now(pI, p_j, ring[0], page_now(pI, p_j));
-  advance(pI, p_it, p_j, p_nb);
-  if (nblk > 1) {
-    const int pg1 = page_now(pI, p_j);
-    Item nI = pI;
-    int n_it = p_it, n_j = p_j, n_nb = p_nb;
-    advance(nI, n_it, n_j, n_nb);
-    if constexpr (!SPARSE) pg_pref = load_dword_async(nblk > 2 ? bt_entry(nI, n_j) : bt);
-    fetch_now(pI, p_j, ring[1], pg1);
-    pI = nI;
-    p_it = n_it;
-    p_j = n_j;
-    p_nb = n_nb;
-  } else {
-    fetch_now(cur, 0, ring[1], 0);
   }
 
   float m_run = -INFINITY, l_run = 0.f;  // head n of the wave (lanes n and n + 32 agree on m_run)
@@ -628,25 +673,43 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     // The fetch of the tile two blocks ahead (a filler past the end): its
     // transfers go between the score MFMAs, unless this tile ends an item and
     // the next item's q loads have to be issued before them (the vmcnt waits
-    // count on that order), or the rows are gathered through indices.
+    // count on that order).
     const bool item_ends = cur_j == cur_nb - 1;
     const bool q_next = item_ends && k + 1 < nblk;
-    const Item fI = k + 2 < nblk ? pI : cur;
-    const int fj = k + 2 < nblk ? p_j : cur_j;
-    int fpg = 0;  // page of the fetched block (dense; the filler reads page 0, never used)
-    if (k + 2 < nblk) {
-      if constexpr (!SPARSE) fpg = take_dword(pg_pref);
-      Item nI = pI;
-      int n_it = p_it, n_j = p_j, n_nb = p_nb;
-      advance(nI, n_it, n_j, n_nb);
-      if constexpr (!SPARSE) pg_pref = load_dword_async(k + 3 < nblk ? bt_entry(nI, n_j) : bt);
-      pI = nI;
-      p_it = n_it;
-      p_j = n_j;
-      p_nb = n_nb;
-    }
     DenseFetch F = {nullptr, 0};
-    if constexpr (!SPARSE) F = dense_prep(fI, fj, fpg);
+    uint32_t fsid = 0, fspg = 0;  // index-sparse: checked row ids and pages of the fetched tile
+    if constexpr (SPARSE) {
+      const uint32_t sid3 = sid_check(c3.I, take_vgpr(sid_fl));  // ids of tile k+3
+      fspg = spg_check(take_vgpr(spg_fl));                       // pages of tile k+2
+      fsid = sid2;
+      spg_fl = load_dword_async(spg_ptr(c3.I, sid3));  // pages of tile k+3
+      sid_fl = load_dword_async(sid_ptr(c4.I, c4.j));  // ids of tile k+4
+      sid2 = sid3;
+      c3 = c4;
+      adv(c4);
+    } else {
+      const Item fI = k + 2 < nblk ? pI : cur;
+      const int fj = k + 2 < nblk ? p_j : cur_j;
+      int fpg = 0;  // page of the fetched block (the filler reads page 0, never used)
+      if (k + 2 < nblk) {
+        fpg = take_dword(pg_pref);
+        Item nI = pI;
+        int n_it = p_it, n_j = p_j, n_nb = p_nb;
+        advance(nI, n_it, n_j, n_nb);
+        pg_pref = load_dword_async(k + 3 < nblk ? bt_entry(nI, n_j) : bt);
+        pI = nI;
+        p_it = n_it;
+        p_j = n_j;
+        p_nb = n_nb;
+      }
+      F = dense_prep(fI, fj, fpg);
+    }
+    auto piece = [&](int q, char* dst) __attribute__((always_inline)) {
+      if constexpr (SPARSE)
+        sparse_piece(fsid, fspg, q, dst);
+      else
+        dense_piece(F, q, dst);
+    };
     char* fdst = ring[st2];
 
     // S^T = K Q^T, 36 k-steps, operands read kPreS k-steps ahead
@@ -670,10 +733,10 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
         else
           mfma32_v(s, kop[ks], qop[ks]);
         if constexpr (kInter)
-          if ((ks & 3) == 2) dense_piece(F, ks >> 2, fdst);
+          if ((ks & 3) == 2) piece(ks >> 2, fdst);
       }
     };
-    if (!SPARSE && !q_next)
+    if (!q_next)
       scores(std::true_type{});
     else
       scores(std::false_type{});
@@ -682,13 +745,9 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       // q of the next item replaces this one as soon as the scores no longer need it
       load_q(uni(items[cur_it + 1].x));
     }
-    if (SPARSE || q_next) {
-      if constexpr (SPARSE) {
-        sparse_fetch(fI, fj, fdst);
-      } else {
+    if (q_next) {
 #pragma unroll
-        for (int q = 0; q < kDmaPerWave; ++q) dense_piece(F, q, fdst);
-      }
+      for (int q = 0; q < kDmaPerWave; ++q) piece(q, fdst);
     }
 
     // scores (base 2), masked past the item end; register r is token 8 (r / 4) + 4 g + r % 4
@@ -780,29 +839,49 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
         }
         const float rinv = r > 0.f ? 1.f / r : 0.f;
         if (g == 0) {
-          ps[hh] = m_run;
-          ps[kPartL + hh] = l_tot;
-          ps[kPartR + hh] = r;
+          partial_store(ps + hh, m_run);
+          partial_store(ps + kPartL + hh, l_tot);
+          partial_store(ps + kPartR + hh, r);
         }
-        _Float16* orow16 = reinterpret_cast<_Float16*>(ps + kPartO) + (size_t)hh * kDv + 4 * g;
-        unroll<16>([&](auto dc) {
-          constexpr int d = decltype(dc)::value;
-          unroll<4>([&](auto jc) {
-            constexpr int jj = decltype(jc)::value;
-            const f16x2 lo = __builtin_convertvector(
-                f32x2{acc_read<16 * d + 4 * jj>() * rinv, acc_read<16 * d + 4 * jj + 1>() * rinv}, f16x2);
-            const f16x2 hi = __builtin_convertvector(
-                f32x2{acc_read<16 * d + 4 * jj + 2>() * rinv, acc_read<16 * d + 4 * jj + 3>() * rinv}, f16x2);
-            *reinterpret_cast<u32x2*>(orow16 + 32 * d + 8 * jj) =
-                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        // The halves go out as whole 256-byte row segments with device-coherent
+        // stores (they reach memory before vmcnt clears, so the arrival below
+        // needs no L2-wide write-back).  A lane holds 4-half pieces of one
+        // head row, so each quarter of the row (4 dv blocks) is transposed
+        // through this wave's 8.5 KB of the stage of the tile just consumed
+        // (every wave is past its last read of it after the barrier).
+        __syncthreads();
+        char* tw = ring[st] + kPartRowLds * kHW * wave;
+        char* prow = reinterpret_cast<char*>(ps + kPartO) + (size_t)(kHW * wave) * (kDv * 2);
+        unroll<4>([&](auto qc) {
+          constexpr int R = decltype(qc)::value;
+          unroll<4>([&](auto dc) {
+            constexpr int d = 4 * R + decltype(dc)::value;
+            unroll<4>([&](auto jc) {
+              constexpr int jj = decltype(jc)::value;
+              const f16x2 lo = __builtin_convertvector(
+                  f32x2{acc_read<16 * d + 4 * jj>() * rinv, acc_read<16 * d + 4 * jj + 1>() * rinv}, f16x2);
+              const f16x2 hi = __builtin_convertvector(
+                  f32x2{acc_read<16 * d + 4 * jj + 2>() * rinv, acc_read<16 * d + 4 * jj + 3>() * rinv}, f16x2);
+              *reinterpret_cast<u32x2*>(tw + kPartRowLds * n + 2 * (32 * (d - 4 * R) + 8 * jj + 4 * g)) =
+                  u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            });
           });
+          wait_lds();
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int row = 4 * t + (lane >> 4);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(tw + kPartRowLds * row + 16 * (lane & 15));
+            store16_coherent(prow + (size_t)row * (kDv * 2) + 256 * R + 16 * (lane & 15), v);
+          }
         });
       }
       if (!whole) {
         if (p.reduce == CC_REDUCE_FUSED) {
-          __syncthreads();  // every wave's share of the partial is written
+          // every wave's share of the partial is in memory (device-coherent
+          // stores complete), then one arrival per piece
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
           if (tid == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             const int old = atomicAdd(&counters[cur.unit], 1);
             const bool last = old == cur.nsplit - 1;
             if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");

@@ -13,8 +13,9 @@
  *       merge),
  *   [4] exit, after merging the units it completed,
  *   [5] the id of the XCD (accelerator complex die) it ran on,
- *   [6], [7] unused (0).
- * Workgroups with no work record [0] == [1] == ... == [4].  From these the caller
+ *   [6], [7] GQA kernel: its merge-slot scan, then the per-head (max, sum)
+ *       pass of [2] are done; MLA kernel: unused (0).
+ * Workgroups with no work record [0] == [1] == ... == [4] (and [6], [7]).  From these the caller
  * computes the busy fraction of the compute units over the launch and checks
  * the workgroup-to-XCD placement the planner assumes (workgroup w on XCD
  * w mod num_xcds).

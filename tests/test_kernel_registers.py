@@ -7,6 +7,13 @@ live values.  If its own register allocation ever placed a value in an AGPR
 would overwrite each other.  This compiles the kernel (hipcc cross-compiles
 for gfx950 without a GPU) and checks that every AGPR access in the decode
 kernels sits inside an inline-asm block, and that nothing spills to scratch.
+
+The kernels also prefetch block-table entries and row ids with dword loads
+written as inline asm, which the compiler's own wait insertion does not
+track: the kernel's explicit vmcnt waits cover them.  The compiler must not
+read or overwrite such a load's destination register (a copy, a spill) before
+the next vmcnt wait, or it would see the register's old contents; the last
+test checks that on the generated code.
 """
 import os
 import re
@@ -43,7 +50,7 @@ def mla_asm(tmp_path_factory):
 def _kernel_body(asm, sparse):
     name = f"_ZN2cc3mla17mla_decode_kernelILb{1 if sparse else 0}EE"
     start = asm.index("\n" + name) + 1
-    end = asm.index("s_endpgm", start)
+    end = asm.index(".Lfunc_end", start)
     return asm[start:end]
 
 
@@ -74,3 +81,72 @@ def test_no_scratch_and_full_agpr_reservation(mla_asm):
         assert re.search(r"\.agpr_count:\s+256", block), "the kernel must reserve a0..a255"
         assert re.search(r"\.private_segment_fixed_size:\s+0\b", block + meta), "scratch spills"
         assert re.search(r"\.vgpr_spill_count:\s+0\b", block + meta), "VGPR spills"
+
+
+VREG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
+
+
+def _vregs(code):
+    regs = set()
+    for m in VREG.finditer(code):
+        if m.group(3) is not None:
+            regs.add(int(m.group(3)))
+        else:
+            regs.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return regs
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_untracked_loads_untouched_until_waited(mla_asm, sparse):
+    """Between an inline-asm global_load_dword and the next vmcnt wait (in code
+    order), no instruction outside inline asm names its destination VGPR."""
+    body = _kernel_body(mla_asm, sparse).splitlines()
+    inside, pending, found, bad = False, {}, 0, []
+    for i, line in enumerate(body):
+        if ";;#ASMSTART" in line:
+            inside = True
+            continue
+        if ";;#ASMEND" in line:
+            inside = False
+            continue
+        code = line.split(";")[0].strip()
+        if not code or code.endswith(":"):
+            continue
+        if "s_waitcnt" in code and "vmcnt" in code:
+            pending.clear()
+            continue
+        if inside:
+            m = re.match(r"global_load_dword\s+v(\d+),", code)
+            if m:
+                pending[int(m.group(1))] = i
+                found += 1
+            continue
+        hit = _vregs(code) & set(pending)
+        if hit:
+            bad.append(f"line {i}: {code} (load at line {pending[min(hit)]})")
+    assert found > 0, "no untracked dword loads found: the check no longer sees them"
+    assert not bad, "destination of an untracked load used before a vmcnt wait: " + "; ".join(bad[:3])
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_wide_asm_stores_end_with_a_wait_state(mla_asm, sparse):
+    """A VMEM store of more than 8 bytes needs one wait state before a VALU
+    write of its data registers.  The compiler adds it only after stores it
+    generates, so every such store written as inline asm must be followed by
+    an s_nop inside its own asm block."""
+    body = _kernel_body(mla_asm, sparse).splitlines()
+    inside, bad, found = False, [], 0
+    for i, line in enumerate(body):
+        if ";;#ASMSTART" in line:
+            inside = True
+            continue
+        if ";;#ASMEND" in line:
+            inside = False
+            continue
+        code = line.split(";")[0].strip()
+        if inside and re.match(r"(global|buffer|flat)_store_dwordx[34]\b", code):
+            found += 1
+            nxt = body[i + 1].split(";")[0].strip() if i + 1 < len(body) else ""
+            if not nxt.startswith("s_nop"):
+                bad.append(f"line {i}: {code} followed by {nxt!r}")
+    assert not bad, "; ".join(bad[:3])
