@@ -11,8 +11,15 @@ evicts the KV from the 256 MB last-level cache without leaving dirty lines
 behind (a write-based flush would leave write-back traffic running into the
 timed step), so each step reads its KV from HBM; the flush is outside the
 timed region.  The same box's plain streaming-read ceiling (1 GiB, the
-library's read probe, same flush) is reported beside the result.  Each step is timed with HIP events recorded on the stream the
-kernels run on.  The two comparison launches of the same computation (one
+library's read probe, same flush) is reported beside the result.
+
+Each step is timed with a pair of HIP events that the library records through
+hipExtLaunchKernel at the start of the call's first kernel and the end of its
+last (cc_debug_kernel_events), on the stream the kernels run on: the interval
+rocprofv3 traces for the kernel.  Events recorded as ordinary markers around
+the call add about 6 us of queue handling per step (a tiny kernel measures
+6.4 us that way); that time is reported beside the result.  The two comparison
+launches of the same computation (one
 workgroup per (sequence, KV head); split + separate combine kernel) are timed
 the same way beside it, and the fp64 CPU oracle is timed on the host cores.
 
@@ -59,8 +66,12 @@ def log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
-def time_steps(torch, run, steps, warmup, flush=None):
+def time_steps(torch, run, steps, warmup, flush=None, kernel_events=None):
     """Per-step event timings (ms) of run(); flush() runs untimed before each step.
+
+    With kernel_events (the binding's debug_kernel_events) the library records
+    each step's events at its kernels' start and end; otherwise the events are
+    recorded on the stream around run().
 
     Python's garbage collector is paused while steps are enqueued: a collection
     between a step's two events would show up as GPU idle time inside it."""
@@ -68,12 +79,12 @@ def time_steps(torch, run, steps, warmup, flush=None):
     gc.collect()
     gc.disable()
     try:
-        return _time_steps(torch, run, steps, warmup, flush)
+        return _time_steps(torch, run, steps, warmup, flush, kernel_events)
     finally:
         gc.enable()
 
 
-def _time_steps(torch, run, steps, warmup, flush):
+def _time_steps(torch, run, steps, warmup, flush, kernel_events):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         if flush:
@@ -81,12 +92,22 @@ def _time_steps(torch, run, steps, warmup, flush):
         run()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    if kernel_events:
+        for a, b in ev:  # torch creates an event at its first record
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
     for a, b in ev:
         if flush:
             flush()
-        a.record(stream)
-        run()
-        b.record(stream)
+        if kernel_events:
+            kernel_events(a, b)
+            run()
+            kernel_events(None, None)  # the next flush must not record into them
+        else:
+            a.record(stream)
+            run()
+            b.record(stream)
     torch.cuda.synchronize()
     return np.array([a.elapsed_time(b) for a, b in ev])
 
@@ -217,6 +238,8 @@ def main():
     def flush():
         B.probe_read(scratch, 0, 1024, sink)
 
+    ke = B.debug_kernel_events
+
     if args.calibrate:   # kernels of known traffic for the profiler's byte counters
         cal = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         for _ in range(2):
@@ -229,14 +252,15 @@ def main():
     probe_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     probe_by_method = {}
     for m in (0, 3):
-        pms = time_steps(torch, lambda: B.probe_read(probe_buf, m, 1024, sink), 20, 3, flush)
+        pms = time_steps(torch, lambda: B.probe_read(probe_buf, m, 1024, sink), 20, 3, flush, ke)
         probe_by_method[m] = (1 << 30) / (float(np.median(pms)) * 1e-3) / 1e9
     probe_gbs = max(probe_by_method.values())
     del probe_buf
     log(args, f"read probe ceiling: {probe_gbs:.0f} GB/s (plain {probe_by_method[0]:.0f}, nt {probe_by_method[3]:.0f})")
 
-    ms = time_steps(torch, s.run, args.steps, args.warmup, flush)
-    warm = time_steps(torch, s.run, args.steps, args.warmup)
+    ms = time_steps(torch, s.run, args.steps, args.warmup, flush, ke)
+    ms_markers = time_steps(torch, s.run, args.steps, args.warmup, flush)
+    warm = time_steps(torch, s.run, args.steps, args.warmup, None, ke)
     st = stats(ms)
     dirty, flags = B.workspace_check(plan, s.workspace)
     assert dirty == 0 and flags == 0, "workspace left dirty"
@@ -249,11 +273,11 @@ def main():
     if not args.no_variants:
         v1_plan = B.plan(prob, wl.seqlens, wl.block_table, num_cus=cus, num_xcds=xcds, policy=B.POLICY_PER_UNIT)
         v1 = B.session(wl, v1_plan)
-        variants["per_unit_workgroup"] = stats(time_steps(torch, v1.run, args.variant_steps, 3, flush))
+        variants["per_unit_workgroup"] = stats(time_steps(torch, v1.run, args.variant_steps, 3, flush, ke))
         del v1
         v2 = B.session(wl, plan)
         variants["split_then_combine"] = stats(time_steps(
-            torch, lambda: v2.run(B.REDUCE_SPLIT_COMBINE), args.variant_steps, 3, flush))
+            torch, lambda: v2.run(B.REDUCE_SPLIT_COMBINE), args.variant_steps, 3, flush, ke))
         del v2
         for k, v in variants.items():
             v["kv_gbs"] = kv / (v["mean_us"] * 1e-6) / 1e9
@@ -285,6 +309,8 @@ def main():
         "us_per_batch_median": st["median_us"],
         "us_p10_p90": [st["p10_us"], st["p90_us"]],
         "warm_us_median": stats(warm)["median_us"],
+        "timing": "kernel start to end (hipExtLaunchKernel events), cold, per step",
+        "us_per_batch_event_markers": stats(ms_markers),
         "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
         "read_probe_ceiling_gbs": probe_gbs,
         "read_probe_gbs_plain_nt": [probe_by_method[0], probe_by_method[3]],

@@ -27,7 +27,7 @@ REDUCE_FUSED, REDUCE_SPLIT_COMBINE = 0, 1
 # every symbol include/*.h declares
 EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_plan_size", "cc_plan",
            "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
-           "cc_decode_variant", "cc_debug_timeline", "cc_probe_read"]
+           "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_probe_read"]
 
 
 class Problem(ctypes.Structure):
@@ -82,6 +82,7 @@ def load() -> ctypes.CDLL:
     lib.cc_decode.argtypes = dec
     lib.cc_decode_variant.argtypes = [ctypes.c_int] + dec
     lib.cc_debug_timeline.argtypes = [_P, _SZ]
+    lib.cc_debug_kernel_events.argtypes = [_P, _P]
     lib.cc_probe_read.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, _P, _P]
     for f in EXPORTS:
@@ -194,6 +195,18 @@ def debug_timeline(buf) -> None:
     else:
         _check(lib.cc_debug_timeline(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()),
                "cc_debug_timeline")
+
+
+def debug_kernel_events(start, stop) -> None:
+    """Sets (two torch.cuda.Event objects with timing, already created by a
+    record) or clears (None, None) the events later decode calls record at the
+    start of their first kernel and the end of their last."""
+    lib = load()
+    if start is None:
+        _check(lib.cc_debug_kernel_events(None, None), "cc_debug_kernel_events")
+    else:
+        _check(lib.cc_debug_kernel_events(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)),
+               "cc_debug_kernel_events")
 
 
 def probe_read(buf, method: int, workgroups: int, sink, pages=None, page_bytes: int = 0,

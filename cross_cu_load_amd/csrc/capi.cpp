@@ -17,6 +17,8 @@ namespace {
 // debug timeline buffer (process-wide; set by cc_debug_timeline)
 void* g_timeline = nullptr;
 size_t g_timeline_bytes = 0;
+// debug kernel events (process-wide; set by cc_debug_kernel_events)
+hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -164,9 +166,14 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
                    ? static_cast<unsigned long long*>(g_timeline)
                    : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool combine = reduce == CC_REDUCE_SPLIT_COMBINE && v.partials() > 0;
+  a.ev_start = g_ev_start;
+  a.ev_stop = combine ? nullptr : g_ev_stop;
   hipError_t e = p.mode == CC_MODE_GQA ? cc::launch_gqa(a, s) : cc::launch_mla(a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (reduce == CC_REDUCE_SPLIT_COMBINE && v.partials() > 0) {
+  if (combine) {
+    a.ev_start = nullptr;
+    a.ev_stop = g_ev_stop;
     e = cc::launch_combine(a, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
@@ -175,6 +182,13 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
 
 }  // namespace
 
+namespace cc {
+void kernel_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = g_ev_start;
+  *stop = g_ev_stop;
+}
+}  // namespace cc
+
 extern "C" {
 
 int cc_version(void) { return 100; }
@@ -182,6 +196,16 @@ int cc_version(void) { return 100; }
 int cc_debug_timeline(void* buf, size_t bytes) {
   g_timeline = buf;
   g_timeline_bytes = buf ? bytes : 0;
+  return CC_OK;
+}
+
+int cc_debug_kernel_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) {
+    cc::set_error("cc_debug_kernel_events: give both events or neither");
+    return CC_ERR_INVALID;
+  }
+  g_ev_start = static_cast<hipEvent_t>(start_event);
+  g_ev_stop = static_cast<hipEvent_t>(stop_event);
   return CC_OK;
 }
 

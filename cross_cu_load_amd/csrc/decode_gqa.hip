@@ -27,6 +27,7 @@
 //
 // Scores are kept in base 2: s2 = scale * log2(e) * q.k, lse = ln2 * (m2 + log2 l).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdint>
 
@@ -710,15 +711,15 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gqa::gqa_decode_kernel<128>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    gqa::gqa_decode_kernel<128><<<a.workers, kThreads, lds, s>>>(
-        p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
+    hipExtLaunchKernelGGL(gqa::gqa_decode_kernel<128>, dim3(a.workers), dim3(kThreads), (uint32_t)lds, s,
+        a.ev_start, a.ev_stop, 0u, p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
         a.out, a.lse, a.err, a.counters, a.partials, a.timeline);
   } else {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gqa::gqa_decode_kernel<64>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    gqa::gqa_decode_kernel<64><<<a.workers, kThreads, lds, s>>>(
-        p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
+    hipExtLaunchKernelGGL(gqa::gqa_decode_kernel<64>, dim3(a.workers), dim3(kThreads), (uint32_t)lds, s,
+        a.ev_start, a.ev_stop, 0u, p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
         a.out, a.lse, a.err, a.counters, a.partials, a.timeline);
   }
   return hipGetLastError();
@@ -726,9 +727,9 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
   if (a.mode != CC_MODE_GQA) return launch_mla_combine(a, s);  // MLA partials hold fp16 rows
-  combine_kernel<<<a.units, kCombineThreads, 0, s>>>(a.hq, a.hkv, a.hq / a.hkv, a.hpu, a.dv,
-                                                     a.slot_floats, a.unit_nsplit, a.unit_pbase,
-                                                     a.partials, a.out, a.lse);
+  hipExtLaunchKernelGGL(combine_kernel, dim3(a.units), dim3(kCombineThreads), 0u, s, a.ev_start, a.ev_stop, 0u,
+                        a.hq, a.hkv, a.hq / a.hkv, a.hpu, a.dv, a.slot_floats, a.unit_nsplit, a.unit_pbase,
+                        a.partials, a.out, a.lse);
   return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@
 // than 2^8 (in base 2): probabilities stay below 256, and the rescale of the
 // accumulators happens on a handful of blocks per sequence.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdint>
 #include <type_traits>
@@ -954,8 +955,9 @@ int ilog2(int x) {
 }  // namespace mla
 
 hipError_t launch_mla_combine(const DecodeArgs& a, hipStream_t s) {
-  mla::mla_combine_kernel<<<dim3(a.units, mla::kHeads / mla::kCombineHeads), mla::kThreads, 0, s>>>(
-      a.slot_floats, a.unit_nsplit, a.unit_pbase, a.partials, a.out, a.lse);
+  hipExtLaunchKernelGGL(mla::mla_combine_kernel, dim3(a.units, mla::kHeads / mla::kCombineHeads),
+                        dim3(mla::kThreads), 0u, s, a.ev_start, a.ev_stop, 0u, a.slot_floats, a.unit_nsplit,
+                        a.unit_pbase, a.partials, a.out, a.lse);
   return hipGetLastError();
 }
 
@@ -971,12 +973,12 @@ hipError_t launch_mla(const DecodeArgs& a, hipStream_t s) {
   p.slot_floats = a.slot_floats;
   p.reduce = a.reduce;
   if (a.mode == CC_MODE_MLA_SPARSE) {
-    mla::mla_decode_kernel<true><<<a.workers, mla::kThreads, 0, s>>>(
-        p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.block_table, a.seqlens, a.indices,
+    hipExtLaunchKernelGGL(mla::mla_decode_kernel<true>, dim3(a.workers), dim3(mla::kThreads), 0u, s, a.ev_start,
+        a.ev_stop, 0u, p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.block_table, a.seqlens, a.indices,
         a.out, a.lse, a.err, a.counters, a.partials, a.timeline);
   } else {
-    mla::mla_decode_kernel<false><<<a.workers, mla::kThreads, 0, s>>>(
-        p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.block_table, a.seqlens, a.indices,
+    hipExtLaunchKernelGGL(mla::mla_decode_kernel<false>, dim3(a.workers), dim3(mla::kThreads), 0u, s, a.ev_start,
+        a.ev_stop, 0u, p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.block_table, a.seqlens, a.indices,
         a.out, a.lse, a.err, a.counters, a.partials, a.timeline);
   }
   return hipGetLastError();

@@ -36,7 +36,14 @@ struct DecodeArgs {
   int reduce;  // CC_REDUCE_*
   // optional in-kernel timeline (kTimelineWords x uint64 per workgroup), null when off
   unsigned long long* timeline;
+  // optional events recorded at the start of the call's first kernel and the
+  // end of its last (hipExtLaunchKernel), null when off
+  hipEvent_t ev_start;
+  hipEvent_t ev_stop;
 };
+
+// The debug kernel events set by cc_debug_kernel_events (null when off).
+void kernel_events(hipEvent_t* start, hipEvent_t* stop);
 
 // uint64 words per workgroup in the debug timeline
 constexpr int kTimelineWords = 8;

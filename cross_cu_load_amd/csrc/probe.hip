@@ -6,11 +6,13 @@
 // list, whole pages in the listed order, as a paged KV cache is read) and
 // folds the data into one word per thread so no load is dead.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdint>
 
 #include "../../include/crosscu.h"
 #include "../../include/crosscu_debug.h"
+#include "launch.h"
 
 namespace cc {
 namespace probe {
@@ -118,11 +120,15 @@ extern "C" int cc_probe_read(const void* buf, long long bytes, int method, const
   const void* fn = nt ? reinterpret_cast<const void*>(&read_probe<true>) : reinterpret_cast<const void*>(&read_probe<false>);
   if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return CC_ERR_HIP;
+  hipEvent_t ev0, ev1;
+  cc::kernel_events(&ev0, &ev1);
   if (nt)
-    read_probe<true><<<workgroups, kThreads, lds, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const char*>(buf), bytes, m, pages, page_bytes, num_pages, static_cast<uint32_t*>(sink));
+    hipExtLaunchKernelGGL(read_probe<true>, dim3(workgroups), dim3(kThreads), (uint32_t)lds,
+                          static_cast<hipStream_t>(stream), ev0, ev1, 0u, static_cast<const char*>(buf), bytes, m,
+                          pages, page_bytes, num_pages, static_cast<uint32_t*>(sink));
   else
-    read_probe<false><<<workgroups, kThreads, lds, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const char*>(buf), bytes, m, pages, page_bytes, num_pages, static_cast<uint32_t*>(sink));
+    hipExtLaunchKernelGGL(read_probe<false>, dim3(workgroups), dim3(kThreads), (uint32_t)lds,
+                          static_cast<hipStream_t>(stream), ev0, ev1, 0u, static_cast<const char*>(buf), bytes, m,
+                          pages, page_bytes, num_pages, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? CC_OK : CC_ERR_HIP;
 }

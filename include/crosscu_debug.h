@@ -37,6 +37,17 @@ extern "C" {
  * CC_OK. */
 int cc_debug_timeline(void* buf, size_t bytes);
 
+/* Sets (both non-NULL) or clears (both NULL) a pair of HIP events
+ * (hipEvent_t, created by the caller with timing enabled) that later
+ * cc_decode / cc_decode_variant / cc_probe_read calls on any stream record
+ * through hipExtLaunchKernel: start_event when the call's first kernel
+ * begins, stop_event when its last kernel ends.  The time between them covers the
+ * call's kernels (both kernels of the split-then-combine variant, and the gap
+ * between them), without the queue markers an ordinary event record adds
+ * around a launch.  The caller owns the events and must keep them alive while
+ * set.  Returns CC_OK, or CC_ERR_INVALID when only one event is given. */
+int cc_debug_kernel_events(void* start_event, void* stop_event);
+
 /* Streaming-read probe: reads `bytes` (a multiple of 16 KiB, >= 16 KiB) of
  * device memory `buf` once with `workgroups` persistent workgroups of 512
  * threads, asynchronously on `stream`, so the caller can time the practical

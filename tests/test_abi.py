@@ -200,3 +200,10 @@ def test_mla_decode_rejects_before_any_launch(lib):
     sparse = B.problem(**{**kw, "mode": B.MODE_MLA_SPARSE, "topk": 16})
     assert call(sparse) == B.CC_ERR_INVALID          # no indices
     assert B.kernel_heads_per_unit(prob) == 128 and B.kernel_heads_per_unit(sparse) == 128
+
+
+def test_debug_kernel_events_needs_both_or_neither(lib):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: the pair is only stored
+    assert lib.cc_debug_kernel_events(None, fake) == B.CC_ERR_INVALID
+    assert lib.cc_debug_kernel_events(fake, None) == B.CC_ERR_INVALID
+    assert lib.cc_debug_kernel_events(None, None) == B.CC_OK

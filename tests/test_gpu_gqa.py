@@ -151,3 +151,37 @@ def test_page_placement_is_bitwise_irrelevant(dev):
     wl2 = W.Workload(wl.cfg, wl.seqlens, bt2, wl.q, k2, v2, None)
     s2, _ = run(wl2, *dev, tag="placement-b")
     assert torch.equal(s2.out, o_a) and torch.equal(s2.lse, s.lse)
+
+
+@pytest.mark.parametrize("reduce", [B.REDUCE_FUSED, B.REDUCE_SPLIT_COMBINE])
+def test_kernel_events_bracket_the_call(dev, reduce):
+    """Events set with cc_debug_kernel_events are recorded at the start of the
+    call's first kernel and the end of its last: their interval is positive and
+    shorter than the same call bracketed by ordinary event records; outputs are
+    unchanged; after clearing them a call records nothing."""
+    cfg = W.small_variant(W.CONFIG_BY_NAME["skewed_gqa"], batch=8, seqlen_hi=20000)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, reduce=reduce, tag="kernel-events")
+    o0 = s.out.clone()
+    stream = torch.cuda.current_stream()
+    a, b, c, d = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (a, b, c, d):
+        e.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms, marker_ms = [], []
+    for _ in range(5):
+        B.debug_kernel_events(a, b)
+        s.run(reduce)
+        B.debug_kernel_events(None, None)
+        c.record(stream)
+        s.run(reduce)
+        d.record(stream)
+        torch.cuda.synchronize()
+        kernel_ms.append(a.elapsed_time(b))
+        marker_ms.append(c.elapsed_time(d))
+        s.run(reduce)  # cleared: must not move a or b
+        torch.cuda.synchronize()
+        assert a.elapsed_time(b) == kernel_ms[-1]
+    assert torch.equal(s.out, o0)
+    assert 0 < np.median(kernel_ms) < np.median(marker_ms)
+    clean(s, plan)
