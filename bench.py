@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--variant-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time back-to-back calls eagerly and replayed from a captured HIP graph")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 256 MiB fill and a 1 GiB read of known size (scales profiler byte counters)")
@@ -115,6 +117,46 @@ def _time_steps(torch, run, steps, warmup, flush, kernel_events):
 def stats(ms):
     return dict(mean_us=float(ms.mean() * 1e3), median_us=float(np.median(ms) * 1e3),
                 p10_us=float(np.percentile(ms, 10) * 1e3), p90_us=float(np.percentile(ms, 90) * 1e3))
+
+
+def graph_pass(torch, s, calls=100, reps=5):
+    """Warm back-to-back decode calls: host-launched one by one, then replayed
+    from a HIP graph that holds the same calls (what a launch-bound caller does).
+    Per-call time between two stream events around all the calls."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        best = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            best.append(a.elapsed_time(b) * 1e3 / calls)
+        return float(np.median(best))
+
+    def eager():
+        for _ in range(calls):
+            s.run()
+
+    eager()
+    torch.cuda.synchronize()
+    eager_us = timed(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        s.run()
+    stream.wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            s.run()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    graph_us = timed(g.replay)
+    return {"calls": calls, "eager_us_per_call": eager_us, "graph_us_per_call": graph_us}
 
 
 def timeline_pass(torch, B, s, workers, xcds, flush):
@@ -324,6 +366,9 @@ def main():
         "variants": variants,
         "timeline": tline,
     }
+    if args.graph:
+        result["graph"] = graph_pass(torch, s)
+        log(args, f"graph: {result['graph']}")
     if variants:
         result["speedup_vs_variants"] = {k: v["mean_us"] / st["mean_us"] for k, v in variants.items()}
     if not args.no_cpu_baseline:
