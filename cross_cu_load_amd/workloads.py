@@ -34,7 +34,7 @@ KV_HND = 1   # pages [Hkv][P][d]: head-major
 _CHUNK = 1 << 22
 
 # stream ids (the second SeedSequence word)
-_S_SEQLENS, _S_PAGES, _S_Q, _S_K, _S_V, _S_IDX = range(6)
+_S_SEQLENS, _S_PAGES, _S_Q, _S_K, _S_V, _S_IDX, _S_IQ, _S_IK = range(8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -235,3 +235,26 @@ def small_variant(cfg: Config, batch: int, seqlen_hi: int, seed_offset: int = 0)
     else:
         kw.update(seqlen_kind="uniform", seqlen_lo=1, seqlen_hi=seqlen_hi)
     return Config(**kw)
+
+
+# ---------------------------------------------------------------- indexer inputs
+# The step before index-sparse attention: a cheap indexer scores every cached
+# token of a request against each decode query token, and the top-k positions
+# become the sparse index sets (GLM-5.2 decode article: "Paged Indexer Score"
+# ahead of TopK and sparse MLA; Top-2048).  One indexer query per decode token
+# and one indexer key per cached token, on the same pages as the latent cache.
+INDEXER_DIM = 128
+
+
+@dataclasses.dataclass
+class IndexerInputs:
+    q: np.ndarray        # uint16 [B, Tq, dim]: indexer query of each decode token
+    k_cache: np.ndarray  # uint16 [num_pages, P, dim]: indexer key of each cached token
+
+
+def make_indexer_inputs(wl: Workload, dim: int = INDEXER_DIM) -> IndexerInputs:
+    """Indexer query and key bits for a workload's requests (same block table and pages)."""
+    c = wl.cfg
+    q = normal_bf16(c.seed, _S_IQ, (c.batch, c.q_tokens, dim))
+    k = normal_bf16(c.seed, _S_IK, (wl.num_pages, c.page_size, dim))
+    return IndexerInputs(q, k)
