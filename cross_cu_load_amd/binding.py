@@ -27,7 +27,14 @@ REDUCE_FUSED, REDUCE_SPLIT_COMBINE = 0, 1
 # every symbol include/*.h declares
 EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_plan_size", "cc_plan",
            "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
-           "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_probe_read"]
+           "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_probe_read",
+           "cc_indexer_scratch_size", "cc_indexer_topk"]
+
+
+class IndexerProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_tokens", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("topk", ctypes.c_int32)]
 
 
 class Problem(ctypes.Structure):
@@ -83,6 +90,8 @@ def load() -> ctypes.CDLL:
     lib.cc_decode_variant.argtypes = [ctypes.c_int] + dec
     lib.cc_debug_timeline.argtypes = [_P, _SZ]
     lib.cc_debug_kernel_events.argtypes = [_P, _P]
+    lib.cc_indexer_scratch_size.argtypes = [ctypes.POINTER(IndexerProblem), _I32P, ctypes.POINTER(_SZ)]
+    lib.cc_indexer_topk.argtypes = [ctypes.POINTER(IndexerProblem), _I32P, _P, _P, _P, _P, _SZ, _P, _P, _P]
     lib.cc_probe_read.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, _P, _P]
     for f in EXPORTS:
@@ -195,6 +204,32 @@ def debug_timeline(buf) -> None:
     else:
         _check(lib.cc_debug_timeline(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()),
                "cc_debug_timeline")
+
+
+def indexer_problem(batch, q_tokens, dim, page_size, max_pages, num_pages, topk) -> IndexerProblem:
+    return IndexerProblem(batch, q_tokens, dim, page_size, max_pages, num_pages, topk)
+
+
+def indexer_scratch_size(p: IndexerProblem, seqlens: np.ndarray) -> int:
+    lib = load()
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    n = _SZ()
+    _check(lib.cc_indexer_scratch_size(ctypes.byref(p), sl.ctypes.data_as(_I32P), ctypes.byref(n)),
+           "cc_indexer_scratch_size")
+    return int(n.value)
+
+
+def indexer_topk(p: IndexerProblem, seqlens: np.ndarray, q, k_cache, block_table, scratch, indices, err=None,
+                 stream=None) -> None:
+    """cc_indexer_topk on device tensors; seqlens is a host array."""
+    lib = load()
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    _check(lib.cc_indexer_topk(ctypes.byref(p), sl.ctypes.data_as(_I32P), ctypes.c_void_p(q.data_ptr()),
+                               ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(block_table.data_ptr()),
+                               ctypes.c_void_p(scratch.data_ptr()), scratch.numel() * scratch.element_size(),
+                               ctypes.c_void_p(indices.data_ptr()),
+                               None if err is None else ctypes.c_void_p(err.data_ptr()), _stream(stream)),
+           "cc_indexer_topk")
 
 
 def debug_kernel_events(start, stop) -> None:

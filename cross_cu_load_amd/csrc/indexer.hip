@@ -1,0 +1,279 @@
+// Paged indexer score and top-k selection (the step that produces the index
+// sets of index-sparse decode attention: GLM-5.2 decode article, "Paged
+// Indexer Score" ahead of TopK and sparse MLA, Summary; the Top-2048 the
+// indexer rank publishes, related-work section on TileRT).
+//
+// Two kernels.  The score kernel gives each lane one cached token: the lane
+// reads that token's 256-byte key row into registers and, for every decode
+// token of the request, runs one fp32 FMA chain over the 128 dimensions in
+// index order (a bf16 x bf16 product is exact in fp32, so each FMA rounds
+// once, exactly as an add of the exact product).  The queries sit in LDS and
+// are read as broadcasts.  It is a streaming read of the key cache, a few MB.
+//
+// The top-k kernel gives each decode token one 1024-thread workgroup: the
+// scores become order-preserving unsigned keys in LDS, a radix select over
+// four 8-bit digits finds the k-th largest key T and how many keys equal to
+// T belong to the result, and a stable compaction in position order writes
+// every key above T plus the first such keys equal to T.  Integer work on
+// the score bits, so the result is exact and deterministic.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/crosscu.h"
+#include "../../include/crosscu_indexer.h"
+#include "plan.h"
+
+namespace cc {
+namespace indexer {
+
+constexpr int kDim = 128;
+constexpr int kMaxTq = 16;
+constexpr int kMaxB = 64;
+constexpr int kMaxL = 16384;
+constexpr int kScoreThreads = 64;  // one wave: 4 x more workgroups than a 256-token tile
+constexpr int kTopkThreads = 1024;
+constexpr int kErrPage = 2;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Lens {
+  int32_t L[kMaxB];
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// grid (ceil(max L / 64), B); lane = cached token j of request blockIdx.y
+__global__ void __launch_bounds__(kScoreThreads)
+indexer_score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                     const int32_t* __restrict__ bt, Lens lens, int tq, int log2p, int max_pages, int num_pages,
+                     int ld, float* __restrict__ scores, int32_t* __restrict__ err) {
+  __shared__ float qs[kMaxTq * kDim];
+  const int b = blockIdx.y;
+  const int L = lens.L[b];
+  for (int i = threadIdx.x; i < tq * kDim; i += kScoreThreads) {
+    const uint32_t h = q[(size_t)b * tq * kDim + i];
+    qs[i] = __uint_as_float(h << 16);
+  }
+  __syncthreads();
+  const int j = blockIdx.x * kScoreThreads + threadIdx.x;
+  if (j >= L) return;
+  int pg = bt[(size_t)b * max_pages + (j >> log2p)];
+  if ((unsigned)pg >= (unsigned)num_pages) {
+    if (err) atomicOr(err, kErrPage);
+    pg = pg < 0 ? 0 : num_pages - 1;
+  }
+  const u32x4* row = reinterpret_cast<const u32x4*>(
+      kc + (((size_t)pg << log2p) + (size_t)(j & ((1 << log2p) - 1))) * kDim);
+  u32x4 r[kDim / 8];
+#pragma unroll
+  for (int c = 0; c < kDim / 8; ++c) r[c] = row[c];
+  for (int m = 0; m < tq; ++m) {
+    const float* qm = qs + m * kDim;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < kDim / 8; ++c) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = __builtin_fmaf(qm[8 * c + 2 * w], bf16_lo(r[c][w]), acc);
+        acc = __builtin_fmaf(qm[8 * c + 2 * w + 1], bf16_hi(r[c][w]), acc);
+      }
+    }
+    scores[(size_t)(b * tq + m) * ld + j] = acc;
+  }
+}
+
+// Exclusive prefix sum over the workgroup (kTopkThreads threads), in thread order.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  __syncthreads();  // wsum free from a previous scan
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  return before + incl - x;
+}
+
+// grid B * Tq; one workgroup per decode token
+__global__ void __launch_bounds__(kTopkThreads)
+indexer_topk_kernel(const float* __restrict__ scores, int ld, Lens lens, int tq, int topk,
+                    int32_t* __restrict__ out) {
+  __shared__ uint32_t keys[kMaxL];
+  __shared__ uint32_t hist[256];
+  __shared__ int wsum[kTopkThreads / 64];
+  __shared__ uint32_t sh_digit, sh_above;
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  const int L = lens.L[r / tq];
+  const float* s = scores + (size_t)r * ld;
+  for (int j = tid; j < L; j += kTopkThreads) {
+    uint32_t u = __float_as_uint(s[j]);
+    if (u == 0x80000000u) u = 0u;  // -0 ranks with +0
+    keys[j] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  // radix select of the topk-th largest key, most significant digit first
+  uint32_t prefix = 0, mask = 0;
+  uint32_t kk = (uint32_t)topk;  // rank still to place among keys matching prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int j = tid; j < L; j += kTopkThreads) {
+      const uint32_t k = keys[j];
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds bins 4l .. 4l+3; the digit is where the count of larger
+      // keys first reaches kk, scanning from the top bin down
+      const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
+      const uint32_t sum = h0 + h1 + h2 + h3;
+      uint32_t incl = sum;  // sum over lanes >= tid
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_down(incl, o);
+        if (tid + o < 64) incl += t;
+      }
+      const uint32_t above = incl - sum;  // keys in bins above 4 tid + 3
+      if (above < kk && kk <= incl) {
+        uint32_t c = above;
+        uint32_t d;
+        if (c + h3 >= kk) {
+          d = 4 * tid + 3;
+        } else if (c += h3, c + h2 >= kk) {
+          d = 4 * tid + 2;
+        } else if (c += h2, c + h1 >= kk) {
+          d = 4 * tid + 1;
+        } else {
+          c += h1;
+          d = 4 * tid;
+        }
+        sh_digit = d;
+        sh_above = c;
+      }
+    }
+    __syncthreads();
+    kk -= sh_above;
+    prefix |= sh_digit << shift;
+    mask |= 255u << shift;
+  }
+  const uint32_t T = prefix;  // the topk-th largest key; kk keys equal to it are kept
+  // stable compaction in position order; thread tid owns positions [j0, j1)
+  const int seg = (L + kTopkThreads - 1) / kTopkThreads;
+  const int j0 = min(L, tid * seg), j1 = min(L, j0 + seg);
+  int gt = 0, eq = 0;
+  for (int j = j0; j < j1; ++j) {
+    gt += keys[j] > T;
+    eq += keys[j] == T;
+  }
+  const int eq_before = block_exclusive_scan(eq, wsum);
+  const int take_eq = max(0, min(eq, (int)kk - eq_before));
+  int pos = block_exclusive_scan(gt + take_eq, wsum);
+  int eqr = eq_before;
+  int32_t* o = out + (size_t)r * topk;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t k = keys[j];
+    if (k > T) {
+      if (pos < topk) o[pos] = j;
+      ++pos;
+    } else if (k == T) {
+      if (eqr < (int)kk) {
+        if (pos < topk) o[pos] = j;
+        ++pos;
+      }
+      ++eqr;
+    }
+  }
+}
+
+}  // namespace indexer
+}  // namespace cc
+
+namespace {
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+// Host checks shared by both calls; max L into *maxl.
+int check(const cc_indexer_problem* p, const int32_t* seqlens, int* maxl) {
+  using namespace cc::indexer;
+  if (!p || !seqlens) {
+    cc::set_error("cc_indexer: null problem or seqlens");
+    return CC_ERR_INVALID;
+  }
+  if (p->batch < 1 || p->q_tokens < 1 || p->dim < 1 || !pow2(p->page_size) || p->max_pages_per_seq < 1 ||
+      p->num_pages < 1 || p->topk < 1) {
+    cc::set_error("cc_indexer: bad problem sizes");
+    return CC_ERR_INVALID;
+  }
+  if (p->dim != kDim || p->q_tokens > kMaxTq || p->batch > kMaxB) {
+    cc::set_error("cc_indexer: implemented for dim 128, q_tokens <= 16, batch <= 64");
+    return CC_ERR_UNSUPPORTED;
+  }
+  int m = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    const int L = seqlens[b];
+    if (L < 1 || p->topk > L || (L + p->page_size - 1) / p->page_size > p->max_pages_per_seq) {
+      cc::set_error("cc_indexer: request %d: length %d, topk %d, pages %d", b, L, p->topk, p->max_pages_per_seq);
+      return CC_ERR_INVALID;
+    }
+    if (L > kMaxL) {
+      cc::set_error("cc_indexer: request %d: length %d above 16384", b, L);
+      return CC_ERR_UNSUPPORTED;
+    }
+    m = L > m ? L : m;
+  }
+  *maxl = m;
+  return CC_OK;
+}
+}  // namespace
+
+extern "C" int cc_indexer_scratch_size(const cc_indexer_problem* p, const int32_t* seqlens, size_t* bytes) {
+  if (!bytes) return CC_ERR_INVALID;
+  int maxl = 0;
+  const int rc = check(p, seqlens, &maxl);
+  if (rc != CC_OK) return rc;
+  *bytes = (size_t)p->batch * p->q_tokens * maxl * sizeof(float);
+  return CC_OK;
+}
+
+extern "C" int cc_indexer_topk(const cc_indexer_problem* p, const int32_t* seqlens, const void* q,
+                               const void* k_cache, const int32_t* block_table, void* scratch, size_t scratch_bytes,
+                               int32_t* indices, int32_t* err, void* stream) {
+  using namespace cc::indexer;
+  int maxl = 0;
+  const int rc = check(p, seqlens, &maxl);
+  if (rc != CC_OK) return rc;
+  if (!q || !k_cache || !block_table || !scratch || !indices) {
+    cc::set_error("cc_indexer_topk: null device pointer");
+    return CC_ERR_INVALID;
+  }
+  const size_t need = (size_t)p->batch * p->q_tokens * maxl * sizeof(float);
+  if (scratch_bytes < need) {
+    cc::set_error("cc_indexer_topk: scratch %zu bytes, need %zu", scratch_bytes, need);
+    return CC_ERR_BUFFER;
+  }
+  Lens lens = {};
+  for (int b = 0; b < p->batch; ++b) lens.L[b] = seqlens[b];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* sc = static_cast<float*>(scratch);
+  indexer_score_kernel<<<dim3((maxl + kScoreThreads - 1) / kScoreThreads, p->batch), kScoreThreads, 0, s>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), block_table, lens, p->q_tokens,
+      ilog2(p->page_size), p->max_pages_per_seq, p->num_pages, maxl, sc, err);
+  indexer_topk_kernel<<<p->batch * p->q_tokens, kTopkThreads, 0, s>>>(sc, maxl, lens, p->q_tokens, p->topk,
+                                                                        indices);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    cc::set_error("cc_indexer_topk: %s", hipGetErrorString(e));
+    return CC_ERR_HIP;
+  }
+  return CC_OK;
+}

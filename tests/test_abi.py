@@ -207,3 +207,27 @@ def test_debug_kernel_events_needs_both_or_neither(lib):
     assert lib.cc_debug_kernel_events(None, fake) == B.CC_ERR_INVALID
     assert lib.cc_debug_kernel_events(fake, None) == B.CC_ERR_INVALID
     assert lib.cc_debug_kernel_events(None, None) == B.CC_OK
+
+
+def test_indexer_rejects_before_any_launch(lib):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails a host check first
+    sl = np.array([3000, 100], np.int32)
+
+    def call(p, seqlens=sl, scratch_bytes=1 << 30, q=fake):
+        return lib.cc_indexer_topk(ctypes.byref(p), seqlens.ctypes.data_as(B._I32P), q, fake, fake, fake,
+                                   scratch_bytes, fake, None, None)
+
+    ok = B.indexer_problem(2, 8, 128, 64, 47, 60, 100)
+    n = ctypes.c_size_t()
+    assert lib.cc_indexer_scratch_size(ctypes.byref(ok), sl.ctypes.data_as(B._I32P), ctypes.byref(n)) == 0
+    assert n.value == 2 * 8 * 3000 * 4
+    assert call(B.indexer_problem(2, 8, 128, 64, 47, 60, 101)) == B.CC_ERR_INVALID     # topk > L_1
+    assert call(B.indexer_problem(2, 8, 64, 64, 47, 60, 100)) == B.CC_ERR_UNSUPPORTED  # dim
+    assert call(B.indexer_problem(2, 17, 128, 64, 47, 60, 100)) == B.CC_ERR_UNSUPPORTED  # q_tokens
+    assert call(B.indexer_problem(2, 8, 128, 48, 47, 60, 100)) == B.CC_ERR_INVALID     # page size
+    assert call(B.indexer_problem(2, 8, 128, 64, 46, 60, 100)) == B.CC_ERR_INVALID     # block table too narrow
+    assert call(ok, seqlens=np.array([20000, 100], np.int32)) == B.CC_ERR_INVALID or \
+        call(B.indexer_problem(2, 8, 128, 64, 400, 60, 100), seqlens=np.array([20000, 100], np.int32)) == \
+        B.CC_ERR_UNSUPPORTED
+    assert call(ok, scratch_bytes=n.value - 4) == B.CC_ERR_BUFFER
+    assert call(ok, q=None) == B.CC_ERR_INVALID
