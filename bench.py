@@ -225,6 +225,35 @@ def mfma_flops(wl):
     return 2.0 * (c.head_dim_qk + c.head_dim_v) * c.num_q_heads * keys
 
 
+def indexer_pass(torch, B, W, wl, flush, ke, steps, warmup):
+    """The indexer that produces the sparse workload's index sets (paged score
+    + top-k over each request's cached tokens), kernel-timed like the decode."""
+    c = wl.cfg
+    ix = W.make_indexer_inputs(wl)
+    p = B.indexer_problem(c.batch, c.q_tokens, W.INDEXER_DIM, c.page_size, wl.max_pages, wl.num_pages, c.topk)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+    q, k, bt = dev(ix.q), dev(ix.k_cache), dev(wl.block_table)
+    scratch = torch.empty(B.indexer_scratch_size(p, wl.seqlens), dtype=torch.uint8, device="cuda")
+    out = torch.empty((c.batch, c.q_tokens, c.topk), dtype=torch.int32, device="cuda")
+    ms = time_steps(torch, lambda: B.indexer_topk(p, wl.seqlens, q, k, bt, scratch, out), steps, warmup, flush, ke)
+    key_bytes = int(wl.seqlens.astype(np.int64).sum()) * W.INDEXER_DIM * 2
+    st = stats(ms)
+    return {"us_mean": st["mean_us"], "us_median": st["median_us"], "key_bytes": key_bytes,
+            "key_gbs": key_bytes / (st["mean_us"] * 1e-6) / 1e9, "selected_per_token": c.topk}, ix
+
+
+def indexer_cpu_baseline(wl, ix):
+    """The indexer oracle on the host: the whole batch once."""
+    from oracle import indexer as I
+    t0 = time.perf_counter()
+    I.indexer_topk(ix.q, ix.k_cache, wl.block_table, wl.seqlens, wl.cfg.topk)
+    return (time.perf_counter() - t0) * 1e6
+
+
 def cpu_baseline(wl, args):
     """The fp64 oracle, as it stands, on the host cores: the whole workload once."""
     from oracle import attention as A
@@ -366,6 +395,11 @@ def main():
         "variants": variants,
         "timeline": tline,
     }
+    if cfg.mode == W.MODE_MLA_SPARSE:
+        result["indexer"], ix = indexer_pass(torch, B, W, wl, flush, ke, args.steps, args.warmup)
+        if not args.no_cpu_baseline:
+            result["indexer"]["cpu_oracle_us"] = indexer_cpu_baseline(wl, ix)
+        log(args, f"indexer: {result['indexer']}")
     if args.graph:
         result["graph"] = graph_pass(torch, s)
         log(args, f"graph: {result['graph']}")

@@ -3,12 +3,13 @@
 // Indexer Score" ahead of TopK and sparse MLA, Summary; the Top-2048 the
 // indexer rank publishes, related-work section on TileRT).
 //
-// Two kernels.  The score kernel gives each lane one cached token: the lane
-// reads that token's 256-byte key row into registers and, for every decode
-// token of the request, runs one fp32 FMA chain over the 128 dimensions in
-// index order (a bf16 x bf16 product is exact in fp32, so each FMA rounds
-// once, exactly as an add of the exact product).  The queries sit in LDS and
-// are read as broadcasts.  It is a streaming read of the key cache, a few MB.
+// Two kernels.  The score kernel gives each lane one (cached token, decode
+// token) pair: the lane reads the token's 256-byte key row and the query row
+// into registers and runs one fp32 FMA chain over the 128 dimensions in index
+// order (a bf16 x bf16 product is exact in fp32, so each FMA rounds once,
+// exactly as an add of the exact product).  The lanes of one cached token
+// share its key row's loads.  It is a streaming read of the key cache, a few
+// MB.
 //
 // The top-k kernel gives each decode token one 1024-thread workgroup: the
 // scores become order-preserving unsigned keys in LDS, a radix select over
@@ -17,11 +18,13 @@
 // every key above T plus the first such keys equal to T.  Integer work on
 // the score bits, so the result is exact and deterministic.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdint>
 
 #include "../../include/crosscu.h"
 #include "../../include/crosscu_indexer.h"
+#include "launch.h"
 #include "plan.h"
 
 namespace cc {
@@ -31,7 +34,7 @@ constexpr int kDim = 128;
 constexpr int kMaxTq = 16;
 constexpr int kMaxB = 64;
 constexpr int kMaxL = 16384;
-constexpr int kScoreThreads = 64;  // one wave: 4 x more workgroups than a 256-token tile
+constexpr int kScoreThreads = 256;
 constexpr int kTopkThreads = 1024;
 constexpr int kErrPage = 2;
 
@@ -44,21 +47,20 @@ struct Lens {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// grid (ceil(max L / 64), B); lane = cached token j of request blockIdx.y
+// grid (ceil(max L * tqp / 256), B): lane = (cached token j, decode token m)
+// of request blockIdx.y, m fastest (tqp = tq rounded up to a power of two),
+// so the tqp lanes of one token read the same key row in the same load
+// instruction; each lane holds its query row and the key row in registers and
+// runs one FMA chain over the 128 dimensions in index order.
 __global__ void __launch_bounds__(kScoreThreads)
 indexer_score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-                     const int32_t* __restrict__ bt, Lens lens, int tq, int log2p, int max_pages, int num_pages,
-                     int ld, float* __restrict__ scores, int32_t* __restrict__ err) {
-  __shared__ float qs[kMaxTq * kDim];
+                     const int32_t* __restrict__ bt, Lens lens, int tq, int log2tqp, int log2p, int max_pages,
+                     int num_pages, int ld, float* __restrict__ scores, int32_t* __restrict__ err) {
   const int b = blockIdx.y;
   const int L = lens.L[b];
-  for (int i = threadIdx.x; i < tq * kDim; i += kScoreThreads) {
-    const uint32_t h = q[(size_t)b * tq * kDim + i];
-    qs[i] = __uint_as_float(h << 16);
-  }
-  __syncthreads();
-  const int j = blockIdx.x * kScoreThreads + threadIdx.x;
-  if (j >= L) return;
+  const int t = blockIdx.x * kScoreThreads + threadIdx.x;
+  const int j = t >> log2tqp, m = t & ((1 << log2tqp) - 1);
+  if (j >= L || m >= tq) return;
   int pg = bt[(size_t)b * max_pages + (j >> log2p)];
   if ((unsigned)pg >= (unsigned)num_pages) {
     if (err) atomicOr(err, kErrPage);
@@ -66,22 +68,23 @@ indexer_score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
   const u32x4* row = reinterpret_cast<const u32x4*>(
       kc + (((size_t)pg << log2p) + (size_t)(j & ((1 << log2p) - 1))) * kDim);
-  u32x4 r[kDim / 8];
+  const u32x4* qrow = reinterpret_cast<const u32x4*>(q + ((size_t)b * tq + m) * kDim);
+  u32x4 r[kDim / 8], qv[kDim / 8];
 #pragma unroll
-  for (int c = 0; c < kDim / 8; ++c) r[c] = row[c];
-  for (int m = 0; m < tq; ++m) {
-    const float* qm = qs + m * kDim;
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < kDim / 8; ++c) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc = __builtin_fmaf(qm[8 * c + 2 * w], bf16_lo(r[c][w]), acc);
-        acc = __builtin_fmaf(qm[8 * c + 2 * w + 1], bf16_hi(r[c][w]), acc);
-      }
-    }
-    scores[(size_t)(b * tq + m) * ld + j] = acc;
+  for (int c = 0; c < kDim / 8; ++c) {
+    r[c] = row[c];
+    qv[c] = qrow[c];
   }
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < kDim / 8; ++c) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = __builtin_fmaf(bf16_lo(qv[c][w]), bf16_lo(r[c][w]), acc);
+      acc = __builtin_fmaf(bf16_hi(qv[c][w]), bf16_hi(r[c][w]), acc);
+    }
+  }
+  scores[(size_t)(b * tq + m) * ld + j] = acc;
 }
 
 // Exclusive prefix sum over the workgroup (kTopkThreads threads), in thread order.
@@ -106,6 +109,7 @@ __global__ void __launch_bounds__(kTopkThreads)
 indexer_topk_kernel(const float* __restrict__ scores, int ld, Lens lens, int tq, int topk,
                     int32_t* __restrict__ out) {
   __shared__ uint32_t keys[kMaxL];
+  __shared__ uint32_t whist[kTopkThreads / 64][256];  // one histogram per wave: fewer same-bin atomics
   __shared__ uint32_t hist[256];
   __shared__ int wsum[kTopkThreads / 64];
   __shared__ uint32_t sh_digit, sh_above;
@@ -113,20 +117,40 @@ indexer_topk_kernel(const float* __restrict__ scores, int ld, Lens lens, int tq,
   const int r = blockIdx.x;
   const int L = lens.L[r / tq];
   const float* s = scores + (size_t)r * ld;
-  for (int j = tid; j < L; j += kTopkThreads) {
-    uint32_t u = __float_as_uint(s[j]);
-    if (u == 0x80000000u) u = 0u;  // -0 ranks with +0
-    keys[j] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  {
+    // every score load of a thread issued before any is used (one round trip)
+    constexpr int kPer = kMaxL / kTopkThreads;
+    uint32_t v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = tid + u * kTopkThreads;
+      v[u] = j < L ? __float_as_uint(s[j]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = tid + u * kTopkThreads;
+      uint32_t x = v[u];
+      if (x == 0x80000000u) x = 0u;  // -0 ranks with +0
+      if (j < L) keys[j] = (x & 0x80000000u) ? ~x : (x | 0x80000000u);
+    }
   }
   // radix select of the topk-th largest key, most significant digit first
   uint32_t prefix = 0, mask = 0;
   uint32_t kk = (uint32_t)topk;  // rank still to place among keys matching prefix
+  uint32_t* wh = whist[tid >> 6];
   for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+    for (int i = tid; i < (kTopkThreads / 64) * 256; i += kTopkThreads) whist[i >> 8][i & 255] = 0;
     __syncthreads();
     for (int j = tid; j < L; j += kTopkThreads) {
       const uint32_t k = keys[j];
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      if ((k & mask) == prefix) atomicAdd(&wh[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kTopkThreads / 64; ++w) t += whist[w][tid];
+      hist[tid] = t;
     }
     __syncthreads();
     if (tid < 64) {
@@ -265,11 +289,16 @@ extern "C" int cc_indexer_topk(const cc_indexer_problem* p, const int32_t* seqle
   for (int b = 0; b < p->batch; ++b) lens.L[b] = seqlens[b];
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* sc = static_cast<float*>(scratch);
-  indexer_score_kernel<<<dim3((maxl + kScoreThreads - 1) / kScoreThreads, p->batch), kScoreThreads, 0, s>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), block_table, lens, p->q_tokens,
-      ilog2(p->page_size), p->max_pages_per_seq, p->num_pages, maxl, sc, err);
-  indexer_topk_kernel<<<p->batch * p->q_tokens, kTopkThreads, 0, s>>>(sc, maxl, lens, p->q_tokens, p->topk,
-                                                                        indices);
+  hipEvent_t ev0, ev1;  // debug kernel events (cc_debug_kernel_events): start of the first, end of the last
+  cc::kernel_events(&ev0, &ev1);
+  const int log2tqp = ilog2(p->q_tokens);
+  const long long lanes = (long long)maxl << log2tqp;
+  hipExtLaunchKernelGGL(indexer_score_kernel, dim3((unsigned)((lanes + kScoreThreads - 1) / kScoreThreads), p->batch),
+                        dim3(kScoreThreads), 0u, s, ev0, nullptr, 0u, static_cast<const uint16_t*>(q),
+                        static_cast<const uint16_t*>(k_cache), block_table, lens, p->q_tokens, log2tqp,
+                        ilog2(p->page_size), p->max_pages_per_seq, p->num_pages, maxl, sc, err);
+  hipExtLaunchKernelGGL(indexer_topk_kernel, dim3(p->batch * p->q_tokens), dim3(kTopkThreads), 0u, s, nullptr, ev1,
+                        0u, static_cast<const float*>(sc), maxl, lens, p->q_tokens, p->topk, indices);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     cc::set_error("cc_indexer_topk: %s", hipGetErrorString(e));

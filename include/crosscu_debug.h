@@ -39,7 +39,8 @@ int cc_debug_timeline(void* buf, size_t bytes);
 
 /* Sets (both non-NULL) or clears (both NULL) a pair of HIP events
  * (hipEvent_t, created by the caller with timing enabled) that later
- * cc_decode / cc_decode_variant / cc_probe_read calls on any stream record
+ * cc_decode / cc_decode_variant / cc_probe_read / cc_indexer_topk calls on
+ * any stream record
  * through hipExtLaunchKernel: start_event when the call's first kernel
  * begins, stop_event when its last kernel ends.  The time between them covers the
  * call's kernels (both kernels of the split-then-combine variant, and the gap
