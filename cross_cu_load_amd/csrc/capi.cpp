@@ -74,6 +74,12 @@ int check_mla(const cc_problem& p, const cc::PlanView& v) {
     cc::set_error("MLA kernel: tile_tokens must be a multiple of 32 (got %d)", v.header[cc::H_TILE]);
     return CC_ERR_UNSUPPORTED;
   }
+  // a workgroup packs each split piece it publishes (unit, split index) into one word
+  if (v.units() >= (1 << 20) || v.header[cc::H_MAXSPLIT] > 512) {
+    cc::set_error("MLA kernel: at most 2^20 - 1 units and 512 splits per unit (got %d units, %d splits)",
+                  v.units(), v.header[cc::H_MAXSPLIT]);
+    return CC_ERR_UNSUPPORTED;
+  }
   return CC_OK;
 }
 
@@ -264,7 +270,7 @@ int cc_workspace_check(const void* plan_host, const void* workspace, void* strea
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-  std::vector<int32_t> cnt(v.units());
+  std::vector<int32_t> cnt(cc::WorkspaceLayout::counter_words(v));
   int32_t flags = 0;
   const char* ws = static_cast<const char*>(workspace);
   e = hipMemcpy(&flags, ws, sizeof flags, hipMemcpyDeviceToHost);

@@ -34,6 +34,7 @@
 #include "../../include/crosscu.h"
 #include "launch.h"
 #include "merge.h"
+#include "plan.h"
 
 namespace cc {
 namespace gqa {
@@ -622,12 +623,12 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       if (on) {
         unit = split_list[lane][0];
         ns = split_list[lane][1];
-        old = atomicAdd(&counters[unit], 1);
+        old = atomicAdd(&counters[kCounterStride * unit], 1);
       }
       const bool done = on && old == ns - 1;
       const unsigned long long db = __ballot(done);
       if (done) {
-        __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&counters[kCounterStride * unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int d = __popcll(db & ((1ull << lane) - 1));
         done_units[d][0] = split_list[lane][2];
         done_units[d][1] = ns;

@@ -46,6 +46,7 @@
 #include "../../include/crosscu.h"
 #include "launch.h"
 #include "merge.h"
+#include "plan.h"
 
 namespace cc {
 namespace mla {
@@ -214,6 +215,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// The value through a VGPR move the compiler cannot see into, so the code
+// that uses it treats it as per-lane.  The post-stream merge takes its split
+// count and slot size this way: as scalars, the loop counts and addresses
+// derived from them raise the kernel's scalar register pressure, and the
+// allocator then spills scalars inside the tile loop.
+__device__ __forceinline__ int in_vgpr(int x) {
+  int r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
 // HBM -> LDS transfer of 16 bytes per active lane: lane i's bytes land at
 // lds + 16 i (lds wave-uniform).  Written as inline asm on purpose: the
 // compiler's own wait insertion cannot tell which stage a transfer targets and
@@ -303,20 +314,35 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
-// Merge of heads h0 .. h0 + nh - 1 of a unit's split partials by one
-// workgroup.  Threads 0 .. nh - 1, one per head, load every split's (m, l) of
-// their head (16 splits in flight), form (M, L) and the lse, and stage the
+// Merge of heads h0 .. h0 + nh - 1 (nh <= 128) of a unit's split partials by
+// one workgroup.  Threads 0 .. nh - 1, one per head, load every split's (m, l)
+// of their head (16 splits in flight), form (M, L) and the lse, and stage the
 // split weights c_s = exp2(m_s - M) r_s / L for up to kMergeChunk splits in
 // LDS.  Then all threads stream the output in 16-byte columns (8 halves),
 // consecutive threads on consecutive columns, kMergeCols columns x
-// kMergeSplits splits = 32 loads in flight per thread.  Splits are combined in
-// index order, so the result does not depend on which piece arrived last.
-// The partials were published with an agent-scope release (or a kernel
-// boundary); the caller has performed the matching acquire.
+// kMergeSplits splits = 32 loads in flight per thread; columns past the head
+// range repeat the thread's first column and are not stored.  Splits are
+// combined in index order, so the result does not depend on which piece
+// arrived last or which workgroup merges the range.  The partials were
+// published with device-coherent stores before their pieces' arrivals (or a
+// kernel boundary); the caller has performed the matching acquire.
 constexpr int kMergeChunk = 64;  // split weights staged per pass
 constexpr int kMergeCols = 4;    // 16-byte columns per thread per round
-static_assert((16 * (512 / 8)) % (256 * 4) == 0, "merged head ranges are whole rounds");
 constexpr int kMergeSplits = 8;  // splits per round
+
+// Arrival counter of a split unit: pieces that have published (low half) and
+// pieces done with the unit's merge (upper half).
+constexpr int kArriveMask = 0xffff;
+constexpr int kLeaveShift = 16;
+constexpr int kLeave = 1 << kLeaveShift;
+// A unit's merge is cut into at most kSlices head ranges of whole 8-head
+// blocks; slice k of nsl starts at head slice_head(k, nsl).
+constexpr int kSlices = 16;
+__device__ __forceinline__ int slice_head(int k, int nsl) { return 8 * ((16 * k) / nsl); }
+// Polls of a unit's counter a finished piece makes (each after a sleep of
+// kPollSleep x 64 clocks) before it leaves the unit's slices to the others.
+constexpr int kSpinLimit = 512;
+constexpr int kPollSleep = 8;
 __host__ __device__ constexpr int merge_lds_floats_mla(int nh) { return 2 * nh + kMergeChunk * nh; }
 __device__ __forceinline__ void merge_unit(const float* pb, int ns, int slot_floats, float* out, float* lse,
                                            float* lds, int h0, int nh) {
@@ -362,18 +388,19 @@ __device__ __forceinline__ void merge_unit(const float* pb, int ns, int slot_flo
       coef[i] = fast_exp2(ps[h0 + hl] - ml[hl]) * ps[kPartR + h0 + hl] * ml[nh + hl];
     }
     __syncthreads();
-    // ncols is a multiple of kThreads * kMergeCols (128 or 16 heads of 64
-    // columns), so no column is out of range; a round past the last split
-    // re-reads the last one with weight 0
+    // a round past the last split re-reads the last one with weight 0; a
+    // column past the range (e >= ncols) re-reads column e0 (< ncols)
     for (int e0 = tid; e0 < ncols; e0 += kThreads * kMergeCols) {
       f32x8 acc[kMergeCols];
+      int col[kMergeCols];
 #pragma unroll
       for (int u = 0; u < kMergeCols; ++u) {
         const int e = e0 + kThreads * u;
+        col[u] = e < ncols ? e : e0;
         if (c0 == 0) {
           acc[u] = f32x8{};
         } else {
-          const f32x4 a = out4[2 * e], b = out4[2 * e + 1];
+          const f32x4 a = out4[2 * col[u]], b = out4[2 * col[u] + 1];
           acc[u] = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         }
       }
@@ -383,12 +410,12 @@ __device__ __forceinline__ void merge_unit(const float* pb, int ns, int slot_flo
         for (int t = 0; t < kMergeSplits; ++t) {
           const u32x4_* src = o16 + (size_t)(c0 + min(s0 + t, nc - 1)) * slot16;  // wave-uniform base
 #pragma unroll
-          for (int u = 0; u < kMergeCols; ++u) v[u][t] = src[e0 + kThreads * u];
+          for (int u = 0; u < kMergeCols; ++u) v[u][t] = src[col[u]];
         }
         __builtin_amdgcn_sched_barrier(0);  // one round of loads live at a time
 #pragma unroll
         for (int u = 0; u < kMergeCols; ++u) {
-          const int hl = (e0 + kThreads * u) / (kDv / 8);
+          const int hl = col[u] / (kDv / 8);
 #pragma unroll
           for (int t = 0; t < kMergeSplits; ++t) {
             const float c = s0 + t < nc ? coef[(s0 + t) * nh + hl] : 0.f;
@@ -399,9 +426,11 @@ __device__ __forceinline__ void merge_unit(const float* pb, int ns, int slot_flo
       }
 #pragma unroll
       for (int u = 0; u < kMergeCols; ++u) {
-        const int e = e0 + kThreads * u;
-        out4[2 * e] = f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
-        out4[2 * e + 1] = f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]};
+        if (e0 + kThreads * u < ncols) {
+          const int e = col[u];
+          out4[2 * e] = f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
+          out4[2 * e + 1] = f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]};
+        }
       }
     }
   }
@@ -416,6 +445,7 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
                   const int32_t* __restrict__ indices, float* __restrict__ out, float* __restrict__ lse,
                   int32_t* err, int32_t* counters, float* partials, unsigned long long* timeline) {
   __shared__ int sh_last;
+  __shared__ uint32_t sh_claim;
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63;
@@ -657,7 +687,11 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   acc_reserve();
   acc_zero();
   bool fresh = true;  // no block of the current item seen yet
-  int pend0 = 0, pend1 = 0, npend = 0;  // units to merge after the stream
+  // split pieces this workgroup published (only a chunk's first and last
+  // items can be split), one word each: unit << 11 | split << 2 | arrived
+  // last << 1 | 1 (0: none); the host keeps units below 2^20 and split
+  // indices below 2^9
+  int pend0 = 0, pend1 = 0;
 
   // one block: tile k in stage st = k % 3; the fetch two blocks ahead goes to stage (k + 2) % 3
   int st = 0, st2 = 2;
@@ -883,20 +917,16 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
           if (tid == 0) {
-            const int old = atomicAdd(&counters[cur.unit], 1);
-            const bool last = old == cur.nsplit - 1;
-            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            sh_last = last;
+            const int old = atomicAdd(&counters[kCounterStride * cur.unit], 1);
+            sh_last = (old & kArriveMask) == cur.nsplit - 1;
           }
           __syncthreads();
-          if (uni(sh_last)) {
-            // merged after the stream: only a chunk's first and last items can be split
-            if (npend == 0) {
-              pend0 = cur.unit;
-            } else {
-              pend1 = cur.unit;
-            }
-            ++npend;
+          // the unit is merged after the stream
+          const int word = (cur.unit << 11) | (cur.split << 2) | (uni(sh_last) << 1) | 1;
+          if (pend0 == 0) {
+            pend0 = word;
+          } else {
+            pend1 = word;
           }
         }
       }
@@ -920,13 +950,85 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     st2 = st2 == 2 ? 0 : st2 + 1;
   }
   if (tl && tid == 0) tl[1] = tl[2] = __builtin_amdgcn_s_memrealtime();
-  // units this workgroup completed last: merge their partials (no q or accumulators live here)
-  for (int i = 0; i < npend; ++i) {
-    const int unit = uni(i == 0 ? pend0 : pend1);
-    merge_unit(partials + (size_t)uni(unit_pbase[unit]) * p.slot_floats, uni(unit_nsplit[unit]), p.slot_floats,
-               out + (size_t)unit * kHeads * kDv, lse + (size_t)unit * kHeads, reinterpret_cast<float*>(ring[0]), 0,
-               kHeads);
-    if (tid == 0) __hip_atomic_store(&counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Merge of the split units this workgroup published pieces of (no q or
+  // accumulators live here).  A unit's 128 heads form nsl = min(nsplit,
+  // kSlices) slices of whole 8-head blocks.  Once every piece of a unit has
+  // arrived, each of its pieces claims slice "split index" if that is still
+  // free, merges it, and then claims and merges any slice still free until
+  // none is left; a claim is an atomic OR on the unit's claim mask, so each
+  // slice is merged exactly once, by whichever workgroup claims it.  A
+  // workgroup polls its (at most two) units in turn and works on whichever is
+  // complete.  The last arriver never waits, so every slice is merged even
+  // when other pieces stop polling (after kSpinLimit polls): no piece's
+  // progress depends on another workgroup being resident.  Each piece then
+  // leaves (the counter's upper half); the last to leave clears the counter
+  // and the mask, so the workspace is left zeroed.
+  int todo = (pend0 ? 1 : 0) | (pend1 ? 2 : 0);
+  for (int spin = 0; todo; ++spin) {
+    const bool give_up = spin >= kSpinLimit;
+    for (int e = 0; e < 2; ++e) {
+      if (!((todo >> e) & 1)) continue;
+      const int word = uni(e == 0 ? pend0 : pend1);
+      const int unit = word >> 11;
+      const int split = (word >> 2) & 511;
+      const int ns = uni(unit_nsplit[unit]);
+      const int nsl = min(ns, kSlices);
+      int32_t* cnt = counters + kCounterStride * unit;
+      uint32_t* claim = reinterpret_cast<uint32_t*>(cnt + 1);
+      __syncthreads();  // every thread has read sh_claim
+      if (tid == 0) {
+        bool ready = (word >> 1) & 1;  // arrived last
+        if (!ready) ready = (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kArriveMask) == ns;
+        if (ready) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        sh_claim = ready;
+      }
+      __syncthreads();
+      const bool ready = uni((int)sh_claim) != 0;
+      if (!ready && !give_up) continue;
+      if (ready) {
+        const float* pb = partials + (size_t)uni(unit_pbase[unit]) * p.slot_floats;
+        float* ou = out + (size_t)unit * kHeads * kDv;
+        float* lu = lse + (size_t)unit * kHeads;
+        const uint32_t every = (1u << nsl) - 1u;
+        int want = split < nsl ? split : -1;
+        uint32_t seen = 0;  // claim bits known to be taken
+        for (;;) {
+          __syncthreads();  // every thread has read sh_claim
+          if (tid == 0) {
+            int got = -1;
+            while (got < 0) {
+              if (want < 0) {
+                const uint32_t free = every & ~seen;
+                if (!free) break;
+                want = __builtin_ctz(free);
+              }
+              const uint32_t bit = 1u << want;
+              const uint32_t old = atomicOr(claim, bit);
+              seen |= old | bit;
+              if (!(old & bit)) got = want;
+              want = -1;
+            }
+            sh_claim = (uint32_t)got;
+          }
+          __syncthreads();
+          const int r = uni((int)sh_claim);
+          if (r < 0) break;
+          const int h0 = slice_head(r, nsl);
+          merge_unit(pb, in_vgpr(ns), in_vgpr(p.slot_floats), ou, lu,
+                     reinterpret_cast<float*>(ring[0]), h0, slice_head(r + 1, nsl) - h0);
+        }
+      }
+      __syncthreads();  // sh_claim is rewritten next
+      if (tid == 0) {
+        const int old = atomicAdd(cnt, kLeave);
+        if ((old >> kLeaveShift) == ns - 1) {
+          __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      todo &= ~(1 << e);
+    }
+    if (todo && tid == 0) __builtin_amdgcn_s_sleep(kPollSleep);
   }
   if (tl && tid == 0) tl[3] = tl[4] = __builtin_amdgcn_s_memrealtime();
 }

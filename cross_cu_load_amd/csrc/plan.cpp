@@ -313,7 +313,7 @@ WorkspaceLayout workspace_layout(const PlanView& v) {
   WorkspaceLayout L;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   L.counters_off = 256;  // the error word lives at offset 0
-  L.partials_off = align(L.counters_off + sizeof(int32_t) * (size_t)v.units());
+  L.partials_off = align(L.counters_off + sizeof(int32_t) * L.counter_words(v));
   const size_t hpu = (size_t)v.header[H_HPU];
   const size_t o_off = (2 * hpu + 3) & ~size_t(3);  // o starts 16-byte aligned
   L.slot_floats = (o_off + hpu * (size_t)v.header[H_DV] + 63) & ~size_t(63);

@@ -67,9 +67,15 @@ constexpr int64_t kUnitCostGqa = 16;
 constexpr int64_t kUnitCostMla = 96;
 inline int64_t unit_cost(int mode) { return mode == CC_MODE_GQA ? kUnitCostGqa : kUnitCostMla; }
 
+// int32 words per unit in the workspace counter area: the arrival counter,
+// the merge-claim mask, then padding, so that every unit's words sit in a
+// 128-byte line of their own (workgroups poll them while others stream).
+constexpr int kCounterStride = 32;
+
 // Workspace layout of a plan: error word and counters first, then partials.
 struct WorkspaceLayout {
-  size_t counters_off = 0;   // bytes; int32[U]
+  size_t counters_off = 0;   // bytes; int32[U][kCounterStride]
+  static size_t counter_words(const PlanView& v) { return kCounterStride * (size_t)v.units(); }
   size_t partials_off = 0;   // bytes; S slots {m[hpu], l[hpu], pad to 4, o[hpu][dv]}
   size_t slot_floats = 0;    // floats per partial slot
   size_t total = 0;

@@ -153,8 +153,9 @@ int cc_plan_size(const cc_problem* prob, const cc_plan_opts* opts, const int32_t
 int cc_plan(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
             const int32_t* block_table, void* plan, size_t bytes);
 
-/* Device workspace bytes a plan needs: an error word, one arrival counter per
- * unit and one partial (m, l, o) slot per piece of a split unit. */
+/* Device workspace bytes a plan needs: an error word, an arrival counter and
+ * a merge-claim mask per unit, and one partial (m, l, o) slot per piece of a
+ * split unit. */
 int cc_workspace_size(const void* plan_host, size_t* bytes);
 
 /* Zero a workspace (device, `bytes` long) on `stream` with a fill kernel.
@@ -164,7 +165,7 @@ int cc_workspace_size(const void* plan_host, size_t* bytes);
 int cc_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* Synchronous debug check of a workspace after the work on `stream`:
- * *dirty_counters = number of non-zero arrival counters, *device_flags = the
+ * *dirty_counters = number of non-zero arrival counters and claim masks, *device_flags = the
  * device error word (bit 0: a plan item ran past seqlens[b]; bit 1: a page id
  * outside [0, num_pages); bit 2: a sparse index outside [0, seqlens[b])).
  * Returns CC_ERR_DEVICE_DATA if either is non-zero. */

@@ -56,10 +56,11 @@ def test_plan_bytes_match_reference_on_workload_lengths(lib, name, C, X, T, poli
         ref = PL.plan(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
                       cfg.head_dim_v, cfg.page_size, maxp, npages, cfg.topk, C, X, T, hu, sl, None, policy)
         assert blob.tobytes() == ref["blob"]
-        # workspace: 256 B error word area, counters, 256-aligned partial slots of
+        # workspace: 256 B error word area, 128 B of counter words per unit,
+        # 256-aligned partial slots of
         # {m[hu], l[hu], pad to 4 floats, o[hu][dv]} rounded up to 64 floats
         slot = -(-(-(-2 * hu // 4) * 4 + hu * cfg.head_dim_v) // 64) * 64
-        cnt_end = 256 + 4 * ref["num_units"]
+        cnt_end = 256 + 128 * ref["num_units"]
         part = -(-cnt_end // 256) * 256
         want = -(-(part + 4 * slot * ref["num_partials"]) // 256) * 256
         assert B.workspace_size(blob) == want

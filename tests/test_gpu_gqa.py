@@ -127,7 +127,7 @@ def test_stale_partials_do_not_leak(dev):
     s, plan = run(wl, *dev, tag="nan-poison")
     o0, l0 = s.out.clone(), s.lse.clone()
     units = int(plan.view(np.int32)[15])
-    partials_off = -(-(256 + 4 * units) // 256) * 256
+    partials_off = -(-(256 + 128 * units) // 256) * 256
     assert int(plan.view(np.int32)[18]) > 0, "the case must split some unit"
     s.workspace[partials_off:].view(torch.float32).fill_(float("nan"))
     s.run()
