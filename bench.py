@@ -186,8 +186,8 @@ def timeline_pass(torch, B, s, workers, xcds, flush):
             "xcd_ids_seen": sorted(set(int(x) for x in xcc))}
 
 
-KERNEL_SOURCES = {"gqa_decode_kernel": ("decode_gqa.hip", "merge.h", "launch.h"),
-                  "mla_decode_kernel": ("decode_mla.hip", "merge.h", "launch.h")}
+KERNEL_SOURCES = {"gqa_decode_kernel": ("decode_gqa.hip", "merge.h", "launch.h", "plan.h"),
+                  "mla_decode_kernel": ("decode_mla.hip", "merge.h", "launch.h", "plan.h")}
 
 
 def kernel_name(mode):

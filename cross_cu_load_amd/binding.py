@@ -27,7 +27,7 @@ REDUCE_FUSED, REDUCE_SPLIT_COMBINE = 0, 1
 # every symbol include/*.h declares
 EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_plan_size", "cc_plan",
            "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
-           "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_probe_read",
+           "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_debug_merge_poll_limit", "cc_probe_read",
            "cc_indexer_scratch_size", "cc_indexer_topk"]
 
 
@@ -90,6 +90,7 @@ def load() -> ctypes.CDLL:
     lib.cc_decode_variant.argtypes = [ctypes.c_int] + dec
     lib.cc_debug_timeline.argtypes = [_P, _SZ]
     lib.cc_debug_kernel_events.argtypes = [_P, _P]
+    lib.cc_debug_merge_poll_limit.argtypes = [ctypes.c_int]
     lib.cc_indexer_scratch_size.argtypes = [ctypes.POINTER(IndexerProblem), _I32P, ctypes.POINTER(_SZ)]
     lib.cc_indexer_topk.argtypes = [ctypes.POINTER(IndexerProblem), _I32P, _P, _P, _P, _P, _SZ, _P, _P, _P]
     lib.cc_probe_read.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
@@ -204,6 +205,11 @@ def debug_timeline(buf) -> None:
     else:
         _check(lib.cc_debug_timeline(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()),
                "cc_debug_timeline")
+
+
+def debug_merge_poll_limit(polls: int) -> None:
+    """MLA in-kernel merge poll limit on the current device (< 0: the default)."""
+    _check(load().cc_debug_merge_poll_limit(int(polls)), "cc_debug_merge_poll_limit")
 
 
 def indexer_problem(batch, q_tokens, dim, page_size, max_pages, num_pages, topk) -> IndexerProblem:

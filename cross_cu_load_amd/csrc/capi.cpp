@@ -215,6 +215,12 @@ int cc_debug_kernel_events(void* start_event, void* stop_event) {
   return CC_OK;
 }
 
+int cc_debug_merge_poll_limit(int polls) {
+  const hipError_t e = cc::set_mla_merge_poll_limit(polls);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyToSymbol(merge poll limit)");
+  return CC_OK;
+}
+
 const char* cc_last_error(void) { return cc::last_error(); }
 
 const char* cc_strerror(int code) {

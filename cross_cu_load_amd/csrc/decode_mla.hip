@@ -343,6 +343,9 @@ __device__ __forceinline__ int slice_head(int k, int nsl) { return 8 * ((16 * k)
 // kPollSleep x 64 clocks) before it leaves the unit's slices to the others.
 constexpr int kSpinLimit = 512;
 constexpr int kPollSleep = 8;
+// The poll limit in use on this device (cc_debug_merge_poll_limit lowers it to
+// exercise the path where pieces stop waiting).
+__device__ int g_merge_poll_limit = kSpinLimit;
 __host__ __device__ constexpr int merge_lds_floats_mla(int nh) { return 2 * nh + kMergeChunk * nh; }
 __device__ __forceinline__ void merge_unit(const float* pb, int ns, int slot_floats, float* out, float* lse,
                                            float* lds, int h0, int nh) {
@@ -964,8 +967,10 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   // leaves (the counter's upper half); the last to leave clears the counter
   // and the mask, so the workspace is left zeroed.
   int todo = (pend0 ? 1 : 0) | (pend1 ? 2 : 0);
+  const int poll_limit = todo ? uni(__hip_atomic_load(&g_merge_poll_limit, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)) : 0;
   for (int spin = 0; todo; ++spin) {
-    const bool give_up = spin >= kSpinLimit;
+    const bool give_up = spin >= poll_limit;
     for (int e = 0; e < 2; ++e) {
       if (!((todo >> e) & 1)) continue;
       const int word = uni(e == 0 ? pend0 : pend1);
@@ -1061,6 +1066,11 @@ hipError_t launch_mla_combine(const DecodeArgs& a, hipStream_t s) {
                         dim3(mla::kThreads), 0u, s, a.ev_start, a.ev_stop, 0u, a.slot_floats, a.unit_nsplit,
                         a.unit_pbase, a.partials, a.out, a.lse);
   return hipGetLastError();
+}
+
+hipError_t set_mla_merge_poll_limit(int polls) {
+  const int v = polls < 0 ? mla::kSpinLimit : polls;
+  return hipMemcpyToSymbol(HIP_SYMBOL(mla::g_merge_poll_limit), &v, sizeof v);
 }
 
 hipError_t launch_mla(const DecodeArgs& a, hipStream_t s) {

@@ -57,6 +57,8 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_mla(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_mla_combine(const DecodeArgs& a, hipStream_t s);
+// Sets the MLA kernel's merge poll limit on the current device (< 0: the default).
+hipError_t set_mla_merge_poll_limit(int polls);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace cc

@@ -15,6 +15,9 @@
  *   [5] the id of the XCD (accelerator complex die) it ran on,
  *   [6], [7] GQA kernel: its merge-slot scan, then the per-head (max, sum)
  *       pass of [2] are done; MLA kernel: unused (0).
+ * The MLA kernel publishes and arrives inside its stream, so its [2] equals
+ * [1]; between [1] and [4] it waits for its split units to complete and merges
+ * head slices of them, and its [3] equals [4].
  * Workgroups with no work record [0] == [1] == ... == [4] (and [6], [7]).  From these the caller
  * computes the busy fraction of the compute units over the launch and checks
  * the workgroup-to-XCD placement the planner assumes (workgroup w on XCD
@@ -48,6 +51,16 @@ int cc_debug_timeline(void* buf, size_t bytes);
  * around a launch.  The caller owns the events and must keep them alive while
  * set.  Returns CC_OK, or CC_ERR_INVALID when only one event is given. */
 int cc_debug_kernel_events(void* start_event, void* stop_event);
+
+/* MLA in-kernel merge: once a workgroup has finished its chunk, it polls each
+ * split unit it holds a piece of until every piece has arrived, then merges
+ * head slices of it.  After `polls` polls it stops waiting and leaves those
+ * slices to the unit's other pieces (the last piece to arrive never waits and
+ * merges whatever is left).  This sets the poll limit for later launches on
+ * the current device; polls < 0 restores the default (512).  Lowering it
+ * exercises the path where pieces stop waiting; the result is the same.
+ * Returns CC_OK or CC_ERR_HIP. */
+int cc_debug_merge_poll_limit(int polls);
 
 /* Streaming-read probe: reads `bytes` (a multiple of 16 KiB, >= 16 KiB) of
  * device memory `buf` once with `workgroups` persistent workgroups of 512

@@ -140,3 +140,30 @@ def test_mla_repeat_runs_bitwise_identical(dev):
     torch.cuda.synchronize()
     assert torch.equal(s.out, o0) and torch.equal(s.lse, l0)
     clean(s, plan)
+
+
+@pytest.mark.parametrize("polls", [0, 1])
+@pytest.mark.parametrize("name", ["deepseek_mla", "sparse_mla"])
+def test_mla_merge_when_pieces_stop_waiting(dev, name, polls):
+    """The in-kernel merge with finished pieces that stop polling at once (poll
+    limit forced low from the host): their head slices fall to the pieces still
+    there, the last arriver never waits, so the output is bitwise the same and
+    the arrival counters and claim masks are left zeroed."""
+    cfg = W.CONFIG_BY_NAME[name]
+    cfg = W.small_variant(cfg, batch=6, seqlen_hi=6000, seed_offset=11) if name == "deepseek_mla" else \
+        W.small_variant(cfg, batch=2, seqlen_hi=4096, seed_offset=11)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, tag=f"mla-merge-polls {name}")
+    assert int(plan.view(np.int32)[18]) > 0, "the case must split some unit"
+    o0, l0 = s.out.clone(), s.lse.clone()
+    try:
+        B.debug_merge_poll_limit(polls)
+        for _ in range(3):
+            s.out.fill_(float("nan"))
+            s.run()
+        torch.cuda.synchronize()
+    finally:
+        B.debug_merge_poll_limit(-1)
+    assert torch.equal(s.out, o0) and torch.equal(s.lse, l0)
+    clean(s, plan)
+    compare(s, wl)
