@@ -9,6 +9,7 @@
 
 #include "../../include/crosscu.h"
 #include "../../include/crosscu_debug.h"
+#include "fill.h"
 #include "launch.h"
 #include "plan.h"
 
@@ -173,9 +174,18 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
                    : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool combine = reduce == CC_REDUCE_SPLIT_COMBINE && v.partials() > 0;
+  bool has_empty = false;  // units the plan gives no piece: sequences with no cached tokens
+  for (int32_t u = 0; u < v.units() && !has_empty; ++u) has_empty = v.unit_nsplit[u] == 0;
   a.ev_start = g_ev_start;
+  hipError_t e;
+  if (has_empty) {
+    a.ev_stop = nullptr;
+    e = cc::launch_empty_units(a, s);
+    if (e != hipSuccess) return hip_fail(e, "empty-unit launch");
+    a.ev_start = nullptr;
+  }
   a.ev_stop = combine ? nullptr : g_ev_stop;
-  hipError_t e = p.mode == CC_MODE_GQA ? cc::launch_gqa(a, s) : cc::launch_mla(a, s);
+  e = p.mode == CC_MODE_GQA ? cc::launch_gqa(a, s) : cc::launch_mla(a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (combine) {
     a.ev_start = nullptr;

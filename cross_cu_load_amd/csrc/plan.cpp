@@ -67,8 +67,8 @@ int validate(const Inputs& in) {
   }
   for (int32_t b = 0; b < p.batch; ++b) {
     const int32_t L = in.seqlens[b];
-    if (L < 1) {
-      set_error("seqlens[%d] = %d; every sequence needs >= 1 token", b, L);
+    if (L < 0) {
+      set_error("seqlens[%d] = %d is negative", b, L);
       return CC_ERR_INVALID;
     }
     const int64_t pages = ceil_div(L, p.page_size);
@@ -123,19 +123,25 @@ int build(const Inputs& in, Built* out) {
   // pieces per logical chunk, as (unit, tok_begin, tok_end)
   struct Piece { int64_t u, t0, t1; };
   std::vector<std::vector<Piece>> chunks(C);
+  // an empty unit (a sequence with no cached tokens) gets no piece and costs
+  // nothing; cc_decode writes its output directly
   if (o.policy == CC_POLICY_PER_UNIT) {
-    for (int64_t u = 0; u < U; ++u) chunks[u].push_back({u, 0, unit_len(u)});
+    for (int64_t u = 0; u < U; ++u)
+      if (unit_len(u) > 0) chunks[u].push_back({u, 0, unit_len(u)});
   } else if (o.policy == CC_POLICY_STREAMK_COST) {
     // equal split of the cost: kCostPerTile per tile plus kUnitCost per unit,
     // the unit's overhead first; a tile goes to the chunk whose cost range
     // holds its starting position
     const int64_t kUnitCost = unit_cost(p.mode);
-    const int64_t total = kUnitCost * U + kCostPerTile * N;
+    int64_t busy_units = 0;
+    for (int64_t u = 0; u < U; ++u) busy_units += first[u + 1] > first[u];
+    const int64_t total = kUnitCost * busy_units + kCostPerTile * N;
     const int64_t q = total / C, r = total % C;
     auto bound = [&](int64_t k) { return k * q + (k < r ? k : r); };  // chunk k: [bound(k), bound(k+1))
     int64_t cs = 0, k = 0;
     for (int64_t u = 0; u < U; ++u) {
       const int64_t n = first[u + 1] - first[u], L = unit_len(u);
+      if (n == 0) continue;
       for (int64_t i = 0; i < n;) {
         const int64_t start = cs + kUnitCost + kCostPerTile * i;
         while (bound(k + 1) <= start) ++k;
@@ -155,6 +161,7 @@ int build(const Inputs& in, Built* out) {
       if (e == a) continue;
       while (first[u + 1] <= a) ++u;           // first unit that ends after a
       for (int64_t v = u; v < U && first[v] < e; ++v) {
+        if (first[v + 1] == first[v]) continue;
         const int64_t tb = (a > first[v] ? a : first[v]) - first[v];
         const int64_t te = (e < first[v + 1] ? e : first[v + 1]) - first[v];
         const int64_t L = unit_len(v);

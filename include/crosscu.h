@@ -90,7 +90,9 @@ enum { CC_REDUCE_FUSED = 0, CC_REDUCE_SPLIT_COMBINE = 1 };
  *   v_cache      bf16  as k_cache with head_dim_v (GQA only)
  *   block_table  int32 [batch][max_pages_per_seq]; token j of sequence b lives
  *                in page block_table[b][j / page_size], slot j % page_size
- *   seqlens      int32 [batch], each >= 1
+ *   seqlens      int32 [batch], each >= 0 (>= topk for MLA_SPARSE); a sequence
+ *                with no cached tokens gets out = 0 and lse = -inf, the
+ *                neutral element of the log-sum-exp merge
  *   indices      int32 [batch][q_tokens][topk] (MLA_SPARSE), distinct
  *                positions in [0, seqlens[b])
  *   out          fp32  [batch][q_tokens][num_q_heads][head_dim_v]
@@ -177,7 +179,9 @@ int cc_workspace_check(const void* plan_host, const void* workspace, void* strea
  * memory.  q, k_cache, v_cache (NULL for MLA modes), block_table, seqlens,
  * indices (MLA_SPARSE, else NULL): device, layouts as in cc_problem.
  * out, lse: device outputs.  workspace: device, >= cc_workspace_size bytes,
- * initialised once with cc_workspace_init.  Asynchronous on `stream`.
+ * initialised once with cc_workspace_init.  Asynchronous on `stream`.  When
+ * the plan holds empty sequences, a first small kernel writes their out (0)
+ * and lse (-inf).
  * Host-side checks (before any launch): null pointers, plan header vs `prob`,
  * supported shapes, workspace size.  Device data is not validated on the
  * host; out-of-range page ids, indices or plan/seqlens mismatches are clamped

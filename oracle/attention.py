@@ -17,6 +17,11 @@ Readings of points the pages leave open
   index-sparse mode it sees exactly its own index set.
 * GQA head map: query head h reads KV head h // (Hq / Hkv) (contiguous groups).
 * MLA: one latent KV row of dk columns serves as K; its first dv columns are V.
+* A sequence with no cached tokens (L_b = 0): lse = log of an empty sum =
+  -inf, and out = 0.  That pair is the neutral element of the log-sum-exp
+  merge (m = -inf, l = 0, o = 0), so an empty key set merged with any other
+  leaves it unchanged; the value of out itself (0/0 in the definition) is a
+  convention.
 * Paged layout: cache[page, slot, kv_head, dim] (token-major, "NHD") or
   cache[page, kv_head, slot, dim] (head-major, "HND"); token j of sequence b
   is page block_table[b, j // P], slot j % P.  Sparse indices are token
@@ -55,6 +60,8 @@ def gather_rows(cache_bits: np.ndarray, block_table: np.ndarray, b: int, J: np.n
 
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> tuple[np.ndarray, np.ndarray]:
     """softmax(scale * q K^T) V and its lse for query rows q [G, dk], K [n, dk], V [n, dv]."""
+    if K.shape[0] == 0:                           # empty key set: see the readings above
+        return np.zeros((q.shape[0], V.shape[1])), np.full(q.shape[0], -np.inf)
     s = scale * (q @ K.T)                         # [G, n]
     m = s.max(axis=1, keepdims=True)
     w = np.exp(s - m)
@@ -70,8 +77,10 @@ def partial_state(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
     m = max score, l = sum exp(s - m), o = sum exp(s - m) v.  These are the
     running max, running sum and un-normalised output that a split piece
     hands to the reduction (MeldKernel summary, "Core method": partial outputs
-    feed a just-in-time reduction).
+    feed a just-in-time reduction).  An empty subset has m = -inf, l = 0, o = 0.
     """
+    if K.shape[0] == 0:
+        return np.full(q.shape[0], -np.inf), np.zeros(q.shape[0]), np.zeros((q.shape[0], V.shape[1]))
     s = scale * (q @ K.T)
     m = s.max(axis=1)
     w = np.exp(s - m[:, None])
@@ -86,7 +95,9 @@ def lse_merge(parts) -> tuple[np.ndarray, np.ndarray]:
     """
     ms = np.stack([p[0] for p in parts])          # [n, G]
     M = ms.max(axis=0)
-    c = np.exp(ms - M)
+    if np.all(M == -np.inf):                      # every part empty: the empty result
+        return np.zeros_like(parts[0][2]), M
+    c = np.exp(ms - M)                            # 0 for an empty part (m = -inf)
     L = sum(ci * p[1] for ci, p in zip(c, parts))
     O = sum(ci[:, None] * p[2] for ci, p in zip(c, parts))
     return O / L[:, None], M + np.log(L)

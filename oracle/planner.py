@@ -15,6 +15,8 @@ Readings (the pages fix only "equal, one chunk per compute unit"):
   u = ((b * Tq + t) * Hkv + g) * (G / Hu) + hb; units are ordered by u.
 * tiles are laid out unit-major; chunk k takes floor(N / C) tiles, plus one
   for the first N mod C chunks, contiguously.
+* an empty unit (a sequence with no cached tokens) has no tiles, gets no
+  piece and carries no cost; its unit_nsplit is 0.
 * POLICY_STREAMK_COST (a refinement of the same equal split): what is split
   evenly is the cost of the work, COST_PER_TILE per tile plus unit_cost(mode)
   per unit, for the fixed work of starting and finishing a unit (loading its
@@ -93,7 +95,7 @@ def validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head
         raise ValueError("opts")
     for b in range(batch):
         L = int(seqlens[b])
-        if L < 1:
+        if L < 0:
             raise ValueError("seqlen")
         if _ceil_div(L, page_size) > max_pages_per_seq:
             raise ValueError("seqlen beyond block table")
@@ -137,7 +139,7 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
     u = 0
     for k in range(C if policy != POLICY_STREAMK_COST else 0):
         if policy == POLICY_PER_UNIT:
-            chunk_pieces.append([(k, 0, lens[k])])
+            chunk_pieces.append([(k, 0, lens[k])] if lens[k] > 0 else [])
             continue
         start = k * base + min(k, rem)
         end = start + base + (1 if k < rem else 0)
@@ -146,6 +148,9 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
             u += 1
         v = u
         while end > start and v < U and first_tile[v] < end:
+            if ntiles[v] == 0:     # an empty unit gets no piece
+                v += 1
+                continue
             tb = max(start, first_tile[v]) - first_tile[v]
             te = min(end, first_tile[v] + ntiles[v]) - first_tile[v]
             pieces.append((v, tb * T, min(te * T, lens[v])))
@@ -211,12 +216,14 @@ def _cost_split(ntiles, lens, C: int, T: int, O: int = UNIT_COST):
     (O + COST_PER_TILE * n), O the unit cost; its tile i starts at cs[u] + O +
     COST_PER_TILE * i and belongs to the chunk whose range holds that position.
     """
-    total = sum(O + COST_PER_TILE * n for n in ntiles)
+    total = sum(O + COST_PER_TILE * n for n in ntiles if n > 0)
     q, r = divmod(total, C)
     bound = [k * q + min(k, r) for k in range(C + 1)]   # chunk k: [bound[k], bound[k+1])
     pieces: list[list[tuple[int, int, int]]] = [[] for _ in range(C)]
     cs, k = 0, 0
     for u, n in enumerate(ntiles):
+        if n == 0:      # an empty unit: no piece, no cost
+            continue
         i = 0
         while i < n:
             start = cs + O + COST_PER_TILE * i

@@ -2,7 +2,8 @@
 compare out / lse with the fp64 oracle.
 
 Bars: max|out - oracle| <= 1e-2 and max|lse - oracle| <= 1e-3 (absolute), no
-NaN/Inf, for bf16 inputs with fp32 accumulation.
+NaN/Inf, for bf16 inputs with fp32 accumulation; a sequence with no cached
+tokens must give exactly out = 0 and lse = -inf.
 """
 import numpy as np
 
@@ -29,7 +30,6 @@ def compare(s, wl, only=None):
     ref_o, ref_l = A.decode_attention_wl(wl, only=only)
     out = s.out.cpu().numpy().astype(np.float64)
     lse = s.lse.cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
     if only is not None:
         G = wl.cfg.group
         mask = np.zeros(lse.shape, bool)
@@ -37,6 +37,13 @@ def compare(s, wl, only=None):
             mask[b, t, g * G:(g + 1) * G] = True
         out, ref_o = out[mask], ref_o[mask]
         lse, ref_l = lse[mask], ref_l[mask]
+    # sequences with no cached tokens: exactly out = 0, lse = -inf
+    empty = ref_l == -np.inf
+    assert np.all(out[empty] == 0) and np.all(lse[empty] == -np.inf)
+    out, ref_o, lse, ref_l = out[~empty], ref_o[~empty], lse[~empty], ref_l[~empty]
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    if lse.size == 0:
+        return 0.0, 0.0
     do = float(np.max(np.abs(out - ref_o)))
     dl = float(np.max(np.abs(lse - ref_l)))
     print(f"       max|dout|={do:.3e} max|dlse|={dl:.3e}", flush=True)

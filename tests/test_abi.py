@@ -78,9 +78,11 @@ def test_plan_bytes_match_reference_fuzz(lib, seed):
     hu = int(rng.choice([d for d in (1, 2, 4, 8) if G % d == 0]))
     P = int(rng.choice([1, 16, 64]))
     sl = rng.integers(1, 3000, size=B_).astype(np.int32)
+    if mode != 2:                     # dense modes: some sequences with no cached tokens
+        sl[rng.random(B_) < 0.25] = 0
     topk = int(rng.integers(1, int(sl.min()) + 1)) if mode == 2 else 0
-    maxp = int(max((int(L) + P - 1) // P for L in sl))
-    npages = int(sum((int(L) + P - 1) // P for L in sl))
+    maxp = max(1, int(max((int(L) + P - 1) // P for L in sl)))
+    npages = max(1, int(sum((int(L) + P - 1) // P for L in sl)))
     bt = W.page_table(sl, P, True, seed)
     C = int(rng.choice([1, 3, 8, 100, 256, 1000]))
     X = int(rng.choice([1, 4, 8]))
@@ -98,7 +100,7 @@ def _base():
 
 
 @pytest.mark.parametrize("bad,code", [
-    ("seqlen0", B.CC_ERR_INVALID), ("heads", B.CC_ERR_INVALID), ("hu", B.CC_ERR_INVALID),
+    ("seqlen_neg", B.CC_ERR_INVALID), ("heads", B.CC_ERR_INVALID), ("hu", B.CC_ERR_INVALID),
     ("page", B.CC_ERR_PAGE), ("tq", B.CC_ERR_INVALID), ("bt_short", B.CC_ERR_INVALID),
     ("topk", B.CC_ERR_INVALID), ("mode", B.CC_ERR_INVALID), ("cus0", B.CC_ERR_INVALID)])
 def test_plan_rejects_invalid_inputs(lib, bad, code):
@@ -106,8 +108,8 @@ def test_plan_rejects_invalid_inputs(lib, bad, code):
     sl = np.array([10, 20], np.int32)
     bt = np.array([[0, -1], [1, 2]], np.int32)
     hu, cus = 4, 8
-    if bad == "seqlen0":
-        sl = np.array([0, 20], np.int32)
+    if bad == "seqlen_neg":
+        sl = np.array([-1, 20], np.int32)
     elif bad == "heads":
         kw["num_q_heads"] = 7
     elif bad == "hu":

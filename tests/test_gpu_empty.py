@@ -1,0 +1,51 @@
+"""GPU results for sequences with no cached tokens (through the C ABI).
+
+Such a sequence gets no piece in the plan; cc_decode writes out = 0 and
+lse = -inf for it, the neutral element of the log-sum-exp merge (the oracle's
+reading of an empty key set).  The other sequences of the batch keep the usual
+bars against the fp64 oracle, for every plan policy and both reductions, and
+the workspace is left clean.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from cross_cu_load_amd import binding as B
+from cross_cu_load_amd import workloads as W
+
+from gpu_helpers import clean, compare, run
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+CASES = [("skewed_gqa", W.KV_NHD), ("skewed_gqa", W.KV_HND), ("deepseek_mla", W.KV_NHD)]
+
+
+@pytest.mark.parametrize("reduce", [B.REDUCE_FUSED, B.REDUCE_SPLIT_COMBINE])
+@pytest.mark.parametrize("policy", [B.POLICY_STREAMK_COST, B.POLICY_STREAMK, B.POLICY_PER_UNIT])
+@pytest.mark.parametrize("name,layout", CASES)
+def test_empty_sequences_in_a_batch(dev, name, layout, policy, reduce):
+    cfg = dataclasses.replace(W.small_variant(W.CONFIG_BY_NAME[name], batch=6, seqlen_hi=5000, seed_offset=21),
+                              kv_layout=layout)
+    sl = np.array([0, 300, 0, 4000, 17, 0], np.int32)
+    wl = W.make_workload(cfg, seqlens=sl)
+    s, plan = run(wl, *dev, policy=policy, reduce=reduce, tag=f"empty {name} layout={layout}")
+    compare(s, wl)
+    clean(s, plan)
+
+
+@pytest.mark.parametrize("name", ["skewed_gqa", "deepseek_mla"])
+def test_every_sequence_empty(dev, name):
+    cfg = W.small_variant(W.CONFIG_BY_NAME[name], batch=3, seqlen_hi=100, seed_offset=22)
+    # a one-page cache to point at; the plan and the device see lengths 0
+    wl = W.make_workload(cfg, seqlens=np.array([1, 0, 0], np.int32))
+    wl = dataclasses.replace(wl, seqlens=np.zeros(3, np.int32))
+    s, plan = run(wl, *dev, tag=f"all-empty {name}")
+    assert int(plan.view(np.int32)[17]) == 0, "no work item"
+    s.out.fill_(float("nan"))
+    s.lse.fill_(float("nan"))
+    s.run()
+    torch.cuda.synchronize()
+    assert bool(torch.all(s.out == 0)) and bool(torch.all(s.lse == float("-inf")))
+    clean(s, plan)

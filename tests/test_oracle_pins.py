@@ -74,6 +74,8 @@ def bruteforce(pr):
     for b in range(B):
         K = A.bf16_to_f64(pr["K"][b])
         V = A.bf16_to_f64(pr["V"][b])
+        if len(K) == 0:      # no key: left to the callers (0/0 in the definition)
+            continue
         for h in range(Hq):
             g = h // G
             s = [pr["scale"] * sum(float(q[b, 0, h, d]) * float(K[j, g, d]) for d in range(dk))
@@ -389,3 +391,42 @@ def test_planted_mistakes_are_caught(mutant):
     elif mutant == "kv_gather_mismatch":
         decode = _mut_kv_gather_mismatch
     assert _pin_suite(attend, merge, partial, decode), "a planted mistake went unnoticed"
+
+
+def test_empty_key_set_is_the_neutral_element_of_the_merge():
+    """A sequence with no cached tokens: lse = log of an empty sum = -inf (as
+    torch.logsumexp of an empty tensor), out = 0.  That state (m = -inf, l = 0,
+    o = 0) merged with any partition of a key set leaves the unsplit result
+    unchanged, wherever the empty pieces sit; all-empty merges to (0, -inf)."""
+    assert float(torch.logsumexp(torch.empty(0, dtype=torch.float64), 0)) == -math.inf
+    rng = np.random.default_rng(31)
+    G, dk, dv = 4, 16, 12
+    q = rng.standard_normal((G, dk))
+    o, s = A.attend(q, np.zeros((0, dk)), np.zeros((0, dv)), 0.25)
+    assert np.array_equal(o, np.zeros((G, dv))) and np.all(s == -np.inf)
+    for trial in range(20):
+        n = int(rng.integers(1, 100))
+        K, V = rng.standard_normal((n, dk)), rng.standard_normal((n, dv))
+        cut = int(rng.integers(0, n + 1))
+        empty = A.partial_state(q, K[:0], V[:0], 0.25)
+        parts = [A.partial_state(q, K[:cut], V[:cut], 0.25), empty, A.partial_state(q, K[cut:], V[cut:], 0.25)]
+        mo, ms = A.lse_merge(parts)
+        ro, rs = A.attend(q, K, V, 0.25)
+        np.testing.assert_allclose(mo, ro, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ms, rs, rtol=1e-12, atol=1e-13)
+    mo, ms = A.lse_merge([empty, empty])
+    assert np.array_equal(mo, np.zeros((G, dv))) and np.all(ms == -np.inf)
+
+
+def test_empty_sequences_in_a_paged_batch():
+    """Empty sequences in a batch give (0, -inf); the others are unchanged
+    from the batch without them (same rows, recomputed by brute force)."""
+    rng = np.random.default_rng(32)
+    pr = rand_problem(rng, B=5, lens=(0, 5, 0, 9, 1))
+    out, lse = run(pr)
+    for b in (0, 2):
+        assert np.array_equal(out[b], np.zeros_like(out[b])) and np.all(lse[b] == -np.inf)
+    bf_o, bf_l = bruteforce(pr)
+    keep = [1, 3, 4]
+    np.testing.assert_allclose(out[keep], bf_o[keep], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse[keep], bf_l[keep], rtol=1e-12, atol=1e-13)

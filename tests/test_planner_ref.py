@@ -22,7 +22,7 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden")
 def _plan(lens, C=8, X=1, T=4, G=1, Hkv=1, mode=PL.MODE_GQA, Tq=1, topk=0, hu=None, policy=PL.POLICY_STREAMK):
     lens = np.asarray(lens, np.int32)
     P = 16
-    maxp = int(max((int(L) + P - 1) // P for L in lens))
+    maxp = max(1, int(max((int(L) + P - 1) // P for L in lens)))
     return PL.plan(mode, len(lens), Tq, G * Hkv, Hkv, 64, 64, P, maxp, 1 << 20, topk, C, X, T,
                    hu if hu is not None else G, lens, None, policy)
 
@@ -71,7 +71,7 @@ def _check_invariants(p, lens, C, X, T, policy=PL.POLICY_STREAMK, mode=PL.MODE_G
         # cost of a chunk (16 per tile, the mode's unit cost per unit it
         # starts) is within one tile plus one unit of its share of the total
         K, O = PL.COST_PER_TILE, PL.unit_cost(mode)
-        q, r = divmod(K * N + O * U, C)
+        q, r = divmod(K * N + O * sum(n > 0 for n in ntiles), C)
         for k, its in enumerate(p["chunk_items"]):
             cost = sum(K * -(-(t1 - t0) // T) + (O if t0 == 0 else 0) for (_, t0, t1, _) in its)
             assert abs(cost - (q + (k < r))) <= K + O
@@ -83,6 +83,9 @@ def _check_invariants(p, lens, C, X, T, policy=PL.POLICY_STREAMK, mode=PL.MODE_G
             assert s == len(cover[u])
             cover[u].append((t0, t1))
     for u in range(U):
+        if lens[u] == 0:     # an empty unit: no piece
+            assert cover[u] == [] and p["unit_nsplit"][u] == 0
+            continue
         assert cover[u][0][0] == 0 and cover[u][-1][1] == lens[u]
         for a, b in zip(cover[u][:-1], cover[u][1:]):
             assert a[1] == b[0]
@@ -138,7 +141,7 @@ def _brute_force_cost(lens, C, T):
     found by scanning the ranges."""
     K, O = PL.COST_PER_TILE, PL.UNIT_COST
     ntiles = [-(-L // T) for L in lens]
-    total = sum(O + K * n for n in ntiles)
+    total = sum(O + K * n for n in ntiles if n > 0)
     ranges = [(k * (total // C) + min(k, total % C), (k + 1) * (total // C) + min(k + 1, total % C))
               for k in range(C)]
     chunks = [[] for _ in range(C)]
@@ -151,7 +154,8 @@ def _brute_force_cost(lens, C, T):
                 chunks[k][-1][2] = min((j + 1) * T, lens[u])
             else:
                 chunks[k].append([u, j * T, min((j + 1) * T, lens[u])])
-        before += O + K * n
+        if n > 0:
+            before += O + K * n
     return [[tuple(x) for x in c] for c in chunks]
 
 
@@ -161,6 +165,9 @@ def test_brute_force_and_invariants_small(seed, policy):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 5))
     lens = [int(x) for x in rng.integers(1, 60, size=B)]
+    for i in range(B):                  # some sequences with no cached tokens
+        if rng.random() < 0.25:
+            lens[i] = 0
     C = int(rng.choice([1, 2, 3, 5, 8, 16]))
     X = int(rng.choice([1, 2, 4, 8]))
     T = int(rng.choice([1, 4, 16, 32]))
@@ -212,15 +219,15 @@ def test_skewed_workload_split_shape():
     assert all(n <= 2 for n in p["unit_nsplit"][8:])
 
 
-@pytest.mark.parametrize("bad", ["seqlen0", "topk", "heads", "hu", "page", "tq", "bt_short"])
+@pytest.mark.parametrize("bad", ["seqlen_neg", "topk", "heads", "hu", "page", "tq", "bt_short"])
 def test_invalid_inputs_rejected(bad):
     lens = np.array([10, 20], np.int32)
     kw = dict(mode=PL.MODE_GQA, batch=2, q_tokens=1, num_q_heads=8, num_kv_heads=2, head_dim_qk=64,
               head_dim_v=64, page_size=16, max_pages_per_seq=2, num_pages=4, topk=0, num_cus=8,
               num_xcds=1, tile_tokens=16, heads_per_unit=4, seqlens=lens,
               block_table=np.array([[0, -1], [1, 2]], np.int32))
-    if bad == "seqlen0":
-        kw["seqlens"] = np.array([0, 20], np.int32)
+    if bad == "seqlen_neg":
+        kw["seqlens"] = np.array([-1, 20], np.int32)
     elif bad == "topk":
         kw.update(mode=PL.MODE_MLA_SPARSE, topk=11, num_q_heads=2, num_kv_heads=1, heads_per_unit=2)
     elif bad == "heads":
@@ -244,3 +251,23 @@ def test_cost_policy_unit_cost_follows_mode():
         p = _plan(lens, C=4, T=32, mode=mode, hu=hu, policy=PL.POLICY_STREAMK_COST)
         assert np.frombuffer(p["blob"][:96], np.int32)[23] == O == PL.unit_cost(mode)
         _check_invariants(p, lens, 4, 1, 32, PL.POLICY_STREAMK_COST, mode)
+
+
+@pytest.mark.parametrize("policy", [PL.POLICY_STREAMK, PL.POLICY_STREAMK_COST, PL.POLICY_PER_UNIT])
+def test_empty_sequences_get_no_piece(policy):
+    """Sequences with no cached tokens: no piece, nsplit 0, no cost; the other
+    units are planned exactly as in the batch without them (cost and tile
+    positions do not count the empty units)."""
+    lens = [0, 37, 0, 0, 120, 5, 0]
+    p = _plan(lens, C=8, X=1, T=4, policy=policy)
+    if policy != PL.POLICY_PER_UNIT:
+        _check_invariants(p, lens, 8, 1, 4, policy)
+    assert [p["unit_nsplit"][u] for u in (0, 2, 3, 6)] == [0, 0, 0, 0]
+    assert all(u not in (0, 2, 3, 6) for its in p["chunk_items"] for (u, _, _, _) in its)
+    if policy != PL.POLICY_PER_UNIT:
+        q = _plan([37, 120, 5], C=8, X=1, T=4, policy=policy)
+        ren = {0: 1, 1: 4, 2: 5}
+        assert [[(ren[u], t0, t1, s) for (u, t0, t1, s) in its] for its in q["chunk_items"]] == p["chunk_items"]
+    allempty = _plan([0, 0, 0], C=8, X=1, T=4, policy=policy)
+    assert allempty["num_items"] == 0 and allempty["num_tiles"] == 0
+    assert allempty["unit_nsplit"] == [0, 0, 0]
