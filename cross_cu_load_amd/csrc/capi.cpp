@@ -174,8 +174,7 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
                    : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool combine = reduce == CC_REDUCE_SPLIT_COMBINE && v.partials() > 0;
-  bool has_empty = false;  // units the plan gives no piece: sequences with no cached tokens
-  for (int32_t u = 0; u < v.units() && !has_empty; ++u) has_empty = v.unit_nsplit[u] == 0;
+  const bool has_empty = v.header[cc::H_EMPTY] > 0;  // sequences with no cached tokens
   a.ev_start = g_ev_start;
   hipError_t e;
   if (has_empty) {

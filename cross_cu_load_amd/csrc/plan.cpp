@@ -227,7 +227,10 @@ int build(const Inputs& in, Built* out) {
   h[H_POLICY] = o.policy;
   h[H_MAXPAGES] = p.max_pages_per_seq;
   h[H_NUMPAGES] = p.num_pages;
-  h[H_RESERVED] = o.policy == CC_POLICY_STREAMK_COST ? (int32_t)unit_cost(p.mode) : 0;
+  h[H_UNIT_COST] = o.policy == CC_POLICY_STREAMK_COST ? (int32_t)unit_cost(p.mode) : 0;
+  int64_t empty = 0;
+  for (int64_t u = 0; u < U; ++u) empty += nsplit[u] == 0;
+  h[H_EMPTY] = (int32_t)empty;
   int32_t* wg = h + kHeaderWords;
   int32_t* it = wg + wg_words(C);
   int64_t n = 0;

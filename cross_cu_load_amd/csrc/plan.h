@@ -1,7 +1,7 @@
 // Host-side view of a work-plan blob (shared by the planner and the launcher).
 //
 // Blob layout, int32 little-endian words:
-//   header[24]
+//   header[32]           fields below (H_*); words past H_EMPTY are zero
 //   wg_off[C + 1]        items of worker w are items[wg_off[w] .. wg_off[w+1]),
 //                        zero-padded to a multiple of 4 words so items[] is
 //                        16-byte aligned
@@ -19,14 +19,16 @@
 namespace cc {
 
 constexpr int32_t kPlanMagic = 0x4C504343;  // "CCPL"
-constexpr int32_t kPlanVersion = 1;
-constexpr int kHeaderWords = 24;
+constexpr int32_t kPlanVersion = 2;
+constexpr int kHeaderWords = 32;
 constexpr int kItemWords = 4;
 
 enum HeaderField {
   H_MAGIC = 0, H_VERSION, H_MODE, H_BATCH, H_QTOKENS, H_HQ, H_HKV, H_DQK, H_DV, H_PAGE, H_TOPK,
   H_WORKERS, H_XCDS, H_TILE, H_HPU, H_UNITS, H_TILES, H_ITEMS, H_PARTIALS, H_MAXSPLIT, H_POLICY,
-  H_MAXPAGES, H_NUMPAGES, H_RESERVED
+  H_MAXPAGES, H_NUMPAGES,
+  H_UNIT_COST,  // per-unit cost of CC_POLICY_STREAMK_COST, else 0
+  H_EMPTY       // units with no piece (sequences with no cached tokens)
 };
 
 struct PlanView {

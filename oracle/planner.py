@@ -42,8 +42,8 @@ import struct
 import numpy as np
 
 PLAN_MAGIC = 0x4C504343          # "CCPL" little-endian
-PLAN_VERSION = 1
-HEADER_WORDS = 24
+PLAN_VERSION = 2
+HEADER_WORDS = 32               # words 0..24 below, the rest zero
 ITEM_WORDS = 4                   # unit, tok_begin, tok_end, split
 
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
@@ -198,6 +198,7 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
                    head_dim_qk, head_dim_v, page_size, topk, C, X, T, heads_per_unit, U, N, W, S,
                    max(nsplit) if nsplit else 0, policy, max_pages_per_seq, num_pages]
     header[23] = unit_cost(mode) if policy == POLICY_STREAMK_COST else 0
+    header[24] = sum(1 for n in nsplit if n == 0)      # units with no piece (empty sequences)
     pad = (-(C + 1)) % 4                 # keeps the item array 16-byte aligned
     words = header + wg_off + [0] * pad + [x for it in items for x in it] + nsplit + pbase
     for x in words:

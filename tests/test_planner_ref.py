@@ -263,6 +263,7 @@ def test_empty_sequences_get_no_piece(policy):
     if policy != PL.POLICY_PER_UNIT:
         _check_invariants(p, lens, 8, 1, 4, policy)
     assert [p["unit_nsplit"][u] for u in (0, 2, 3, 6)] == [0, 0, 0, 0]
+    assert np.frombuffer(p["blob"], np.int32)[24] == 4       # empty units counted in the header
     assert all(u not in (0, 2, 3, 6) for its in p["chunk_items"] for (u, _, _, _) in its)
     if policy != PL.POLICY_PER_UNIT:
         q = _plan([37, 120, 5], C=8, X=1, T=4, policy=policy)
