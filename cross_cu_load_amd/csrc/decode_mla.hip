@@ -447,7 +447,7 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
                   const int32_t* __restrict__ bt, const int32_t* __restrict__ seqlens,
                   const int32_t* __restrict__ indices, float* __restrict__ out, float* __restrict__ lse,
                   int32_t* err, int32_t* counters, float* partials, unsigned long long* timeline) {
-  __shared__ int sh_last;
+  __shared__ int sh_pend[2];
   __shared__ uint32_t sh_claim;
 
   const int tid = threadIdx.x;
@@ -692,8 +692,8 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   bool fresh = true;  // no block of the current item seen yet
   // split pieces this workgroup published (only a chunk's first and last
   // items can be split), one word each: unit << 11 | split << 2 | arrived
-  // last << 1 | 1 (0: none); the host keeps units below 2^20 and split
-  // indices below 2^9
+  // last << 1 | 1 (0: none; the arrival bit is set after the stream); the
+  // host keeps units below 2^20 and split indices below 2^9
   int pend0 = 0, pend1 = 0;
 
   // one block: tile k in stage st = k % 3; the fetch two blocks ahead goes to stage (k + 2) % 3
@@ -915,17 +915,9 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       }
       if (!whole) {
         if (p.reduce == CC_REDUCE_FUSED) {
-          // every wave's share of the partial is in memory (device-coherent
-          // stores complete), then one arrival per piece
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-          if (tid == 0) {
-            const int old = atomicAdd(&counters[kCounterStride * cur.unit], 1);
-            sh_last = (old & kArriveMask) == cur.nsplit - 1;
-          }
-          __syncthreads();
-          // the unit is merged after the stream
-          const int word = (cur.unit << 11) | (cur.split << 2) | (uni(sh_last) << 1) | 1;
+          // the piece arrives after the stream (so the stream never waits for
+          // its stores), and the unit is merged then
+          const int word = (cur.unit << 11) | (cur.split << 2) | 1;
           if (pend0 == 0) {
             pend0 = word;
           } else {
@@ -953,6 +945,22 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     st2 = st2 == 2 ? 0 : st2 + 1;
   }
   if (tl && tid == 0) tl[1] = tl[2] = __builtin_amdgcn_s_memrealtime();
+  if (pend0) {
+    // every wave's partial stores are complete (device-coherent stores reach
+    // memory before vmcnt clears), then one arrival per piece, both in flight
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      const int u0 = pend0 >> 11, u1 = pend1 >> 11;
+      const int o0 = atomicAdd(&counters[kCounterStride * u0], 1);
+      const int o1 = pend1 ? atomicAdd(&counters[kCounterStride * u1], 1) : 0;
+      sh_pend[0] = pend0 | ((o0 & kArriveMask) == unit_nsplit[u0] - 1 ? 2 : 0);
+      sh_pend[1] = pend1 ? pend1 | ((o1 & kArriveMask) == unit_nsplit[u1] - 1 ? 2 : 0) : 0;
+    }
+    __syncthreads();
+    pend0 = uni(sh_pend[0]);
+    pend1 = uni(sh_pend[1]);
+  }
   // Merge of the split units this workgroup published pieces of (no q or
   // accumulators live here).  A unit's 128 heads form nsl = min(nsplit,
   // kSlices) slices of whole 8-head blocks.  Once every piece of a unit has

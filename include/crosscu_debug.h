@@ -15,9 +15,10 @@
  *   [5] the id of the XCD (accelerator complex die) it ran on,
  *   [6], [7] GQA kernel: its merge-slot scan, then the per-head (max, sum)
  *       pass of [2] are done; MLA kernel: unused (0).
- * The MLA kernel publishes and arrives inside its stream, so its [2] equals
- * [1]; between [1] and [4] it waits for its split units to complete and merges
- * head slices of them, and its [3] equals [4].
+ * The MLA kernel publishes its pieces' partials inside its stream and
+ * arrives after it, so its [2] equals [1]; between [1] and [4] it arrives,
+ * waits for its split units to complete and merges head slices of them, and
+ * its [3] equals [4].
  * Workgroups with no work record [0] == [1] == ... == [4] (and [6], [7]).  From these the caller
  * computes the busy fraction of the compute units over the launch and checks
  * the workgroup-to-XCD placement the planner assumes (workgroup w on XCD
