@@ -31,9 +31,12 @@ constexpr int kMergeInflight = 8; // o_s loads in flight per thread
 // agent-scope release/acquire fence does for ordinary data).  The writer makes
 // the stores complete (s_waitcnt vmcnt(0)) before its arrival on the unit's
 // counter; the reader issues its loads after observing the last arrival.
-// Large partials (MLA: 128 KB per piece) use ordinary vector stores and the
-// fences instead: per-element device-scope accesses cost more than the fences
-// there.
+// Large partials (MLA: 128 KB per piece) are written with device-coherent
+// 16-byte stores, which write through the XCD's L2, so the writer needs no
+// release fence either; every workgroup that merges a slice of them issues an
+// agent-scope acquire fence (its L2 may hold stale lines of the slots from an
+// earlier call) and then reads them with ordinary 16-byte loads, which cost
+// less there than per-element device-scope loads.
 __device__ __forceinline__ void partial_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
