@@ -379,7 +379,7 @@ def main():
                    "seqlen_max": int(wl.seqlens.max()), "num_q_heads": cfg.num_q_heads,
                    "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim_qk, "page_size": cfg.page_size,
                    "num_cus": cus, "num_xcds": xcds, "tile_tokens": 32, "kv_bytes": kv,
-                   "plan_policy": "streamk_cost (16 per tile + 16 per unit)",
+                   "plan_policy": f"streamk_cost (16 per tile + {int(plan.view(np.int32)[23])} per unit)",
                    "kv_layout": layout_name},
         "us_per_batch": st["mean_us"],
         "us_per_batch_median": st["median_us"],
