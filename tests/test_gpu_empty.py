@@ -49,3 +49,41 @@ def test_every_sequence_empty(dev, name):
     torch.cuda.synchronize()
     assert bool(torch.all(s.out == 0)) and bool(torch.all(s.lse == float("-inf")))
     clean(s, plan)
+
+
+@pytest.mark.parametrize("reduce", [B.REDUCE_FUSED, B.REDUCE_SPLIT_COMBINE])
+def test_kernel_events_bracket_a_call_with_empty_sequences(dev, reduce):
+    """With empty sequences the call's first kernel is the output fill: the
+    debug kernel events still bracket the whole call (about as long as the
+    same call between ordinary event records, not just the fill), the outputs
+    do not change, and a call after clearing them records nothing."""
+    cfg = W.small_variant(W.CONFIG_BY_NAME["skewed_gqa"], batch=6, seqlen_hi=8000, seed_offset=23)
+    wl = W.make_workload(cfg, seqlens=np.array([0, 3000, 0, 7000, 40, 0], np.int32))
+    s, plan = run(wl, *dev, reduce=reduce, tag="empty kernel-events")
+    o0, l0 = s.out.clone(), s.lse.clone()
+    stream = torch.cuda.current_stream()
+    a, b, c, d = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (a, b, c, d):
+        e.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms, marker_ms = [], []
+    for _ in range(5):
+        B.debug_kernel_events(a, b)
+        s.run(reduce)
+        B.debug_kernel_events(None, None)
+        c.record(stream)
+        s.run(reduce)
+        d.record(stream)
+        torch.cuda.synchronize()
+        kernel_ms.append(a.elapsed_time(b))
+        marker_ms.append(c.elapsed_time(d))
+        s.run(reduce)
+        torch.cuda.synchronize()
+        assert a.elapsed_time(b) == kernel_ms[-1]
+    assert torch.equal(s.out, o0) and torch.equal(s.lse, l0)
+    # the interval covers the decode, not just the short fill kernel, and is no
+    # longer than the marker-bracketed call beyond timing noise
+    km, mk = float(np.median(kernel_ms)), float(np.median(marker_ms))
+    assert 0.5 * mk <= km <= 1.1 * mk + 0.005
+    compare(s, wl)
+    clean(s, plan)
