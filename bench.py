@@ -254,15 +254,29 @@ def indexer_cpu_baseline(wl, ix):
     return (time.perf_counter() - t0) * 1e6
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 def cpu_baseline(wl, args, min_seconds=10.0, max_reps=8):
     """The fp64 oracle, as it stands, on the host cores: the whole workload,
-    repeated until about ten seconds of CPU work have run (at most 8 times)."""
+    repeated until about ten seconds of CPU work have run (at most 8 times).
+    ``cores`` is the number of threads the oracle's BLAS actually ran with
+    (bounded by the cores this process may run on)."""
     from oracle import attention as A
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        blas = 1
     reps = 0
     t0 = time.perf_counter()
     while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
@@ -270,9 +284,10 @@ def cpu_baseline(wl, args, min_seconds=10.0, max_reps=8):
         reps += 1
     total = time.perf_counter() - t0
     dt = total / reps
-    return {"value": wl.kv_bytes() / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": wl.kv_bytes() / dt / 1e9, "unit": "GB/s", "cores": int(min(blas, affinity)), "kind": "oracle",
             "sample": f"the whole {wl.cfg.name} batch, {reps} times ({total:.1f} s, {dt * 1e6:.0f} us/batch)",
-            "us_per_batch": dt * 1e6}
+            "us_per_batch": dt * 1e6, "affinity_cores": affinity, "blas_threads": int(blas),
+            "cpu_model": cpu_model()}
 
 
 def main():
@@ -379,7 +394,7 @@ def main():
                    "seqlen_max": int(wl.seqlens.max()), "num_q_heads": cfg.num_q_heads,
                    "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim_qk, "page_size": cfg.page_size,
                    "num_cus": cus, "num_xcds": xcds, "tile_tokens": 32, "kv_bytes": kv,
-                   "plan_policy": f"streamk_cost (16 per tile + {int(plan.view(np.int32)[23])} per unit)",
+                   "plan_policy": f"streamk, equal cost chunks: 1 per tile + {int(plan.view(np.int32)[23])} per unit",
                    "kv_layout": layout_name},
         "us_per_batch": st["mean_us"],
         "us_per_batch_median": st["median_us"],

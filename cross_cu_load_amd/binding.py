@@ -20,12 +20,14 @@ CC_OK = 0
 CC_ERR_INVALID, CC_ERR_UNSUPPORTED, CC_ERR_BUFFER, CC_ERR_PLAN = -1, -2, -3, -4
 CC_ERR_PAGE, CC_ERR_HIP, CC_ERR_DEVICE_DATA = -5, -6, -7
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
-POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_COST = 0, 1, 2
+POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
+UNIT_COST_GQA, UNIT_COST_MLA = 1, 6     # CC_UNIT_COST_GQA / CC_UNIT_COST_MLA
 KV_NHD, KV_HND = 0, 1
 REDUCE_FUSED, REDUCE_SPLIT_COMBINE = 0, 1
 
 # every symbol include/*.h declares
 EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_plan_size", "cc_plan",
+           "cc_plan_check",
            "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
            "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_debug_merge_poll_limit", "cc_probe_read",
            "cc_indexer_scratch_size", "cc_indexer_topk"]
@@ -49,7 +51,7 @@ class Problem(ctypes.Structure):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("num_xcds", ctypes.c_int32),
                 ("tile_tokens", ctypes.c_int32), ("heads_per_unit", ctypes.c_int32),
-                ("policy", ctypes.c_int32)]
+                ("policy", ctypes.c_int32), ("unit_cost", ctypes.c_int32)]
 
 
 class CrossCUError(RuntimeError):
@@ -82,6 +84,7 @@ def load() -> ctypes.CDLL:
     lib.cc_plan_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), _I32P,
                                  ctypes.POINTER(_SZ)]
     lib.cc_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), _I32P, _I32P, _P, _SZ]
+    lib.cc_plan_check.argtypes = [_P, ctypes.POINTER(Problem), _I32P]
     lib.cc_workspace_size.argtypes = [_P, ctypes.POINTER(_SZ)]
     lib.cc_workspace_init.argtypes = [_P, _SZ, _P]
     lib.cc_workspace_check.argtypes = [_P, _P, _P, _I32P, _I32P]
@@ -137,17 +140,24 @@ def kernel_heads_per_unit(prob: Problem) -> int:
     return 128
 
 
+def default_unit_cost(mode: int) -> int:
+    """The unit cost (in tiles) measured for the library's kernel of this mode."""
+    return UNIT_COST_GQA if mode == MODE_GQA else UNIT_COST_MLA
+
+
 def plan(prob: Problem, seqlens, block_table=None, num_cus=256, num_xcds=8, tile_tokens=32,
-         heads_per_unit=None, policy=POLICY_STREAMK_COST) -> np.ndarray:
+         heads_per_unit=None, policy=POLICY_STREAMK, unit_cost=None) -> np.ndarray:
     """Host plan blob (uint8 array) from cc_plan_size + cc_plan.
 
-    The default policy is the cost-balanced Stream-K split (equal chunks of
-    tile cost plus a fixed cost per unit); POLICY_STREAMK cuts equal tile
-    counts; POLICY_PER_UNIT is one worker per unit."""
+    POLICY_STREAMK cuts equal chunks of cost (one per tile plus ``unit_cost``
+    per unit; None: the mode's measured default, 0: equal tile counts);
+    POLICY_PER_UNIT is one worker per unit."""
     lib = load()
     if heads_per_unit is None:
         heads_per_unit = kernel_heads_per_unit(prob)
-    opts = PlanOpts(num_cus, num_xcds, tile_tokens, heads_per_unit, policy)
+    if unit_cost is None:
+        unit_cost = default_unit_cost(prob.mode)
+    opts = PlanOpts(num_cus, num_xcds, tile_tokens, heads_per_unit, policy, unit_cost)
     sl = _i32(seqlens)
     if sl.shape != (prob.batch,):
         raise ValueError("seqlens must have shape [batch]")
@@ -164,6 +174,14 @@ def plan(prob: Problem, seqlens, block_table=None, num_cus=256, num_xcds=8, tile
     _check(lib.cc_plan(ctypes.byref(prob), ctypes.byref(opts), _ptr_i32(sl), btp,
                        buf.ctypes.data_as(_P), buf.nbytes), "cc_plan")
     return buf
+
+
+def plan_check(plan_host: np.ndarray, prob: Problem, seqlens) -> None:
+    """Raises CrossCUError (CC_ERR_PLAN) unless the plan was built for ``prob`` and these lengths."""
+    sl = _i32(seqlens)
+    if sl.shape != (prob.batch,):
+        raise ValueError("seqlens must have shape [batch]")
+    _check(load().cc_plan_check(plan_host.ctypes.data_as(_P), ctypes.byref(prob), _ptr_i32(sl)), "cc_plan_check")
 
 
 def workspace_size(plan_host: np.ndarray) -> int:

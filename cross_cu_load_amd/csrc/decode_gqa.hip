@@ -149,6 +149,7 @@ struct Cursor {
   int nb;     // blocks in the item (from the plan)
   int unit, tb, te, split;
   int lim;    // min(te, seqlens[b]): tokens at or past it are masked
+  bool bad;   // the plan does not match seqlens[b] for this item
   int nsplit; // pieces of the unit across the grid
   int pbase;  // first partial slot of the unit (split units)
 };
@@ -225,12 +226,14 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     c.nb = blocks_of(c.tb, c.te);
     c.nsplit = uni(unit_nsplit[c.unit]);
     c.pbase = uni(unit_pbase[c.unit]);
+    // a plan built for other lengths: a piece past the sequence end, or the
+    // unit's last piece ending before it.  Such an item is flagged and its
+    // running sum starts at NaN, so the unit's out and lse come out NaN
+    // through every merge; tokens past the sequence end are masked.
     const int L = uni(seqlens[c.unit / p.hkv]);
-    c.lim = c.te;
-    if (c.te > L) {  // plan built for other lengths: mask past the sequence end
-      atomicOr(err, kErrSeqlen);
-      c.lim = L;
-    }
+    c.bad = c.te > L || (c.split == c.nsplit - 1 && c.te != L);
+    c.lim = min(c.te, L);
+    if (c.bad && lane == 0) atomicOr(err, kErrSeqlen);
   };
 
   auto page_of = [&](const int32_t* row, int tok) {
@@ -383,7 +386,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       // -------- item c.it, blocks c.j .. jend-1 of it
       const int j0 = c.j;
       const int jend = min(c.nb, c.j + (e - k));
-      float m_run = -INFINITY, l_run = 0.f;
+      float m_run = -INFINITY, l_run = c.bad ? __builtin_nanf("") : 0.f;
       f32x4 o[W];
 #pragma unroll
       for (int cc = 0; cc < W; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -476,11 +476,35 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     I.L = SPARSE ? uni(seqlens[I.unit / p.q_tokens]) : 0;
     return I;
   };
+  // The workgroup's items, one lane each (64 at a time, every load in
+  // flight together): their block count, and whether the plan matches the
+  // lengths — no piece may end past its unit's key count (seqlens[b] dense,
+  // topk index-sparse) and a unit's last piece must end exactly there.  A
+  // plan built for other lengths turns this workgroup's softmax scale into
+  // NaN, which carries through every merge into the out and lse of each unit
+  // it works on, and sets the error word's seqlen bit.
   int nblk = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int4 t = items[i];
-    nblk += (uni(t.z) - uni(t.y) + kBlk - 1) / kBlk;
+  bool stale = false;
+  for (int i = i0; i < i1; i += 64) {
+    const int ii = i + lane;
+    int nb = 0;
+    bool bad = false;
+    if (ii < i1) {
+      const int4 t = items[ii];
+      nb = (t.z - t.y + kBlk - 1) / kBlk;
+      const int len = SPARSE ? p.topk : seqlens[t.x / p.q_tokens];
+      bad = t.z > len || (t.w == unit_nsplit[t.x] - 1 && t.z != len);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) nb += __shfl_xor(nb, o);
+    nblk += uni(nb);
+    stale |= __builtin_amdgcn_ballot_w64(bad) != 0;
   }
+  if (stale && tid == 0) atomicOr(err, kErrSeqlen);
+  // wave-uniform, kept in a scalar register (a per-lane copy would cost the
+  // tile loop a VGPR)
+  const float scale_log2 =
+      __builtin_bit_cast(float, uni(__builtin_bit_cast(int, stale ? __builtin_nanf("") : p.scale_log2)));
 
   // unit = b * Tq + t (one unit per query token)
   const int page_mask = (1 << p.log2_page) - 1;
@@ -791,7 +815,7 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     // scores (base 2), masked past the item end; register r is token 8 (r / 4) + 4 g + r % 4
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (8 * (r >> 2) + 4 * g + (r & 3) < nv) ? s[r] * p.scale_log2 : -INFINITY;
+    for (int r = 0; r < 16; ++r) x[r] = (8 * (r >> 2) + 4 * g + (r & 3) < nv) ? s[r] * scale_log2 : -INFINITY;
     float bmax = x[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, x[r]);

@@ -35,8 +35,12 @@ int validate(const Inputs& in) {
     set_error("unknown mode %d", p.mode);
     return CC_ERR_INVALID;
   }
-  if (o.policy != CC_POLICY_STREAMK && o.policy != CC_POLICY_PER_UNIT && o.policy != CC_POLICY_STREAMK_COST) {
+  if (o.policy != CC_POLICY_STREAMK && o.policy != CC_POLICY_PER_UNIT) {
     set_error("unknown policy %d", o.policy);
+    return CC_ERR_INVALID;
+  }
+  if (o.unit_cost < 0) {
+    set_error("unit_cost %d must be >= 0", o.unit_cost);
     return CC_ERR_INVALID;
   }
   if (p.batch < 1 || p.q_tokens < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1) {
@@ -128,14 +132,14 @@ int build(const Inputs& in, Built* out) {
   if (o.policy == CC_POLICY_PER_UNIT) {
     for (int64_t u = 0; u < U; ++u)
       if (unit_len(u) > 0) chunks[u].push_back({u, 0, unit_len(u)});
-  } else if (o.policy == CC_POLICY_STREAMK_COST) {
-    // equal split of the cost: kCostPerTile per tile plus kUnitCost per unit,
-    // the unit's overhead first; a tile goes to the chunk whose cost range
-    // holds its starting position
-    const int64_t kUnitCost = unit_cost(p.mode);
+  } else {
+    // equal split of the cost: one per tile plus unit_cost per non-empty unit,
+    // the unit's cost first; a tile goes to the chunk whose cost range holds
+    // its starting position (with unit_cost 0, the equal tile split)
+    const int64_t O = o.unit_cost;
     int64_t busy_units = 0;
     for (int64_t u = 0; u < U; ++u) busy_units += first[u + 1] > first[u];
-    const int64_t total = kUnitCost * busy_units + kCostPerTile * N;
+    const int64_t total = O * busy_units + N;
     const int64_t q = total / C, r = total % C;
     auto bound = [&](int64_t k) { return k * q + (k < r ? k : r); };  // chunk k: [bound(k), bound(k+1))
     int64_t cs = 0, k = 0;
@@ -143,30 +147,13 @@ int build(const Inputs& in, Built* out) {
       const int64_t n = first[u + 1] - first[u], L = unit_len(u);
       if (n == 0) continue;
       for (int64_t i = 0; i < n;) {
-        const int64_t start = cs + kUnitCost + kCostPerTile * i;
-        while (bound(k + 1) <= start) ++k;
-        int64_t last = ceil_div(bound(k + 1) - cs - kUnitCost, kCostPerTile);
+        while (bound(k + 1) <= cs + O + i) ++k;
+        int64_t last = bound(k + 1) - cs - O;  // tiles of u starting before chunk k ends
         if (last > n) last = n;
         chunks[k].push_back({u, i * T, last * T < L ? last * T : L});
         i = last;
       }
-      cs += kUnitCost + kCostPerTile * n;
-    }
-  } else {
-    const int64_t q = N / C, r = N % C;
-    int64_t u = 0;
-    for (int64_t k = 0; k < C; ++k) {
-      const int64_t a = k * q + (k < r ? k : r);
-      const int64_t e = a + q + (k < r ? 1 : 0);
-      if (e == a) continue;
-      while (first[u + 1] <= a) ++u;           // first unit that ends after a
-      for (int64_t v = u; v < U && first[v] < e; ++v) {
-        if (first[v + 1] == first[v]) continue;
-        const int64_t tb = (a > first[v] ? a : first[v]) - first[v];
-        const int64_t te = (e < first[v + 1] ? e : first[v + 1]) - first[v];
-        const int64_t L = unit_len(v);
-        chunks[k].push_back({v, tb * T, te * T < L ? te * T : L});
-      }
+      cs += O + n;
     }
   }
 
@@ -227,10 +214,11 @@ int build(const Inputs& in, Built* out) {
   h[H_POLICY] = o.policy;
   h[H_MAXPAGES] = p.max_pages_per_seq;
   h[H_NUMPAGES] = p.num_pages;
-  h[H_UNIT_COST] = o.policy == CC_POLICY_STREAMK_COST ? (int32_t)unit_cost(p.mode) : 0;
+  h[H_UNIT_COST] = o.policy == CC_POLICY_STREAMK ? o.unit_cost : 0;
   int64_t empty = 0;
   for (int64_t u = 0; u < U; ++u) empty += nsplit[u] == 0;
   h[H_EMPTY] = (int32_t)empty;
+  h[H_HASH] = input_hash(p, in.seqlens);
   int32_t* wg = h + kHeaderWords;
   int32_t* it = wg + wg_words(C);
   int64_t n = 0;
@@ -285,8 +273,10 @@ int parse_plan(const void* blob, PlanView* v) {
     set_error("not a plan blob (magic %08x, version %d)", (unsigned)h[H_MAGIC], h[H_VERSION]);
     return CC_ERR_PLAN;
   }
-  const int64_t C = h[H_WORKERS], W = h[H_ITEMS], U = h[H_UNITS];
-  if (C < 1 || W < 0 || U < 1) {
+  const int64_t C = h[H_WORKERS], W = h[H_ITEMS], U = h[H_UNITS], S = h[H_PARTIALS];
+  const int64_t T = h[H_TILE], hpu = h[H_HPU];
+  if (C < 1 || W < 0 || U < 1 || S < 0 || T < 1 || hpu < 1 || h[H_BATCH] < 1 || h[H_QTOKENS] < 1 ||
+      h[H_PAGE] < 1 || h[H_MAXPAGES] < 1) {
     set_error("corrupt plan header");
     return CC_ERR_PLAN;
   }
@@ -304,7 +294,59 @@ int parse_plan(const void* blob, PlanView* v) {
     set_error("corrupt plan offsets");
     return CC_ERR_PLAN;
   }
+  for (int64_t w = 0; w < C; ++w) {
+    if (v->wg_off[w + 1] < v->wg_off[w]) {
+      set_error("plan worker offsets descend at worker %lld", (long long)w);
+      return CC_ERR_PLAN;
+    }
+  }
+  // partial slots: consecutive blocks for split units, -1 for the others
+  int64_t slots = 0, maxsplit = 0, empty = 0;
+  for (int64_t u = 0; u < U; ++u) {
+    const int64_t ns = v->unit_nsplit[u], pb = v->unit_pbase[u];
+    if (ns < 0 || (ns > 1 ? pb != slots : pb != -1)) {
+      set_error("plan unit %lld: %lld pieces, partial base %lld", (long long)u, (long long)ns, (long long)pb);
+      return CC_ERR_PLAN;
+    }
+    if (ns > 1) slots += ns;
+    if (ns > maxsplit) maxsplit = ns;
+    empty += ns == 0;
+  }
+  if (slots != S || maxsplit != h[H_MAXSPLIT] || empty != h[H_EMPTY]) {
+    set_error("plan unit table disagrees with its header");
+    return CC_ERR_PLAN;
+  }
+  // items: unit in range, a non-empty tile-aligned token range inside the
+  // unit's key set, a split index below the unit's piece count
+  const bool sparse = h[H_MODE] == CC_MODE_MLA_SPARSE;
+  const int64_t tmax = sparse ? (int64_t)h[H_TOPK] : (int64_t)h[H_MAXPAGES] * h[H_PAGE];
+  for (int64_t i = 0; i < W; ++i) {
+    const int32_t* it = v->items + kItemWords * i;
+    const int64_t u = it[0], tb = it[1], te = it[2], s = it[3];
+    if (u < 0 || u >= U || tb < 0 || tb % T || te <= tb || te > tmax || s < 0 ||
+        s >= v->unit_nsplit[u]) {
+      set_error("plan item %lld (unit %lld, tokens [%lld, %lld), split %lld) out of range", (long long)i,
+                (long long)u, (long long)tb, (long long)te, (long long)s);
+      return CC_ERR_PLAN;
+    }
+  }
   return CC_OK;
+}
+
+int32_t input_hash(const cc_problem& p, const int32_t* seqlens) {
+  uint32_t h = 2166136261u;
+  auto word = [&](int32_t x) {
+    const uint32_t u = (uint32_t)x;
+    for (int i = 0; i < 4; ++i) {
+      h ^= (u >> (8 * i)) & 0xffu;
+      h *= 16777619u;
+    }
+  };
+  for (int32_t x : {p.mode, p.batch, p.q_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim_qk, p.head_dim_v,
+                    p.page_size, p.max_pages_per_seq, p.num_pages, p.topk})
+    word(x);
+  for (int32_t b = 0; b < p.batch; ++b) word(seqlens[b]);
+  return (int32_t)h;
 }
 
 int plan_matches(const PlanView& v, const cc_problem& p) {
@@ -367,6 +409,25 @@ int cc_plan(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seq
     return CC_ERR_BUFFER;
   }
   std::memcpy(plan, b.words.data(), need);
+  return CC_OK;
+}
+
+int cc_plan_check(const void* plan, const cc_problem* prob, const int32_t* seqlens) {
+  if (!plan || !prob || !seqlens) {
+    cc::set_error("null argument");
+    return CC_ERR_INVALID;
+  }
+  cc::PlanView v;
+  int rc = cc::parse_plan(plan, &v);
+  if (rc) return rc;
+  rc = cc::plan_matches(v, *prob);
+  if (rc) return rc;
+  const int32_t want = cc::input_hash(*prob, seqlens);
+  if (v.header[cc::H_HASH] != want) {
+    cc::set_error("plan was built for other sequence lengths (hash %08x, these inputs %08x)",
+                  (unsigned)v.header[cc::H_HASH], (unsigned)want);
+    return CC_ERR_PLAN;
+  }
   return CC_OK;
 }
 

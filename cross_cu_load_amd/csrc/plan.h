@@ -1,7 +1,7 @@
 // Host-side view of a work-plan blob (shared by the planner and the launcher).
 //
 // Blob layout, int32 little-endian words:
-//   header[32]           fields below (H_*); words past H_EMPTY are zero
+//   header[32]           fields below (H_*); words past H_HASH are zero
 //   wg_off[C + 1]        items of worker w are items[wg_off[w] .. wg_off[w+1]),
 //                        zero-padded to a multiple of 4 words so items[] is
 //                        16-byte aligned
@@ -19,7 +19,7 @@
 namespace cc {
 
 constexpr int32_t kPlanMagic = 0x4C504343;  // "CCPL"
-constexpr int32_t kPlanVersion = 2;
+constexpr int32_t kPlanVersion = 3;
 constexpr int kHeaderWords = 32;
 constexpr int kItemWords = 4;
 
@@ -27,8 +27,9 @@ enum HeaderField {
   H_MAGIC = 0, H_VERSION, H_MODE, H_BATCH, H_QTOKENS, H_HQ, H_HKV, H_DQK, H_DV, H_PAGE, H_TOPK,
   H_WORKERS, H_XCDS, H_TILE, H_HPU, H_UNITS, H_TILES, H_ITEMS, H_PARTIALS, H_MAXSPLIT, H_POLICY,
   H_MAXPAGES, H_NUMPAGES,
-  H_UNIT_COST,  // per-unit cost of CC_POLICY_STREAMK_COST, else 0
-  H_EMPTY       // units with no piece (sequences with no cached tokens)
+  H_UNIT_COST,  // per-unit cost (tiles) of CC_POLICY_STREAMK, else 0
+  H_EMPTY,      // units with no piece (sequences with no cached tokens)
+  H_HASH        // FNV-1a of the problem's int32 fields and seqlens (input_hash)
 };
 
 struct PlanView {
@@ -47,8 +48,15 @@ struct PlanView {
   int32_t partials() const { return header[H_PARTIALS]; }
 };
 
-// Parses and checks a host blob; returns CC_OK or CC_ERR_PLAN (message set).
+// Parses and checks a host blob: header, worker offsets ascending, every
+// item's unit, token range and split index in range, partial slots laid out
+// consecutively.  Returns CC_OK or CC_ERR_PLAN (message set).
 int parse_plan(const void* blob, PlanView* v);
+
+// 32-bit FNV-1a of the little-endian bytes of (mode, batch, q_tokens,
+// num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+// max_pages_per_seq, num_pages, topk, seqlens[0 .. batch)) as int32 words.
+int32_t input_hash(const cc_problem& p, const int32_t* seqlens);
 
 // Checks that a parsed plan was built for `prob`.
 int plan_matches(const PlanView& v, const cc_problem& prob);
@@ -59,15 +67,6 @@ const char* last_error();
 
 // Words of wg_off[] including the alignment padding.
 inline int64_t wg_words(int64_t workers) { return (workers + 1 + 3) & ~int64_t(3); }
-
-// Cost model of CC_POLICY_STREAMK_COST: one tile costs kCostPerTile, and each
-// unit adds unit_cost(mode) (the plan header's last word records it).  A GQA
-// unit's start and finish cost about one tile; an MLA unit's (the 128-head
-// partial written and published, the next query token's q loaded) about six.
-constexpr int64_t kCostPerTile = 16;
-constexpr int64_t kUnitCostGqa = 16;
-constexpr int64_t kUnitCostMla = 96;
-inline int64_t unit_cost(int mode) { return mode == CC_MODE_GQA ? kUnitCostGqa : kUnitCostMla; }
 
 // int32 words per unit in the workspace counter area: the arrival counter,
 // the merge-claim mask, then padding, so that every unit's words sit in a

@@ -63,19 +63,29 @@ enum { CC_MODE_GQA = 0, CC_MODE_MLA = 1, CC_MODE_MLA_SPARSE = 2 };
 enum { CC_KV_NHD = 0, CC_KV_HND = 1 };
 
 /* How a plan divides the work.
- *  STREAMK:      the total tile count is cut into num_cus equal contiguous
- *                chunks (one per compute unit, one wave); a sequence may be
- *                split.
- *  PER_UNIT:     one worker per unit (query heads sharing one K/V stream), no
- *                split — the classic one-workgroup-per-(sequence, head) launch.
- *  STREAMK_COST: as STREAMK, but what is cut into equal chunks is the cost of
- *                the work: one tile costs 16, and every unit adds 16 more for
- *                the fixed work of finishing it (merging its pieces inside a
- *                compute unit, writing its output), so compute units holding
- *                many short sequences get fewer tiles.  Units are laid out in
- *                order, each unit's overhead before its tiles, and a tile goes
- *                to the chunk whose cost range holds its starting position.  */
-enum { CC_POLICY_STREAMK = 0, CC_POLICY_PER_UNIT = 1, CC_POLICY_STREAMK_COST = 2 };
+ *  STREAMK:   the work is cut into num_cus equal contiguous chunks (one per
+ *             compute unit, one wave); a sequence may be split.  What is cut
+ *             evenly is the cost of the work: one per KV tile plus
+ *             cc_plan_opts.unit_cost per non-empty unit (the fixed work of
+ *             starting and finishing it).  Units are laid out in order, each
+ *             unit's cost first, and a tile goes to the chunk whose cost range
+ *             holds its starting position.  With unit_cost = 0 this is the
+ *             plain equal split of the tile count: chunk k takes
+ *             floor(N / C) tiles, one more for k < N mod C (CSDN Q&A on
+ *             waves and FlashMLA's Stream-K, "Summary"; GLM-5.2 decode
+ *             article, MegaRTP design: 732 tasks over 148 workers give 140
+ *             workers 5 tasks and 8 workers 4).
+ *  PER_UNIT:  one worker per unit (query heads sharing one K/V stream), no
+ *             split — the classic one-workgroup-per-(sequence, head) launch. */
+enum { CC_POLICY_STREAMK = 0, CC_POLICY_PER_UNIT = 1 };
+
+/* Unit costs (in tiles) measured for this library's kernels: a GQA unit's
+ * start and finish cost about one 32-token tile, a 128-head MLA unit's (its
+ * queries loaded, its 128 KiB partial written and published) about six.  They
+ * are tuning values of these kernels, not part of the method; 0 gives the
+ * pages' equal tile split. */
+#define CC_UNIT_COST_GQA 1
+#define CC_UNIT_COST_MLA 6
 
 /* Reduction of split units inside cc_decode_variant.
  *  FUSED:          the last piece of a unit to finish merges the partials in
@@ -119,13 +129,15 @@ typedef struct cc_problem {
  * heads processed together on one K/V stream (divides Hq / Hkv; cc_decode's
  * GQA kernel needs Hq / Hkv, its MLA kernels need 128: all heads of a query
  * token form one unit, so each latent row is read once per query token).
- * policy: CC_POLICY_*.                                                      */
+ * policy: CC_POLICY_*.  unit_cost: CC_POLICY_STREAMK's cost of a unit in
+ * tiles, >= 0 (0: the equal tile split; see CC_UNIT_COST_*).               */
 typedef struct cc_plan_opts {
   int32_t num_cus;
   int32_t num_xcds;
   int32_t tile_tokens;
   int32_t heads_per_unit;
   int32_t policy;
+  int32_t unit_cost;
 } cc_plan_opts;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -151,9 +163,20 @@ int cc_plan_size(const cc_problem* prob, const cc_plan_opts* opts, const int32_t
  * or NULL; when given, every page a sequence uses is checked to lie in
  * [0, num_pages) (CC_ERR_PAGE otherwise).  plan: host buffer of `bytes` bytes
  * (>= cc_plan_size).  The blob is self-describing (header + arrays, int32
- * little-endian); copy it verbatim to device memory for cc_decode.          */
+ * little-endian); copy it verbatim to device memory for cc_decode.  Its header
+ * holds a 32-bit FNV-1a hash of the problem's int32 fields (mode .. topk, in
+ * struct order) followed by seqlens[0 .. batch), which cc_plan_check compares:
+ * a plan serves only the lengths it was built for (GLM-5.2 decode article,
+ * MegaRTP design: the host plan is rebuilt when the lengths change).        */
 int cc_plan(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
             const int32_t* block_table, void* plan, size_t bytes);
+
+/* CC_OK if the host blob `plan` is a well-formed plan built for exactly `prob`
+ * and these lengths (seqlens: host int32[batch]), else CC_ERR_PLAN with the
+ * reason in cc_last_error().  Host only; no device work.  cc_decode cannot
+ * make this check itself (its seqlens live in device memory); its kernels
+ * instead flag a plan whose pieces do not end at seqlens (see cc_decode). */
+int cc_plan_check(const void* plan, const cc_problem* prob, const int32_t* seqlens);
 
 /* Device workspace bytes a plan needs: an error word, an arrival counter and
  * a merge-claim mask per unit, and one partial (m, l, o) slot per piece of a
@@ -183,10 +206,16 @@ int cc_workspace_check(const void* plan_host, const void* workspace, void* strea
  * the plan holds empty sequences, a first small kernel writes their out (0)
  * and lse (-inf).
  * Host-side checks (before any launch): null pointers, plan header vs `prob`,
- * supported shapes, workspace size.  Device data is not validated on the
- * host; out-of-range page ids, indices or plan/seqlens mismatches are clamped
- * on the device so no access leaves its buffer, the affected outputs are
- * unspecified, and cc_workspace_check reports them. */
+ * the plan's own structure (every item's unit, token range and split index
+ * in range, worker offsets ascending), supported shapes, workspace size.
+ * Device data is not validated on the host.  On the device:
+ *  - a plan that does not match seqlens (a piece ends past seqlens[b], or the
+ *    last piece of a unit ends before it) sets bit 0 of the workspace error
+ *    word and turns that unit's out and lse into NaN: a stale plan never
+ *    yields a plausible-looking result;
+ *  - out-of-range page ids (bit 1) and sparse indices (bit 2) are clamped so
+ *    no access leaves its buffer; the affected outputs are unspecified.
+ * cc_workspace_check reports the error word. */
 int cc_decode(const cc_problem* prob, const void* plan_host, const void* plan_dev, const void* q,
               const void* k_cache, const void* v_cache, const int32_t* block_table,
               const int32_t* seqlens, const int32_t* indices, float* out, float* lse,

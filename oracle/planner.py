@@ -17,20 +17,27 @@ Readings (the pages fix only "equal, one chunk per compute unit"):
   for the first N mod C chunks, contiguously.
 * an empty unit (a sequence with no cached tokens) has no tiles, gets no
   piece and carries no cost; its unit_nsplit is 0.
-* POLICY_STREAMK_COST (a refinement of the same equal split): what is split
-  evenly is the cost of the work, COST_PER_TILE per tile plus unit_cost(mode)
-  per unit, for the fixed work of starting and finishing a unit (loading its
-  queries, publishing or writing its output; six tiles' worth for a 128-head
-  MLA unit, one for a GQA group); a unit occupies a contiguous cost range
-  with its overhead first, and a tile belongs to the chunk whose cost range
-  holds the tile's starting position.  Chunk k's range is
-  [k * q + min(k, r), (k+1) * q + min(k+1, r)) for total cost = q C + r.
+* unit_cost (a plan input, in tiles, default 0): with unit_cost = 0 the
+  split is exactly the equal tile split above.  With unit_cost = c > 0 what
+  is split evenly is the cost of the work, one per tile plus c per non-empty
+  unit for the fixed work of starting and finishing it; a unit occupies a
+  contiguous cost range with its overhead first, and a tile belongs to the
+  chunk whose cost range holds the tile's starting position.  Chunk k's
+  range is [k * q + min(k, r), (k+1) * q + min(k+1, r)) for total cost =
+  q C + r.  The value of c is a caller's choice (a measured property of a
+  kernel), not part of the method; the pages' split is c = 0.
 * a piece is a chunk's intersection with one unit; its split index counts the
   unit's pieces in chunk order; split units get consecutive partial slots.
 * placement: with X locality domains (XCDs) and C divisible by X, logical
   chunk k runs on worker w = (k mod C/X) * X + k div (C/X), so consecutive
   chunks (the pieces of one unit) share a domain when the hardware places
   worker w in domain w mod X.  Otherwise w = k.
+* binding to the inputs: header word 25 is the 32-bit FNV-1a hash of the
+  little-endian bytes of the int32 words (mode, batch, q_tokens, num_q_heads,
+  num_kv_heads, head_dim_qk, head_dim_v, page_size, max_pages_per_seq,
+  num_pages, topk, seqlens[0 .. batch)), so a plan can be checked against the
+  lengths it is used with (GLM-5.2 decode article, MegaRTP design: the plan is
+  rebuilt, not reused, when the lengths change).
 
 The byte layout below is the contract with the C planner; it is written out
 here independently and compared byte for byte.
@@ -42,20 +49,29 @@ import struct
 import numpy as np
 
 PLAN_MAGIC = 0x4C504343          # "CCPL" little-endian
-PLAN_VERSION = 2
-HEADER_WORDS = 32               # words 0..24 below, the rest zero
+PLAN_VERSION = 3
+HEADER_WORDS = 32               # words 0..25 below, the rest zero
 ITEM_WORDS = 4                   # unit, tok_begin, tok_end, split
 
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
-POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_COST = 0, 1, 2
-COST_PER_TILE = 16                # cost units of one tile (POLICY_STREAMK_COST)
-UNIT_COST = 16                    # cost units charged once per GQA unit (= one tile)
-UNIT_COST_MLA = 96                # ... per MLA unit (= six tiles)
+POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
 
 
-def unit_cost(mode: int) -> int:
-    """Cost units charged once per unit of POLICY_STREAMK_COST in this mode."""
-    return UNIT_COST if mode == MODE_GQA else UNIT_COST_MLA
+def fnv1a32(words) -> int:
+    """32-bit FNV-1a (offset basis 2166136261, prime 16777619) of the
+    little-endian bytes of int32 ``words``, returned as a signed int32."""
+    h = 2166136261
+    for byte in struct.pack("<%di" % len(words), *[int(w) for w in words]):
+        h ^= byte
+        h = (h * 16777619) & 0xFFFFFFFF
+    return h - (1 << 32) if h >= 1 << 31 else h
+
+
+def input_hash(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+               max_pages_per_seq, num_pages, topk, seqlens) -> int:
+    """Header word 25: the hash that ties a plan to its problem and lengths."""
+    return fnv1a32([mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+                    max_pages_per_seq, num_pages, topk] + [int(L) for L in seqlens])
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -75,11 +91,13 @@ def unit_lengths(mode: int, batch: int, q_tokens: int, num_q_heads: int, num_kv_
 
 def validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
              max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, heads_per_unit,
-             seqlens, block_table=None, policy=POLICY_STREAMK) -> None:
+             seqlens, block_table=None, policy=POLICY_STREAMK, unit_cost=0) -> None:
     if mode not in (MODE_GQA, MODE_MLA, MODE_MLA_SPARSE):
         raise ValueError("mode")
-    if policy not in (POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_COST):
+    if policy not in (POLICY_STREAMK, POLICY_PER_UNIT):
         raise ValueError("policy")
+    if unit_cost < 0:
+        raise ValueError("unit_cost")
     if batch < 1 or q_tokens < 1 or num_q_heads < 1 or num_kv_heads < 1:
         raise ValueError("shape")
     if mode != MODE_MLA_SPARSE and q_tokens != 1:
@@ -109,15 +127,16 @@ def validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head
 
 def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
          max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, heads_per_unit,
-         seqlens, block_table=None, policy=POLICY_STREAMK) -> dict:
+         seqlens, block_table=None, policy=POLICY_STREAMK, unit_cost=0) -> dict:
     """Build the plan; returns its fields and the serialised ``blob``.
 
     ``policy`` POLICY_PER_UNIT is the comparison launch with one worker per
     unit and no split (num_cus is then ignored and the worker count is U).
+    ``unit_cost`` (POLICY_STREAMK, in tiles): 0 is the equal tile split.
     """
     validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
              max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, heads_per_unit,
-             seqlens, block_table, policy)
+             seqlens, block_table, policy, unit_cost)
     C, X, T = num_cus, num_xcds, tile_tokens
     lens = unit_lengths(mode, batch, q_tokens, num_q_heads, num_kv_heads, heads_per_unit, seqlens, topk)
     U = len(lens)
@@ -132,12 +151,13 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
     N = acc
 
     chunk_pieces: list[list[tuple[int, int, int]]] = []
-    if policy == POLICY_STREAMK_COST:
-        chunk_pieces = _cost_split(ntiles, lens, C, T, unit_cost(mode))
+    cost_split = policy == POLICY_STREAMK and unit_cost > 0
+    if cost_split:
+        chunk_pieces = _cost_split(ntiles, lens, C, T, unit_cost)
     # equal split of N tiles into C contiguous chunks (+1 for the first N mod C)
     base, rem = divmod(N, C)
     u = 0
-    for k in range(C if policy != POLICY_STREAMK_COST else 0):
+    for k in range(C if not cost_split else 0):
         if policy == POLICY_PER_UNIT:
             chunk_pieces.append([(k, 0, lens[k])] if lens[k] > 0 else [])
             continue
@@ -197,8 +217,10 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
     header[:23] = [PLAN_MAGIC, PLAN_VERSION, mode, batch, q_tokens, num_q_heads, num_kv_heads,
                    head_dim_qk, head_dim_v, page_size, topk, C, X, T, heads_per_unit, U, N, W, S,
                    max(nsplit) if nsplit else 0, policy, max_pages_per_seq, num_pages]
-    header[23] = unit_cost(mode) if policy == POLICY_STREAMK_COST else 0
+    header[23] = unit_cost if policy == POLICY_STREAMK else 0
     header[24] = sum(1 for n in nsplit if n == 0)      # units with no piece (empty sequences)
+    header[25] = input_hash(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v,
+                            page_size, max_pages_per_seq, num_pages, topk, seqlens)
     pad = (-(C + 1)) % 4                 # keeps the item array 16-byte aligned
     words = header + wg_off + [0] * pad + [x for it in items for x in it] + nsplit + pbase
     for x in words:
@@ -210,14 +232,16 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
                 worker_of_chunk=worker_of_chunk, unit_len=lens, chunk_items=items_by_chunk)
 
 
-def _cost_split(ntiles, lens, C: int, T: int, O: int = UNIT_COST):
-    """Chunks of POLICY_STREAMK_COST: pieces (unit, tok_begin, tok_end) per chunk.
+def _cost_split(ntiles, lens, C: int, T: int, O: int):
+    """Chunks of the cost split: pieces (unit, tok_begin, tok_end) per chunk.
 
-    Unit u's cost range starts at cs[u] = sum over earlier units of
-    (O + COST_PER_TILE * n), O the unit cost; its tile i starts at cs[u] + O +
-    COST_PER_TILE * i and belongs to the chunk whose range holds that position.
+    Unit u's cost range starts at cs[u] = sum over earlier non-empty units of
+    (O + n), O the unit cost in tiles; its tile i starts at cs[u] + O + i and
+    belongs to the chunk whose range holds that position.  With O = 0 a tile's
+    position is its index in the unit-major tile order, so this is the equal
+    tile split.
     """
-    total = sum(O + COST_PER_TILE * n for n in ntiles if n > 0)
+    total = sum(O + n for n in ntiles if n > 0)
     q, r = divmod(total, C)
     bound = [k * q + min(k, r) for k in range(C + 1)]   # chunk k: [bound[k], bound[k+1])
     pieces: list[list[tuple[int, int, int]]] = [[] for _ in range(C)]
@@ -227,25 +251,25 @@ def _cost_split(ntiles, lens, C: int, T: int, O: int = UNIT_COST):
             continue
         i = 0
         while i < n:
-            start = cs + O + COST_PER_TILE * i
+            start = cs + O + i
             while bound[k + 1] <= start:
                 k += 1
             # tiles of u whose start lies before the end of chunk k
-            last = min(n, _ceil_div(bound[k + 1] - cs - O, COST_PER_TILE))
+            last = min(n, bound[k + 1] - cs - O)
             pieces[k].append((u, i * T, min(last * T, lens[u])))
             i = last
-        cs += O + COST_PER_TILE * n
+        cs += O + n
     return pieces
 
 
 def plan_for(wl, num_cus=256, num_xcds=8, tile_tokens=32, heads_per_unit=None,
-             policy=POLICY_STREAMK) -> dict:
+             policy=POLICY_STREAMK, unit_cost=0) -> dict:
     """``plan`` for a workload object from the seeded input generator."""
     c = wl.cfg
     hu = heads_per_unit if heads_per_unit is not None else c.num_q_heads // c.num_kv_heads
     return plan(c.mode, c.batch, c.q_tokens, c.num_q_heads, c.num_kv_heads, c.head_dim_qk, c.head_dim_v,
                 c.page_size, wl.max_pages, wl.num_pages, c.topk, num_cus, num_xcds, tile_tokens, hu,
-                wl.seqlens, wl.block_table, policy)
+                wl.seqlens, wl.block_table, policy, unit_cost)
 
 
 def list_schedule(task_times, num_workers: int):

@@ -4,30 +4,66 @@ compare out / lse with the fp64 oracle.
 Bars: max|out - oracle| <= 1e-2 and max|lse - oracle| <= 1e-3 (absolute), no
 NaN/Inf, for bf16 inputs with fp32 accumulation; a sequence with no cached
 tokens must give exactly out = 0 and lse = -inf.
+
+Every comparison's margins (max|dout|, max|dlse|, outputs compared) are
+collected in MARGINS; when the environment names a file in CC_PARITY_LOG the
+session writes them there as JSON at its end (tests/conftest.py).
 """
 import numpy as np
 
 from cross_cu_load_amd import binding as B
+from cross_cu_load_amd import workloads as W
 from oracle import attention as A
 
 TOL_OUT, TOL_LSE = 1e-2, 1e-3
+MARGINS = []
+
+# full-size workloads and their oracle results, built once per session
+_WL, _REF = {}, {}
 
 
-def run(wl, cus, xcds, tile=32, policy=B.POLICY_STREAMK_COST, reduce=B.REDUCE_FUSED, tag=""):
+def full_workload(name, layout=None):
+    """The full-size workload `name` (optionally with another page layout), cached."""
+    import dataclasses
+    key = (name, layout)
+    if key not in _WL:
+        cfg = W.CONFIG_BY_NAME[name]
+        if layout is not None:
+            cfg = dataclasses.replace(cfg, kv_layout=layout)
+        _WL[key] = W.make_workload(cfg)
+    return _WL[key]
+
+
+def full_oracle(name, layout=None):
+    """fp64 oracle (out, lse) of every output of the full-size workload `name`,
+    cached (the page layouts hold the same logical values, so one result
+    serves both)."""
+    if name not in _REF:
+        _REF[name] = A.decode_attention_wl(full_workload(name, layout))
+    return _REF[name]
+
+
+def run(wl, cus, xcds, tile=32, policy=B.POLICY_STREAMK, unit_cost=None, reduce=B.REDUCE_FUSED, tag=""):
     import torch
     print(f"[gpu] {tag} cfg={wl.cfg.name} B={wl.cfg.batch} C={cus} X={xcds} T={tile} policy={policy} "
-          f"reduce={reduce}", flush=True)
+          f"unit_cost={unit_cost} reduce={reduce}", flush=True)
     plan = B.plan(B.problem_for(wl), wl.seqlens, wl.block_table, num_cus=cus, num_xcds=xcds,
-                  tile_tokens=tile, policy=policy)
+                  tile_tokens=tile, policy=policy, unit_cost=unit_cost)
     s = B.session(wl, plan)
     s.run(reduce)
     torch.cuda.synchronize()
     return s, plan
 
 
-def compare(s, wl, only=None):
-    """Element-wise comparison with the oracle; ``only`` = (b, t, kv_head) units to check."""
-    ref_o, ref_l = A.decode_attention_wl(wl, only=only)
+def compare(s, wl, only=None, ref=None, label=None):
+    """Element-wise comparison with the oracle; ``only`` = (b, t, kv_head) units to check.
+
+    ``ref`` = a precomputed oracle (out, lse) of every output; ``label`` names
+    the case in MARGINS."""
+    if ref is None:
+        ref_o, ref_l = A.decode_attention_wl(wl, only=only)
+    else:
+        ref_o, ref_l = ref
     out = s.out.cpu().numpy().astype(np.float64)
     lse = s.lse.cpu().numpy().astype(np.float64)
     if only is not None:
@@ -46,7 +82,9 @@ def compare(s, wl, only=None):
         return 0.0, 0.0
     do = float(np.max(np.abs(out - ref_o)))
     dl = float(np.max(np.abs(lse - ref_l)))
-    print(f"       max|dout|={do:.3e} max|dlse|={dl:.3e}", flush=True)
+    print(f"       max|dout|={do:.3e} max|dlse|={dl:.3e} over {out.size} outputs", flush=True)
+    MARGINS.append({"case": label or wl.cfg.name, "max_dout": do, "max_dlse": dl, "outputs": int(out.size),
+                    "lse_values": int(lse.size)})
     assert do <= TOL_OUT and dl <= TOL_LSE
     return do, dl
 

@@ -46,16 +46,20 @@ def _prob(cfg, sl):
 
 @pytest.mark.parametrize("name", [c.name for c in W.CONFIGS])
 @pytest.mark.parametrize("C,X,T", [(256, 8, 32), (256, 8, 64), (304, 8, 32), (148, 1, 32), (8, 8, 32)])
-@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_PER_UNIT, B.POLICY_STREAMK_COST])
-def test_plan_bytes_match_reference_on_workload_lengths(lib, name, C, X, T, policy):
+@pytest.mark.parametrize("policy,unit_cost", [(B.POLICY_STREAMK, 0), (B.POLICY_STREAMK, 1),
+                                              (B.POLICY_STREAMK, 6), (B.POLICY_PER_UNIT, 0)])
+def test_plan_bytes_match_reference_on_workload_lengths(lib, name, C, X, T, policy, unit_cost):
     cfg = W.CONFIG_BY_NAME[name]
     sl = W.draw_seqlens(cfg)
     prob, maxp, npages = _prob(cfg, sl)
-    for hu in ([cfg.group] if cfg.mode == W.MODE_GQA else [64, 128]):
-        blob = B.plan(prob, sl, None, num_cus=C, num_xcds=X, tile_tokens=T, heads_per_unit=hu, policy=policy)
+    for hu in ([cfg.group] if cfg.mode == W.MODE_GQA else [32, 64, 128]):
+        blob = B.plan(prob, sl, None, num_cus=C, num_xcds=X, tile_tokens=T, heads_per_unit=hu, policy=policy,
+                      unit_cost=unit_cost)
         ref = PL.plan(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
-                      cfg.head_dim_v, cfg.page_size, maxp, npages, cfg.topk, C, X, T, hu, sl, None, policy)
+                      cfg.head_dim_v, cfg.page_size, maxp, npages, cfg.topk, C, X, T, hu, sl, None, policy,
+                      unit_cost)
         assert blob.tobytes() == ref["blob"]
+        B.plan_check(blob, prob, sl)
         # workspace: 256 B error word area, 128 B of counter words per unit,
         # 256-aligned partial slots of
         # {m[hu], l[hu], pad to 4 floats, o[hu][dv]} rounded up to 64 floats
@@ -87,11 +91,14 @@ def test_plan_bytes_match_reference_fuzz(lib, seed):
     C = int(rng.choice([1, 3, 8, 100, 256, 1000]))
     X = int(rng.choice([1, 4, 8]))
     T = int(rng.choice([1, 7, 32, 64]))
-    policy = int(rng.integers(0, 3))
+    policy = int(rng.integers(0, 2))
+    unit_cost = int(rng.choice([0, 1, 2, 6, 40])) if policy == B.POLICY_STREAMK else 0
     prob = B.problem(mode, B_, Tq, Hq, Hkv, 64, 64, P, maxp, npages, topk, 0.125)
-    blob = B.plan(prob, sl, bt, num_cus=C, num_xcds=X, tile_tokens=T, heads_per_unit=hu, policy=policy)
-    ref = PL.plan(mode, B_, Tq, Hq, Hkv, 64, 64, P, maxp, npages, topk, C, X, T, hu, sl, bt, policy)
+    blob = B.plan(prob, sl, bt, num_cus=C, num_xcds=X, tile_tokens=T, heads_per_unit=hu, policy=policy,
+                  unit_cost=unit_cost)
+    ref = PL.plan(mode, B_, Tq, Hq, Hkv, 64, 64, P, maxp, npages, topk, C, X, T, hu, sl, bt, policy, unit_cost)
     assert blob.tobytes() == ref["blob"]
+    B.plan_check(blob, prob, sl)
 
 
 def _base():
@@ -137,10 +144,71 @@ def test_plan_rejects_invalid_inputs(lib, bad, code):
                 4, kw["topk"], cus, 1, 32, hu, sl, bt)
 
 
+def test_plan_check_binds_the_plan_to_its_lengths(lib):
+    """cc_plan_check accepts the inputs a plan was built for and refuses any
+    other lengths or shape; cc_plan refuses a negative unit cost."""
+    kw = _base()
+    prob = B.problem(**kw)
+    sl = np.array([10, 20], np.int32)
+    blob = B.plan(prob, sl, None, num_cus=8, num_xcds=1, tile_tokens=32, heads_per_unit=4)
+    B.plan_check(blob, prob, sl)
+    for other in (np.array([10, 19], np.int32), np.array([11, 20], np.int32), np.array([20, 10], np.int32)):
+        with pytest.raises(B.CrossCUError) as ei:
+            B.plan_check(blob, prob, other)
+        assert ei.value.code == B.CC_ERR_PLAN
+    with pytest.raises(B.CrossCUError) as ei:
+        B.plan_check(blob, B.problem(**{**kw, "num_pages": 5}), sl)
+    assert ei.value.code == B.CC_ERR_PLAN
+    with pytest.raises(B.CrossCUError) as ei:
+        B.plan(prob, sl, None, num_cus=8, num_xcds=1, tile_tokens=32, heads_per_unit=4, unit_cost=-1)
+    assert ei.value.code == B.CC_ERR_INVALID
+
+
+def _corrupt(blob, word, value):
+    w = blob.view(np.int32).copy()
+    w[word] = value
+    return w.view(np.uint8)
+
+
+def test_plan_structure_is_validated_on_the_host(lib):
+    """A blob whose items or unit table are out of range is refused by every
+    call that reads a plan (cc_plan_check, cc_workspace_size, cc_decode)
+    before anything touches a device."""
+    kw = _base()
+    prob = B.problem(**kw)
+    sl = np.array([10, 20], np.int32)
+    blob = B.plan(prob, sl, None, num_cus=3, num_xcds=1, tile_tokens=1, heads_per_unit=4)
+    h = blob.view(np.int32)
+    C, W_, U = int(h[11]), int(h[17]), int(h[15])
+    assert W_ > 3       # several split units
+    wg = 32
+    it = wg + ((C + 1 + 3) & ~3)
+    ns = it + 4 * W_
+    bad = {
+        "unit": _corrupt(blob, it + 0, U),
+        "unit_neg": _corrupt(blob, it + 0, -1),
+        "empty_range": _corrupt(blob, it + 2, int(h[it + 1])),
+        "past_block_table": _corrupt(blob, it + 4 * (W_ - 1) + 2, 2 * 16 + 1),
+        "split": _corrupt(blob, it + 3, int(h[ns + int(h[it])])),
+        "wg_descending": _corrupt(blob, wg + 1, W_ + 1),
+        "nsplit": _corrupt(blob, ns, int(h[ns]) + 1),
+        "pbase": _corrupt(blob, ns + U, 5),
+    }
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails a host check first
+    n = ctypes.c_size_t()
+    for name, b in bad.items():
+        with pytest.raises(B.CrossCUError) as ei:
+            B.plan_check(b, prob, sl)
+        assert ei.value.code == B.CC_ERR_PLAN, name
+        assert lib.cc_workspace_size(b.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)) == B.CC_ERR_PLAN, name
+        assert lib.cc_decode(ctypes.byref(prob), b.ctypes.data_as(ctypes.c_void_p), fake, fake, fake, fake, fake,
+                             fake, None, fake, fake, fake, 1 << 30, None) == B.CC_ERR_PLAN, name
+
+
 def test_plan_buffer_too_small_and_bad_blobs(lib):
     prob = B.problem(**_base())
     sl = np.array([10, 20], np.int32)
-    opts = B.PlanOpts(8, 1, 32, 4, 0)
+    opts = B.PlanOpts(8, 1, 32, 4, 0, 0)
     n = ctypes.c_size_t()
     assert lib.cc_plan_size(ctypes.byref(prob), ctypes.byref(opts), sl.ctypes.data_as(B._I32P),
                             ctypes.byref(n)) == 0

@@ -23,14 +23,15 @@ CASES = [("skewed_gqa", W.KV_NHD), ("skewed_gqa", W.KV_HND), ("deepseek_mla", W.
 
 
 @pytest.mark.parametrize("reduce", [B.REDUCE_FUSED, B.REDUCE_SPLIT_COMBINE])
-@pytest.mark.parametrize("policy", [B.POLICY_STREAMK_COST, B.POLICY_STREAMK, B.POLICY_PER_UNIT])
+@pytest.mark.parametrize("policy,unit_cost", [(B.POLICY_STREAMK, None), (B.POLICY_STREAMK, 0),
+                                              (B.POLICY_PER_UNIT, 0)])
 @pytest.mark.parametrize("name,layout", CASES)
-def test_empty_sequences_in_a_batch(dev, name, layout, policy, reduce):
+def test_empty_sequences_in_a_batch(dev, name, layout, policy, unit_cost, reduce):
     cfg = dataclasses.replace(W.small_variant(W.CONFIG_BY_NAME[name], batch=6, seqlen_hi=5000, seed_offset=21),
                               kv_layout=layout)
     sl = np.array([0, 300, 0, 4000, 17, 0], np.int32)
     wl = W.make_workload(cfg, seqlens=sl)
-    s, plan = run(wl, *dev, policy=policy, reduce=reduce, tag=f"empty {name} layout={layout}")
+    s, plan = run(wl, *dev, policy=policy, unit_cost=unit_cost, reduce=reduce, tag=f"empty {name} layout={layout}")
     compare(s, wl)
     clean(s, plan)
 

@@ -3,9 +3,8 @@
 Bars: max|out - oracle| <= 1e-2 and max|lse - oracle| <= 1e-3 (absolute), no
 NaN/Inf, for bf16 inputs with fp32 accumulation.  Full-size workloads run in
 the launch configuration the benchmark times (one chunk per compute unit,
-32-token tiles, the device's XCD count); the oracle checks every output where
-it finishes in seconds and a sample of units (always including split ones)
-otherwise.
+32-token tiles, the device's XCD count) and are checked on every output, for
+the fused path and for both comparison launches.
 """
 import dataclasses
 
@@ -16,16 +15,20 @@ from cross_cu_load_amd import binding as B
 from cross_cu_load_amd import workloads as W
 from oracle import attention as A
 
-from gpu_helpers import clean, compare, run
+from gpu_helpers import clean, compare, full_oracle, full_workload, run
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def test_tiny_gqa_config(dev):
-    wl = W.make_workload(W.CONFIG_BY_NAME["tiny_gqa"])
-    s, plan = run(wl, *dev, tag="tiny")
-    compare(s, wl)
+@pytest.mark.parametrize("variant", ["fused", "per_unit", "split_combine"])
+def test_tiny_gqa_config(dev, variant):
+    wl = full_workload("tiny_gqa")
+    policy, reduce = {"fused": (B.POLICY_STREAMK, B.REDUCE_FUSED),
+                      "per_unit": (B.POLICY_PER_UNIT, B.REDUCE_FUSED),
+                      "split_combine": (B.POLICY_STREAMK, B.REDUCE_SPLIT_COMBINE)}[variant]
+    s, plan = run(wl, *dev, policy=policy, reduce=reduce, tag="tiny")
+    compare(s, wl, ref=full_oracle("tiny_gqa"), label=f"tiny_gqa {variant}")
     clean(s, plan)
 
 
@@ -59,33 +62,44 @@ def test_ragged_and_single_token_sequences(dev):
             assert np.array_equal(out[b, 0, h], v)
 
 
-@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_STREAMK_COST])
+@pytest.mark.parametrize("unit_cost", [0, None])
 @pytest.mark.parametrize("layout", [W.KV_NHD, W.KV_HND])
-def test_skewed_full_size_all_outputs(dev, layout, policy):
-    wl = W.make_workload(dataclasses.replace(W.CONFIG_BY_NAME["skewed_gqa"], kv_layout=layout))
-    s, plan = run(wl, *dev, policy=policy, tag="skewed-full")
-    compare(s, wl)
+def test_skewed_full_size_all_outputs(dev, layout, unit_cost):
+    """Every output of the skewed workload (one 131072-token sequence and 31 of
+    256), for the pages' equal tile split (unit cost 0) and the measured
+    default unit cost."""
+    wl = full_workload("skewed_gqa", layout)
+    s, plan = run(wl, *dev, unit_cost=unit_cost, tag="skewed-full")
+    compare(s, wl, ref=full_oracle("skewed_gqa"),
+            label=f"skewed_gqa fused {'HND' if layout else 'NHD'} unit_cost={unit_cost}")
     clean(s, plan)
 
 
-def test_llama_full_size_sampled(dev):
-    cfg = W.CONFIG_BY_NAME["llama3_8b_gqa"]
-    wl = W.make_workload(cfg)
+@pytest.mark.parametrize("layout", [W.KV_NHD, W.KV_HND])
+def test_llama_full_size_all_outputs(dev, layout):
+    """Every output of the Llama-3-8B-shaped workload (64 sequences, log-uniform
+    lengths in [128, 32768])."""
+    wl = full_workload("llama3_8b_gqa", layout)
     s, plan = run(wl, *dev, tag="llama-full")
-    from oracle import planner as PL
-    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1], policy=PL.POLICY_STREAMK_COST)
-    split_units = [u for u, n in enumerate(ref["unit_nsplit"]) if n > 1]
-    rng = np.random.default_rng(5)
-    pick = set(split_units[:24]) | set(int(u) for u in rng.choice(len(ref["unit_nsplit"]), 24, replace=False))
-    longest = int(np.argmax(wl.seqlens))
-    pick |= {longest * cfg.num_kv_heads + g for g in range(cfg.num_kv_heads)}
-    only = [(u // cfg.num_kv_heads, 0, u % cfg.num_kv_heads) for u in sorted(pick)]
-    compare(s, wl, only=only)
+    compare(s, wl, ref=full_oracle("llama3_8b_gqa"), label=f"llama3_8b_gqa fused {'HND' if layout else 'NHD'}")
+    clean(s, plan)
+
+
+@pytest.mark.parametrize("variant", ["per_unit", "split_combine"])
+@pytest.mark.parametrize("name", ["skewed_gqa", "llama3_8b_gqa"])
+def test_full_size_comparison_variants(dev, name, variant):
+    """The two comparison launches at full size, in the page layout the
+    benchmark times, on every output."""
+    wl = full_workload(name, W.KV_HND)
+    policy, reduce = ((B.POLICY_PER_UNIT, B.REDUCE_FUSED) if variant == "per_unit"
+                      else (B.POLICY_STREAMK, B.REDUCE_SPLIT_COMBINE))
+    s, plan = run(wl, *dev, policy=policy, reduce=reduce, tag=f"{name}-{variant}")
+    compare(s, wl, ref=full_oracle(name), label=f"{name} {variant} HND")
     clean(s, plan)
 
 
 @pytest.mark.parametrize("policy,reduce", [(B.POLICY_PER_UNIT, B.REDUCE_FUSED),
-                                           (B.POLICY_STREAMK_COST, B.REDUCE_SPLIT_COMBINE)])
+                                           (B.POLICY_STREAMK, B.REDUCE_SPLIT_COMBINE)])
 @pytest.mark.parametrize("name", ["tiny_gqa", "skewed_gqa"])
 def test_comparison_variants(dev, policy, reduce, name):
     cfg = W.CONFIG_BY_NAME[name]
@@ -97,12 +111,12 @@ def test_comparison_variants(dev, policy, reduce, name):
     clean(s, plan)
 
 
-@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_STREAMK_COST])
+@pytest.mark.parametrize("unit_cost", [0, None])
 @pytest.mark.parametrize("cus", [1, 8, 64, 255, 256, 1024])
-def test_split_points_move_with_cu_count(dev, cus, policy):
+def test_split_points_move_with_cu_count(dev, cus, unit_cost):
     cfg = W.small_variant(W.CONFIG_BY_NAME["skewed_gqa"], batch=5, seqlen_hi=4000, seed_offset=cus)
     wl = W.make_workload(cfg)
-    s, plan = run(wl, cus, dev[1], policy=policy, tag="cus")
+    s, plan = run(wl, cus, dev[1], unit_cost=unit_cost, tag="cus")
     compare(s, wl)
     clean(s, plan)
 

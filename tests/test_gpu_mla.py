@@ -3,10 +3,9 @@ oracle (through the C ABI).
 
 Bars as for GQA: max|out - oracle| <= 1e-2, max|lse - oracle| <= 1e-3, no
 NaN/Inf.  The full-size dense workload (64 sequences of 1024..16384 tokens)
-runs in the launch configuration the benchmark times and is checked on a
-sample of query tokens that always includes split ones and the longest
-sequence; the full-size sparse workload (2 requests x 8 query tokens, 2048
-indices each) is checked on every output.
+and the full-size sparse workload (2 requests x 8 query tokens, 2048 indices
+each) run in the launch configuration the benchmark times and are checked on
+every output, for the fused path and for both comparison launches.
 """
 import dataclasses
 
@@ -18,7 +17,7 @@ from cross_cu_load_amd import workloads as W
 from oracle import attention as A
 from oracle import planner as PL
 
-from gpu_helpers import clean, compare, run
+from gpu_helpers import clean, compare, full_oracle, full_workload, run
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -57,16 +56,25 @@ def test_mla_ragged_and_single_token(dev):
             assert np.array_equal(out[b, 0, h], v)
 
 
-def test_mla_full_size_sampled(dev):
-    wl = W.make_workload(MLA)
-    s, plan = run(wl, *dev, tag="mla-full")
-    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1], heads_per_unit=128, policy=PL.POLICY_STREAMK_COST)
+@pytest.mark.parametrize("unit_cost", [0, None])
+def test_mla_full_size_all_outputs(dev, unit_cost):
+    wl = full_workload("deepseek_mla")
+    s, plan = run(wl, *dev, unit_cost=unit_cost, tag="mla-full")
+    ref = PL.plan_for(wl, num_cus=dev[0], num_xcds=dev[1], heads_per_unit=128,
+                      unit_cost=B.default_unit_cost(B.MODE_MLA) if unit_cost is None else unit_cost)
     assert plan.tobytes() == ref["blob"]
-    split_tok = sorted({u // 2 for u, n in enumerate(ref["unit_nsplit"]) if n > 1})
-    rng = np.random.default_rng(7)
-    pick = set(split_tok[:8]) | set(int(b) for b in rng.choice(MLA.batch, 4, replace=False))
-    pick.add(int(np.argmax(wl.seqlens)))
-    compare(s, wl, only=[(b, 0, 0) for b in sorted(pick)])
+    compare(s, wl, ref=full_oracle("deepseek_mla"), label=f"deepseek_mla fused unit_cost={unit_cost}")
+    clean(s, plan)
+
+
+@pytest.mark.parametrize("variant", ["per_unit", "split_combine"])
+@pytest.mark.parametrize("name", ["deepseek_mla", "sparse_mla"])
+def test_mla_full_size_comparison_variants(dev, name, variant):
+    wl = full_workload(name)
+    policy, reduce = ((B.POLICY_PER_UNIT, B.REDUCE_FUSED) if variant == "per_unit"
+                      else (B.POLICY_STREAMK, B.REDUCE_SPLIT_COMBINE))
+    s, plan = run(wl, *dev, policy=policy, reduce=reduce, tag=f"{name}-{variant}")
+    compare(s, wl, ref=full_oracle(name), label=f"{name} {variant}")
     clean(s, plan)
 
 
@@ -87,9 +95,9 @@ def test_sparse_small_all_outputs(dev, L, topk):
 
 
 def test_sparse_full_size_all_outputs(dev):
-    wl = W.make_workload(SPARSE)
+    wl = full_workload("sparse_mla")
     s, plan = run(wl, *dev, tag="sparse-full")
-    compare(s, wl)
+    compare(s, wl, ref=full_oracle("sparse_mla"), label="sparse_mla fused")
     clean(s, plan)
 
 
@@ -108,7 +116,7 @@ def test_sparse_index_order_irrelevant(dev):
 
 
 @pytest.mark.parametrize("policy,reduce", [(B.POLICY_PER_UNIT, B.REDUCE_FUSED),
-                                           (B.POLICY_STREAMK_COST, B.REDUCE_SPLIT_COMBINE)])
+                                           (B.POLICY_STREAMK, B.REDUCE_SPLIT_COMBINE)])
 @pytest.mark.parametrize("name", ["deepseek_mla", "sparse_mla"])
 def test_mla_comparison_variants(dev, policy, reduce, name):
     cfg = W.CONFIG_BY_NAME[name]
@@ -119,12 +127,12 @@ def test_mla_comparison_variants(dev, policy, reduce, name):
     clean(s, plan)
 
 
-@pytest.mark.parametrize("policy", [B.POLICY_STREAMK, B.POLICY_STREAMK_COST])
+@pytest.mark.parametrize("unit_cost", [0, None])
 @pytest.mark.parametrize("cus", [1, 7, 64, 256, 1024])
-def test_mla_split_points_move_with_cu_count(dev, cus, policy):
+def test_mla_split_points_move_with_cu_count(dev, cus, unit_cost):
     cfg = W.small_variant(MLA, batch=3, seqlen_hi=4000, seed_offset=cus)
     wl = W.make_workload(cfg)
-    s, plan = run(wl, cus, dev[1], policy=policy, tag="mla-cus")
+    s, plan = run(wl, cus, dev[1], unit_cost=unit_cost, tag="mla-cus")
     compare(s, wl)
     clean(s, plan)
 

@@ -19,12 +19,13 @@ from oracle import planner as PL
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _plan(lens, C=8, X=1, T=4, G=1, Hkv=1, mode=PL.MODE_GQA, Tq=1, topk=0, hu=None, policy=PL.POLICY_STREAMK):
+def _plan(lens, C=8, X=1, T=4, G=1, Hkv=1, mode=PL.MODE_GQA, Tq=1, topk=0, hu=None, policy=PL.POLICY_STREAMK,
+          unit_cost=0):
     lens = np.asarray(lens, np.int32)
     P = 16
     maxp = max(1, int(max((int(L) + P - 1) // P for L in lens)))
     return PL.plan(mode, len(lens), Tq, G * Hkv, Hkv, 64, 64, P, maxp, 1 << 20, topk, C, X, T,
-                   hu if hu is not None else G, lens, None, policy)
+                   hu if hu is not None else G, lens, None, policy, unit_cost)
 
 
 def test_golden_732_tasks_over_148_workers():
@@ -35,6 +36,29 @@ def test_golden_732_tasks_over_148_workers():
     assert int((sizes == 5).sum()) == g["workers_with_5"]
     assert int((sizes == 4).sum()) == g["workers_with_4"]
     assert p["num_tiles"] == g["tasks"]
+    # the same 732 tasks through the cost split with unit cost 0 (the code
+    # path that carries a unit cost): the printed counts again
+    pieces = PL._cost_split([1] * g["tasks"], [4] * g["tasks"], g["workers"], 4, 0)
+    sizes = np.array([len(c) for c in pieces])
+    assert int((sizes == 5).sum()) == g["workers_with_5"] and int((sizes == 4).sum()) == g["workers_with_4"]
+
+
+def _equal_split_pieces(p):
+    return [[(u, t0, t1) for (u, t0, t1, _) in its] for its in p["chunk_items"]]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_cost_split_with_unit_cost_zero_is_the_equal_split(seed):
+    """The cost split at unit cost 0 and the plain equal tile split give the
+    same pieces (chunk by chunk), and the whole plan blob is byte-identical."""
+    rng = np.random.default_rng(7000 + seed)
+    B = int(rng.integers(1, 9))
+    lens = [int(x) for x in rng.integers(0, 400, size=B)]
+    C = int(rng.choice([1, 2, 3, 7, 16, 148, 256]))
+    T = int(rng.choice([1, 4, 16, 32]))
+    eq = _plan(lens, C=C, X=1, T=T)
+    ntiles = [-(-L // T) for L in lens]
+    assert PL._cost_split(ntiles, lens, C, T, 0) == _equal_split_pieces(eq)
 
 
 def test_golden_tail_effect_and_equal_split():
@@ -56,25 +80,25 @@ def test_golden_tail_effect_and_equal_split():
     assert chunk.max() == total / g["num_sms"] == 155
 
 
-def _check_invariants(p, lens, C, X, T, policy=PL.POLICY_STREAMK, mode=PL.MODE_GQA):
+def _check_invariants(p, lens, C, X, T, unit_cost=0):
     U = len(lens)
     ntiles = [-(-L // T) for L in lens]
     N = sum(ntiles)
     assert p["num_tiles"] == N and p["num_units"] == U
     # chunk sizes: floor(N/C), +1 on the first N mod C logical chunks
-    if policy == PL.POLICY_STREAMK:
+    if unit_cost == 0:
         base, rem = divmod(N, C)
         for k, its in enumerate(p["chunk_items"]):
             tiles = sum(-(-(t1 - t0) // T) for (_, t0, t1, _) in its)
             assert tiles == base + (k < rem)
     else:
-        # cost of a chunk (16 per tile, the mode's unit cost per unit it
-        # starts) is within one tile plus one unit of its share of the total
-        K, O = PL.COST_PER_TILE, PL.unit_cost(mode)
-        q, r = divmod(K * N + O * sum(n > 0 for n in ntiles), C)
+        # cost of a chunk (one per tile, the unit cost per unit it starts) is
+        # within one tile plus one unit of its share of the total
+        O = unit_cost
+        q, r = divmod(N + O * sum(n > 0 for n in ntiles), C)
         for k, its in enumerate(p["chunk_items"]):
-            cost = sum(K * -(-(t1 - t0) // T) + (O if t0 == 0 else 0) for (_, t0, t1, _) in its)
-            assert abs(cost - (q + (k < r))) <= K + O
+            cost = sum(-(-(t1 - t0) // T) + (O if t0 == 0 else 0) for (_, t0, t1, _) in its)
+            assert abs(cost - (q + (k < r))) <= 1 + O
     # every token of every unit covered exactly once, in order
     cover = [[] for _ in range(U)]
     for its in p["chunk_items"]:
@@ -134,12 +158,12 @@ def _brute_force(lens, C, T):
     return [[tuple(x) for x in c] for c in chunks]
 
 
-def _brute_force_cost(lens, C, T):
-    """Cost policy, tile by tile: a tile's cost position is the cost of all
-    earlier units (16 + 16 per tile each), 16 for its own unit and 16 per
-    earlier tile of it; the tile goes to the chunk whose range holds it,
-    found by scanning the ranges."""
-    K, O = PL.COST_PER_TILE, PL.UNIT_COST
+def _brute_force_cost(lens, C, T, O):
+    """Cost split, tile by tile: a tile's cost position is the cost of all
+    earlier non-empty units (O + one per tile each), O for its own unit and
+    one per earlier tile of it; the tile goes to the chunk whose range holds
+    it, found by scanning the ranges."""
+    K = 1
     ntiles = [-(-L // T) for L in lens]
     total = sum(O + K * n for n in ntiles if n > 0)
     ranges = [(k * (total // C) + min(k, total % C), (k + 1) * (total // C) + min(k + 1, total % C))
@@ -159,9 +183,9 @@ def _brute_force_cost(lens, C, T):
     return [[tuple(x) for x in c] for c in chunks]
 
 
-@pytest.mark.parametrize("policy", [PL.POLICY_STREAMK, PL.POLICY_STREAMK_COST])
+@pytest.mark.parametrize("unit_cost", [0, 1, 3, 6])
 @pytest.mark.parametrize("seed", range(30))
-def test_brute_force_and_invariants_small(seed, policy):
+def test_brute_force_and_invariants_small(seed, unit_cost):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 5))
     lens = [int(x) for x in rng.integers(1, 60, size=B)]
@@ -171,11 +195,12 @@ def test_brute_force_and_invariants_small(seed, policy):
     C = int(rng.choice([1, 2, 3, 5, 8, 16]))
     X = int(rng.choice([1, 2, 4, 8]))
     T = int(rng.choice([1, 4, 16, 32]))
-    p = _plan(lens, C=C, X=X, T=T, policy=policy)
-    _check_invariants(p, lens, C, X, T, policy)
-    bf = _brute_force(lens, C, T) if policy == PL.POLICY_STREAMK else _brute_force_cost(lens, C, T)
+    p = _plan(lens, C=C, X=X, T=T, unit_cost=unit_cost)
+    _check_invariants(p, lens, C, X, T, unit_cost)
     got = [[(u, t0, t1) for (u, t0, t1, _) in its] for its in p["chunk_items"]]
-    assert got == bf
+    assert got == _brute_force_cost(lens, C, T, unit_cost)
+    if unit_cost == 0:      # the two brute forces agree where they should
+        assert got == _brute_force(lens, C, T)
 
 
 def test_cost_policy_gives_short_units_fewer_tiles():
@@ -184,18 +209,43 @@ def test_cost_policy_gives_short_units_fewer_tiles():
     lens = [4096] + [64] * 60
     C, T = 16, 32
     eq = _plan(lens, C=C, T=T)
-    co = _plan(lens, C=C, T=T, policy=PL.POLICY_STREAMK_COST)
+    co = _plan(lens, C=C, T=T, unit_cost=1)
     tiles = lambda p, k: sum(-(-(t1 - t0) // T) for (_, t0, t1, _) in p["chunk_items"][k])
     assert tiles(co, C - 1) < tiles(eq, C - 1)          # the last chunk holds only short units
     assert tiles(co, 0) >= tiles(eq, 0)                 # the first holds only the long one
-    assert co["blob"][80:84] != b"\x00\x00\x00\x00"      # header word 20: policy
-    assert np.frombuffer(co["blob"][:96], np.int32)[23] == PL.UNIT_COST
+    assert np.frombuffer(co["blob"][:128], np.int32)[23] == 1      # header word 23: the unit cost
+    assert np.frombuffer(eq["blob"][:128], np.int32)[23] == 0
 
 
-@pytest.mark.parametrize("policy", [PL.POLICY_STREAMK, PL.POLICY_STREAMK_COST])
+def test_input_hash_is_fnv1a():
+    """Header word 25 is FNV-1a over the problem words and the lengths: the
+    published FNV-1a test vectors, and a hash that moves with every length."""
+    # FNV-1a 32 of the empty input is the offset basis; of b"a" 0xe40c292c
+    assert PL.fnv1a32([]) == 2166136261 - (1 << 32)
+    h = 2166136261
+    for byte in b"a":
+        h = ((h ^ byte) * 16777619) & 0xFFFFFFFF
+    assert h == 0xE40C292C
+    # one int32 word 0x61 hashes its four little-endian bytes 61 00 00 00
+    h = 2166136261
+    for byte in bytes([0x61, 0, 0, 0]):
+        h = ((h ^ byte) * 16777619) & 0xFFFFFFFF
+    assert PL.fnv1a32([0x61]) == (h - (1 << 32) if h >= 1 << 31 else h)
+    lens = [300, 70, 1000]
+    p = _plan(lens, C=4, T=32)
+    word = int(np.frombuffer(p["blob"][:128], np.int32)[25])
+    for b in range(3):
+        other = list(lens)
+        other[b] += 1
+        assert int(np.frombuffer(_plan(other, C=4, T=32)["blob"][:128], np.int32)[25]) != word
+    # knobs of the plan are not inputs: the same inputs under another split hash the same
+    assert int(np.frombuffer(_plan(lens, C=7, T=16, unit_cost=6)["blob"][:128], np.int32)[25]) == word
+
+
+@pytest.mark.parametrize("unit_cost", [0, 1, 6])
 @pytest.mark.parametrize("C", [1, 3, 8, 148, 256, 304, 1000])
 @pytest.mark.parametrize("T", [16, 32, 64])
-def test_invariants_on_the_workload_lengths(C, T, policy):
+def test_invariants_on_the_workload_lengths(C, T, unit_cost):
     for cfg in W.CONFIGS:
         lens_b = W.draw_seqlens(cfg)
         hu = cfg.group if cfg.mode == W.MODE_GQA else min(cfg.num_q_heads, 128)
@@ -205,8 +255,9 @@ def test_invariants_on_the_workload_lengths(C, T, policy):
         P = cfg.page_size
         maxp = int(max((int(L) + P - 1) // P for L in lens_b))
         p = PL.plan(cfg.mode, cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim_qk,
-                    cfg.head_dim_v, P, maxp, 1 << 20, cfg.topk, C, 8, T, hu, lens_b, None, policy)
-        _check_invariants(p, lens, C, 8, T, policy, cfg.mode)
+                    cfg.head_dim_v, P, maxp, 1 << 20, cfg.topk, C, 8, T, hu, lens_b, None, PL.POLICY_STREAMK,
+                    unit_cost)
+        _check_invariants(p, lens, C, 8, T, unit_cost)
 
 
 def test_skewed_workload_split_shape():
@@ -244,31 +295,38 @@ def test_invalid_inputs_rejected(bad):
         PL.plan(**kw)
 
 
-def test_cost_policy_unit_cost_follows_mode():
-    """An MLA unit is charged six tiles, a GQA unit one, and the header says which."""
+def test_unit_cost_is_recorded_and_independent_of_mode():
+    """The unit cost is an input of the plan, recorded in the header; the
+    oracle holds no per-mode tuning (the same lengths and cost give the same
+    pieces in every mode)."""
     lens = [300, 70, 1000]
-    for mode, hu, O in ((PL.MODE_GQA, 1, 16), (PL.MODE_MLA, 1, 96)):
-        p = _plan(lens, C=4, T=32, mode=mode, hu=hu, policy=PL.POLICY_STREAMK_COST)
-        assert np.frombuffer(p["blob"][:96], np.int32)[23] == O == PL.unit_cost(mode)
-        _check_invariants(p, lens, 4, 1, 32, PL.POLICY_STREAMK_COST, mode)
+    for O in (0, 1, 6):
+        ps = [_plan(lens, C=4, T=32, mode=mode, hu=1, unit_cost=O) for mode in (PL.MODE_GQA, PL.MODE_MLA)]
+        for p in ps:
+            assert np.frombuffer(p["blob"][:128], np.int32)[23] == O
+            _check_invariants(p, lens, 4, 1, 32, O)
+        assert ps[0]["chunk_items"] == ps[1]["chunk_items"]
+    with pytest.raises(ValueError):
+        _plan(lens, unit_cost=-1)
 
 
-@pytest.mark.parametrize("policy", [PL.POLICY_STREAMK, PL.POLICY_STREAMK_COST, PL.POLICY_PER_UNIT])
-def test_empty_sequences_get_no_piece(policy):
+@pytest.mark.parametrize("policy,unit_cost", [(PL.POLICY_STREAMK, 0), (PL.POLICY_STREAMK, 1),
+                                              (PL.POLICY_STREAMK, 6), (PL.POLICY_PER_UNIT, 0)])
+def test_empty_sequences_get_no_piece(policy, unit_cost):
     """Sequences with no cached tokens: no piece, nsplit 0, no cost; the other
     units are planned exactly as in the batch without them (cost and tile
     positions do not count the empty units)."""
     lens = [0, 37, 0, 0, 120, 5, 0]
-    p = _plan(lens, C=8, X=1, T=4, policy=policy)
+    p = _plan(lens, C=8, X=1, T=4, policy=policy, unit_cost=unit_cost)
     if policy != PL.POLICY_PER_UNIT:
-        _check_invariants(p, lens, 8, 1, 4, policy)
+        _check_invariants(p, lens, 8, 1, 4, unit_cost)
     assert [p["unit_nsplit"][u] for u in (0, 2, 3, 6)] == [0, 0, 0, 0]
     assert np.frombuffer(p["blob"], np.int32)[24] == 4       # empty units counted in the header
     assert all(u not in (0, 2, 3, 6) for its in p["chunk_items"] for (u, _, _, _) in its)
     if policy != PL.POLICY_PER_UNIT:
-        q = _plan([37, 120, 5], C=8, X=1, T=4, policy=policy)
+        q = _plan([37, 120, 5], C=8, X=1, T=4, policy=policy, unit_cost=unit_cost)
         ren = {0: 1, 1: 4, 2: 5}
         assert [[(ren[u], t0, t1, s) for (u, t0, t1, s) in its] for its in q["chunk_items"]] == p["chunk_items"]
-    allempty = _plan([0, 0, 0], C=8, X=1, T=4, policy=policy)
+    allempty = _plan([0, 0, 0], C=8, X=1, T=4, policy=policy, unit_cost=unit_cost)
     assert allempty["num_items"] == 0 and allempty["num_tiles"] == 0
     assert allempty["unit_nsplit"] == [0, 0, 0]
