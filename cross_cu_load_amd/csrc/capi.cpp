@@ -285,7 +285,7 @@ int cc_workspace_check(const void* plan_host, const void* workspace, void* strea
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-  std::vector<int32_t> cnt(cc::WorkspaceLayout::counter_words(v));
+  std::vector<int32_t> cnt(cc::WorkspaceLayout::counter_words(v.units()));
   int32_t flags = 0;
   const char* ws = static_cast<const char*>(workspace);
   e = hipMemcpy(&flags, ws, sizeof flags, hipMemcpyDeviceToHost);

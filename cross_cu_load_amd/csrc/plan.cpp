@@ -361,14 +361,21 @@ int plan_matches(const PlanView& v, const cc_problem& p) {
   return CC_OK;
 }
 
-WorkspaceLayout workspace_layout(const PlanView& v) {
+WorkspaceLayout workspace_layout(const PlanView& v, int64_t counter_units) {
   WorkspaceLayout L;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   L.counters_off = 256;  // the error word lives at offset 0
-  L.partials_off = align(L.counters_off + sizeof(int32_t) * L.counter_words(v));
-  const size_t hpu = (size_t)v.header[H_HPU];
-  const size_t o_off = (2 * hpu + 3) & ~size_t(3);  // o starts 16-byte aligned
-  L.slot_floats = (o_off + hpu * (size_t)v.header[H_DV] + 63) & ~size_t(63);
+  if (counter_units < v.units()) counter_units = v.units();
+  L.partials_off = align(L.counters_off + sizeof(int32_t) * L.counter_words(counter_units));
+  const size_t hpu = (size_t)v.header[H_HPU], dv = (size_t)v.header[H_DV];
+  if (v.header[H_MODE] == CC_MODE_GQA) {
+    // fp32 {m[hpu], l[hpu], pad to 4 floats, o[hpu][dv]}: o starts 16-byte aligned
+    const size_t o_off = (2 * hpu + 3) & ~size_t(3);
+    L.slot_floats = (o_off + hpu * dv + 63) & ~size_t(63);
+  } else {
+    // fp32 {m[hpu], l[hpu], r[hpu]}, then o[hpu][dv] as fp16 row / r (the MLA kernels)
+    L.slot_floats = (3 * hpu + (hpu * dv + 1) / 2 + 63) & ~size_t(63);
+  }
   L.total = align(L.partials_off + sizeof(float) * L.slot_floats * (size_t)v.partials());
   return L;
 }

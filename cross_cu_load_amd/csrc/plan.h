@@ -76,11 +76,15 @@ constexpr int kCounterStride = 32;
 // Workspace layout of a plan: error word and counters first, then partials.
 struct WorkspaceLayout {
   size_t counters_off = 0;   // bytes; int32[U][kCounterStride]
-  static size_t counter_words(const PlanView& v) { return kCounterStride * (size_t)v.units(); }
-  size_t partials_off = 0;   // bytes; S slots {m[hpu], l[hpu], pad to 4, o[hpu][dv]}
+  static size_t counter_words(int64_t units) { return kCounterStride * (size_t)units; }
+  size_t partials_off = 0;   // bytes; S slots: GQA fp32 {m[hpu], l[hpu], pad to 4, o[hpu][dv]},
+                             // MLA fp32 {m[hpu], l[hpu], r[hpu]} + fp16 o[hpu][dv]
   size_t slot_floats = 0;    // floats per partial slot
   size_t total = 0;
 };
-WorkspaceLayout workspace_layout(const PlanView& v);
+// counter_units: units the counter area is sized for (>= the plan's units; -1:
+// exactly the plan's), so that a workspace shared by plans of different sizes
+// can keep its counters and its partials apart.
+WorkspaceLayout workspace_layout(const PlanView& v, int64_t counter_units = -1);
 
 }  // namespace cc

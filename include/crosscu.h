@@ -184,9 +184,11 @@ int cc_plan_check(const void* plan, const cc_problem* prob, const int32_t* seqle
 int cc_workspace_size(const void* plan_host, size_t* bytes);
 
 /* Zero a workspace (device, `bytes` long) on `stream` with a fill kernel.
- * Needed once after allocation; every cc_decode leaves the counters zero, so
- * calls ordered on one stream can share a workspace.  Calls that may run
- * concurrently need separate workspaces. */
+ * Needed after allocation and whenever the plan used with the workspace
+ * changes: every cc_decode leaves its plan's counters at zero, so calls with
+ * one plan ordered on one stream can share a workspace, but another plan may
+ * place its counters where the previous one kept partials.  Calls that may
+ * run concurrently need separate workspaces. */
 int cc_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* Synchronous debug check of a workspace after the work on `stream`:

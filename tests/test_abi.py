@@ -61,9 +61,13 @@ def test_plan_bytes_match_reference_on_workload_lengths(lib, name, C, X, T, poli
         assert blob.tobytes() == ref["blob"]
         B.plan_check(blob, prob, sl)
         # workspace: 256 B error word area, 128 B of counter words per unit,
-        # 256-aligned partial slots of
-        # {m[hu], l[hu], pad to 4 floats, o[hu][dv]} rounded up to 64 floats
-        slot = -(-(-(-2 * hu // 4) * 4 + hu * cfg.head_dim_v) // 64) * 64
+        # 256-aligned partial slots of (GQA) fp32 {m[hu], l[hu], pad to 4
+        # floats, o[hu][dv]} or (MLA) fp32 {m, l, r}[hu] + fp16 o[hu][dv],
+        # rounded up to 64 floats
+        if cfg.mode == W.MODE_GQA:
+            slot = -(-(-(-2 * hu // 4) * 4 + hu * cfg.head_dim_v) // 64) * 64
+        else:
+            slot = -(-(3 * hu + hu * cfg.head_dim_v // 2) // 64) * 64
         cnt_end = 256 + 128 * ref["num_units"]
         part = -(-cnt_end // 256) * 256
         want = -(-(part + 4 * slot * ref["num_partials"]) // 256) * 256
