@@ -30,7 +30,7 @@ EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_
            "cc_plan_check",
            "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
            "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_debug_merge_poll_limit", "cc_probe_read",
-           "cc_indexer_scratch_size", "cc_indexer_topk"]
+           "cc_indexer_scratch_size", "cc_indexer_topk", "cc_decode_noalloc"]
 
 
 class IndexerProblem(ctypes.Structure):
@@ -91,6 +91,7 @@ def load() -> ctypes.CDLL:
     dec = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.cc_decode.argtypes = dec
     lib.cc_decode_variant.argtypes = [ctypes.c_int] + dec
+    lib.cc_decode_noalloc.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.cc_debug_timeline.argtypes = [_P, _SZ]
     lib.cc_debug_kernel_events.argtypes = [_P, _P]
     lib.cc_debug_merge_poll_limit.argtypes = [ctypes.c_int]
@@ -291,6 +292,19 @@ def decode(prob: Problem, plan_host: np.ndarray, plan_dev, q, k_cache, v_cache, 
                                  _dp(indices), _dp(out), _dp(lse), _dp(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "cc_decode")
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20     # CC_NOALLOC_WORKSPACE_BYTES
+
+
+def decode_noalloc(prob: Problem, plan_host: np.ndarray, plan_dev, q, k_cache, v_cache, block_table, seqlens,
+                   indices, out, lse, stream=None) -> None:
+    """cc_decode_noalloc on device tensors: the library's own scratch array
+    instead of a workspace (asynchronous on the stream)."""
+    lib = load()
+    _check(lib.cc_decode_noalloc(ctypes.byref(prob), plan_host.ctypes.data_as(_P), _dp(plan_dev), _dp(q),
+                                 _dp(k_cache), _dp(v_cache), _dp(block_table), _dp(seqlens), _dp(indices),
+                                 _dp(out), _dp(lse), _stream(stream)), "cc_decode_noalloc")
 
 
 @dataclass

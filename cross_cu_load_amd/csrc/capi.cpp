@@ -87,7 +87,7 @@ int check_mla(const cc_problem& p, const cc::PlanView& v) {
 int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const void* plan_dev,
                 const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                 const int32_t* seqlens, const int32_t* indices, float* out, float* lse,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream, int64_t counter_units = -1) {
   if (!prob || !plan_host || !plan_dev || !q || !k_cache || !block_table || !seqlens || !out ||
       !lse || !workspace) {
     cc::set_error("null argument");
@@ -102,7 +102,7 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
   if (rc) return rc;
   rc = cc::plan_matches(v, *prob);
   if (rc) return rc;
-  const cc::WorkspaceLayout wl = cc::workspace_layout(v);
+  const cc::WorkspaceLayout wl = cc::workspace_layout(v, counter_units);
   if (workspace_bytes < wl.total) {
     cc::set_error("workspace holds %zu bytes, the plan needs %zu", workspace_bytes, wl.total);
     return CC_ERR_BUFFER;
@@ -198,6 +198,14 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
 }  // namespace
 
 namespace cc {
+int decode_checked(int reduce, const cc_problem* prob, const void* plan_host, const void* plan_dev, const void* q,
+                   const void* k_cache, const void* v_cache, const int32_t* block_table, const int32_t* seqlens,
+                   const int32_t* indices, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream, int64_t counter_units) {
+  return decode_impl(reduce, prob, plan_host, plan_dev, q, k_cache, v_cache, block_table, seqlens, indices, out,
+                     lse, workspace, workspace_bytes, stream, counter_units);
+}
+
 void kernel_events(hipEvent_t* start, hipEvent_t* stop) {
   *start = g_ev_start;
   *stop = g_ev_stop;

@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "../../include/crosscu.h"
+
 namespace cc {
 
 // Everything a decode launch needs, resolved on the host from the problem,
@@ -44,6 +46,14 @@ struct DecodeArgs {
 
 // The debug kernel events set by cc_debug_kernel_events (null when off).
 void kernel_events(hipEvent_t* start, hipEvent_t* stop);
+
+// cc_decode_variant's checks and launches on a given workspace whose counter
+// area is sized for counter_units units (-1: the plan's own count).  The
+// no-allocation entry point passes its scratch array and a fixed capacity.
+int decode_checked(int reduce, const cc_problem* prob, const void* plan_host, const void* plan_dev, const void* q,
+                   const void* k_cache, const void* v_cache, const int32_t* block_table, const int32_t* seqlens,
+                   const int32_t* indices, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream, int64_t counter_units);
 
 // uint64 words per workgroup in the debug timeline
 constexpr int kTimelineWords = 8;

@@ -233,6 +233,37 @@ int cc_decode_variant(int reduce, const cc_problem* prob, const void* plan_host,
                       const int32_t* indices, float* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Bytes of the scratch array cc_decode_noalloc uses on each device (64 MiB:
+ * the workspace of a 256-chunk plan for any of the five benchmark workloads,
+ * up to 40 MiB for 64 DeepSeek-style MLA sequences of up to 16K tokens), and
+ * the most units (query-head groups sharing one K/V stream) a plan may have
+ * there: its first 2 MiB hold that many arrival counters at fixed places, so
+ * the partials of one call never land on the counters of the next. */
+#define CC_NOALLOC_WORKSPACE_BYTES (64u << 20)
+#define CC_NOALLOC_MAX_UNITS 16384
+
+/* cc_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * arguments are cc_decode's without the workspace: its partials, counters and
+ * error word live instead in a library-owned device array of
+ * CC_NOALLOC_WORKSPACE_BYTES, one per GPU, held until the process ends.
+ *  - A plan with more than CC_NOALLOC_MAX_UNITS units, or whose partials do
+ *    not fit beside the counters, returns CC_ERR_BUFFER before any device
+ *    work; other errors as for cc_decode.
+ *  - The call allocates nothing: no hipMalloc or hipFree, no allocating
+ *    library routine.  The first call on a device looks up the array's address
+ *    and enqueues one clear of it on `stream`.
+ *  - Every call on a device shares that device's array, which keeps the last
+ *    call's contents; calls with different plans may follow each other (the
+ *    counters sit at fixed places and the kernels leave them at zero).  Calls
+ *    on one device must be ordered (one stream, or streams ordered by
+ *    events): overlapping calls race.
+ *  - The device error word is not readable through this interface; a plan
+ *    that does not match seqlens still turns the affected outputs into NaN. */
+int cc_decode_noalloc(const cc_problem* prob, const void* plan_host, const void* plan_dev, const void* q,
+                      const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seqlens, const int32_t* indices, float* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
