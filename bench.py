@@ -284,7 +284,7 @@ def cpu_baseline(wl, args, min_seconds=10.0, max_reps=8):
         reps += 1
     total = time.perf_counter() - t0
     dt = total / reps
-    return {"value": wl.kv_bytes() / dt / 1e9, "unit": "GB/s", "cores": int(min(blas, affinity)), "kind": "oracle",
+    return {"value": wl.unique_kv_bytes() / dt / 1e9, "unit": "GB/s", "cores": int(min(blas, affinity)), "kind": "oracle",
             "sample": f"the whole {wl.cfg.name} batch, {reps} times ({total:.1f} s, {dt * 1e6:.0f} us/batch)",
             "us_per_batch": dt * 1e6, "affinity_cores": affinity, "blas_threads": int(blas),
             "cpu_model": cpu_model()}
@@ -312,15 +312,24 @@ def main():
     if cfg.mode == W.MODE_GQA:
         cfg = dataclasses.replace(cfg, kv_layout=W.KV_HND if args.layout == "hnd" else W.KV_NHD)
     wl = W.make_workload(cfg)
-    kv = wl.kv_bytes()
+    shared = wl.prefix_group is not None
+    # algorithmic bytes: every distinct K/V row the batch attends over once (a
+    # shared prefix once per group)
+    kv = wl.unique_kv_bytes()
     prob = B.problem_for(wl)
     log(args, f"workload {cfg.name}: batch {cfg.batch}, sum L {int(wl.seqlens.sum())}, KV {kv / 1e6:.1f} MB, "
               f"CUs {cus}, XCDs {xcds}")
 
     # host plan, timed on its own
+    def make_plan():
+        if shared:
+            return B.plan_prefix(prob, wl.seqlens, wl.prefix_group, wl.prefix_len, wl.block_table, num_cus=cus,
+                                 num_xcds=xcds)
+        return B.plan(prob, wl.seqlens, wl.block_table, num_cus=cus, num_xcds=xcds)
+
     t0 = time.perf_counter()
     for _ in range(20):
-        plan = B.plan(prob, wl.seqlens, wl.block_table, num_cus=cus, num_xcds=xcds)
+        plan = make_plan()
     plan_us = (time.perf_counter() - t0) / 20 * 1e6
     s = B.session(wl, plan)
     scratch = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -370,6 +379,11 @@ def main():
         variants["split_then_combine"] = stats(time_steps(
             torch, lambda: v2.run(B.REDUCE_SPLIT_COMBINE), args.variant_steps, 3, flush, ke))
         del v2
+        if shared:   # the same batch with every sequence reading its own copy of the prefix
+            plain = B.plan(prob, wl.seqlens, wl.block_table, num_cus=cus, num_xcds=xcds)
+            v3 = B.session(wl, plain)
+            variants["no_prefix_sharing"] = stats(time_steps(torch, v3.run, args.variant_steps, 3, flush, ke))
+            del v3
         for k, v in variants.items():
             v["kv_gbs"] = kv / (v["mean_us"] * 1e-6) / 1e9
             log(args, f"{k}: {v}")
@@ -397,6 +411,8 @@ def main():
                    "plan_policy": f"streamk, equal cost chunks: 1 per tile + {int(plan.view(np.int32)[23])} per unit",
                    "kv_layout": layout_name},
         "us_per_batch": st["mean_us"],
+        **({"shared_prefix": {"prefix_len": int(cfg.prefix_len), "prefix_units": int(plan.view(np.int32)[26]),
+                              "unique_kv_bytes": kv, "kv_bytes_without_sharing": wl.kv_bytes()}} if shared else {}),
         "us_per_batch_median": st["median_us"],
         "us_p10_p90": [st["p10_us"], st["p90_us"]],
         "warm_us_median": stats(warm)["median_us"],

@@ -27,7 +27,7 @@ REDUCE_FUSED, REDUCE_SPLIT_COMBINE = 0, 1
 
 # every symbol include/*.h declares
 EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_plan_size", "cc_plan",
-           "cc_plan_check",
+           "cc_plan_check", "cc_plan_prefix_size", "cc_plan_prefix",
            "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
            "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_debug_merge_poll_limit", "cc_probe_read",
            "cc_indexer_scratch_size", "cc_indexer_topk", "cc_decode_noalloc"]
@@ -85,6 +85,10 @@ def load() -> ctypes.CDLL:
                                  ctypes.POINTER(_SZ)]
     lib.cc_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), _I32P, _I32P, _P, _SZ]
     lib.cc_plan_check.argtypes = [_P, ctypes.POINTER(Problem), _I32P]
+    lib.cc_plan_prefix_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), _I32P, _I32P,
+                                        ctypes.c_int32, _I32P, ctypes.POINTER(_SZ)]
+    lib.cc_plan_prefix.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), _I32P, _I32P, _I32P,
+                                   ctypes.c_int32, _I32P, _P, _SZ]
     lib.cc_workspace_size.argtypes = [_P, ctypes.POINTER(_SZ)]
     lib.cc_workspace_init.argtypes = [_P, _SZ, _P]
     lib.cc_workspace_check.argtypes = [_P, _P, _P, _I32P, _I32P]
@@ -174,6 +178,32 @@ def plan(prob: Problem, seqlens, block_table=None, num_cus=256, num_xcds=8, tile
         btp = _ptr_i32(bt)
     _check(lib.cc_plan(ctypes.byref(prob), ctypes.byref(opts), _ptr_i32(sl), btp,
                        buf.ctypes.data_as(_P), buf.nbytes), "cc_plan")
+    return buf
+
+
+def plan_prefix(prob: Problem, seqlens, prefix_group, prefix_len, block_table=None, num_cus=256, num_xcds=8,
+                tile_tokens=32, unit_cost=None) -> np.ndarray:
+    """Shared-prefix plan blob (uint8 array) from cc_plan_prefix_size + cc_plan_prefix."""
+    lib = load()
+    if unit_cost is None:
+        unit_cost = default_unit_cost(prob.mode)
+    G = prob.num_q_heads // max(prob.num_kv_heads, 1)
+    opts = PlanOpts(num_cus, num_xcds, tile_tokens, G, POLICY_STREAMK, unit_cost)
+    sl, grp, ln = _i32(seqlens), _i32(prefix_group), _i32(prefix_len)
+    if sl.shape != (prob.batch,) or grp.shape != (prob.batch,):
+        raise ValueError("seqlens and prefix_group must have shape [batch]")
+    nbytes = _SZ()
+    _check(lib.cc_plan_prefix_size(ctypes.byref(prob), ctypes.byref(opts), _ptr_i32(sl), _ptr_i32(grp),
+                                   len(ln), _ptr_i32(ln), ctypes.byref(nbytes)), "cc_plan_prefix_size")
+    buf = np.zeros(nbytes.value, dtype=np.uint8)
+    btp = None
+    if block_table is not None:
+        bt = _i32(block_table)
+        if bt.shape != (prob.batch, prob.max_pages_per_seq):
+            raise ValueError("block_table must have shape [batch, max_pages_per_seq]")
+        btp = _ptr_i32(bt)
+    _check(lib.cc_plan_prefix(ctypes.byref(prob), ctypes.byref(opts), _ptr_i32(sl), btp, _ptr_i32(grp), len(ln),
+                              _ptr_i32(ln), buf.ctypes.data_as(_P), buf.nbytes), "cc_plan_prefix")
     return buf
 
 

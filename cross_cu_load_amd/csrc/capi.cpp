@@ -156,6 +156,8 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
   a.items = reinterpret_cast<const int4*>(pd + v.off_items);
   a.unit_nsplit = pd + v.off_nsplit;
   a.unit_pbase = pd + v.off_pbase;
+  a.prefix = pd + v.off_prefix;
+  a.prefix_units = v.prefix_units();
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_cache);
   a.v = static_cast<const uint16_t*>(v_cache);

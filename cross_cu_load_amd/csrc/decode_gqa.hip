@@ -68,6 +68,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Marks a value the whole wave agrees on, so it lives in a scalar register and
 // addresses built from it use the scalar-base load forms.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ size_t uni64(size_t x) {
+  return (size_t)(uint32_t)uni((int)(uint32_t)x) | ((size_t)(uint32_t)uni((int)(uint32_t)(x >> 32)) << 32);
+}
 
 // Asynchronous copy global -> LDS: lane i's bytes from sbase + voff land at
 // lds + i * bytes (sbase and lds wave-uniform, voff per lane).  Inline asm on
@@ -140,6 +143,7 @@ struct Params {
   int slot_floats;   // floats per partial slot in the workspace
   int region_bytes;  // LDS bytes per wave (stream slot, later its merge slots)
   int reduce;
+  int units;         // sequence units (b, g); items name shared-prefix unit p as units + p
 };
 
 // wave-uniform position in the chunk
@@ -149,17 +153,30 @@ struct Cursor {
   int nb;     // blocks in the item (from the plan)
   int unit, tb, te, split;
   int lim;    // min(te, seqlens[b]): tokens at or past it are masked
-  bool bad;   // the plan does not match seqlens[b] for this item
+  int bad;    // the plan does not match seqlens[b] for this item (an int: no padding)
   int nsplit; // pieces of the unit across the grid
   int pbase;  // first partial slot of the unit (split units)
+  // shared-prefix plans: the KV head, the sequence whose block-table row is
+  // read, the prefix unit (-1: a sequence's own unit) and its query rows
+  int g, b0, pu, rows;
 };
 
 __device__ __forceinline__ int blocks_of(int tb, int te) { return (te - tb + kBlk - 1) / kBlk; }
 
-template <int D>
+// PREFIX: the plan has shared-prefix units (items with unit >= p.units): a
+// prefix unit gathers the G query heads of up to 16 / G member sequences as
+// its query rows over the prefix they share, and each member counts the
+// prefix unit's pieces as splits of its own (the prefix table row: KV head,
+// members, prefix length, pieces, member ids).  A member's own pieces are
+// then splits too, wherever they sit in a chunk, so a wave that holds a whole
+// piece of a split unit (prefix or own) finishes it itself: each member's
+// output or partial, its arrival, and the merge of a member it completes.  A
+// piece shared by waves goes through the LDS slots like any shared item.
+template <int D, bool PREFIX>
 __global__ void __launch_bounds__(kThreads, 1)
 gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* __restrict__ items,
                   const int32_t* __restrict__ unit_nsplit, const int32_t* __restrict__ unit_pbase,
+                  const int32_t* __restrict__ prefix_tab,
                   const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kc,
                   const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt,
                   const int32_t* __restrict__ seqlens, float* __restrict__ out,
@@ -170,16 +187,20 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   constexpr int W = GE::W;
   using vvec = typename GE::vvec;
   extern __shared__ __attribute__((aligned(16))) char smem[];  // kWaves regions
+  // arrivals one workgroup makes after its stream: one per split item, and
+  // with shared prefixes one per member of each prefix item in the slots
+  // (at most 8 such items of at most 16 members)
+  constexpr int kArrivals = PREFIX ? 2 * kWaves + 8 * kPrefixRows : 2 * kWaves;
   __shared__ int slot_item[2 * kWaves];
   __shared__ int slot_meta[2 * kWaves][4];  // unit, split, nsplit, pbase of the slot's item
-  __shared__ int done_units[2 * kWaves][3];  // units this workgroup completes: {pbase, nsplit, out row}
+  __shared__ int done_units[kArrivals][3];  // units this workgroup completes: {pbase, nsplit, out row}
   __shared__ float slot_w[2 * kWaves][16];    // phase-1 weight of each merge slot, per head
   __shared__ float item_L[2 * kWaves][16];    // phase-1 sum L of each item, per head
   __shared__ float item_M[2 * kWaves][16];    // phase-1 max M of each item, per head
   __shared__ int it_slot[2 * kWaves];         // phase-1 items: first slot,
   __shared__ unsigned it_mask[2 * kWaves];    // the slots holding it,
   __shared__ int num_items;                   // and how many
-  __shared__ int split_list[2 * kWaves][3];   // split items: unit, nsplit, first partial slot
+  __shared__ int split_list[kArrivals][3];    // arrivals: unit, nsplit, first partial slot
   __shared__ int num_split;
   __shared__ int num_done;
 
@@ -187,7 +208,10 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   const int wave = uni(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
   const int G = p.group;
-  const int slot_stride = G * (D + 2);  // floats of one (m, l, o) merge slot
+  // rows of a merge slot: a unit's G heads, or with shared prefixes the up
+  // to 16 query rows of a prefix unit
+  const int SR = PREFIX ? kPrefixRows : G;
+  const int slot_stride = SR * (D + 2);  // floats of one (m, l, o) merge slot
   const int page_mask = (1 << p.log2_page) - 1;
   char* const region = smem + wave * p.region_bytes;
   auto merge_slot = [&](int sl) -> float* {
@@ -224,6 +248,35 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     c.te = uni(t.z);
     c.split = uni(t.w);
     c.nb = blocks_of(c.tb, c.te);
+    if constexpr (PREFIX) {
+      if (c.unit >= p.units) {
+        // a shared-prefix piece: its unit's row of the prefix table.  The
+        // plan must still match the lengths: the prefix's last piece ends at
+        // the prefix, every member holds the prefix, and a member whose last
+        // split this piece is has no tokens past it.
+        c.pu = c.unit - p.units;
+        const int32_t* r = prefix_tab + kPrefixWords * c.pu;
+        c.g = uni(r[0]);
+        const int nmem = uni(r[1]), Lp = uni(r[2]);
+        c.nsplit = uni(r[3]);
+        c.pbase = -1;
+        c.b0 = uni(r[4]);
+        c.rows = nmem * G;
+        c.bad = c.te > Lp || (c.split == c.nsplit - 1 && c.te != Lp);
+        for (int j = 0; j < nmem; ++j) {
+          const int b = uni(r[4 + j]);
+          const int L = uni(seqlens[b]), ns = uni(unit_nsplit[b * p.hkv + c.g]);
+          c.bad = c.bad || L < Lp || (c.split == ns - 1 && L != Lp);
+        }
+        c.lim = min(c.te, Lp);
+        if (c.bad && lane == 0) atomicOr(err, kErrSeqlen);
+        return;
+      }
+      c.pu = -1;
+      c.b0 = c.unit / p.hkv;
+      c.g = c.unit - c.b0 * p.hkv;
+      c.rows = G;
+    }
     c.nsplit = uni(unit_nsplit[c.unit]);
     c.pbase = uni(unit_pbase[c.unit]);
     // a plan built for other lengths: a piece past the sequence end, or the
@@ -247,7 +300,8 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   };
 
   // Every 16-token half of a block lies inside one page (blocks start at
-  // multiples of 32 and pages hold a power of two >= 16 tokens), so a lane's
+  // multiples of 16 — an item starts at a multiple of 32, or of the page size
+  // past a shared prefix — and pages hold a power of two >= 16 tokens), so a lane's
   // offset from the half's first row never changes: only the two half bases,
   // wave-uniform, move from block to block.  A half with no valid token
   // reads half 0 again; rows past the valid length stay inside their page and
@@ -266,14 +320,18 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     const char* v1;
   };
   auto sources = [&](const Cursor& c) {
-    const int b = c.unit / p.hkv;
-    const int g = c.unit - b * p.hkv;
+    // a prefix unit reads its first member's block-table row (every member
+    // names the same prefix pages)
+    const int b = uni(PREFIX ? c.b0 : c.unit / p.hkv);
+    const int g = uni(PREFIX ? c.g : c.unit - b * p.hkv);
     const int32_t* row = bt + (size_t)b * p.max_pages;
     const int tok0 = c.tb + c.j * kBlk;
     const int h1 = (tok0 + 16 < c.lim) ? tok0 + 16 : tok0;
     const size_t go = (size_t)g * p.head_bytes;
-    const size_t o0 = (size_t)page_of(row, tok0) * p.page_bytes + go + (size_t)(tok0 & page_mask) * tstride;
-    const size_t o1 = (size_t)page_of(row, h1) * p.page_bytes + go + (size_t)(h1 & page_mask) * tstride;
+    // wave-uniform by construction; through readfirstlane so that the
+    // transfers' scalar base operands stay scalar whatever the compiler infers
+    const size_t o0 = uni64((size_t)page_of(row, tok0) * p.page_bytes + go + (size_t)(tok0 & page_mask) * tstride);
+    const size_t o1 = uni64((size_t)page_of(row, h1) * p.page_bytes + go + (size_t)(h1 & page_mask) * tstride);
     Src S;
     S.k0 = reinterpret_cast<const char*>(kc) + o0;
     S.k1 = reinterpret_cast<const char*>(kc) + o1;
@@ -323,18 +381,20 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   };
 
   // (m, l, o) of this wave for item `it` into merge slot sl (real heads only).
+  // slot layout: m[SR], l[SR], o[SR][D] (rows past the item's own are not written)
   auto put_slot = [&](int sl, const Cursor& cu, float m, float l, const f32x4* o) {
     float* sb = merge_slot(sl);
-    if (lane < G) {
+    const int rows = PREFIX ? cu.rows : G;
+    if (lane < rows) {
       sb[lane] = m;
-      sb[G + lane] = l;
+      sb[SR + lane] = l;
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int hh = 4 * lg + rr;
-      if (hh < G) {
+      if (hh < rows) {
 #pragma unroll
-        for (int cc = 0; cc < W; ++cc) sb[2 * G + hh * D + W * lr + cc] = o[cc][rr];
+        for (int cc = 0; cc < W; ++cc) sb[2 * SR + hh * D + W * lr + cc] = o[cc][rr];
       }
     }
     if (lane == 0) {
@@ -343,6 +403,80 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       slot_meta[sl][1] = cu.split;
       slot_meta[sl][2] = cu.nsplit;
       slot_meta[sl][3] = cu.pbase;
+    }
+  };
+
+  // A whole piece of a split unit in one wave (with shared prefixes any
+  // piece can be one: a prefix piece, and a sequence's own piece, which the
+  // prefix makes a split, anywhere in a chunk).  Its rows belong to members
+  // j = row / G: the prefix unit's members, or the sequence itself.  Each
+  // member's rows go out as its output when it has no other split, else as
+  // its partial of split cu.split; the wave then arrives for those members
+  // once its stores are complete and merges any member it completes.
+  auto wave_finish = [&](const Cursor& cu, float m, float l, const f32x4* o) {
+    if constexpr (PREFIX) {
+      const bool pre = cu.pu >= 0;
+      const int32_t* r = prefix_tab + kPrefixWords * (pre ? cu.pu : 0);
+      const int nmem = pre ? uni(r[1]) : 1;
+      const int o_off = partial_o_offset(G);
+      unsigned arrive = 0;  // members with a partial (bit j)
+      for (int j = 0; j < nmem; ++j) {
+        const int b = pre ? uni(r[4 + j]) : cu.b0;
+        const int mu = b * p.hkv + cu.g;
+        const int ns = uni(unit_nsplit[mu]);
+        const size_t row0 = (size_t)b * p.hq + (size_t)cu.g * G;  // the member's first output row
+        if (ns == 1) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int hh = 4 * lg + rr;
+            const float inv = 1.f / __shfl(l, hh);
+            if (hh / G == j) {
+              float* op = out + (row0 + hh - j * G) * D + W * lr;
+#pragma unroll
+              for (int c4 = 0; c4 < W; c4 += 4)
+                *reinterpret_cast<f32x4*>(op + c4) = f32x4{o[c4][rr] * inv, o[c4 + 1][rr] * inv,
+                                                           o[c4 + 2][rr] * inv, o[c4 + 3][rr] * inv};
+            }
+          }
+          if (lane < kPrefixRows && lane / G == j) lse[row0 + lane - j * G] = (m + __log2f(l)) * kLn2;
+        } else {
+          float* ps = partials + (size_t)(uni(unit_pbase[mu]) + cu.split) * p.slot_floats;
+          if (lane < kPrefixRows && lane / G == j) {
+            partial_store(ps + lane - j * G, m);
+            partial_store(ps + G + lane - j * G, l);
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int hh = 4 * lg + rr;
+            if (hh / G == j) {
+#pragma unroll
+              for (int cc = 0; cc < W; ++cc) partial_store(ps + o_off + (hh - j * G) * D + W * lr + cc, o[cc][rr]);
+            }
+          }
+          arrive |= 1u << j;
+        }
+      }
+      if (arrive && p.reduce == CC_REDUCE_FUSED) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+        const bool on = lane < nmem && ((arrive >> lane) & 1);
+        int b = 0, mu = 0, ns = 0, old = -1;
+        if (on) {
+          b = pre ? r[4 + lane] : cu.b0;
+          mu = b * p.hkv + cu.g;
+          ns = unit_nsplit[mu];
+          old = atomicAdd(&counters[kCounterStride * mu], 1);
+        }
+        const bool done = on && old == ns - 1;
+        if (done) __hip_atomic_store(&counters[kCounterStride * mu], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (unsigned long long db = __ballot(done); db; db &= db - 1) {
+          const int j = __builtin_ctzll(db);
+          const int bj = __builtin_amdgcn_readlane(b, j), muj = __builtin_amdgcn_readlane(mu, j);
+          const int nsj = __builtin_amdgcn_readlane(ns, j);
+          const float* pb = partials + (size_t)uni(unit_pbase[muj]) * p.slot_floats;
+          merge_unit_direct<64, 4>(pb, nsj, (size_t)bj * p.hq + (size_t)cu.g * G, p.slot_floats, G, D, out, lse,
+                                   lane);
+        }
+      }
     }
   };
 
@@ -361,18 +495,41 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     const int first_it = c.it;
 
     // Q^T operand of a unit: lane holds head lr, dims 32*ks + 8*lg .. +8 (zero rows past G)
-    auto load_q = [&](int unit, u32x4* qd) {
-      const int b = unit / p.hkv, g = unit - (unit / p.hkv) * p.hkv;
-      const uint16_t* qp = qg + ((size_t)b * p.hq + (size_t)g * G + min(lr, G - 1)) * D + lg * 8;
+    // (a prefix unit's row lr is head lr % G of member lr / G)
+    auto load_q = [&](const Cursor& cu, u32x4* qd) {
+      int b, g, hh, rows;
+      if constexpr (PREFIX) {
+        g = cu.g;
+        rows = cu.rows;
+        hh = min(lr, rows - 1);
+        b = cu.b0;
+        if (cu.pu >= 0) {
+          // member ids as scalars, the lane's one picked out by selects
+          const int32_t* r = prefix_tab + kPrefixWords * cu.pu + 4;
+          const int jm = hh / G;
+#pragma unroll
+          for (int j = 1; j < kPrefixRows; ++j) {
+            const int v = uni(r[j]);
+            b = jm == j ? v : b;
+          }
+          hh -= jm * G;
+        }
+      } else {
+        b = cu.unit / p.hkv;
+        g = cu.unit - b * p.hkv;
+        rows = G;
+        hh = min(lr, G - 1);
+      }
+      const uint16_t* qp = qg + ((size_t)b * p.hq + (size_t)g * G + hh) * D + lg * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 t = *reinterpret_cast<const u32x4*>(qp + ks * 32);
-        qd[ks] = lr < G ? t : u32x4{0, 0, 0, 0};
+        qd[ks] = lr < rows ? t : u32x4{0, 0, 0, 0};
       }
     };
 
     u32x4 qv[KS], qn[KS];
-    load_q(c.unit, qv);
+    load_q(c, qv);
     fetch(sources(c));
 
     // the first item's state when it is neither written out nor the last item
@@ -400,7 +557,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
           } else {  // the next block opens the next item: fetch its q as well
             load_item(n, c.it + 1);
             n.j = 0;
-            load_q(n.unit, qn);
+            load_q(n, qn);
           }
           S = sources(n);
         }
@@ -475,7 +632,9 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       float l_tot = l_run + __shfl_xor(l_run, 16);
       l_tot += __shfl_xor(l_tot, 32);
       const bool whole = j0 == 0 && c.j == c.nb - 1;
-      if (whole && c.nsplit == 1) {
+      if (PREFIX && whole && (c.pu >= 0 || c.nsplit > 1)) {
+        wave_finish(c, m_run, l_tot, o);
+      } else if (whole && c.nsplit == 1) {
         const int b = c.unit / p.hkv, g = c.unit - (c.unit / p.hkv) * p.hkv;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -536,7 +695,8 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     }
     const bool first = lane < 2 * kWaves && me >= 0 && !before;
     const int ns = first ? slot_meta[lane][2] : 0;
-    const bool split = ns > 1;
+    // (a prefix item's arrivals are its members', listed below)
+    const bool split = ns > 1 && (!PREFIX || slot_meta[lane][0] < p.units);
     const unsigned long long fb = __ballot(first), sb = __ballot(split);
     const unsigned long long below = (1ull << lane) - 1;
     if (first) {
@@ -550,18 +710,46 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       split_list[k][1] = ns;
       split_list[k][2] = slot_meta[lane][3];
     }
+    int nsp = __popcll(sb);
+    if constexpr (PREFIX) {
+      // each member with other splits arrives once for a prefix item
+      for (unsigned long long pm = __ballot(first && slot_meta[lane][0] >= p.units); pm; pm &= pm - 1) {
+        const int sl = __builtin_ctzll(pm);
+        const int32_t* r = prefix_tab + kPrefixWords * (uni(slot_meta[sl][0]) - p.units);
+        const int g = uni(r[0]), nmem = uni(r[1]);
+        for (int j0 = 0; j0 < nmem; j0 += 64) {
+          const int j = j0 + lane;
+          int mu = 0, ns2 = 0, pb = 0;
+          if (j < nmem) {
+            mu = r[4 + j] * p.hkv + g;
+            ns2 = unit_nsplit[mu];
+            pb = unit_pbase[mu];
+          }
+          const bool add = j < nmem && ns2 > 1;
+          const unsigned long long ab = __ballot(add);
+          if (add) {
+            const int k = nsp + __popcll(ab & below);
+            split_list[k][0] = mu;
+            split_list[k][1] = ns2;
+            split_list[k][2] = pb;
+          }
+          nsp += __popcll(ab);
+        }
+      }
+    }
     if (lane == 0) {
       num_items = __popcll(fb);
-      num_split = __popcll(sb);
+      num_split = nsp;
     }
   }
   __syncthreads();
   if (tl && tid == 0) tl[6] = __builtin_amdgcn_s_memrealtime();
   const int nit = uni(num_items);
   const int GD = G * D;
-  if (tid < nit * G) {
-    // (item, head): all slots' (m, l) loaded together (only the item's count)
-    const int ii = tid / G, hh = tid - (tid / G) * G;
+  const int SD = SR * D;  // elements of a slot's output (rows past an item's own are skipped)
+  if (tid < nit * SR) {
+    // (item, row): all slots' (m, l) loaded together (only the item's count)
+    const int ii = tid / SR, hh = tid - (tid / SR) * SR;
     const unsigned mask = it_mask[ii];
     float mt[2 * kWaves], lt[2 * kWaves];
 #pragma unroll
@@ -569,7 +757,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       const bool on = (mask >> t) & 1;
       const float* sb = merge_slot(t);
       mt[t] = on ? sb[hh] : -INFINITY;
-      lt[t] = on ? sb[G + hh] : 0.f;
+      lt[t] = on ? sb[SR + hh] : 0.f;
     }
     float M = -INFINITY;
 #pragma unroll
@@ -586,19 +774,37 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   }
   __syncthreads();
   if (tl && tid == 0) tl[7] = __builtin_amdgcn_s_memrealtime();
-  for (int idx = tid; idx < nit * GD; idx += kThreads) {
-    const int ii = uni(idx / GD);  // G * D is a multiple of 64: one item per wave and pass
-    const int e = idx - ii * GD, hh = e / D;
+  for (int idx = tid; idx < nit * SD; idx += kThreads) {
+    const int ii = uni(idx / SD);  // SR * D is a multiple of 64: one item per wave and pass
+    const int e = idx - ii * SD, hh = e / D;
     const unsigned mask = uni(it_mask[ii]);
     const int sl0 = uni(it_slot[ii]);
+    const int unit = uni(slot_meta[sl0][0]), split = uni(slot_meta[sl0][1]), ns = uni(slot_meta[sl0][2]);
+    if (PREFIX && hh >= (unit >= p.units ? uni(prefix_tab[kPrefixWords * (unit - p.units) + 1]) * G : G)) continue;
     float O = 0.f;
     for (unsigned mm = mask; mm; mm &= mm - 1) {
       const int t = __builtin_ctz(mm);
-      O += merge_slot(t)[2 * G + e] * slot_w[t][hh];
+      O += merge_slot(t)[2 * SR + e] * slot_w[t][hh];
     }
-    const int unit = uni(slot_meta[sl0][0]), split = uni(slot_meta[sl0][1]), ns = uni(slot_meta[sl0][2]);
     const bool head_lane = e - hh * D == 0;
-    if (ns == 1) {
+    if (PREFIX && unit >= p.units) {
+      // a prefix item: row hh is head hh % G of member hh / G
+      const int32_t* r = prefix_tab + kPrefixWords * (unit - p.units);
+      const int j = hh / G, hr = hh - j * G, col = e - hh * D;
+      const int b = r[4 + j], mu = b * p.hkv + r[0];
+      const size_t row = (size_t)b * p.hq + (size_t)r[0] * G + hr;
+      if (unit_nsplit[mu] == 1) {
+        out[row * D + col] = O / item_L[ii][hh];
+        if (head_lane) lse[row] = (item_M[ii][hh] + __log2f(item_L[ii][hh])) * kLn2;
+      } else {
+        float* pslot = partials + (size_t)(unit_pbase[mu] + split) * p.slot_floats;
+        partial_store(pslot + partial_o_offset(G) + hr * D + col, O);
+        if (head_lane) {
+          partial_store(pslot + hr, item_M[ii][hh]);
+          partial_store(pslot + G + hr, item_L[ii][hh]);
+        }
+      }
+    } else if (ns == 1) {
       out[(size_t)unit * GD + e] = O / item_L[ii][hh];  // row of unit (b, g): b Hq + g G = unit G
       if (head_lane) lse[(size_t)unit * G + hh] = (item_M[ii][hh] + __log2f(item_L[ii][hh])) * kLn2;
     } else {
@@ -619,25 +825,32 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid < 64) {
-      // one lane per split item: all arrivals in one atomic instruction; the
-      // lanes that completed their unit are compacted in split-list order
-      const bool on = lane < num_split;
-      int unit = 0, ns = 0, old = -1;
-      if (on) {
-        unit = split_list[lane][0];
-        ns = split_list[lane][1];
-        old = atomicAdd(&counters[kCounterStride * unit], 1);
+      // one lane per arrival (64 at a time): the arrivals in one atomic
+      // instruction; the lanes that completed their unit are compacted in
+      // list order
+      const int nsp = uni(num_split);
+      int nd = 0;
+      for (int i0a = 0; i0a < nsp; i0a += 64) {
+        const int i = i0a + lane;
+        const bool on = i < nsp;
+        int unit = 0, ns = 0, old = -1;
+        if (on) {
+          unit = split_list[i][0];
+          ns = split_list[i][1];
+          old = atomicAdd(&counters[kCounterStride * unit], 1);
+        }
+        const bool done = on && old == ns - 1;
+        const unsigned long long db = __ballot(done);
+        if (done) {
+          __hip_atomic_store(&counters[kCounterStride * unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int d = nd + __popcll(db & ((1ull << lane) - 1));
+          done_units[d][0] = split_list[i][2];
+          done_units[d][1] = ns;
+          done_units[d][2] = unit * G;  // output row of unit (b, g): b Hq + g G
+        }
+        nd += __popcll(db);
       }
-      const bool done = on && old == ns - 1;
-      const unsigned long long db = __ballot(done);
-      if (done) {
-        __hip_atomic_store(&counters[kCounterStride * unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int d = __popcll(db & ((1ull << lane) - 1));
-        done_units[d][0] = split_list[lane][2];
-        done_units[d][1] = ns;
-        done_units[d][2] = unit * G;  // output row of unit (b, g): b Hq + g G
-      }
-      if (lane == 0) num_done = __popcll(db);
+      if (lane == 0) num_done = nd;
     }
     __syncthreads();
     if (tl && tid == 0) tl[3] = __builtin_amdgcn_s_memrealtime();
@@ -686,6 +899,17 @@ int ilog2(int x) {
 
 using namespace gqa;
 
+template <int D, bool PREFIX>
+hipError_t launch_gqa_kernel(const Params& p, const DecodeArgs& a, size_t lds, hipStream_t s) {
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gqa::gqa_decode_kernel<D, PREFIX>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipExtLaunchKernelGGL(gqa::gqa_decode_kernel<D, PREFIX>, dim3(a.workers), dim3(kThreads), (uint32_t)lds, s,
+                        a.ev_start, a.ev_stop, 0u, p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.prefix, a.q,
+                        a.k, a.v, a.block_table, a.seqlens, a.out, a.lse, a.err, a.counters, a.partials, a.timeline);
+  return hipGetLastError();
+}
+
 hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s) {
   Params p;
   p.hq = a.hq;
@@ -706,27 +930,16 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s) {
   p.scale_log2 = a.scale_log2;
   p.slot_floats = a.slot_floats;
   p.reduce = a.reduce;
+  p.units = a.units;
+  const bool prefix = a.prefix_units > 0;
   const int ring = a.dqk == 128 ? Geo<128>::ring : Geo<64>::ring;
-  const int slots = 2 * p.group * (a.dqk + 2) * (int)sizeof(float);
+  const int slot_rows = prefix ? kPrefixRows : p.group;
+  const int slots = 2 * slot_rows * (a.dqk + 2) * (int)sizeof(float);
   p.region_bytes = ((ring > slots ? ring : slots) + 15) & ~15;
   const size_t lds = (size_t)kWaves * p.region_bytes;
-  hipError_t e;
-  if (a.dqk == 128) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gqa::gqa_decode_kernel<128>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipExtLaunchKernelGGL(gqa::gqa_decode_kernel<128>, dim3(a.workers), dim3(kThreads), (uint32_t)lds, s,
-        a.ev_start, a.ev_stop, 0u, p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
-        a.out, a.lse, a.err, a.counters, a.partials, a.timeline);
-  } else {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gqa::gqa_decode_kernel<64>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipExtLaunchKernelGGL(gqa::gqa_decode_kernel<64>, dim3(a.workers), dim3(kThreads), (uint32_t)lds, s,
-        a.ev_start, a.ev_stop, 0u, p, a.wg_off, a.items, a.unit_nsplit, a.unit_pbase, a.q, a.k, a.v, a.block_table, a.seqlens,
-        a.out, a.lse, a.err, a.counters, a.partials, a.timeline);
-  }
-  return hipGetLastError();
+  if (a.dqk == 128)
+    return prefix ? launch_gqa_kernel<128, true>(p, a, lds, s) : launch_gqa_kernel<128, false>(p, a, lds, s);
+  return prefix ? launch_gqa_kernel<64, true>(p, a, lds, s) : launch_gqa_kernel<64, false>(p, a, lds, s);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {

@@ -21,6 +21,8 @@ struct DecodeArgs {
   const int4* items;  // unit, tok_begin, tok_end, split
   const int32_t* unit_nsplit;
   const int32_t* unit_pbase;
+  const int32_t* prefix;  // shared-prefix table rows (prefix_units of them)
+  int prefix_units;
   // tensors (device)
   const uint16_t* q;
   const uint16_t* k;

@@ -189,48 +189,56 @@ __device__ void merge_splits(const float* pb, int ns, int slot_floats, int hpu, 
 // units[i] = {partial base slot, nsplit, output row}; out/lse rows are
 // dv / 1 floats apart.
 constexpr int kDirectChunk = 32;
-template <int NT>
-__device__ __forceinline__ void merge_units_direct(const float* partials, const int (*units)[3], int nu, int slot_floats, int hpu,
-                                   int dv, float* out, float* lse) {
+// One unit of merge_units_direct: ns splits from partial slot pb on, output
+// rows row0 .. row0 + hpu - 1; thread t of NT; CH splits' loads in flight.
+template <int NT, int CH = kDirectChunk>
+__device__ __forceinline__ void merge_unit_direct(const float* pb, int ns, size_t row0, int slot_floats, int hpu,
+                                                  int dv, float* out, float* lse, int t) {
   constexpr float kLn2 = 0.69314718055994531f;
   const int E = hpu * dv;
   const int o_off = partial_o_offset(hpu);
+  for (int e = t; e < E; e += NT) {
+    const int hh = e / dv, col = e - (e / dv) * dv;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += CH) {
+      float mt[CH], lt[CH], ot[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const bool ok = s0 + i < ns;
+        const float* ps = pb + (size_t)(ok ? s0 + i : 0) * slot_floats;
+        mt[i] = ok ? partial_load(ps + hh) : -INFINITY;
+        lt[i] = ok ? partial_load(ps + hpu + hh) : 0.f;
+        ot[i] = ok ? partial_load(ps + o_off + e) : 0.f;
+      }
+      float Mc = M;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) Mc = fmaxf(Mc, mt[i]);
+      const float a = __builtin_amdgcn_exp2f(M - Mc);  // 0 on the first chunk (M = -inf, Mc finite)
+      L *= a;
+      O *= a;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const float f = __builtin_amdgcn_exp2f(mt[i] - Mc);
+        L += lt[i] * f;
+        O += ot[i] * f;
+      }
+      M = Mc;
+    }
+    const size_t row = row0 + hh;
+    out[row * dv + col] = O / L;
+    if (col == 0) lse[row] = (M + __log2f(L)) * kLn2;
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void merge_units_direct(const float* partials, const int (*units)[3], int nu, int slot_floats, int hpu,
+                                   int dv, float* out, float* lse) {
   for (int u = 0; u < nu; ++u) {
     // unit fields are the same for every thread: split bases stay scalar
     const int ns = __builtin_amdgcn_readfirstlane(units[u][1]);
     const float* pb = partials + (size_t)__builtin_amdgcn_readfirstlane(units[u][0]) * slot_floats;
     const size_t row0 = (size_t)__builtin_amdgcn_readfirstlane(units[u][2]);
-    for (int e = threadIdx.x; e < E; e += NT) {
-      const int hh = e / dv, col = e - (e / dv) * dv;
-      float M = -INFINITY, L = 0.f, O = 0.f;
-      for (int s0 = 0; s0 < ns; s0 += kDirectChunk) {
-        float mt[kDirectChunk], lt[kDirectChunk], ot[kDirectChunk];
-#pragma unroll
-        for (int i = 0; i < kDirectChunk; ++i) {
-          const bool ok = s0 + i < ns;
-          const float* ps = pb + (size_t)(ok ? s0 + i : 0) * slot_floats;
-          mt[i] = ok ? partial_load(ps + hh) : -INFINITY;
-          lt[i] = ok ? partial_load(ps + hpu + hh) : 0.f;
-          ot[i] = ok ? partial_load(ps + o_off + e) : 0.f;
-        }
-        float Mc = M;
-#pragma unroll
-        for (int i = 0; i < kDirectChunk; ++i) Mc = fmaxf(Mc, mt[i]);
-        const float a = __builtin_amdgcn_exp2f(M - Mc);  // 0 on the first chunk (M = -inf, Mc finite)
-        L *= a;
-        O *= a;
-#pragma unroll
-        for (int i = 0; i < kDirectChunk; ++i) {
-          const float f = __builtin_amdgcn_exp2f(mt[i] - Mc);
-          L += lt[i] * f;
-          O += ot[i] * f;
-        }
-        M = Mc;
-      }
-      const size_t row = row0 + hh;
-      out[row * dv + col] = O / L;
-      if (col == 0) lse[row] = (M + __log2f(L)) * kLn2;
-    }
+    merge_unit_direct<NT>(pb, ns, row0, slot_floats, hpu, dv, out, lse, threadIdx.x);
   }
 }
 

@@ -6,6 +6,7 @@
 // (GLM-5.2 decode article, MegaRTP design: host-built per-worker queues).
 //
 // Plain C++17 with no HIP dependency.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -103,73 +104,62 @@ struct Built {
   std::vector<int32_t> words;
 };
 
-// The whole plan as int32 words.  Returns CC_OK or an error code.
-int build(const Inputs& in, Built* out) {
-  int rc = validate(in);
-  if (rc) return rc;
-  const cc_problem& p = *in.p;
-  const cc_plan_opts& o = *in.o;
-  const int64_t G = p.num_q_heads / p.num_kv_heads;
-  const int64_t blocks_per_kv = G / o.heads_per_unit;
-  const int64_t units_per_seq = (int64_t)p.q_tokens * p.num_kv_heads * blocks_per_kv;
-  const int64_t U = units_per_seq * p.batch;
-  const int64_t T = o.tile_tokens;
+// Shared-prefix inputs of cc_plan_prefix (absent for cc_plan).
+struct PrefixInputs {
+  const int32_t* group;  // [batch]: -1 or a group id in [0, num_groups)
+  int32_t num_groups;
+  const int32_t* len;    // [num_groups]: prefix tokens, whole pages
+};
 
-  // unit u belongs to sequence u / units_per_seq
-  auto unit_len = [&](int64_t u) -> int64_t {
-    return p.mode == CC_MODE_MLA_SPARSE ? p.topk : in.seqlens[u / units_per_seq];
-  };
-  std::vector<int64_t> first(U + 1, 0);
-  for (int64_t u = 0; u < U; ++u) first[u + 1] = first[u] + ceil_div(unit_len(u), T);
-  const int64_t N = first[U];
-  const int64_t C = o.policy == CC_POLICY_PER_UNIT ? U : o.num_cus;
+// The split cuts a list of work entries in order: a unit id and the token
+// range [t0, t0 + len) of it that the entry covers.
+struct Work { int64_t unit, t0, len; };
+// A piece: work entry w, tokens [a, e) relative to the entry's t0.
+struct Piece { int64_t w, a, e; };
+struct Item { int64_t u, t0, t1, s; };
 
-  // pieces per logical chunk, as (unit, tok_begin, tok_end)
-  struct Piece { int64_t u, t0, t1; };
+// Pieces per chunk of the equal split of cost: one per tile plus O per
+// non-empty entry, each entry's cost first; a tile goes to the chunk whose
+// cost range holds its starting position (with O = 0, the equal tile split).
+std::vector<std::vector<Piece>> split_chunks(const std::vector<Work>& work, int64_t C, int64_t T, int64_t O) {
   std::vector<std::vector<Piece>> chunks(C);
-  // an empty unit (a sequence with no cached tokens) gets no piece and costs
-  // nothing; cc_decode writes its output directly
-  if (o.policy == CC_POLICY_PER_UNIT) {
-    for (int64_t u = 0; u < U; ++u)
-      if (unit_len(u) > 0) chunks[u].push_back({u, 0, unit_len(u)});
-  } else {
-    // equal split of the cost: one per tile plus unit_cost per non-empty unit,
-    // the unit's cost first; a tile goes to the chunk whose cost range holds
-    // its starting position (with unit_cost 0, the equal tile split)
-    const int64_t O = o.unit_cost;
-    int64_t busy_units = 0;
-    for (int64_t u = 0; u < U; ++u) busy_units += first[u + 1] > first[u];
-    const int64_t total = O * busy_units + N;
-    const int64_t q = total / C, r = total % C;
-    auto bound = [&](int64_t k) { return k * q + (k < r ? k : r); };  // chunk k: [bound(k), bound(k+1))
-    int64_t cs = 0, k = 0;
-    for (int64_t u = 0; u < U; ++u) {
-      const int64_t n = first[u + 1] - first[u], L = unit_len(u);
-      if (n == 0) continue;
-      for (int64_t i = 0; i < n;) {
-        while (bound(k + 1) <= cs + O + i) ++k;
-        int64_t last = bound(k + 1) - cs - O;  // tiles of u starting before chunk k ends
-        if (last > n) last = n;
-        chunks[k].push_back({u, i * T, last * T < L ? last * T : L});
-        i = last;
-      }
-      cs += O + n;
-    }
+  int64_t busy = 0, N = 0;
+  for (const Work& x : work) {
+    const int64_t n = ceil_div(x.len, T);
+    N += n;
+    busy += n > 0;
   }
+  const int64_t total = O * busy + N;
+  const int64_t q = total / C, r = total % C;
+  auto bound = [&](int64_t k) { return k * q + (k < r ? k : r); };  // chunk k: [bound(k), bound(k+1))
+  int64_t cs = 0, k = 0;
+  for (int64_t w = 0; w < (int64_t)work.size(); ++w) {
+    const int64_t n = ceil_div(work[w].len, T), L = work[w].len;
+    if (n == 0) continue;  // an empty entry gets no piece and costs nothing
+    for (int64_t i = 0; i < n;) {
+      while (bound(k + 1) <= cs + O + i) ++k;
+      int64_t last = bound(k + 1) - cs - O;  // tiles of w starting before chunk k ends
+      if (last > n) last = n;
+      chunks[k].push_back({w, i * T, last * T < L ? last * T : L});
+      i = last;
+    }
+    cs += O + n;
+  }
+  return chunks;
+}
 
-  // split indices in chunk order, partial slots for split units
-  std::vector<int64_t> nsplit(U, 0);
-  struct Item { int64_t u, t0, t1, s; };
-  std::vector<std::vector<Item>> items(C);
-  for (int64_t k = 0; k < C; ++k)
-    for (const Piece& pc : chunks[k]) items[k].push_back({pc.u, pc.t0, pc.t1, nsplit[pc.u]++});
+// The blob: header, wg_off (padded), items in worker order, unit_nsplit,
+// unit_pbase, prefix table rows.  items[k] are logical chunk k's items.
+int serialise(const cc_problem& p, const cc_plan_opts& o, const int32_t* seqlens, int64_t C, int64_t U,
+              int64_t N, int64_t hpu, const std::vector<std::vector<Item>>& items,
+              const std::vector<int64_t>& nsplit, const std::vector<int32_t>& prefix_rows, Built* out) {
   std::vector<int64_t> pbase(U, -1);
-  int64_t S = 0, maxsplit = 0;
+  int64_t S = 0, maxsplit = 0, empty = 0;
   for (int64_t u = 0; u < U; ++u) {
     if (nsplit[u] > 1) { pbase[u] = S; S += nsplit[u]; }
     if (nsplit[u] > maxsplit) maxsplit = nsplit[u];
+    empty += nsplit[u] == 0;
   }
-
   // worker of each logical chunk: consecutive chunks share an XCD
   std::vector<int64_t> chunk_of_worker(C);
   const int64_t X = o.num_xcds;
@@ -178,10 +168,10 @@ int build(const Inputs& in, Built* out) {
     const int64_t w = spread ? (k % (C / X)) * X + k / (C / X) : k;
     chunk_of_worker[w] = k;
   }
-
   int64_t W = 0;
   for (int64_t k = 0; k < C; ++k) W += (int64_t)items[k].size();
-  const int64_t total = kHeaderWords + wg_words(C) + kItemWords * W + 2 * U;
+  const int64_t P = (int64_t)prefix_rows.size() / kPrefixWords;
+  const int64_t total = kHeaderWords + wg_words(C) + kItemWords * W + 2 * U + (int64_t)prefix_rows.size();
   for (int64_t x : {N, C, W, U, S, total}) {
     if (x > INT32_MAX) {
       set_error("plan too large for int32 fields");
@@ -205,7 +195,7 @@ int build(const Inputs& in, Built* out) {
   h[H_WORKERS] = (int32_t)C;
   h[H_XCDS] = o.num_xcds;
   h[H_TILE] = o.tile_tokens;
-  h[H_HPU] = o.heads_per_unit;
+  h[H_HPU] = (int32_t)hpu;
   h[H_UNITS] = (int32_t)U;
   h[H_TILES] = (int32_t)N;
   h[H_ITEMS] = (int32_t)W;
@@ -215,10 +205,9 @@ int build(const Inputs& in, Built* out) {
   h[H_MAXPAGES] = p.max_pages_per_seq;
   h[H_NUMPAGES] = p.num_pages;
   h[H_UNIT_COST] = o.policy == CC_POLICY_STREAMK ? o.unit_cost : 0;
-  int64_t empty = 0;
-  for (int64_t u = 0; u < U; ++u) empty += nsplit[u] == 0;
   h[H_EMPTY] = (int32_t)empty;
-  h[H_HASH] = input_hash(p, in.seqlens);
+  h[H_HASH] = input_hash(p, seqlens);
+  h[H_PREFIX] = (int32_t)P;
   int32_t* wg = h + kHeaderWords;
   int32_t* it = wg + wg_words(C);
   int64_t n = 0;
@@ -239,7 +228,180 @@ int build(const Inputs& in, Built* out) {
     ns[u] = (int32_t)nsplit[u];
     pb[u] = (int32_t)pbase[u];
   }
+  std::copy(prefix_rows.begin(), prefix_rows.end(), pb + U);
   return CC_OK;
+}
+
+// The whole plan as int32 words.  Returns CC_OK or an error code.
+int build(const Inputs& in, Built* out) {
+  int rc = validate(in);
+  if (rc) return rc;
+  const cc_problem& p = *in.p;
+  const cc_plan_opts& o = *in.o;
+  const int64_t G = p.num_q_heads / p.num_kv_heads;
+  const int64_t blocks_per_kv = G / o.heads_per_unit;
+  const int64_t units_per_seq = (int64_t)p.q_tokens * p.num_kv_heads * blocks_per_kv;
+  const int64_t U = units_per_seq * p.batch;
+  const int64_t T = o.tile_tokens;
+
+  // unit u belongs to sequence u / units_per_seq
+  std::vector<Work> work(U);
+  int64_t N = 0;
+  for (int64_t u = 0; u < U; ++u) {
+    work[u] = {u, 0, p.mode == CC_MODE_MLA_SPARSE ? p.topk : in.seqlens[u / units_per_seq]};
+    N += ceil_div(work[u].len, T);
+  }
+  const int64_t C = o.policy == CC_POLICY_PER_UNIT ? U : o.num_cus;
+  std::vector<std::vector<Piece>> chunks;
+  if (o.policy == CC_POLICY_PER_UNIT) {
+    chunks.resize(C);
+    for (int64_t u = 0; u < U; ++u)
+      if (work[u].len > 0) chunks[u].push_back({u, 0, work[u].len});
+  } else {
+    chunks = split_chunks(work, C, T, o.unit_cost);
+  }
+  // split indices in chunk order
+  std::vector<int64_t> nsplit(U, 0);
+  std::vector<std::vector<Item>> items(C);
+  for (int64_t k = 0; k < C; ++k)
+    for (const Piece& pc : chunks[k]) items[k].push_back({pc.w, pc.a, pc.e, nsplit[pc.w]++});
+  return serialise(p, o, in.seqlens, C, U, N, o.heads_per_unit, items, nsplit, {}, out);
+}
+
+// Shared-prefix inputs: group ids in range, prefixes of whole pages, members
+// at least as long as their prefix and (with a block table) holding the same
+// prefix pages.
+int validate_prefix(const Inputs& in, const PrefixInputs& pre) {
+  const cc_problem& p = *in.p;
+  const cc_plan_opts& o = *in.o;
+  if (p.mode != CC_MODE_GQA || p.q_tokens != 1) {
+    set_error("shared prefixes: GQA decode with one query token");
+    return CC_ERR_INVALID;
+  }
+  if (o.policy != CC_POLICY_STREAMK) {
+    set_error("shared prefixes: policy must be CC_POLICY_STREAMK");
+    return CC_ERR_INVALID;
+  }
+  const int32_t G = p.num_q_heads / p.num_kv_heads;
+  if (kPrefixRows % G || o.heads_per_unit != G) {
+    set_error("shared prefixes: the group size %d must divide 16 and heads_per_unit equal it", G);
+    return CC_ERR_INVALID;
+  }
+  if (pre.num_groups < 0 || !pre.group || (pre.num_groups > 0 && !pre.len)) {
+    set_error("shared prefixes: null group ids or lengths");
+    return CC_ERR_INVALID;
+  }
+  for (int32_t g = 0; g < pre.num_groups; ++g) {
+    if (pre.len[g] < 0 || pre.len[g] % p.page_size) {
+      set_error("prefix_len[%d] = %d is not a whole number of %d-token pages", g, pre.len[g], p.page_size);
+      return CC_ERR_INVALID;
+    }
+  }
+  std::vector<int32_t> first(pre.num_groups, -1);  // first member of each group
+  for (int32_t b = 0; b < p.batch; ++b) {
+    const int32_t g = pre.group[b];
+    if (g == -1) continue;
+    if (g < 0 || g >= pre.num_groups) {
+      set_error("prefix_group[%d] = %d outside [-1, %d)", b, g, pre.num_groups);
+      return CC_ERR_INVALID;
+    }
+    const int32_t Lp = pre.len[g];
+    if (in.seqlens[b] < Lp) {
+      set_error("sequence %d (length %d) is shorter than its group's prefix of %d", b, in.seqlens[b], Lp);
+      return CC_ERR_INVALID;
+    }
+    if (in.block_table && Lp > 0) {
+      if (first[g] < 0) {
+        first[g] = b;
+      } else {
+        const int32_t* r0 = in.block_table + (int64_t)first[g] * p.max_pages_per_seq;
+        const int32_t* r1 = in.block_table + (int64_t)b * p.max_pages_per_seq;
+        for (int32_t i = 0; i < Lp / p.page_size; ++i) {
+          if (r0[i] != r1[i]) {
+            set_error("sequences %d and %d share prefix group %d but not its page %d", first[g], b, g, i);
+            return CC_ERR_INVALID;
+          }
+        }
+      }
+    }
+  }
+  return CC_OK;
+}
+
+// A shared-prefix plan: prefix units (group, KV head, block of 16 / G
+// members) over [0, prefix_len), then every sequence's own units over
+// [prefix_len_b, L_b); a member's splits are its prefix unit's pieces, then
+// its own.
+int build_prefix(const Inputs& in, const PrefixInputs& pre, Built* out) {
+  int rc = validate(in);
+  if (rc) return rc;
+  rc = validate_prefix(in, pre);
+  if (rc) return rc;
+  const cc_problem& p = *in.p;
+  const cc_plan_opts& o = *in.o;
+  const int64_t G = p.num_q_heads / p.num_kv_heads, Hkv = p.num_kv_heads, Mp = kPrefixRows / G;
+  const int64_t U = (int64_t)p.batch * Hkv, T = o.tile_tokens, C = o.num_cus;
+
+  std::vector<int64_t> lp_of(p.batch, 0);
+  std::vector<int32_t> rows;                  // prefix table
+  std::vector<int64_t> prefix_of(U, -1);      // member unit -> prefix unit
+  std::vector<int64_t> members;
+  for (int32_t g = 0; g < pre.num_groups; ++g) {
+    members.clear();
+    for (int32_t b = 0; b < p.batch; ++b)
+      if (pre.group[b] == g) members.push_back(b);
+    const int32_t Lp = pre.len[g];
+    if (Lp == 0 || members.empty()) continue;
+    for (int64_t b : members) lp_of[b] = Lp;
+    for (int64_t h = 0; h < Hkv; ++h) {
+      for (size_t i = 0; i < members.size(); i += Mp) {
+        const int64_t pu = (int64_t)rows.size() / kPrefixWords;
+        const size_t n = std::min<size_t>(Mp, members.size() - i);
+        rows.push_back((int32_t)h);
+        rows.push_back((int32_t)n);
+        rows.push_back(Lp);
+        rows.push_back(0);  // pieces, filled below
+        for (size_t j = 0; j < (size_t)kPrefixRows; ++j) {
+          const int32_t b = j < n ? (int32_t)members[i + j] : -1;
+          rows.push_back(b);
+          if (b >= 0) prefix_of[b * Hkv + h] = pu;
+        }
+      }
+    }
+  }
+  const int64_t P = (int64_t)rows.size() / kPrefixWords;
+  // work list in split order: every prefix unit, then the sequences' own units
+  std::vector<Work> work;
+  work.reserve(P + U);
+  int64_t N = 0;
+  for (int64_t pu = 0; pu < P; ++pu) work.push_back({U + pu, 0, rows[pu * kPrefixWords + 2]});
+  for (int64_t b = 0; b < p.batch; ++b)
+    for (int64_t h = 0; h < Hkv; ++h) work.push_back({b * Hkv + h, lp_of[b], in.seqlens[b] - lp_of[b]});
+  for (const Work& x : work) N += ceil_div(x.len, T);
+  const std::vector<std::vector<Piece>> chunks = split_chunks(work, C, T, o.unit_cost);
+
+  std::vector<int64_t> pieces(P, 0);
+  for (const auto& ch : chunks)
+    for (const Piece& pc : ch)
+      if (work[pc.w].unit >= U) ++pieces[work[pc.w].unit - U];
+  std::vector<int64_t> own(U, 0), seen(P, 0);
+  std::vector<std::vector<Item>> items(C);
+  for (int64_t k = 0; k < C; ++k) {
+    for (const Piece& pc : chunks[k]) {
+      const Work& x = work[pc.w];
+      int64_t s;
+      if (x.unit >= U) {
+        s = seen[x.unit - U]++;
+      } else {
+        s = (prefix_of[x.unit] >= 0 ? pieces[prefix_of[x.unit]] : 0) + own[x.unit]++;
+      }
+      items[k].push_back({x.unit, x.t0 + pc.a, x.t0 + pc.e, s});
+    }
+  }
+  std::vector<int64_t> nsplit(U);
+  for (int64_t u = 0; u < U; ++u) nsplit[u] = own[u] + (prefix_of[u] >= 0 ? pieces[prefix_of[u]] : 0);
+  for (int64_t pu = 0; pu < P; ++pu) rows[pu * kPrefixWords + 3] = (int32_t)pieces[pu];
+  return serialise(p, o, in.seqlens, C, U, N, G, items, nsplit, rows, out);
 }
 
 int check_args(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens) {
@@ -289,7 +451,14 @@ int parse_plan(const void* blob, PlanView* v) {
   v->items = h + v->off_items;
   v->unit_nsplit = h + v->off_nsplit;
   v->unit_pbase = h + v->off_pbase;
-  v->bytes = (v->off_pbase + U) * sizeof(int32_t);
+  const int64_t P = h[H_PREFIX];
+  if (P < 0 || (P > 0 && (h[H_MODE] != CC_MODE_GQA || hpu < 1 || kPrefixRows % hpu))) {
+    set_error("corrupt plan header (prefix units)");
+    return CC_ERR_PLAN;
+  }
+  v->off_prefix = v->off_pbase + U;
+  v->prefix = h + v->off_prefix;
+  v->bytes = (v->off_prefix + kPrefixWords * P) * sizeof(int32_t);
   if (v->wg_off[0] != 0 || v->wg_off[C] != W) {
     set_error("corrupt plan offsets");
     return CC_ERR_PLAN;
@@ -316,6 +485,22 @@ int parse_plan(const void* blob, PlanView* v) {
     set_error("plan unit table disagrees with its header");
     return CC_ERR_PLAN;
   }
+  // prefix table: KV head, 1 .. 16 / hpu members (sequences), a prefix of
+  // whole pages, at least one piece; every member's unit counts the pieces
+  const int64_t B = h[H_BATCH], Hkv = h[H_HKV];
+  for (int64_t pu = 0; pu < P; ++pu) {
+    const int32_t* r = v->prefix + kPrefixWords * pu;
+    bool ok = r[0] >= 0 && r[0] < Hkv && r[1] >= 1 && r[1] <= kPrefixRows / hpu && r[2] > 0 &&
+              r[2] % h[H_PAGE] == 0 && r[3] >= 1;
+    for (int32_t j = 0; ok && j < kPrefixRows; ++j) {
+      const int64_t b = r[4 + j];
+      ok = j < r[1] ? (b >= 0 && b < B && v->unit_nsplit[b * Hkv + r[0]] >= r[3]) : b == -1;
+    }
+    if (!ok) {
+      set_error("plan prefix unit %lld is malformed", (long long)pu);
+      return CC_ERR_PLAN;
+    }
+  }
   // items: unit in range, a non-empty tile-aligned token range inside the
   // unit's key set, a split index below the unit's piece count
   const bool sparse = h[H_MODE] == CC_MODE_MLA_SPARSE;
@@ -323,8 +508,11 @@ int parse_plan(const void* blob, PlanView* v) {
   for (int64_t i = 0; i < W; ++i) {
     const int32_t* it = v->items + kItemWords * i;
     const int64_t u = it[0], tb = it[1], te = it[2], s = it[3];
-    if (u < 0 || u >= U || tb < 0 || tb % T || te <= tb || te > tmax || s < 0 ||
-        s >= v->unit_nsplit[u]) {
+    const bool pre = u >= U && u < U + P;
+    const int64_t end = pre ? v->prefix[kPrefixWords * (u - U) + 2] : tmax;
+    const int64_t ns = pre ? v->prefix[kPrefixWords * (u - U) + 3] : (u >= 0 && u < U ? v->unit_nsplit[u] : 0);
+    if (u < 0 || u >= U + P || tb < 0 || (pre ? tb % T : (tb % T && tb % h[H_PAGE])) || te <= tb || te > end ||
+        s < 0 || s >= ns) {
       set_error("plan item %lld (unit %lld, tokens [%lld, %lld), split %lld) out of range", (long long)i,
                 (long long)u, (long long)tb, (long long)te, (long long)s);
       return CC_ERR_PLAN;
@@ -409,6 +597,43 @@ int cc_plan(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seq
   }
   cc::Built b;
   rc = cc::build({prob, opts, seqlens, block_table}, &b);
+  if (rc) return rc;
+  const size_t need = b.words.size() * sizeof(int32_t);
+  if (bytes < need) {
+    cc::set_error("plan buffer holds %zu bytes, needs %zu", bytes, need);
+    return CC_ERR_BUFFER;
+  }
+  std::memcpy(plan, b.words.data(), need);
+  return CC_OK;
+}
+
+int cc_plan_prefix_size(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
+                        const int32_t* prefix_group, int32_t num_groups, const int32_t* prefix_len,
+                        size_t* bytes) {
+  int rc = cc::check_args(prob, opts, seqlens);
+  if (rc) return rc;
+  if (!bytes) {
+    cc::set_error("null bytes");
+    return CC_ERR_INVALID;
+  }
+  cc::Built b;
+  rc = cc::build_prefix({prob, opts, seqlens, nullptr}, {prefix_group, num_groups, prefix_len}, &b);
+  if (rc) return rc;
+  *bytes = b.words.size() * sizeof(int32_t);
+  return CC_OK;
+}
+
+int cc_plan_prefix(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
+                   const int32_t* block_table, const int32_t* prefix_group, int32_t num_groups,
+                   const int32_t* prefix_len, void* plan, size_t bytes) {
+  int rc = cc::check_args(prob, opts, seqlens);
+  if (rc) return rc;
+  if (!plan) {
+    cc::set_error("null plan buffer");
+    return CC_ERR_INVALID;
+  }
+  cc::Built b;
+  rc = cc::build_prefix({prob, opts, seqlens, block_table}, {prefix_group, num_groups, prefix_len}, &b);
   if (rc) return rc;
   const size_t need = b.words.size() * sizeof(int32_t);
   if (bytes < need) {

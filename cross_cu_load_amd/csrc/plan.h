@@ -9,6 +9,10 @@
 //                        within its unit, in token order)
 //   unit_nsplit[U]       pieces of each unit
 //   unit_pbase[U]        first partial slot of a split unit, -1 if unsplit
+//   prefix[P][20]        shared-prefix units (cc_plan_prefix): KV head, number
+//                        of members, prefix length, number of pieces, member
+//                        sequence ids (-1 padded to 16); items name prefix
+//                        unit p as unit U + p
 #pragma once
 
 #include <cstddef>
@@ -22,6 +26,8 @@ constexpr int32_t kPlanMagic = 0x4C504343;  // "CCPL"
 constexpr int32_t kPlanVersion = 3;
 constexpr int kHeaderWords = 32;
 constexpr int kItemWords = 4;
+constexpr int kPrefixWords = 20;
+constexpr int kPrefixRows = 16;  // query rows a prefix unit gathers (members x group size)
 
 enum HeaderField {
   H_MAGIC = 0, H_VERSION, H_MODE, H_BATCH, H_QTOKENS, H_HQ, H_HKV, H_DQK, H_DV, H_PAGE, H_TOPK,
@@ -29,7 +35,8 @@ enum HeaderField {
   H_MAXPAGES, H_NUMPAGES,
   H_UNIT_COST,  // per-unit cost (tiles) of CC_POLICY_STREAMK, else 0
   H_EMPTY,      // units with no piece (sequences with no cached tokens)
-  H_HASH        // FNV-1a of the problem's int32 fields and seqlens (input_hash)
+  H_HASH,       // FNV-1a of the problem's int32 fields and seqlens (input_hash)
+  H_PREFIX      // shared-prefix units (rows of the prefix table)
 };
 
 struct PlanView {
@@ -38,14 +45,16 @@ struct PlanView {
   const int32_t* items = nullptr;
   const int32_t* unit_nsplit = nullptr;
   const int32_t* unit_pbase = nullptr;
+  const int32_t* prefix = nullptr;
   size_t bytes = 0;
   // word offsets of the arrays inside the blob (valid for a device copy too)
-  size_t off_wg = 0, off_items = 0, off_nsplit = 0, off_pbase = 0;
+  size_t off_wg = 0, off_items = 0, off_nsplit = 0, off_pbase = 0, off_prefix = 0;
 
   int32_t workers() const { return header[H_WORKERS]; }
   int32_t units() const { return header[H_UNITS]; }
   int32_t num_items() const { return header[H_ITEMS]; }
   int32_t partials() const { return header[H_PARTIALS]; }
+  int32_t prefix_units() const { return header[H_PREFIX]; }
 };
 
 // Parses and checks a host blob: header, worker offsets ascending, every

@@ -57,6 +57,7 @@ class Config:
     long_len: int = 0           # skewed: the one long sequence
     short_len: int = 0          # skewed: all the others
     topk: int = 0               # sparse: distinct indices per query token
+    prefix_len: int = 0         # shared_prefix: tokens every sequence of the batch shares
     shuffle_pages: bool = True
     seed: int = 0
     kv_layout: int = KV_NHD
@@ -84,7 +85,16 @@ CONFIGS: list[Config] = [
            head_dim_qk=576, head_dim_v=512, page_size=64, softmax_scale=1 / math.sqrt(192),
            seqlen_kind="fixed", seqlen_lo=8192, topk=2048, seed=1005),
 ]
-CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+# Shared-prefix decode (the workload shape of the MeldKernel summary's
+# shared-prefix experiment, Fig. 11, whose sizes the page does not give): the
+# Llama-3-8B-shaped heads over 64 sequences that all begin with the same
+# 4096-token prefix (one set of pages named by every block-table row),
+# followed by their own log-uniform [64, 4096]-token suffixes.
+SHARED_PREFIX = Config("shared_prefix_gqa", MODE_GQA, batch=64, q_tokens=1, num_q_heads=32, num_kv_heads=8,
+                       head_dim_qk=128, head_dim_v=128, page_size=16, softmax_scale=1 / math.sqrt(128),
+                       seqlen_kind="shared_prefix", seqlen_lo=64, seqlen_hi=4096, prefix_len=4096, seed=1006)
+EXTRA_CONFIGS: list[Config] = [SHARED_PREFIX]
+CONFIG_BY_NAME = {c.name: c for c in CONFIGS + EXTRA_CONFIGS}
 
 
 @dataclasses.dataclass
@@ -98,6 +108,8 @@ class Workload:
     k_cache: np.ndarray        # uint16 [num_pages, P, Hkv, dk] (NHD) or [num_pages, Hkv, P, dk] (HND)
     v_cache: np.ndarray | None  # uint16, as k_cache with dv; None for MLA
     indices: np.ndarray | None  # int32 [B, Tq, topk]; sparse mode only
+    prefix_group: np.ndarray | None = None  # int32 [B]: shared-prefix group of each sequence (-1: none)
+    prefix_len: np.ndarray | None = None    # int32 [groups]: tokens each group shares
 
     @property
     def kv_layout(self) -> int:
@@ -110,6 +122,20 @@ class Workload:
     @property
     def max_pages(self) -> int:
         return int(self.block_table.shape[1])
+
+    def unique_kv_bytes(self) -> int:
+        """Bytes of the distinct K/V rows the batch attends over: a shared
+        prefix counted once per group (equal to kv_bytes without one)."""
+        if self.prefix_group is None:
+            return self.kv_bytes()
+        c = self.cfg
+        per_tok = c.num_kv_heads * (c.head_dim_qk + c.head_dim_v) * 2
+        toks = int(self.seqlens.astype(np.int64).sum())
+        for g, Lp in enumerate(self.prefix_len):
+            n = int((self.prefix_group == g).sum())
+            if n:
+                toks -= (n - 1) * int(Lp)
+        return toks * per_tok
 
     def kv_bytes(self) -> int:
         """Bytes of K/V the attention must read (each used row once)."""
@@ -174,6 +200,9 @@ def draw_seqlens(cfg: Config) -> np.ndarray:
         s[0] = cfg.long_len
     elif cfg.seqlen_kind == "fixed":
         s = np.full(b, cfg.seqlen_lo)
+    elif cfg.seqlen_kind == "shared_prefix":  # the prefix, then a log-uniform suffix
+        u = g.uniform(math.log(cfg.seqlen_lo), math.log(cfg.seqlen_hi), size=b)
+        s = cfg.prefix_len + np.clip(np.rint(np.exp(u)), cfg.seqlen_lo, cfg.seqlen_hi)
     else:
         raise ValueError(cfg.seqlen_kind)
     return s.astype(np.int32)
@@ -200,13 +229,77 @@ def page_table(seqlens: np.ndarray, page_size: int, shuffle: bool, seed: int) ->
     return bt
 
 
+def shared_page_table(seqlens: np.ndarray, page_size: int, prefix_pages: int, shuffle: bool,
+                      seed: int) -> np.ndarray:
+    """Block table in which every sequence's first ``prefix_pages`` entries name
+    the same pages (a shared prefix) and the rest its own pages; physical ids
+    are a seeded permutation of all the pages with ``shuffle``."""
+    return grouped_page_table(seqlens, np.zeros(len(seqlens), np.int32), np.array([prefix_pages * page_size]),
+                              page_size, shuffle, seed)
+
+
+def grouped_page_table(seqlens: np.ndarray, prefix_group: np.ndarray, prefix_len: np.ndarray, page_size: int,
+                       shuffle: bool, seed: int) -> np.ndarray:
+    """Block table for prefix groups: the members of group g (prefix_group[b]
+    == g) name the same first prefix_len[g] / page_size pages, every other
+    page belongs to one sequence; physical ids are a seeded permutation of all
+    the pages with ``shuffle``."""
+    npg_prefix = [int(L) // page_size for L in prefix_len]
+    own = np.array([(int(L) - (int(prefix_len[g]) if g >= 0 else 0) + page_size - 1) // page_size
+                    for L, g in zip(seqlens, prefix_group)], np.int64)
+    total = sum(npg_prefix) + int(own.sum())
+    phys = np.arange(total, dtype=np.int32)
+    if shuffle:
+        phys = _gen(seed, _S_PAGES, 0).permutation(total).astype(np.int32)
+    first = np.cumsum([0] + npg_prefix)          # group g's pages: phys[first[g]:first[g + 1]]
+    maxp = max([(npg_prefix[g] if g >= 0 else 0) + int(n) for g, n in zip(prefix_group, own)] + [1])
+    bt = np.full((len(seqlens), maxp), -1, dtype=np.int32)
+    off = int(first[-1])
+    for b, (g, n) in enumerate(zip(prefix_group, own)):
+        k = 0
+        if g >= 0:
+            k = npg_prefix[g]
+            bt[b, :k] = phys[first[g]:first[g + 1]]
+        bt[b, k:k + n] = phys[off:off + n]
+        off += int(n)
+    return bt
+
+
+def make_grouped_workload(cfg: Config, seqlens, prefix_group, prefix_len) -> Workload:
+    """A GQA workload whose sequences share prefixes by group (-1: none); the
+    values are drawn as in make_workload."""
+    seqlens = np.asarray(seqlens, np.int32)
+    prefix_group = np.asarray(prefix_group, np.int32)
+    prefix_len = np.asarray(prefix_len, np.int32)
+    bt = grouped_page_table(seqlens, prefix_group, prefix_len, cfg.page_size, cfg.shuffle_pages, cfg.seed)
+    num_pages = max(int(bt.max()) + 1, 1)
+    P = cfg.page_size
+    q = normal_bf16(cfg.seed, _S_Q, (cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.head_dim_qk))
+    k = normal_bf16(cfg.seed, _S_K, (num_pages, P, cfg.num_kv_heads, cfg.head_dim_qk))
+    v = normal_bf16(cfg.seed, _S_V, (num_pages, P, cfg.num_kv_heads, cfg.head_dim_v))
+    if cfg.kv_layout == KV_HND:
+        k = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+        v = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    return Workload(cfg, seqlens, bt, q, k, v, None, prefix_group, prefix_len)
+
+
 def make_workload(cfg: Config, seqlens: np.ndarray | None = None) -> Workload:
     """Draw one workload.  ``seqlens`` overrides the configured length draw."""
     if seqlens is None:
         seqlens = draw_seqlens(cfg)
     seqlens = np.asarray(seqlens, dtype=np.int32)
-    bt = page_table(seqlens, cfg.page_size, cfg.shuffle_pages, cfg.seed)
-    num_pages = int(((seqlens.astype(np.int64) + cfg.page_size - 1) // cfg.page_size).sum())
+    prefix_group = prefix_len = None
+    if cfg.prefix_len > 0:   # one group: every sequence shares the prefix pages
+        if cfg.prefix_len % cfg.page_size or int(seqlens.min()) < cfg.prefix_len:
+            raise ValueError("the prefix must be whole pages and no longer than any sequence")
+        bt = shared_page_table(seqlens, cfg.page_size, cfg.prefix_len // cfg.page_size, cfg.shuffle_pages,
+                               cfg.seed)
+        num_pages = int(bt.max()) + 1
+        prefix_group = np.zeros(len(seqlens), np.int32)
+        prefix_len = np.array([cfg.prefix_len], np.int32)
+    else:
+        bt = page_table(seqlens, cfg.page_size, cfg.shuffle_pages, cfg.seed)
+        num_pages = int(((seqlens.astype(np.int64) + cfg.page_size - 1) // cfg.page_size).sum())
     P = cfg.page_size
     q = normal_bf16(cfg.seed, _S_Q, (cfg.batch, cfg.q_tokens, cfg.num_q_heads, cfg.head_dim_qk))
     k = normal_bf16(cfg.seed, _S_K, (num_pages, P, cfg.num_kv_heads, cfg.head_dim_qk))
@@ -223,7 +316,7 @@ def make_workload(cfg: Config, seqlens: np.ndarray | None = None) -> Workload:
             for t in range(cfg.q_tokens):
                 g = _gen(cfg.seed, _S_IDX, b * cfg.q_tokens + t)
                 idx[b, t] = g.choice(int(seqlens[b]), size=cfg.topk, replace=False)
-    return Workload(cfg, seqlens, bt, q, k, v, idx)
+    return Workload(cfg, seqlens, bt, q, k, v, idx, prefix_group, prefix_len)
 
 
 def small_variant(cfg: Config, batch: int, seqlen_hi: int, seed_offset: int = 0) -> Config:
@@ -232,6 +325,9 @@ def small_variant(cfg: Config, batch: int, seqlen_hi: int, seed_offset: int = 0)
     kw.update(name=cfg.name + "_small", batch=batch, seed=cfg.seed + 100 + seed_offset)
     if cfg.mode == MODE_MLA_SPARSE:
         kw.update(seqlen_kind="fixed", seqlen_lo=seqlen_hi, topk=min(cfg.topk, seqlen_hi))
+    elif cfg.prefix_len > 0:   # keep the prefix shape: a shorter prefix and suffixes
+        plen = max(cfg.page_size, (seqlen_hi // 2) // cfg.page_size * cfg.page_size)
+        kw.update(prefix_len=plen, seqlen_lo=1, seqlen_hi=max(1, seqlen_hi - plen))
     else:
         kw.update(seqlen_kind="uniform", seqlen_lo=1, seqlen_hi=seqlen_hi)
     return Config(**kw)

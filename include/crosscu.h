@@ -171,6 +171,31 @@ int cc_plan_size(const cc_problem* prob, const cc_plan_opts* opts, const int32_t
 int cc_plan(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
             const int32_t* block_table, void* plan, size_t bytes);
 
+/* Shared-prefix decode (MeldKernel summary, "Experiments and results": the
+ * shared-prefix experiment of Fig. 11).  Sequences b with prefix_group[b] = g
+ * (-1: none; g < num_groups) begin with the same prefix_len[g] tokens, held in
+ * the same pages of every member's block-table row.  The plan reads such a
+ * prefix once per KV head for up to 16 / G members at a time (a "prefix
+ * unit" whose 16 query rows are the members' G heads) and each sequence's own
+ * KV only past its prefix; a prefix piece is one more split of each member,
+ * merged by the same in-kernel log-sum-exp merge, so the result is the same
+ * attention over each sequence's whole KV.
+ *  - GQA with one query token; Hq / Hkv must divide 16; heads_per_unit = G;
+ *    policy CC_POLICY_STREAMK (unit_cost as for cc_plan).
+ *  - prefix_len[g]: a whole number of pages (0: the group shares nothing);
+ *    every member's seqlens[b] >= prefix_len[g].
+ *  - block_table (host, or NULL): when given, pages are checked as for
+ *    cc_plan and every member of a group must name the same first
+ *    prefix_len[g] / page_size pages (CC_ERR_INVALID otherwise).
+ * The blob is used with cc_decode like any plan (the problem is unchanged).
+ * cc_plan_check covers the lengths, not the grouping.                      */
+int cc_plan_prefix_size(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
+                        const int32_t* prefix_group, int32_t num_groups, const int32_t* prefix_len,
+                        size_t* bytes);
+int cc_plan_prefix(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
+                   const int32_t* block_table, const int32_t* prefix_group, int32_t num_groups,
+                   const int32_t* prefix_len, void* plan, size_t bytes);
+
 /* CC_OK if the host blob `plan` is a well-formed plan built for exactly `prob`
  * and these lengths (seqlens: host int32[batch]), else CC_ERR_PLAN with the
  * reason in cc_last_error().  Host only; no device work.  cc_decode cannot

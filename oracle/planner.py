@@ -50,8 +50,10 @@ import numpy as np
 
 PLAN_MAGIC = 0x4C504343          # "CCPL" little-endian
 PLAN_VERSION = 3
-HEADER_WORDS = 32               # words 0..25 below, the rest zero
+HEADER_WORDS = 32               # words 0..26 below, the rest zero
 ITEM_WORDS = 4                   # unit, tok_begin, tok_end, split
+PREFIX_WORDS = 20                # a prefix-table row: kv_head, members, prefix_len, pieces, member ids[16]
+PREFIX_ROWS = 16                 # query rows one prefix unit gathers (members x group size)
 
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
 POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
@@ -143,41 +145,12 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
     if policy == POLICY_PER_UNIT:
         C = U
     ntiles = [_ceil_div(L, T) for L in lens]
-    first_tile = []
-    acc = 0
-    for n in ntiles:
-        first_tile.append(acc)
-        acc += n
-    N = acc
+    N = sum(ntiles)
 
-    chunk_pieces: list[list[tuple[int, int, int]]] = []
-    cost_split = policy == POLICY_STREAMK and unit_cost > 0
-    if cost_split:
-        chunk_pieces = _cost_split(ntiles, lens, C, T, unit_cost)
-    # equal split of N tiles into C contiguous chunks (+1 for the first N mod C)
-    base, rem = divmod(N, C)
-    u = 0
-    for k in range(C if not cost_split else 0):
-        if policy == POLICY_PER_UNIT:
-            chunk_pieces.append([(k, 0, lens[k])] if lens[k] > 0 else [])
-            continue
-        start = k * base + min(k, rem)
-        end = start + base + (1 if k < rem else 0)
-        pieces = []
-        while u < U and first_tile[u] + ntiles[u] <= start:
-            u += 1
-        v = u
-        while end > start and v < U and first_tile[v] < end:
-            if ntiles[v] == 0:     # an empty unit gets no piece
-                v += 1
-                continue
-            tb = max(start, first_tile[v]) - first_tile[v]
-            te = min(end, first_tile[v] + ntiles[v]) - first_tile[v]
-            pieces.append((v, tb * T, min(te * T, lens[v])))
-            if first_tile[v] + ntiles[v] > end:
-                break
-            v += 1
-        chunk_pieces.append(pieces)
+    if policy == POLICY_PER_UNIT:
+        chunk_pieces = [[(k, 0, lens[k])] if lens[k] > 0 else [] for k in range(C)]
+    else:
+        chunk_pieces = _chunks(ntiles, lens, C, T, unit_cost)
 
     nsplit = [0] * U
     items_by_chunk = []
@@ -196,7 +169,22 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
         else:
             pbase.append(-1)
 
-    if policy != POLICY_PER_UNIT and X > 1 and C % X == 0:
+    header = [0] * HEADER_WORDS
+    header[:23] = [PLAN_MAGIC, PLAN_VERSION, mode, batch, q_tokens, num_q_heads, num_kv_heads,
+                   head_dim_qk, head_dim_v, page_size, topk, C, X, T, heads_per_unit, U, N, 0, S,
+                   max(nsplit) if nsplit else 0, policy, max_pages_per_seq, num_pages]
+    header[23] = unit_cost if policy == POLICY_STREAMK else 0
+    header[24] = sum(1 for n in nsplit if n == 0)      # units with no piece (empty sequences)
+    header[25] = input_hash(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v,
+                            page_size, max_pages_per_seq, num_pages, topk, seqlens)
+    return _serialise(header, items_by_chunk, nsplit, pbase, [], policy != POLICY_PER_UNIT, C, X,
+                      dict(num_units=U, num_tiles=N, num_partials=S, unit_len=lens))
+
+
+def _serialise(header, items_by_chunk, nsplit, pbase, prefix_rows, spread, C, X, fields) -> dict:
+    """Worker placement, then the blob: header, wg_off (padded to 4 words),
+    items, unit_nsplit, unit_pbase and the prefix table rows."""
+    if spread and X > 1 and C % X == 0:
         CX = C // X
         worker_of_chunk = [(k % CX) * X + k // CX for k in range(C)]
     else:
@@ -212,24 +200,57 @@ def plan(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim
         items.extend(its)
         wg_off.append(len(items))
     W = len(items)
-
-    header = [0] * HEADER_WORDS
-    header[:23] = [PLAN_MAGIC, PLAN_VERSION, mode, batch, q_tokens, num_q_heads, num_kv_heads,
-                   head_dim_qk, head_dim_v, page_size, topk, C, X, T, heads_per_unit, U, N, W, S,
-                   max(nsplit) if nsplit else 0, policy, max_pages_per_seq, num_pages]
-    header[23] = unit_cost if policy == POLICY_STREAMK else 0
-    header[24] = sum(1 for n in nsplit if n == 0)      # units with no piece (empty sequences)
-    header[25] = input_hash(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v,
-                            page_size, max_pages_per_seq, num_pages, topk, seqlens)
+    header = list(header)
+    header[17] = W
     pad = (-(C + 1)) % 4                 # keeps the item array 16-byte aligned
-    words = header + wg_off + [0] * pad + [x for it in items for x in it] + nsplit + pbase
+    words = (header + wg_off + [0] * pad + [x for it in items for x in it] + nsplit + pbase +
+             [x for row in prefix_rows for x in row])
     for x in words:
         if not (-2**31 <= x < 2**31):
             raise ValueError("plan does not fit int32")
     blob = struct.pack("<%di" % len(words), *words)
-    return dict(blob=blob, num_units=U, num_tiles=N, num_items=W, num_partials=S,
-                wg_off=wg_off, items=items, unit_nsplit=nsplit, unit_pbase=pbase,
-                worker_of_chunk=worker_of_chunk, unit_len=lens, chunk_items=items_by_chunk)
+    return dict(blob=blob, num_items=W, wg_off=wg_off, items=items, unit_nsplit=nsplit, unit_pbase=pbase,
+                worker_of_chunk=worker_of_chunk, chunk_items=items_by_chunk, **fields)
+
+
+def _equal_split(ntiles, lens, C: int, T: int):
+    """The equal tile split: chunk k takes floor(N / C) tiles, one more for
+    k < N mod C, contiguously in the unit-major tile order; pieces
+    (unit, tok_begin, tok_end) per chunk, an empty unit getting none."""
+    first_tile = []
+    acc = 0
+    for n in ntiles:
+        first_tile.append(acc)
+        acc += n
+    N, U = acc, len(ntiles)
+    base, rem = divmod(N, C)
+    u = 0
+    chunk_pieces = []
+    for k in range(C):
+        start = k * base + min(k, rem)
+        end = start + base + (1 if k < rem else 0)
+        pieces = []
+        while u < U and first_tile[u] + ntiles[u] <= start:
+            u += 1
+        v = u
+        while end > start and v < U and first_tile[v] < end:
+            if ntiles[v] == 0:     # an empty unit gets no piece
+                v += 1
+                continue
+            tb = max(start, first_tile[v]) - first_tile[v]
+            te = min(end, first_tile[v] + ntiles[v]) - first_tile[v]
+            pieces.append((v, tb * T, min(te * T, lens[v])))
+            if first_tile[v] + ntiles[v] > end:
+                break
+            v += 1
+        chunk_pieces.append(pieces)
+    return chunk_pieces
+
+
+def _chunks(ntiles, lens, C: int, T: int, unit_cost: int):
+    """Pieces per chunk of the Stream-K split: the equal tile split at unit
+    cost 0, the cost split otherwise."""
+    return _cost_split(ntiles, lens, C, T, unit_cost) if unit_cost > 0 else _equal_split(ntiles, lens, C, T)
 
 
 def _cost_split(ntiles, lens, C: int, T: int, O: int):
@@ -260,6 +281,151 @@ def _cost_split(ntiles, lens, C: int, T: int, O: int):
             i = last
         cs += O + n
     return pieces
+
+
+def validate_prefix(batch, num_q_heads, num_kv_heads, page_size, seqlens, prefix_group, prefix_len,
+                    block_table=None) -> None:
+    """Shared-prefix inputs: prefix_group[b] is -1 or a group id in
+    [0, len(prefix_len)); prefix_len[g] is a whole number of pages; every
+    member of a group holds at least its prefix; with a block table, every
+    member's first prefix_len / page_size pages are the same pages."""
+    G = num_q_heads // num_kv_heads
+    if PREFIX_ROWS % G:
+        raise ValueError("group size must divide 16")
+    NG = len(prefix_len)
+    if len(prefix_group) != batch:
+        raise ValueError("prefix_group")
+    for g in range(NG):
+        if prefix_len[g] < 0 or prefix_len[g] % page_size:
+            raise ValueError("prefix_len must be a whole number of pages")
+    first = {}
+    for b in range(batch):
+        g = int(prefix_group[b])
+        if g == -1:
+            continue
+        if not (0 <= g < NG):
+            raise ValueError("prefix group id")
+        Lp = int(prefix_len[g])
+        if int(seqlens[b]) < Lp:
+            raise ValueError("a member is shorter than its group's prefix")
+        if block_table is not None and Lp > 0:
+            row = list(np.asarray(block_table)[b, :Lp // page_size])
+            if g in first and first[g] != row:
+                raise ValueError("members of a group do not share the prefix pages")
+            first.setdefault(g, row)
+
+
+def plan_prefix(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+                max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, seqlens,
+                prefix_group, prefix_len, block_table=None, unit_cost=0) -> dict:
+    """A Stream-K plan in which sequences sharing a prefix read it once.
+
+    The shared-prefix decode the MeldKernel summary measures ("Experiments and
+    results", Fig. 11): sequences b with prefix_group[b] = g hold the same
+    first prefix_len[g] tokens (the same pages).  Readings:
+    * prefix units: for each group in id order, each KV head, and each block
+      of 16 / G members (in sequence order), one unit over tokens
+      [0, prefix_len) whose 16 query rows are the members' G heads; its work
+      is read once for all of them.
+    * the sequences' own units (b, h) then cover [prefix_len_b, L_b) only
+      (prefix_len_b = 0 outside a group or for a group with no prefix).
+    * unit order for the split: every prefix unit (ids U .. U + P - 1, U =
+      batch * Hkv), then the sequences' units in the usual order; the chunks
+      are cut as in ``plan`` (equal tiles at unit cost 0).
+    * splits of a member unit: the pieces of its prefix unit first (split
+      index = the piece's index within the prefix unit, in chunk order), then
+      its own pieces; unit_nsplit counts both, and partial slots are laid out
+      as in ``plan``.  A prefix piece's partial for a member holds that
+      member's rows, so each member's result is the log-sum-exp merge of all
+      its splits, the same identity as for any split.
+    * the blob appends one PREFIX_WORDS row per prefix unit: KV head, number
+      of members, prefix length, number of pieces, member sequence ids (-1
+      padded to 16); header word 26 counts the rows.
+    GQA with one query token, heads_per_unit = G, only.
+    """
+    if mode != MODE_GQA or q_tokens != 1:
+        raise ValueError("shared prefixes: GQA decode with one query token")
+    G = num_q_heads // num_kv_heads if num_kv_heads and num_q_heads % num_kv_heads == 0 else 0
+    validate(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,
+             max_pages_per_seq, num_pages, topk, num_cus, num_xcds, tile_tokens, max(G, 1), seqlens,
+             block_table, POLICY_STREAMK, unit_cost)
+    validate_prefix(batch, num_q_heads, num_kv_heads, page_size, seqlens, prefix_group, prefix_len,
+                    block_table)
+    C, X, T, Hkv = num_cus, num_xcds, tile_tokens, num_kv_heads
+    Mp = PREFIX_ROWS // G
+    U = batch * Hkv
+
+    lp_of = [0] * batch
+    prefix_units = []           # (kv_head, prefix_len, member sequences)
+    for g in range(len(prefix_len)):
+        members = [b for b in range(batch) if int(prefix_group[b]) == g]
+        Lp = int(prefix_len[g])
+        if Lp == 0 or not members:
+            continue
+        for b in members:
+            lp_of[b] = Lp
+        for h in range(Hkv):
+            for i in range(0, len(members), Mp):
+                prefix_units.append((h, Lp, members[i:i + Mp]))
+    P = len(prefix_units)
+    prefix_of = {}              # member unit -> its prefix unit
+    for p, (h, Lp, members) in enumerate(prefix_units):
+        for b in members:
+            prefix_of[b * Hkv + h] = p
+
+    # the work list in split order: (unit id, first token, end token)
+    work = [(U + p, 0, Lp) for p, (h, Lp, members) in enumerate(prefix_units)]
+    work += [(b * Hkv + h, lp_of[b], int(seqlens[b])) for b in range(batch) for h in range(Hkv)]
+    lens = [te - t0 for (_, t0, te) in work]
+    ntiles = [_ceil_div(L, T) for L in lens]
+    N = sum(ntiles)
+    chunk_pieces = _chunks(ntiles, lens, C, T, unit_cost)
+
+    pieces_of_prefix = [0] * P
+    for pieces in chunk_pieces:
+        for (v, _, _) in pieces:
+            if work[v][0] >= U:
+                pieces_of_prefix[work[v][0] - U] += 1
+    own = [0] * U               # own pieces numbered so far
+    seen_prefix = [0] * P
+    items_by_chunk = []
+    for pieces in chunk_pieces:
+        its = []
+        for (v, a, e) in pieces:
+            unit, t0, _ = work[v]
+            if unit >= U:
+                split = seen_prefix[unit - U]
+                seen_prefix[unit - U] += 1
+            else:
+                before = pieces_of_prefix[prefix_of[unit]] if unit in prefix_of else 0
+                split = before + own[unit]
+                own[unit] += 1
+            its.append((unit, t0 + a, t0 + e, split))
+        items_by_chunk.append(its)
+    nsplit = [own[u] + (pieces_of_prefix[prefix_of[u]] if u in prefix_of else 0) for u in range(U)]
+    pbase = []
+    S = 0
+    for n in nsplit:
+        if n > 1:
+            pbase.append(S)
+            S += n
+        else:
+            pbase.append(-1)
+    rows = [[h, len(members), Lp, pieces_of_prefix[p]] + members + [-1] * (PREFIX_ROWS - len(members))
+            for p, (h, Lp, members) in enumerate(prefix_units)]
+
+    header = [0] * HEADER_WORDS
+    header[:23] = [PLAN_MAGIC, PLAN_VERSION, mode, batch, q_tokens, num_q_heads, num_kv_heads,
+                   head_dim_qk, head_dim_v, page_size, topk, C, X, T, G, U, N, 0, S,
+                   max(nsplit) if nsplit else 0, POLICY_STREAMK, max_pages_per_seq, num_pages]
+    header[23] = unit_cost
+    header[24] = sum(1 for n in nsplit if n == 0)
+    header[25] = input_hash(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v,
+                            page_size, max_pages_per_seq, num_pages, topk, seqlens)
+    header[26] = P
+    return _serialise(header, items_by_chunk, nsplit, pbase, rows, True, C, X,
+                      dict(num_units=U, num_tiles=N, num_partials=S, unit_len=lens, prefix_units=prefix_units,
+                           prefix_pieces=pieces_of_prefix))
 
 
 def plan_for(wl, num_cus=256, num_xcds=8, tile_tokens=32, heads_per_unit=None,

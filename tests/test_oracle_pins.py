@@ -430,3 +430,45 @@ def test_empty_sequences_in_a_paged_batch():
     keep = [1, 3, 4]
     np.testing.assert_allclose(out[keep], bf_o[keep], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(lse[keep], bf_l[keep], rtol=1e-12, atol=1e-13)
+
+
+def test_shared_prefix_pages_equal_private_copies():
+    """Sequences whose block tables name the same prefix pages (the shared-prefix
+    decode) get exactly the results of the same batch with every prefix page
+    copied into each sequence's own pages; and each sequence's result is the
+    log-sum-exp merge of its prefix part and its own part."""
+    import dataclasses
+    cfg = dataclasses.replace(W.CONFIG_BY_NAME["shared_prefix_gqa"], prefix_len=0, batch=5, num_q_heads=8,
+                              num_kv_heads=2, head_dim_qk=32, head_dim_v=32, softmax_scale=0.2, seed=77)
+    sl = np.array([80, 64, 100, 70, 33], np.int32)
+    wl = W.make_grouped_workload(cfg, sl, [0, 0, 0, 1, -1], [64, 48])
+    o, l = A.decode_attention_wl(wl)
+    # private copies: a fresh cache where every (sequence, logical page) has its own page
+    P = cfg.page_size
+    npg = [(int(L) + P - 1) // P for L in sl]
+    bt2 = np.full_like(wl.block_table, -1)
+    k2 = np.zeros((sum(npg),) + wl.k_cache.shape[1:], wl.k_cache.dtype)
+    v2 = np.zeros_like(k2)
+    nxt = 0
+    for b, n in enumerate(npg):
+        for i in range(n):
+            k2[nxt] = wl.k_cache[wl.block_table[b, i]]
+            v2[nxt] = wl.v_cache[wl.block_table[b, i]]
+            bt2[b, i] = nxt
+            nxt += 1
+    assert len(set(wl.block_table[:3, :4].ravel())) == 4     # members 0..2 share their 4 prefix pages
+    o2, l2 = A.decode_attention(wl.q, k2, v2, bt2, sl, cfg.softmax_scale)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    # prefix part + own part, merged
+    G = cfg.group
+    for b, Lp in ((0, 64), (2, 64), (3, 48)):
+        for g in range(cfg.num_kv_heads):
+            q = A.bf16_to_f64(wl.q[b, 0, g * G:(g + 1) * G])
+            parts = []
+            for J in (np.arange(Lp), np.arange(Lp, int(sl[b]))):
+                K = A.gather_rows(wl.k_cache, wl.block_table, b, J, P)[:, g]
+                V = A.gather_rows(wl.v_cache, wl.block_table, b, J, P)[:, g]
+                parts.append(A.partial_state(q, K, V, cfg.softmax_scale))
+            mo, ml = A.lse_merge(parts)
+            assert np.allclose(mo, o[b, 0, g * G:(g + 1) * G], rtol=0, atol=1e-12)
+            assert np.allclose(ml, l[b, 0, g * G:(g + 1) * G], rtol=0, atol=1e-12)
