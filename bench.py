@@ -169,6 +169,7 @@ def timeline_pass(torch, B, s, workers, xcds, flush):
     B.debug_timeline(None)
     t = buf.view(workers, 8).cpu().numpy().astype(np.int64)
     start, stream_end, merged, arrived, end, xcc = t[:, 0], t[:, 1], t[:, 2], t[:, 3], t[:, 4], t[:, 5]
+    listed, weighed = t[:, 6], t[:, 7]   # GQA: after the slot lists, after the per-row max and sum
     t0 = start.min()
     span = float(end.max() - t0)                      # 100 MHz ticks
     busy = float((end - start).sum()) / (workers * span) if span > 0 else 0.0
@@ -180,6 +181,9 @@ def timeline_pass(torch, B, s, workers, xcds, flush):
             "post_stream_us_median_max": [float(np.median(end - stream_end)) * to_us,
                                           float((end - stream_end).max()) * to_us],
             "piece_merge_us_median": float(np.median(merged - stream_end)) * to_us,
+            "piece_merge_steps_us_median": ([float(np.median(listed - stream_end)) * to_us,
+                                             float(np.median(weighed - listed)) * to_us,
+                                             float(np.median(merged - weighed)) * to_us] if listed.any() else None),
             "arrival_us_median": float(np.median(arrived - merged)) * to_us,
             "unit_merge_us_max": float((end - arrived).max()) * to_us,
             "xcd_is_w_mod_x": bool(np.all(xcc == np.arange(workers) % xcds)),

@@ -50,6 +50,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;  // tokens per wave step
+constexpr int kPrefixMergeChunk = 4;  // splits per merge round in the shared-prefix kernel
 constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
@@ -189,10 +190,18 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   extern __shared__ __attribute__((aligned(16))) char smem[];  // kWaves regions
   // arrivals one workgroup makes after its stream: one per split item, and
   // with shared prefixes one per member of each prefix item in the slots
-  // (at most 8 such items of at most 16 members)
-  constexpr int kArrivals = PREFIX ? 2 * kWaves + 8 * kPrefixRows : 2 * kWaves;
+  // (at most 8 such items of at most 16 members), plus those the waves put off
+  // for the whole split pieces they finished (kWaveArrivals each)
+  constexpr int kWaveArrivals = PREFIX ? 32 : 1;
+  constexpr int kArrivals = PREFIX ? 2 * kWaves + 8 * kPrefixRows + kWaves * kWaveArrivals : 2 * kWaves;
+  __shared__ int wave_arr[kWaves][kWaveArrivals][3];  // a wave's put-off arrivals: unit, nsplit, first slot
+  __shared__ int wave_narr[kWaves];
+  // a prefix item in a merge slot: per member, its unit, its first output
+  // row, its splits and its first partial slot (filled when the slot is)
+  constexpr int kMemSlots = PREFIX ? 2 * kWaves : 1;
+  __shared__ int slot_mem[kMemSlots][kPrefixRows][4];
   __shared__ int slot_item[2 * kWaves];
-  __shared__ int slot_meta[2 * kWaves][4];  // unit, split, nsplit, pbase of the slot's item
+  __shared__ int slot_meta[2 * kWaves][4];  // unit, split, nsplit, pbase (a prefix item: rows) of the slot's item
   __shared__ int done_units[kArrivals][3];  // units this workgroup completes: {pbase, nsplit, out row}
   __shared__ float slot_w[2 * kWaves][16];    // phase-1 weight of each merge slot, per head
   __shared__ float item_L[2 * kWaves][16];    // phase-1 sum L of each item, per head
@@ -238,6 +247,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   const int e = (int)(((long long)nblk * (wave + 1)) / kWaves);
 
   if (tid < 2 * kWaves) slot_item[tid] = -1;
+  if (PREFIX && tid < kWaves) wave_narr[tid] = 0;
   __syncthreads();
 
   auto load_item = [&](Cursor& c, int it) {
@@ -397,12 +407,24 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
         for (int cc = 0; cc < W; ++cc) sb[2 * SR + hh * D + W * lr + cc] = o[cc][rr];
       }
     }
+    if constexpr (PREFIX) {
+      if (cu.pu >= 0) {
+        const int32_t* r = prefix_tab + kPrefixWords * cu.pu;
+        if (lane < uni(r[1])) {
+          const int b = r[4 + lane], mu = b * p.hkv + cu.g;
+          slot_mem[sl][lane][0] = mu;
+          slot_mem[sl][lane][1] = b * p.hq + cu.g * G;
+          slot_mem[sl][lane][2] = unit_nsplit[mu];
+          slot_mem[sl][lane][3] = unit_pbase[mu];
+        }
+      }
+    }
     if (lane == 0) {
       slot_item[sl] = cu.it;
       slot_meta[sl][0] = cu.unit;
       slot_meta[sl][1] = cu.split;
       slot_meta[sl][2] = cu.nsplit;
-      slot_meta[sl][3] = cu.pbase;
+      slot_meta[sl][3] = PREFIX && cu.pu >= 0 ? cu.rows : cu.pbase;  // a prefix item's query rows
     }
   };
 
@@ -411,8 +433,12 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   // prefix makes a split, anywhere in a chunk).  Its rows belong to members
   // j = row / G: the prefix unit's members, or the sequence itself.  Each
   // member's rows go out as its output when it has no other split, else as
-  // its partial of split cu.split; the wave then arrives for those members
-  // once its stores are complete and merges any member it completes.
+  // its partial of split cu.split.  The arrivals for those partials are put
+  // off to the end of the workgroup's stream (the wave's list in LDS), so
+  // the stream does not stop for them; only when the wave's list is full
+  // does the wave arrive itself, once its stores are complete, and merge any
+  // member it completes.
+  int narr = 0;  // this wave's put-off arrivals
   auto wave_finish = [&](const Cursor& cu, float m, float l, const f32x4* o) {
     if constexpr (PREFIX) {
       const bool pre = cu.pu >= 0;
@@ -453,7 +479,16 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
               for (int cc = 0; cc < W; ++cc) partial_store(ps + o_off + (hh - j * G) * D + W * lr + cc, o[cc][rr]);
             }
           }
-          arrive |= 1u << j;
+          if (p.reduce == CC_REDUCE_FUSED && narr < kWaveArrivals) {
+            if (lane == 0) {
+              wave_arr[wave][narr][0] = mu;
+              wave_arr[wave][narr][1] = ns;
+              wave_arr[wave][narr][2] = uni(unit_pbase[mu]);
+            }
+            ++narr;
+          } else {
+            arrive |= 1u << j;
+          }
         }
       }
       if (arrive && p.reduce == CC_REDUCE_FUSED) {
@@ -473,8 +508,8 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
           const int bj = __builtin_amdgcn_readlane(b, j), muj = __builtin_amdgcn_readlane(mu, j);
           const int nsj = __builtin_amdgcn_readlane(ns, j);
           const float* pb = partials + (size_t)uni(unit_pbase[muj]) * p.slot_floats;
-          merge_unit_direct<64, 4>(pb, nsj, (size_t)bj * p.hq + (size_t)cu.g * G, p.slot_floats, G, D, out, lse,
-                                   lane);
+          merge_unit_direct<64, kPrefixMergeChunk>(pb, nsj, (size_t)bj * p.hq + (size_t)cu.g * G, p.slot_floats, G,
+                                                   D, out, lse, lane);
         }
       }
     }
@@ -668,6 +703,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       for (int ks = 0; ks < KS; ++ks) qv[ks] = qn[ks];
     }
     if (stashed) put_slot(2 * wave, c_first, m_first, l_first, o_first);
+    if (PREFIX && lane == 0) wave_narr[wave] = narr;
   }
 
   __syncthreads();
@@ -715,15 +751,14 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       // each member with other splits arrives once for a prefix item
       for (unsigned long long pm = __ballot(first && slot_meta[lane][0] >= p.units); pm; pm &= pm - 1) {
         const int sl = __builtin_ctzll(pm);
-        const int32_t* r = prefix_tab + kPrefixWords * (uni(slot_meta[sl][0]) - p.units);
-        const int g = uni(r[0]), nmem = uni(r[1]);
+        const int nmem = uni(slot_meta[sl][3]) / G;
         for (int j0 = 0; j0 < nmem; j0 += 64) {
           const int j = j0 + lane;
           int mu = 0, ns2 = 0, pb = 0;
           if (j < nmem) {
-            mu = r[4 + j] * p.hkv + g;
-            ns2 = unit_nsplit[mu];
-            pb = unit_pbase[mu];
+            mu = slot_mem[sl][j][0];
+            ns2 = slot_mem[sl][j][2];
+            pb = slot_mem[sl][j][3];
           }
           const bool add = j < nmem && ns2 > 1;
           const unsigned long long ab = __ballot(add);
@@ -735,6 +770,18 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
           }
           nsp += __popcll(ab);
         }
+      }
+    }
+    if constexpr (PREFIX) {
+      // the waves' put-off arrivals
+      for (int w = 0; w < kWaves; ++w) {
+        const int n = wave_narr[w];
+        for (int i = lane; i < n; i += 64) {
+          split_list[nsp + i][0] = wave_arr[w][i][0];
+          split_list[nsp + i][1] = wave_arr[w][i][1];
+          split_list[nsp + i][2] = wave_arr[w][i][2];
+        }
+        nsp += n;
       }
     }
     if (lane == 0) {
@@ -780,7 +827,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     const unsigned mask = uni(it_mask[ii]);
     const int sl0 = uni(it_slot[ii]);
     const int unit = uni(slot_meta[sl0][0]), split = uni(slot_meta[sl0][1]), ns = uni(slot_meta[sl0][2]);
-    if (PREFIX && hh >= (unit >= p.units ? uni(prefix_tab[kPrefixWords * (unit - p.units) + 1]) * G : G)) continue;
+    if (PREFIX && hh >= (unit >= p.units ? uni(slot_meta[sl0][3]) : G)) continue;  // rows of the item
     float O = 0.f;
     for (unsigned mm = mask; mm; mm &= mm - 1) {
       const int t = __builtin_ctz(mm);
@@ -789,15 +836,13 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     const bool head_lane = e - hh * D == 0;
     if (PREFIX && unit >= p.units) {
       // a prefix item: row hh is head hh % G of member hh / G
-      const int32_t* r = prefix_tab + kPrefixWords * (unit - p.units);
       const int j = hh / G, hr = hh - j * G, col = e - hh * D;
-      const int b = r[4 + j], mu = b * p.hkv + r[0];
-      const size_t row = (size_t)b * p.hq + (size_t)r[0] * G + hr;
-      if (unit_nsplit[mu] == 1) {
+      const size_t row = (size_t)slot_mem[sl0][j][1] + hr;
+      if (slot_mem[sl0][j][2] == 1) {
         out[row * D + col] = O / item_L[ii][hh];
         if (head_lane) lse[row] = (item_M[ii][hh] + __log2f(item_L[ii][hh])) * kLn2;
       } else {
-        float* pslot = partials + (size_t)(unit_pbase[mu] + split) * p.slot_floats;
+        float* pslot = partials + (size_t)(slot_mem[sl0][j][3] + split) * p.slot_floats;
         partial_store(pslot + partial_o_offset(G) + hr * D + col, O);
         if (head_lane) {
           partial_store(pslot + hr, item_M[ii][hh]);
@@ -856,7 +901,16 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     if (tl && tid == 0) tl[3] = __builtin_amdgcn_s_memrealtime();
     // Phase 3: the units this workgroup completed, merged together
     const int nd = uni(num_done);
-    if (nd > 0) merge_units_direct<kThreads>(partials, done_units, nd, p.slot_floats, G, D, out, lse);
+    if (nd > 0) {
+      // with shared prefixes a workgroup may complete many small units
+      // (members): all at once.  Every merge of this kernel then takes its
+      // splits 4 at a time (kPrefixMergeChunk, also in wave_finish), so the
+      // bits of a unit do not depend on which workgroup completes it.
+      if (PREFIX)
+        merge_units_batched<kThreads, 4, kPrefixMergeChunk>(partials, done_units, nd, p.slot_floats, G, D, out, lse);
+      else
+        merge_units_direct<kThreads>(partials, done_units, nd, p.slot_floats, G, D, out, lse);
+    }
   }
   if (tl && tid == 0) {
     if (p.reduce != CC_REDUCE_FUSED) tl[3] = tl[2];

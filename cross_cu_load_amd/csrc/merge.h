@@ -213,7 +213,9 @@ __device__ __forceinline__ void merge_unit_direct(const float* pb, int ns, size_
       float Mc = M;
 #pragma unroll
       for (int i = 0; i < CH; ++i) Mc = fmaxf(Mc, mt[i]);
-      const float a = __builtin_amdgcn_exp2f(M - Mc);  // 0 on the first chunk (M = -inf, Mc finite)
+      // 0 on the first chunk (M = -inf); the same guard as merge_units_batched,
+      // so both give the same bits for the same splits and chunk
+      const float a = Mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
       L *= a;
       O *= a;
 #pragma unroll
@@ -227,6 +229,81 @@ __device__ __forceinline__ void merge_unit_direct(const float* pb, int ns, size_
     const size_t row = row0 + hh;
     out[row * dv + col] = O / L;
     if (col == 0) lse[row] = (M + __log2f(L)) * kLn2;
+  }
+}
+
+// merge_units_direct for many units at once: the (unit, element) pairs of all
+// nu units are spread over the NT threads, each thread merging UB pairs
+// together with CH splits' loads of every pair in flight, so a workgroup that
+// completes many small units (a few splits each) pays a few load round trips
+// in all rather than one or more per unit.  Splits are combined in index
+// order, as in merge_unit_direct.
+template <int NT, int UB, int CH>
+__device__ void merge_units_batched(const float* partials, const int (*units)[3], int nu, int slot_floats, int hpu,
+                                    int dv, float* out, float* lse) {
+  constexpr float kLn2 = 0.69314718055994531f;
+  const int E = hpu * dv;
+  const int o_off = partial_o_offset(hpu);
+  const int total = nu * E;
+  for (int base = threadIdx.x; base < total; base += NT * UB) {
+    const float* pb[UB];
+    int ns[UB], hh[UB], ee[UB], nsmax = 0;
+    float M[UB], L[UB], O[UB];
+#pragma unroll
+    for (int k = 0; k < UB; ++k) {
+      const int pr = base + k * NT;
+      const bool ok = pr < total;
+      const int u = ok ? pr / E : 0;
+      ee[k] = ok ? pr - u * E : 0;
+      hh[k] = ee[k] / dv;
+      ns[k] = ok ? units[u][1] : 0;
+      pb[k] = partials + (size_t)units[u][0] * slot_floats;
+      nsmax = max(nsmax, ns[k]);
+      M[k] = -INFINITY;
+      L[k] = 0.f;
+      O[k] = 0.f;
+    }
+    for (int s0 = 0; s0 < nsmax; s0 += CH) {
+      float mt[UB][CH], lt[UB][CH], ot[UB][CH];
+#pragma unroll
+      for (int k = 0; k < UB; ++k) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const bool ok = s0 + i < ns[k];
+          const float* ps = pb[k] + (size_t)(ok ? s0 + i : 0) * slot_floats;
+          mt[k][i] = ok ? partial_load(ps + hh[k]) : -INFINITY;
+          lt[k][i] = ok ? partial_load(ps + hpu + hh[k]) : 0.f;
+          ot[k][i] = ok ? partial_load(ps + o_off + ee[k]) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < UB; ++k) {
+        float Mc = M[k];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) Mc = fmaxf(Mc, mt[k][i]);
+        const float a = Mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mc);
+        L[k] *= a;
+        O[k] *= a;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const float f = __builtin_amdgcn_exp2f(mt[k][i] - Mc);
+          L[k] += lt[k][i] * f;
+          O[k] += ot[k][i] * f;
+        }
+        M[k] = Mc;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UB; ++k) {
+      const int pr = base + k * NT;
+      if (pr < total) {
+        const int u = pr / E;
+        const size_t row = (size_t)units[u][2] + hh[k];
+        const int col = ee[k] - hh[k] * dv;
+        out[row * dv + col] = O[k] / L[k];
+        if (col == 0) lse[row] = (M[k] + __log2f(L[k])) * kLn2;
+      }
+    }
   }
 }
 

@@ -197,5 +197,6 @@ def test_kernel_events_bracket_the_call(dev, reduce):
         torch.cuda.synchronize()
         assert a.elapsed_time(b) == kernel_ms[-1]
     assert torch.equal(s.out, o0)
-    assert 0 < np.median(kernel_ms) < np.median(marker_ms)
+    # the kernel interval is not longer than the marker interval beyond noise
+    assert 0 < np.median(kernel_ms) <= 1.05 * np.median(marker_ms)
     clean(s, plan)

@@ -62,6 +62,27 @@ def test_one_group(dev, cus, layout):
     clean(s, plan)
 
 
+def test_waves_with_more_arrivals_than_their_list(dev):
+    """One workgroup (C = 1) over 40 members of a group: each wave finishes
+    far more whole split pieces than its list of put-off arrivals holds, so it
+    arrives and merges the rest itself; every output meets the oracle bars."""
+    rng = np.random.default_rng(40)
+    Lp = 256
+    sl = (Lp + rng.integers(0, 300, size=40)).astype(np.int32)
+    wl = grouped(BASE, sl, np.zeros(40, np.int32), [Lp], 40)
+    s, plan = run_prefix(wl, 1, dev[1], tag="arrival-overflow")
+    compare(s, wl, label="prefix C=1 40 members")
+    clean(s, plan)
+    # the members merged by their wave and those merged after the stream give
+    # the same bits from run to run
+    o0, l0 = s.out.clone(), s.lse.clone()
+    for _ in range(5):
+        s.out.fill_(float("nan"))
+        s.run()
+    torch.cuda.synchronize()
+    assert torch.equal(s.out, o0) and torch.equal(s.lse, l0)
+
+
 @pytest.mark.parametrize("unit_cost", [0, None])
 @pytest.mark.parametrize("cus", [7, 64, 256])
 def test_several_groups_and_loners(dev, cus, unit_cost):
