@@ -294,6 +294,85 @@ def cpu_baseline(wl, args, min_seconds=10.0, max_reps=8):
             "cpu_model": cpu_model()}
 
 
+MOE_METRIC = "MoE grouped GEMM TFLOP/s & fraction of 2.5 PFLOP/s bf16 dense MFMA peak"
+
+
+def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
+    """The varlen MoE grouped GEMM: all experts in one persistent launch."""
+    cfg = W.MOE_BY_NAME[args.workload]
+    wl = W.make_moe_workload(cfg)
+    prob = B.moe_problem(cfg.num_experts, cfg.hidden, cfg.out_dim)
+    log(args, f"workload {cfg.name}: {cfg.num_experts} experts, rows {int(wl.expert_tokens.sum())} "
+              f"(max {int(wl.expert_tokens.max())}, min {int(wl.expert_tokens.min())}), K {cfg.hidden}, N {cfg.out_dim}")
+    t0 = time.perf_counter()
+    workers = cus * B.MOE_WORKGROUPS_PER_CU   # two resident workgroups per compute unit: one wave
+    for _ in range(20):
+        plan = B.moe_plan(prob, wl.expert_tokens, num_cus=workers, num_xcds=xcds)
+    plan_us = (time.perf_counter() - t0) / 20 * 1e6
+    s = B.moe_session(wl, plan)
+    ms = time_steps(torch, s.run, args.steps, args.warmup, flush, ke)
+    ms_markers = time_steps(torch, s.run, args.steps, args.warmup, flush)
+    st = stats(ms)
+    dirty, flags = B.workspace_check(plan, s.workspace)
+    assert dirty == 0 and flags == 0, "workspace left dirty"
+    workers = int(plan.view(np.int32)[11])
+    tline = timeline_pass(torch, B, s, workers, xcds, flush)
+    variants = {}
+    if not args.no_variants:
+        v1_plan = B.moe_plan(prob, wl.expert_tokens, num_cus=workers, num_xcds=xcds, policy=B.POLICY_PER_UNIT)
+        v1 = B.moe_session(wl, v1_plan)
+        variants["per_tile_workgroup"] = stats(time_steps(torch, v1.run, args.variant_steps, 3, flush, ke))
+        del v1
+        v2 = B.moe_session(wl, plan)
+        variants["split_then_combine"] = stats(time_steps(
+            torch, lambda: v2.run(B.REDUCE_SPLIT_COMBINE), args.variant_steps, 3, flush, ke))
+        del v2
+        for v in variants.values():
+            v["tflops"] = wl.flops() / (v["mean_us"] * 1e-6) / 1e12
+    tflops = wl.flops() / (st["mean_us"] * 1e-6) / 1e12
+    result = {
+        "metric": MOE_METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": st["mean_us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "experts": cfg.num_experts, "hidden": cfg.hidden, "out_dim": cfg.out_dim,
+                   "tokens": cfg.tokens, "top_k": cfg.top_k, "rows": int(wl.expert_tokens.sum()),
+                   "rows_max_min": [int(wl.expert_tokens.max()), int(wl.expert_tokens.min())],
+                   "tile": [128, 128, 64], "num_cus": cus, "num_xcds": xcds, "workers": workers,
+                   "plan_policy": (f"streamk_dp: whole tiles round-robin, the last partial round split in equal "
+                                   f"cost chunks (1 per k tile + {int(plan.view(np.int32)[23])} per tile)")},
+        "us_per_batch": st["mean_us"], "us_per_batch_median": st["median_us"],
+        "us_p10_p90": [st["p10_us"], st["p90_us"]],
+        "timing": "kernel start to end (hipExtLaunchKernel events), cold, per step",
+        "us_per_batch_event_markers": stats(ms_markers),
+        "plan_host_us": plan_us,
+        "min_bytes": wl.bytes_min(), "min_bytes_gbs": wl.bytes_min() / (st["mean_us"] * 1e-6) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_DENSE_PEAK_TFLOPS, "traffic": None},
+        "variants": variants,
+        "timeline": tline,
+    }
+    if variants:
+        result["speedup_vs_variants"] = {k: v["mean_us"] / st["mean_us"] for k, v in variants.items()}
+    if not args.no_cpu_baseline:
+        from oracle import moe as M
+        t0 = time.perf_counter()
+        M.grouped_gemm(wl.x, wl.w, wl.offsets)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": wl.flops() / dt / 1e12, "unit": "TFLOP/s",
+                                  "cores": min(len(os.sched_getaffinity(0)), _blas_threads()), "kind": "oracle",
+                                  "sample": f"the whole {cfg.name} batch once ({dt:.1f} s, fp64)",
+                                  "cpu_model": cpu_model()}
+    print(json.dumps(result), flush=True)
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -312,6 +391,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     cus, xcds = B.device_query(0)
+    if args.workload in W.MOE_BY_NAME:
+        scratch = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        sink = torch.empty(1024 * 512, dtype=torch.int32, device="cuda")
+        bench_moe(args, torch, B, W, cus, xcds, lambda: B.probe_read(scratch, 0, 1024, sink), B.debug_kernel_events)
+        return
     cfg = W.CONFIG_BY_NAME[args.workload]
     if cfg.mode == W.MODE_GQA:
         cfg = dataclasses.replace(cfg, kv_layout=W.KV_HND if args.layout == "hnd" else W.KV_NHD)

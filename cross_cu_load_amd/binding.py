@@ -20,7 +20,7 @@ CC_OK = 0
 CC_ERR_INVALID, CC_ERR_UNSUPPORTED, CC_ERR_BUFFER, CC_ERR_PLAN = -1, -2, -3, -4
 CC_ERR_PAGE, CC_ERR_HIP, CC_ERR_DEVICE_DATA = -5, -6, -7
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
-POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
+POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_DP = 0, 1, 2
 UNIT_COST_GQA, UNIT_COST_MLA = 1, 6     # CC_UNIT_COST_GQA / CC_UNIT_COST_MLA
 KV_NHD, KV_HND = 0, 1
 REDUCE_FUSED, REDUCE_SPLIT_COMBINE = 0, 1
@@ -30,7 +30,8 @@ EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_
            "cc_plan_check", "cc_plan_prefix_size", "cc_plan_prefix",
            "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
            "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_debug_merge_poll_limit", "cc_probe_read",
-           "cc_indexer_scratch_size", "cc_indexer_topk", "cc_decode_noalloc"]
+           "cc_indexer_scratch_size", "cc_indexer_topk", "cc_decode_noalloc", "cc_moe_plan_size", "cc_moe_plan",
+           "cc_moe_gemm", "cc_moe_gemm_variant"]
 
 
 class IndexerProblem(ctypes.Structure):
@@ -52,6 +53,10 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("num_xcds", ctypes.c_int32),
                 ("tile_tokens", ctypes.c_int32), ("heads_per_unit", ctypes.c_int32),
                 ("policy", ctypes.c_int32), ("unit_cost", ctypes.c_int32)]
+
+
+class MoEProblem(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("out_dim", ctypes.c_int32)]
 
 
 class CrossCUError(RuntimeError):
@@ -96,6 +101,11 @@ def load() -> ctypes.CDLL:
     lib.cc_decode.argtypes = dec
     lib.cc_decode_variant.argtypes = [ctypes.c_int] + dec
     lib.cc_decode_noalloc.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.cc_moe_plan_size.argtypes = [ctypes.POINTER(MoEProblem), ctypes.POINTER(PlanOpts), _I32P, ctypes.POINTER(_SZ)]
+    lib.cc_moe_plan.argtypes = [ctypes.POINTER(MoEProblem), ctypes.POINTER(PlanOpts), _I32P, _P, _SZ]
+    moe = [ctypes.POINTER(MoEProblem), _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.cc_moe_gemm.argtypes = moe
+    lib.cc_moe_gemm_variant.argtypes = [ctypes.c_int] + moe
     lib.cc_debug_timeline.argtypes = [_P, _SZ]
     lib.cc_debug_kernel_events.argtypes = [_P, _P]
     lib.cc_debug_merge_poll_limit.argtypes = [ctypes.c_int]
@@ -325,6 +335,74 @@ def decode(prob: Problem, plan_host: np.ndarray, plan_dev, q, k_cache, v_cache, 
 
 
 NOALLOC_WORKSPACE_BYTES = 64 << 20     # CC_NOALLOC_WORKSPACE_BYTES
+MODE_MOE = 3
+MOE_TILE_ROWS, MOE_TILE_K = 128, 64    # the MoE kernel's output-tile rows and k tile
+
+
+def moe_problem(num_experts: int, hidden: int, out_dim: int) -> MoEProblem:
+    return MoEProblem(num_experts, hidden, out_dim)
+
+
+MOE_WORKGROUPS_PER_CU = 2  # the MoE kernel's workgroups (64 KiB of LDS each) that fit on one compute unit
+
+
+def moe_plan(prob: MoEProblem, expert_tokens, num_cus=256 * MOE_WORKGROUPS_PER_CU, num_xcds=8,
+             policy=POLICY_STREAMK_DP, unit_cost=None, tile_rows=MOE_TILE_ROWS, tile_k=MOE_TILE_K) -> np.ndarray:
+    """MoE grouped-GEMM plan blob (uint8 array).  num_cus: the workers of the
+    one wave, MOE_WORKGROUPS_PER_CU per compute unit.  The default policy
+    deals whole tiles round-robin and splits only the last partial round
+    (POLICY_STREAMK_DP); unit_cost None: one k tile per output tile."""
+    lib = load()
+    opts = PlanOpts(num_cus, num_xcds, tile_k, tile_rows, policy, 1 if unit_cost is None else unit_cost)
+    et = _i32(expert_tokens)
+    if et.shape != (prob.num_experts,):
+        raise ValueError("expert_tokens must have shape [num_experts]")
+    n = _SZ()
+    _check(lib.cc_moe_plan_size(ctypes.byref(prob), ctypes.byref(opts), _ptr_i32(et), ctypes.byref(n)),
+           "cc_moe_plan_size")
+    buf = np.zeros(n.value, dtype=np.uint8)
+    _check(lib.cc_moe_plan(ctypes.byref(prob), ctypes.byref(opts), _ptr_i32(et), buf.ctypes.data_as(_P), buf.nbytes),
+           "cc_moe_plan")
+    return buf
+
+
+def moe_gemm(prob: MoEProblem, plan_host: np.ndarray, plan_dev, x, w, y, workspace, reduce: int = REDUCE_FUSED,
+             stream=None) -> None:
+    """cc_moe_gemm_variant on device tensors (asynchronous on the stream)."""
+    lib = load()
+    _check(lib.cc_moe_gemm_variant(reduce, ctypes.byref(prob), plan_host.ctypes.data_as(_P), _dp(plan_dev), _dp(x),
+                                   _dp(w), _dp(y), _dp(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "cc_moe_gemm")
+
+
+@dataclass
+class MoESession:
+    """Device-resident MoE inputs, plan and workspace for repeated calls."""
+
+    prob: MoEProblem
+    plan_host: np.ndarray
+    plan_dev: object
+    x: object
+    w: object
+    y: object
+    workspace: object
+
+    def run(self, reduce: int = REDUCE_FUSED, stream=None) -> None:
+        moe_gemm(self.prob, self.plan_host, self.plan_dev, self.x, self.w, self.y, self.workspace, reduce, stream)
+
+
+def moe_session(wl, plan_host: np.ndarray, device="cuda") -> MoESession:
+    """Copies a MoE workload (from the seeded generator) and its plan to the device."""
+    import torch
+    dev = torch.device(device)
+    c = wl.cfg
+    prob = moe_problem(c.num_experts, c.hidden, c.out_dim)
+    ws = torch.empty(workspace_size(plan_host), dtype=torch.uint8, device=dev)
+    workspace_init(ws)
+    x = torch.from_numpy(np.ascontiguousarray(wl.x).view(np.int16)).to(dev)
+    w = torch.from_numpy(np.ascontiguousarray(wl.w).view(np.int16)).to(dev)
+    y = torch.empty((wl.x.shape[0], c.out_dim), dtype=torch.float32, device=dev)
+    return MoESession(prob, plan_host, torch.from_numpy(plan_host).to(dev), x, w, y, ws)
 
 
 def decode_noalloc(prob: Problem, plan_host: np.ndarray, plan_dev, q, k_cache, v_cache, block_table, seqlens,

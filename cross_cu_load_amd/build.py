@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcrosscu.so")
 SOURCES = ["plan.cpp", "capi.cpp", "decode_gqa.hip", "decode_mla.hip", "probe.hip", "indexer.hip", "fill.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "moe.hip"]
 ARCH = "gfx950"
 
 

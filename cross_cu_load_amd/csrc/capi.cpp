@@ -3,6 +3,7 @@
 // and touches device memory only through enqueued kernels.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -320,6 +321,76 @@ int cc_decode(const cc_problem* prob, const void* plan_host, const void* plan_de
               void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(CC_REDUCE_FUSED, prob, plan_host, plan_dev, q, k_cache, v_cache, block_table,
                      seqlens, indices, out, lse, workspace, workspace_bytes, stream);
+}
+
+int cc_moe_gemm_variant(int reduce, const cc_moe_problem* prob, const void* plan_host, const void* plan_dev,
+                        const void* x, const void* w, float* y, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!prob || !plan_host || !plan_dev || !x || !w || !y || !workspace) {
+    cc::set_error("null argument");
+    return CC_ERR_INVALID;
+  }
+  if (reduce != CC_REDUCE_FUSED && reduce != CC_REDUCE_SPLIT_COMBINE) {
+    cc::set_error("unknown reduction %d", reduce);
+    return CC_ERR_INVALID;
+  }
+  cc::PlanView v;
+  int rc = cc::parse_plan(plan_host, &v);
+  if (rc) return rc;
+  const int32_t* h = v.header;
+  if (h[cc::H_MODE] != CC_MODE_MOE || h[cc::H_BATCH] != prob->num_experts || h[cc::H_DQK] != prob->hidden ||
+      h[cc::H_DV] != prob->out_dim) {
+    cc::set_error("plan was not built for this MoE problem");
+    return CC_ERR_PLAN;
+  }
+  if (h[cc::H_HPU] != 128 || h[cc::H_TILE] != 64 || prob->hidden % 64 || prob->out_dim % cc::kMoeTileCols) {
+    cc::set_error("MoE kernel: 128-row tiles (heads_per_unit), 64-wide k tiles (tile_tokens), hidden %% 64 == 0, "
+                  "out_dim %% 128 == 0");
+    return CC_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)prob->hidden * 127 * 2 + 1024 > INT32_MAX || (int64_t)v.units() >= (1 << 21)) {
+    cc::set_error("MoE kernel: hidden too large for 32-bit row offsets or too many tiles");
+    return CC_ERR_UNSUPPORTED;
+  }
+  const cc::WorkspaceLayout wl = cc::workspace_layout(v);
+  if (workspace_bytes < wl.total) {
+    cc::set_error("workspace holds %zu bytes, the plan needs %zu", workspace_bytes, wl.total);
+    return CC_ERR_BUFFER;
+  }
+  const int32_t* pd = static_cast<const int32_t*>(plan_dev);
+  char* ws = static_cast<char*>(workspace);
+  cc::MoeArgs a{};
+  a.K = prob->hidden;
+  a.N = prob->out_dim;
+  a.workers = v.workers();
+  a.units = v.units();
+  a.slot_floats = (int)wl.slot_floats;
+  a.reduce = reduce;
+  a.partials_count = v.partials();
+  a.wg_off = pd + v.off_wg;
+  a.items = reinterpret_cast<const int4*>(pd + v.off_items);
+  a.unit_nsplit = pd + v.off_nsplit;
+  a.unit_pbase = pd + v.off_pbase;
+  a.desc = pd + v.off_moe;
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(w);
+  a.y = y;
+  a.counters = reinterpret_cast<int32_t*>(ws + wl.counters_off);
+  a.partials = reinterpret_cast<float*>(ws + wl.partials_off);
+  a.timeline = (g_timeline && g_timeline_bytes >= (size_t)v.workers() * 8 * cc::kTimelineWords)
+                   ? static_cast<unsigned long long*>(g_timeline)
+                   : nullptr;
+  a.ev_start = g_ev_start;
+  a.ev_stop = g_ev_stop;
+  const hipError_t e = cc::launch_moe(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "MoE launch");
+  return CC_OK;
+}
+
+int cc_moe_gemm(const cc_moe_problem* prob, const void* plan_host, const void* plan_dev, const void* x,
+                const void* w, float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return cc_moe_gemm_variant(CC_REDUCE_FUSED, prob, plan_host, plan_dev, x, w, y, workspace, workspace_bytes,
+                             stream);
 }
 
 int cc_decode_variant(int reduce, const cc_problem* prob, const void* plan_host,

@@ -46,6 +46,25 @@ struct DecodeArgs {
   hipEvent_t ev_stop;
 };
 
+// Everything a MoE grouped GEMM launch needs.
+struct MoeArgs {
+  int K, N, workers, units, slot_floats, reduce, partials_count;
+  const int32_t* wg_off;
+  const int4* items;  // unit, k_begin, k_end, split
+  const int32_t* unit_nsplit;
+  const int32_t* unit_pbase;
+  const int32_t* desc;  // per unit: expert, first row, rows, first column
+  const uint16_t* x;
+  const uint16_t* w;
+  float* y;
+  int32_t* counters;
+  float* partials;
+  unsigned long long* timeline;
+  hipEvent_t ev_start;
+  hipEvent_t ev_stop;
+};
+hipError_t launch_moe(const MoeArgs& a, hipStream_t s);
+
 // The debug kernel events set by cc_debug_kernel_events (null when off).
 void kernel_events(hipEvent_t* start, hipEvent_t* stop);
 

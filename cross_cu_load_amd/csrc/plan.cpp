@@ -204,7 +204,7 @@ int serialise(const cc_problem& p, const cc_plan_opts& o, const int32_t* seqlens
   h[H_POLICY] = o.policy;
   h[H_MAXPAGES] = p.max_pages_per_seq;
   h[H_NUMPAGES] = p.num_pages;
-  h[H_UNIT_COST] = o.policy == CC_POLICY_STREAMK ? o.unit_cost : 0;
+  h[H_UNIT_COST] = o.policy != CC_POLICY_PER_UNIT ? o.unit_cost : 0;
   h[H_EMPTY] = (int32_t)empty;
   h[H_HASH] = input_hash(p, seqlens);
   h[H_PREFIX] = (int32_t)P;
@@ -404,6 +404,93 @@ int build_prefix(const Inputs& in, const PrefixInputs& pre, Built* out) {
   return serialise(p, o, in.seqlens, C, U, N, G, items, nsplit, rows, out);
 }
 
+// MoE grouped GEMM plan: output tiles (expert, column block, row block) of
+// heads_per_unit rows and 128 columns, each of length K cut into tile_tokens-
+// wide k tiles, split as any plan.
+int build_moe(const cc_moe_problem& mp, const cc_plan_opts& o, const int32_t* expert_tokens, Built* out) {
+  const int64_t E = mp.num_experts, K = mp.hidden, N = mp.out_dim;
+  const int64_t BM = o.heads_per_unit, BN = kMoeTileCols, BK = o.tile_tokens;
+  if (E < 1 || K < 1 || N < 1 || BM < 1 || BK < 1 || K % BK || N % BN) {
+    set_error("MoE plan: experts, hidden and out_dim >= 1, hidden a multiple of tile_tokens %lld and out_dim of %lld",
+              (long long)BK, (long long)BN);
+    return CC_ERR_INVALID;
+  }
+  if (o.policy != CC_POLICY_STREAMK && o.policy != CC_POLICY_PER_UNIT && o.policy != CC_POLICY_STREAMK_DP) {
+    set_error("unknown policy %d", o.policy);
+    return CC_ERR_INVALID;
+  }
+  if (o.unit_cost < 0 || o.num_cus < 1 || o.num_xcds < 1) {
+    set_error("num_cus, num_xcds >= 1 and unit_cost >= 0");
+    return CC_ERR_INVALID;
+  }
+  std::vector<int32_t> desc;
+  int64_t row0 = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    const int64_t n = expert_tokens[e];
+    if (n < 0) {
+      set_error("expert_tokens[%lld] = %lld is negative", (long long)e, (long long)n);
+      return CC_ERR_INVALID;
+    }
+    for (int64_t nt = 0; nt < N / BN; ++nt) {
+      for (int64_t mt = 0; mt < ceil_div(n, BM); ++mt) {
+        desc.push_back((int32_t)e);
+        desc.push_back((int32_t)(row0 + mt * BM));
+        desc.push_back((int32_t)std::min<int64_t>(BM, n - mt * BM));
+        desc.push_back((int32_t)(nt * BN));
+      }
+    }
+    row0 += n;
+  }
+  const int64_t U = (int64_t)desc.size() / kMoeDescWords;
+  if (U == 0) {
+    set_error("MoE plan: no expert has rows");
+    return CC_ERR_INVALID;
+  }
+  std::vector<Work> work(U);
+  for (int64_t u = 0; u < U; ++u) work[u] = {u, 0, K};
+  const int64_t C = o.policy == CC_POLICY_PER_UNIT ? U : o.num_cus;
+  std::vector<std::vector<Piece>> chunks;
+  if (o.policy == CC_POLICY_PER_UNIT) {
+    chunks.resize(C);
+    for (int64_t u = 0; u < U; ++u) chunks[u].push_back({u, 0, K});
+  } else if (o.policy == CC_POLICY_STREAMK_DP) {
+    // whole tiles round-robin, round by round; the last U mod C tiles split
+    const int64_t full = U / C;
+    chunks.resize(C);
+    for (int64_t k = 0; k < C; ++k)
+      for (int64_t r = 0; r < full; ++r) chunks[k].push_back({r * C + k, 0, K});
+    if (U > full * C) {
+      const std::vector<Work> rest(work.begin() + full * C, work.end());
+      const std::vector<std::vector<Piece>> sk = split_chunks(rest, C, BK, o.unit_cost);
+      for (int64_t k = 0; k < C; ++k)
+        for (const Piece& pc : sk[k]) chunks[k].push_back({full * C + pc.w, pc.a, pc.e});
+    }
+  } else {
+    chunks = split_chunks(work, C, BK, o.unit_cost);
+  }
+  std::vector<int64_t> nsplit(U, 0);
+  std::vector<std::vector<Item>> items(C);
+  for (int64_t k = 0; k < C; ++k)
+    for (const Piece& pc : chunks[k]) items[k].push_back({pc.w, pc.a, pc.e, nsplit[pc.w]++});
+  // the header words of a plan, with the MoE meanings
+  cc_problem p{};
+  p.mode = CC_MODE_MOE;
+  p.batch = (int32_t)E;
+  p.q_tokens = 1;
+  p.num_q_heads = 1;
+  p.num_kv_heads = 1;
+  p.head_dim_qk = (int32_t)K;
+  p.head_dim_v = (int32_t)N;
+  p.page_size = (int32_t)BN;
+  p.max_pages_per_seq = 1;
+  p.num_pages = 1;
+  const int64_t N_tiles = U * (K / BK);
+  int rc = serialise(p, o, expert_tokens, C, U, N_tiles, BM, items, nsplit, desc, out);
+  if (rc) return rc;
+  out->words[H_PREFIX] = 0;  // the trailing table holds tile descriptors, not prefix units
+  return CC_OK;
+}
+
 int check_args(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens) {
   if (!prob || !opts || !seqlens) {
     set_error("null argument");
@@ -452,13 +539,16 @@ int parse_plan(const void* blob, PlanView* v) {
   v->unit_nsplit = h + v->off_nsplit;
   v->unit_pbase = h + v->off_pbase;
   const int64_t P = h[H_PREFIX];
+  const bool moe = h[H_MODE] == CC_MODE_MOE;
   if (P < 0 || (P > 0 && (h[H_MODE] != CC_MODE_GQA || hpu < 1 || kPrefixRows % hpu))) {
     set_error("corrupt plan header (prefix units)");
     return CC_ERR_PLAN;
   }
   v->off_prefix = v->off_pbase + U;
   v->prefix = h + v->off_prefix;
-  v->bytes = (v->off_prefix + kPrefixWords * P) * sizeof(int32_t);
+  v->off_moe = v->off_prefix;
+  v->moe_desc = moe ? h + v->off_moe : nullptr;
+  v->bytes = (v->off_prefix + kPrefixWords * P + (moe ? kMoeDescWords * U : 0)) * sizeof(int32_t);
   if (v->wg_off[0] != 0 || v->wg_off[C] != W) {
     set_error("corrupt plan offsets");
     return CC_ERR_PLAN;
@@ -503,8 +593,17 @@ int parse_plan(const void* blob, PlanView* v) {
   }
   // items: unit in range, a non-empty tile-aligned token range inside the
   // unit's key set, a split index below the unit's piece count
+  // MoE output tiles: expert in range, rows 1 .. rows per tile, whole column blocks
+  for (int64_t u = 0; moe && u < U; ++u) {
+    const int32_t* d = v->moe_desc + kMoeDescWords * u;
+    if (d[0] < 0 || d[0] >= h[H_BATCH] || d[1] < 0 || d[2] < 1 || d[2] > hpu || d[3] < 0 ||
+        d[3] % h[H_PAGE] || d[3] + h[H_PAGE] > h[H_DV]) {
+      set_error("plan MoE tile %lld is malformed", (long long)u);
+      return CC_ERR_PLAN;
+    }
+  }
   const bool sparse = h[H_MODE] == CC_MODE_MLA_SPARSE;
-  const int64_t tmax = sparse ? (int64_t)h[H_TOPK] : (int64_t)h[H_MAXPAGES] * h[H_PAGE];
+  const int64_t tmax = moe ? (int64_t)h[H_DQK] : sparse ? (int64_t)h[H_TOPK] : (int64_t)h[H_MAXPAGES] * h[H_PAGE];
   for (int64_t i = 0; i < W; ++i) {
     const int32_t* it = v->items + kItemWords * i;
     const int64_t u = it[0], tb = it[1], te = it[2], s = it[3];
@@ -556,7 +655,10 @@ WorkspaceLayout workspace_layout(const PlanView& v, int64_t counter_units) {
   if (counter_units < v.units()) counter_units = v.units();
   L.partials_off = align(L.counters_off + sizeof(int32_t) * L.counter_words(counter_units));
   const size_t hpu = (size_t)v.header[H_HPU], dv = (size_t)v.header[H_DV];
-  if (v.header[H_MODE] == CC_MODE_GQA) {
+  if (v.header[H_MODE] == CC_MODE_MOE) {
+    // an fp32 output tile: rows per tile x columns per tile
+    L.slot_floats = (hpu * (size_t)v.header[H_PAGE] + 63) & ~size_t(63);
+  } else if (v.header[H_MODE] == CC_MODE_GQA) {
     // fp32 {m[hpu], l[hpu], pad to 4 floats, o[hpu][dv]}: o starts 16-byte aligned
     const size_t o_off = (2 * hpu + 3) & ~size_t(3);
     L.slot_floats = (o_off + hpu * dv + 63) & ~size_t(63);
@@ -634,6 +736,37 @@ int cc_plan_prefix(const cc_problem* prob, const cc_plan_opts* opts, const int32
   }
   cc::Built b;
   rc = cc::build_prefix({prob, opts, seqlens, block_table}, {prefix_group, num_groups, prefix_len}, &b);
+  if (rc) return rc;
+  const size_t need = b.words.size() * sizeof(int32_t);
+  if (bytes < need) {
+    cc::set_error("plan buffer holds %zu bytes, needs %zu", bytes, need);
+    return CC_ERR_BUFFER;
+  }
+  std::memcpy(plan, b.words.data(), need);
+  return CC_OK;
+}
+
+int cc_moe_plan_size(const cc_moe_problem* prob, const cc_plan_opts* opts, const int32_t* expert_tokens,
+                     size_t* bytes) {
+  if (!prob || !opts || !expert_tokens || !bytes) {
+    cc::set_error("null argument");
+    return CC_ERR_INVALID;
+  }
+  cc::Built b;
+  const int rc = cc::build_moe(*prob, *opts, expert_tokens, &b);
+  if (rc) return rc;
+  *bytes = b.words.size() * sizeof(int32_t);
+  return CC_OK;
+}
+
+int cc_moe_plan(const cc_moe_problem* prob, const cc_plan_opts* opts, const int32_t* expert_tokens, void* plan,
+                size_t bytes) {
+  if (!prob || !opts || !expert_tokens || !plan) {
+    cc::set_error("null argument");
+    return CC_ERR_INVALID;
+  }
+  cc::Built b;
+  const int rc = cc::build_moe(*prob, *opts, expert_tokens, &b);
   if (rc) return rc;
   const size_t need = b.words.size() * sizeof(int32_t);
   if (bytes < need) {

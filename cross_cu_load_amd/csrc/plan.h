@@ -13,6 +13,12 @@
 //                        of members, prefix length, number of pieces, member
 //                        sequence ids (-1 padded to 16); items name prefix
 //                        unit p as unit U + p
+//   moe_desc[U][4]       MoE plans (mode CC_MODE_MOE, cc_moe_plan): expert,
+//                        first row, rows, first column of each output tile.
+//                        Their header reuses words: batch = experts, dqk =
+//                        hidden K, dv = output N, tile = k per tile, hpu = rows
+//                        per tile, page = columns per tile; items' token
+//                        ranges are k ranges
 #pragma once
 
 #include <cstddef>
@@ -27,6 +33,8 @@ constexpr int32_t kPlanVersion = 3;
 constexpr int kHeaderWords = 32;
 constexpr int kItemWords = 4;
 constexpr int kPrefixWords = 20;
+constexpr int kMoeDescWords = 4;  // a MoE unit: expert, first row, rows, first column
+constexpr int kMoeTileCols = 128; // output columns of a MoE tile
 constexpr int kPrefixRows = 16;  // query rows a prefix unit gathers (members x group size)
 
 enum HeaderField {
@@ -46,9 +54,10 @@ struct PlanView {
   const int32_t* unit_nsplit = nullptr;
   const int32_t* unit_pbase = nullptr;
   const int32_t* prefix = nullptr;
+  const int32_t* moe_desc = nullptr;
   size_t bytes = 0;
   // word offsets of the arrays inside the blob (valid for a device copy too)
-  size_t off_wg = 0, off_items = 0, off_nsplit = 0, off_pbase = 0, off_prefix = 0;
+  size_t off_wg = 0, off_items = 0, off_nsplit = 0, off_pbase = 0, off_prefix = 0, off_moe = 0;
 
   int32_t workers() const { return header[H_WORKERS]; }
   int32_t units() const { return header[H_UNITS]; }

@@ -354,3 +354,88 @@ def make_indexer_inputs(wl: Workload, dim: int = INDEXER_DIM) -> IndexerInputs:
     q = normal_bf16(c.seed, _S_IQ, (c.batch, c.q_tokens, dim))
     k = normal_bf16(c.seed, _S_IK, (wl.num_pages, c.page_size, dim))
     return IndexerInputs(q, k)
+
+
+# ---------------------------------------------------------------- MoE grouped GEMM
+# Routing sends each token to top_k of E experts, so the experts receive very
+# different row counts (MeldKernel summary, "Problem and motivation": expert
+# token counts differ from SM to SM).  The pages give no MoE shapes; these are
+# a DeepSeek/Qwen-like layer: 64 experts, hidden 4096, expert output 2048,
+# 4096 tokens routed top-8 with Zipf-skewed expert popularity (a seeded
+# permutation of p_e proportional to 1 / (rank + 1)).
+_S_MOE_ROUTE, _S_MOE_X, _S_MOE_W = 20, 21, 22
+
+
+@dataclasses.dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    num_experts: int
+    hidden: int          # K
+    out_dim: int         # N
+    tokens: int
+    top_k: int
+    zipf: float = 1.0    # popularity of the expert of rank i proportional to (i + 1) ** -zipf
+    seed: int = 0
+
+
+MOE_CONFIGS = [
+    MoEConfig("moe_grouped_gemm", num_experts=64, hidden=4096, out_dim=2048, tokens=4096, top_k=8, seed=1007),
+]
+MOE_BY_NAME = {c.name: c for c in MOE_CONFIGS}
+
+
+@dataclasses.dataclass
+class MoEWorkload:
+    cfg: MoEConfig
+    expert_tokens: np.ndarray   # int32 [E]: rows routed to each expert
+    offsets: np.ndarray         # int32 [E + 1]: expert e owns rows offsets[e] .. offsets[e + 1] - 1
+    token_of_row: np.ndarray    # int32 [R]: the token each routed row copies
+    x: np.ndarray               # uint16 [R, K]: routed rows, sorted by expert
+    w: np.ndarray               # uint16 [E, N, K]: expert weights ([out, in])
+
+    def flops(self) -> float:
+        c = self.cfg
+        return 2.0 * float(self.expert_tokens.sum()) * c.hidden * c.out_dim
+
+    def bytes_min(self) -> int:
+        """Each input read once and the output written once: X, the weights of
+        experts with rows, Y (fp32)."""
+        c = self.cfg
+        used = int((self.expert_tokens > 0).sum())
+        R = int(self.expert_tokens.sum())
+        return R * c.hidden * 2 + used * c.out_dim * c.hidden * 2 + R * c.out_dim * 4
+
+
+def route(cfg: MoEConfig) -> tuple[np.ndarray, np.ndarray]:
+    """(expert_tokens [E], token_of_row [R]): each token picks top_k distinct
+    experts with probability proportional to the Zipf popularity."""
+    g = _gen(cfg.seed, _S_MOE_ROUTE, 0)
+    rank = g.permutation(cfg.num_experts)
+    p = (rank + 1.0) ** -cfg.zipf
+    p /= p.sum()
+    picks = [g.choice(cfg.num_experts, size=cfg.top_k, replace=False, p=p) for _ in range(cfg.tokens)]
+    pairs = sorted((int(e), t) for t, es in enumerate(picks) for e in es)
+    expert_tokens = np.bincount([e for e, _ in pairs], minlength=cfg.num_experts).astype(np.int32)
+    token_of_row = np.array([t for _, t in pairs], np.int32)
+    return expert_tokens, token_of_row
+
+
+def make_moe_workload(cfg: MoEConfig, expert_tokens=None) -> MoEWorkload:
+    """Draw a MoE workload; ``expert_tokens`` overrides the routing (rows then
+    copy tokens 0, 1, ... in order)."""
+    if expert_tokens is None:
+        expert_tokens, token_of_row = route(cfg)
+    else:
+        expert_tokens = np.asarray(expert_tokens, np.int32)
+        token_of_row = np.arange(int(expert_tokens.sum()), dtype=np.int32) % max(cfg.tokens, 1)
+    offsets = np.concatenate([[0], np.cumsum(expert_tokens)]).astype(np.int32)
+    xt = normal_bf16(cfg.seed, _S_MOE_X, (max(cfg.tokens, 1), cfg.hidden))
+    x = np.ascontiguousarray(xt[token_of_row]) if len(token_of_row) else np.zeros((0, cfg.hidden), np.uint16)
+    w = normal_bf16(cfg.seed, _S_MOE_W, (cfg.num_experts, cfg.out_dim, cfg.hidden))
+    return MoEWorkload(cfg, expert_tokens, offsets, token_of_row, x, w)
+
+
+def small_moe(cfg: MoEConfig, num_experts: int, hidden: int, out_dim: int, tokens: int, top_k: int,
+              seed_offset: int = 0) -> MoEConfig:
+    return dataclasses.replace(cfg, name=cfg.name + "_small", num_experts=num_experts, hidden=hidden,
+                               out_dim=out_dim, tokens=tokens, top_k=top_k, seed=cfg.seed + 100 + seed_offset)

@@ -54,7 +54,7 @@ enum {
  *              K; its first head_dim_v columns are V; Hkv = 1; one query token.
  *  MLA_SPARSE: as MLA, but query token t of request b attends only to the
  *              topk cache positions indices[b][t][0..topk).                    */
-enum { CC_MODE_GQA = 0, CC_MODE_MLA = 1, CC_MODE_MLA_SPARSE = 2 };
+enum { CC_MODE_GQA = 0, CC_MODE_MLA = 1, CC_MODE_MLA_SPARSE = 2, CC_MODE_MOE = 3 /* cc_moe_* */ };
 
 /* Page layouts of the GQA K and V caches (MLA caches have one head: both are
  * [num_pages][page_size][head_dim_qk]).
@@ -77,7 +77,13 @@ enum { CC_KV_NHD = 0, CC_KV_HND = 1 };
  *             workers 5 tasks and 8 workers 4).
  *  PER_UNIT:  one worker per unit (query heads sharing one K/V stream), no
  *             split — the classic one-workgroup-per-(sequence, head) launch. */
-enum { CC_POLICY_STREAMK = 0, CC_POLICY_PER_UNIT = 1 };
+/*  STREAMK_DP: (cc_moe_plan only) the data-parallel + Stream-K form of the
+ *             same equal split: the first U - U mod C units go whole, unit
+ *             r C + k to chunk k in round r (so units computed at the same
+ *             time are neighbours and share operand tiles in cache), and only
+ *             the last U mod C units are split as STREAMK splits.  Every
+ *             chunk gets the same work to within one tile.                  */
+enum { CC_POLICY_STREAMK = 0, CC_POLICY_PER_UNIT = 1, CC_POLICY_STREAMK_DP = 2 };
 
 /* Unit costs (in tiles) measured for this library's kernels: a GQA unit's
  * start and finish cost about one 32-token tile, a 128-head MLA unit's (its
@@ -195,6 +201,49 @@ int cc_plan_prefix_size(const cc_problem* prob, const cc_plan_opts* opts, const 
 int cc_plan_prefix(const cc_problem* prob, const cc_plan_opts* opts, const int32_t* seqlens,
                    const int32_t* block_table, const int32_t* prefix_group, int32_t num_groups,
                    const int32_t* prefix_len, void* plan, size_t bytes);
+
+/* ---------------------------------------------------- MoE grouped GEMM
+ * The second imbalanced workload the method is instantiated on (MeldKernel
+ * summary, "Problem and motivation": expert token counts differ from SM to
+ * SM; "Core method": the mapping follows the real counts at run time).
+ * Routed rows sorted by expert, expert e owning rows offsets[e] ..
+ * offsets[e+1] - 1 (offsets = exclusive prefix sum of expert_tokens):
+ *   Y[r, :] = X[r, :] . W[e]^T      (bf16 inputs, fp32 accumulation and out)
+ *   x  bf16 [R][hidden], w bf16 [num_experts][out_dim][hidden] (row n of
+ *   expert e is its output column n), y fp32 [R][out_dim], R = sum of
+ *   expert_tokens.
+ * The plan cuts the output into tiles of opts.heads_per_unit rows x 128
+ * columns (unit = expert, column block, row block) and each tile's hidden
+ * range into k tiles of opts.tile_tokens; the (tile, k tile) work is split
+ * into num_cus equal chunks as for decode (CC_POLICY_STREAMK, unit_cost) or
+ * one worker per output tile (CC_POLICY_PER_UNIT).  A tile split across
+ * compute units is summed in split order by its last piece to finish
+ * (cc_moe_gemm) or by a second kernel (cc_moe_gemm_variant with
+ * CC_REDUCE_SPLIT_COMBINE).  cc_moe_gemm needs heads_per_unit = 128,
+ * tile_tokens = 64, hidden % 64 == 0, out_dim % 128 == 0.  The plan blob has
+ * the layout of a decode plan (mode CC_MODE_MOE) and works with
+ * cc_workspace_size / cc_workspace_init / cc_workspace_check. */
+typedef struct cc_moe_problem {
+  int32_t num_experts;
+  int32_t hidden;   /* K */
+  int32_t out_dim;  /* N */
+} cc_moe_problem;
+
+/* Plan size / plan for these per-expert row counts (host int32[num_experts]). */
+int cc_moe_plan_size(const cc_moe_problem* prob, const cc_plan_opts* opts, const int32_t* expert_tokens,
+                     size_t* bytes);
+int cc_moe_plan(const cc_moe_problem* prob, const cc_plan_opts* opts, const int32_t* expert_tokens, void* plan,
+                size_t bytes);
+
+/* Y for all experts in one persistent launch (device x, w, y, workspace;
+ * host and device copies of the plan).  Asynchronous on `stream`. */
+int cc_moe_gemm(const cc_moe_problem* prob, const void* plan_host, const void* plan_dev, const void* x,
+                const void* w, float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* cc_moe_gemm with an explicit reduction of split tiles (CC_REDUCE_*). */
+int cc_moe_gemm_variant(int reduce, const cc_moe_problem* prob, const void* plan_host, const void* plan_dev,
+                        const void* x, const void* w, float* y, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* CC_OK if the host blob `plan` is a well-formed plan built for exactly `prob`
  * and these lengths (seqlens: host int32[batch]), else CC_ERR_PLAN with the

@@ -55,8 +55,9 @@ ITEM_WORDS = 4                   # unit, tok_begin, tok_end, split
 PREFIX_WORDS = 20                # a prefix-table row: kv_head, members, prefix_len, pieces, member ids[16]
 PREFIX_ROWS = 16                 # query rows one prefix unit gathers (members x group size)
 
-MODE_GQA, MODE_MLA, MODE_MLA_SPARSE = 0, 1, 2
-POLICY_STREAMK, POLICY_PER_UNIT = 0, 1
+MODE_GQA, MODE_MLA, MODE_MLA_SPARSE, MODE_MOE = 0, 1, 2, 3
+MOE_DESC_WORDS = 4               # a MoE unit: expert, first row, rows, first column
+POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_DP = 0, 1, 2
 
 
 def fnv1a32(words) -> int:
@@ -426,6 +427,93 @@ def plan_prefix(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, h
     return _serialise(header, items_by_chunk, nsplit, pbase, rows, True, C, X,
                       dict(num_units=U, num_tiles=N, num_partials=S, unit_len=lens, prefix_units=prefix_units,
                            prefix_pieces=pieces_of_prefix))
+
+
+def plan_moe(num_experts, hidden, out_dim, expert_tokens, num_cus, num_xcds, tile_rows=128, tile_cols=128,
+             tile_k=64, policy=POLICY_STREAMK, unit_cost=0) -> dict:
+    """A Stream-K plan for the MoE grouped GEMM Y_e = X_e W_e^T.
+
+    The same split as ``plan`` applied to another imbalanced workload (the
+    MeldKernel summary instantiates the method on MoE: "Problem and
+    motivation", "Core method").  Readings:
+    * unit: one tile_rows x tile_cols output tile of one expert, (expert e,
+      column block, row block) in that order, so the row blocks of one
+      column block (which read the same weight tile) are adjacent; an expert
+      with no rows has no unit.
+    * a unit's length is the hidden size K, cut into tiles of tile_k: the
+      split is over the (unit, k tile) work exactly as ``plan`` splits
+      (unit, KV tile) work; a piece is a unit's k range within one chunk and
+      its split index counts the unit's pieces in chunk order.
+    * POLICY_STREAMK_DP (the data-parallel + Stream-K form of the same equal
+      split): the first U - U mod C tiles go whole, tile r C + k to chunk k in
+      round r, so the tiles computed at the same time are neighbours that
+      share weight and row tiles in cache; only the last U mod C tiles' k
+      tiles are split over the chunks as above.  Every chunk still gets the
+      same work to within one k tile.
+    * the blob has ``plan``'s layout with mode 3, batch = E, head_dim_qk = K,
+      head_dim_v = N, page_size = tile_cols, heads_per_unit = tile_rows,
+      tile_tokens = tile_k, one page, and then MOE_DESC_WORDS per unit
+      (expert, first row, rows, first column); word 25 is ``input_hash`` of
+      those header values with expert_tokens in place of seqlens.
+    """
+    E, K, N = num_experts, hidden, out_dim
+    if E < 1 or K < 1 or N < 1 or K % tile_k or N % tile_cols:
+        raise ValueError("MoE shape: K a multiple of tile_k, N of tile_cols")
+    if (policy not in (POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_DP) or unit_cost < 0 or num_cus < 1
+            or num_xcds < 1):
+        raise ValueError("opts")
+    counts = [int(n) for n in expert_tokens]
+    if len(counts) != E or min(counts) < 0:
+        raise ValueError("expert_tokens")
+    units = []
+    row0 = 0
+    for e in range(E):
+        for nt in range(N // tile_cols):
+            for mt in range(_ceil_div(counts[e], tile_rows)):
+                units.append((e, row0 + mt * tile_rows, min(tile_rows, counts[e] - mt * tile_rows),
+                              nt * tile_cols))
+        row0 += counts[e]
+    U = len(units)
+    if U == 0:
+        raise ValueError("no rows")
+    lens = [K] * U
+    ntiles = [K // tile_k] * U
+    C = U if policy == POLICY_PER_UNIT else num_cus
+    if policy == POLICY_PER_UNIT:
+        chunk_pieces = [[(k, 0, K)] for k in range(C)]
+    elif policy == POLICY_STREAMK_DP:
+        # whole tiles dealt round-robin (tile r C + k to chunk k, round by
+        # round), then the last U mod C tiles' k tiles split as in ``plan``
+        full = U // C
+        chunk_pieces = [[(r * C + k, 0, K) for r in range(full)] for k in range(C)]
+        rest = _chunks(ntiles[full * C:], lens[full * C:], C, tile_k, unit_cost) if U > full * C else [[]] * C
+        for k in range(C):
+            chunk_pieces[k] += [(full * C + v, a, b) for (v, a, b) in rest[k]]
+    else:
+        chunk_pieces = _chunks(ntiles, lens, C, tile_k, unit_cost)
+    nsplit = [0] * U
+    items_by_chunk = []
+    for pieces in chunk_pieces:
+        its = []
+        for (v, t0, t1) in pieces:
+            its.append((v, t0, t1, nsplit[v]))
+            nsplit[v] += 1
+        items_by_chunk.append(its)
+    pbase, S = [], 0
+    for n in nsplit:
+        if n > 1:
+            pbase.append(S)
+            S += n
+        else:
+            pbase.append(-1)
+    header = [0] * HEADER_WORDS
+    header[:23] = [PLAN_MAGIC, PLAN_VERSION, MODE_MOE, E, 1, 1, 1, K, N, tile_cols, 0, C, num_xcds, tile_k,
+                   tile_rows, U, sum(ntiles), 0, S, max(nsplit), policy, 1, 1]
+    header[23] = unit_cost if policy != POLICY_PER_UNIT else 0
+    header[24] = 0
+    header[25] = input_hash(MODE_MOE, E, 1, 1, 1, K, N, tile_cols, 1, 1, 0, counts)
+    return _serialise(header, items_by_chunk, nsplit, pbase, [list(u) for u in units], policy != POLICY_PER_UNIT,
+                      C, num_xcds, dict(num_units=U, num_tiles=sum(ntiles), num_partials=S, units=units))
 
 
 def plan_for(wl, num_cus=256, num_xcds=8, tile_tokens=32, heads_per_unit=None,
