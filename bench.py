@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also time back-to-back calls eagerly and replayed from a captured HIP graph")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="also time the MFMA ceiling probe (dense bf16, register operands)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 256 MiB fill and a 1 GiB read of known size (scales profiler byte counters)")
     return ap.parse_args()
@@ -297,6 +299,18 @@ def cpu_baseline(wl, args, min_seconds=10.0, max_reps=8):
 MOE_METRIC = "MoE grouped GEMM TFLOP/s & fraction of 2.5 PFLOP/s bf16 dense MFMA peak"
 
 
+def mfma_probe_pass(torch, B, cus, ke):
+    """The practical dense bf16 MFMA ceiling: TFLOP/s of register-operand
+    MFMA chains with one and two waves per SIMD."""
+    out = {}
+    for waves in (4, 8):
+        sink = torch.empty(cus * waves * 64, dtype=torch.int32, device="cuda")
+        flops = B.probe_mfma(cus, waves, 4096, sink)
+        ms = time_steps(torch, lambda: B.probe_mfma(cus, waves, 4096, sink), 10, 2, None, ke)
+        out[f"waves_per_simd_{waves // 4}"] = flops / (float(np.median(ms)) * 1e-3) / 1e12
+    return out
+
+
 def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
     """The varlen MoE grouped GEMM: all experts in one persistent launch."""
     cfg = W.MOE_BY_NAME[args.workload]
@@ -353,6 +367,8 @@ def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
     }
     if variants:
         result["speedup_vs_variants"] = {k: v["mean_us"] / st["mean_us"] for k, v in variants.items()}
+    if args.mfma_probe:
+        result["mfma_probe_tflops"] = mfma_probe_pass(torch, B, cus, ke)
     if not args.no_cpu_baseline:
         from oracle import moe as M
         t0 = time.perf_counter()
@@ -524,6 +540,8 @@ def main():
         if not args.no_cpu_baseline:
             result["indexer"]["cpu_oracle_us"] = indexer_cpu_baseline(wl, ix)
         log(args, f"indexer: {result['indexer']}")
+    if args.mfma_probe:
+        result["mfma_probe_tflops"] = mfma_probe_pass(torch, B, cus, ke)
     if args.graph:
         result["graph"] = graph_pass(torch, s)
         log(args, f"graph: {result['graph']}")

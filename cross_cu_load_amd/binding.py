@@ -30,6 +30,7 @@ EXPORTS = ["cc_version", "cc_last_error", "cc_strerror", "cc_device_query", "cc_
            "cc_plan_check", "cc_plan_prefix_size", "cc_plan_prefix",
            "cc_workspace_size", "cc_workspace_init", "cc_workspace_check", "cc_decode",
            "cc_decode_variant", "cc_debug_timeline", "cc_debug_kernel_events", "cc_debug_merge_poll_limit", "cc_probe_read",
+           "cc_probe_mfma",
            "cc_indexer_scratch_size", "cc_indexer_topk", "cc_decode_noalloc", "cc_moe_plan_size", "cc_moe_plan",
            "cc_moe_gemm", "cc_moe_gemm_variant"]
 
@@ -113,6 +114,7 @@ def load() -> ctypes.CDLL:
     lib.cc_indexer_topk.argtypes = [ctypes.POINTER(IndexerProblem), _I32P, _P, _P, _P, _P, _SZ, _P, _P, _P]
     lib.cc_probe_read.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, _P, _P]
+    lib.cc_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]
     for f in EXPORTS:
         if f not in ("cc_last_error", "cc_strerror"):
             getattr(lib, f).restype = ctypes.c_int
@@ -317,6 +319,12 @@ def probe_read(buf, method: int, workgroups: int, sink, pages=None, page_bytes: 
     _check(lib.cc_probe_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(), method,
                              _dp(pages), page_bytes, npages, workgroups, _dp(sink), _stream(stream)),
            "cc_probe_read")
+
+
+def probe_mfma(workgroups: int, waves_per_workgroup: int, iters: int, sink, stream=None) -> float:
+    """cc_probe_mfma (asynchronous); returns the flops of the call."""
+    _check(load().cc_probe_mfma(workgroups, waves_per_workgroup, iters, _dp(sink), _stream(stream)), "cc_probe_mfma")
+    return float(workgroups) * waves_per_workgroup * iters * 8 * 32768
 
 
 def _dp(t):

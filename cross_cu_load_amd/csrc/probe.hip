@@ -106,6 +106,36 @@ read_probe(const char* __restrict__ buf, long long bytes, int method, const int*
   sink[blockIdx.x * kThreads + tid] = acc;
 }
 
+// MFMA ceiling probe: each wave runs `iters` rounds of kChains independent
+// v_mfma_f32_32x32x16_bf16 accumulations on register operands (no memory
+// traffic), so the rate it reaches is the practical dense bf16 MFMA rate of
+// the device for that many waves per SIMD.  The accumulators are folded
+// into sink so no product is dead.
+constexpr int kChains = 8;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kProbeMaxWaves = 8;
+__global__ void __launch_bounds__(64 * kProbeMaxWaves) mfma_probe(int iters, uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  u32x4 a = {0x3f803f80u ^ (uint32_t)lane, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  u32x4 b = {0x3f803f80u, 0x3f803f80u ^ (uint32_t)lane, 0x3f803f80u, 0x3f803f80u};
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = __builtin_bit_cast(uint32_t, s);
+}
+
 }  // namespace probe
 }  // namespace cc
 
@@ -130,5 +160,16 @@ extern "C" int cc_probe_read(const void* buf, long long bytes, int method, const
     hipExtLaunchKernelGGL(read_probe<false>, dim3(workgroups), dim3(kThreads), (uint32_t)lds,
                           static_cast<hipStream_t>(stream), ev0, ev1, 0u, static_cast<const char*>(buf), bytes, m,
                           pages, page_bytes, num_pages, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? CC_OK : CC_ERR_HIP;
+}
+
+extern "C" int cc_probe_mfma(int workgroups, int waves_per_workgroup, int iters, void* sink, void* stream) {
+  using namespace cc::probe;
+  if (!sink || workgroups < 1 || waves_per_workgroup < 1 || waves_per_workgroup > kProbeMaxWaves || iters < 1)
+    return CC_ERR_INVALID;
+  hipEvent_t ev0, ev1;
+  cc::kernel_events(&ev0, &ev1);
+  hipExtLaunchKernelGGL(mfma_probe, dim3(workgroups), dim3(64 * waves_per_workgroup), 0u,
+                        static_cast<hipStream_t>(stream), ev0, ev1, 0u, iters, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? CC_OK : CC_ERR_HIP;
 }

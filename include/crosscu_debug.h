@@ -43,7 +43,7 @@ int cc_debug_timeline(void* buf, size_t bytes);
 
 /* Sets (both non-NULL) or clears (both NULL) a pair of HIP events
  * (hipEvent_t, created by the caller with timing enabled) that later
- * cc_decode / cc_decode_variant / cc_probe_read / cc_indexer_topk calls on
+ * cc_decode / cc_decode_variant / cc_probe_read / cc_probe_mfma / cc_indexer_topk / cc_moe_gemm calls on
  * any stream record
  * through hipExtLaunchKernel: start_event when the call's first kernel
  * begins, stop_event when its last kernel ends.  The time between them covers the
@@ -79,6 +79,17 @@ int cc_debug_merge_poll_limit(int polls);
  * CC_ERR_HIP. */
 int cc_probe_read(const void* buf, long long bytes, int method, const int32_t* pages, int page_bytes,
                   int num_pages, int workgroups, void* sink, void* stream);
+
+/* MFMA ceiling probe: `workgroups` x `waves_per_workgroup` waves (1..8 per
+ * workgroup) each run `iters` rounds of 8 independent
+ * v_mfma_f32_32x32x16_bf16 accumulations (32768 flops each) on register
+ * operands, with no memory traffic, asynchronously on `stream`; the rate the
+ * caller times is the practical dense bf16 MFMA ceiling the MLA and MoE
+ * kernels' MFMA fractions can be placed against.  Flops of one call:
+ * workgroups * waves_per_workgroup * iters * 8 * 32768.  sink: device
+ * uint32[workgroups * waves_per_workgroup * 64], written.  Returns CC_OK,
+ * CC_ERR_INVALID or CC_ERR_HIP. */
+int cc_probe_mfma(int workgroups, int waves_per_workgroup, int iters, void* sink, void* stream);
 
 #ifdef __cplusplus
 }
