@@ -193,7 +193,8 @@ def timeline_pass(torch, B, s, workers, xcds, flush):
 
 
 KERNEL_SOURCES = {"gqa_decode_kernel": ("decode_gqa.hip", "merge.h", "launch.h", "plan.h"),
-                  "mla_decode_kernel": ("decode_mla.hip", "merge.h", "launch.h", "plan.h")}
+                  "mla_decode_kernel": ("decode_mla.hip", "merge.h", "launch.h", "plan.h"),
+                  "moe_gemm_kernel": ("moe.hip", "launch.h", "plan.h")}
 
 
 def kernel_name(mode):
@@ -209,11 +210,12 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(kernel, workload, layout):
+def profiled_traffic(kernel, workload, layout=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if the
-    decode kernel's sources are unchanged since it was taken (else None)."""
+    kernel's sources are unchanged since it was taken (else None)."""
     import re
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_{layout}.md")
+    name = f"{kernel}_{workload}_{layout}.md" if layout else f"{kernel}_{workload}.md"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -361,7 +363,8 @@ def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
         "plan_host_us": plan_us,
         "min_bytes": wl.bytes_min(), "min_bytes_gbs": wl.bytes_min() / (st["mean_us"] * 1e-6) / 1e9,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / BF16_DENSE_PEAK_TFLOPS, "traffic": None},
+                     "frac": tflops / BF16_DENSE_PEAK_TFLOPS,
+                     "traffic": profiled_traffic("moe_gemm_kernel", cfg.name)},
         "variants": variants,
         "timeline": tline,
     }
@@ -407,6 +410,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     cus, xcds = B.device_query(0)
+    if args.calibrate:   # kernels of known traffic for the profiler's byte counters
+        cal = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            B.workspace_init(cal)          # writes exactly 256 MiB
+        torch.cuda.synchronize()
+        del cal
     if args.workload in W.MOE_BY_NAME:
         scratch = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
         sink = torch.empty(1024 * 512, dtype=torch.int32, device="cuda")
@@ -443,13 +452,6 @@ def main():
         B.probe_read(scratch, 0, 1024, sink)
 
     ke = B.debug_kernel_events
-
-    if args.calibrate:   # kernels of known traffic for the profiler's byte counters
-        cal = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        for _ in range(2):
-            B.workspace_init(cal)          # writes exactly 256 MiB
-        torch.cuda.synchronize()
-        del cal
 
     # practical ceiling: a plain 1 GiB streaming read, same flush; plain loads
     # (method 0) and the non-temporal loads the kernels use (method 3)

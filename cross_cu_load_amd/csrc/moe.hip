@@ -17,8 +17,9 @@
 // MFMA operand is one 16-byte LDS read.  Each 64-wide k step of both operand
 // tiles (16 KiB each) goes HBM -> LDS with global_load_lds_dwordx4 into one
 // of two stages while the other stage computes.  In LDS, row r's 16-byte
-// chunk c sits at chunk position c ^ (r % 8) of the row's 128 bytes, so the
-// 8 lanes that read 8 consecutive rows' chunk c hit 8 different bank groups.
+// chunk c sits at chunk position c ^ ((r / 2) % 8) of the row's 128 bytes:
+// a 16-byte read by 16 lanes of 16 consecutive rows' chunk c then covers the
+// 64 banks (256 bytes) once, as two rows share one 256-byte bank line.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -158,13 +159,13 @@ moe_gemm_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* 
   };
 
   // transfer i of this wave moves rows 8 q .. 8 q + 7 (q = 4 wave + i) of an
-  // operand tile: lane L takes row 8 q + L / 8, k chunk (L % 8) ^ (row % 8);
+  // operand tile: lane L takes row 8 q + L / 8, k chunk (L % 8) ^ ((row / 2) % 8);
   // rows of X past the tile's last row repeat it (their outputs are dropped)
   uint32_t voff_b[kDma];
 #pragma unroll
   for (int i = 0; i < kDma; ++i) {
     const int n = 8 * (kDma * wave + i) + (lane >> 3);
-    voff_b[i] = (uint32_t)((n * K + 8 * ((lane & 7) ^ (n & 7))) * 2);
+    voff_b[i] = (uint32_t)((n * K + 8 * ((lane & 7) ^ ((n >> 1) & 7))) * 2);
   }
   auto issue = [&](const Cur& c, int stage) {
     const char* sa = uni_ptr(reinterpret_cast<const char*>(x) + ((size_t)c.row0 * K + c.kb) * 2);
@@ -173,16 +174,17 @@ moe_gemm_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* 
     for (int i = 0; i < kDma; ++i) {
       const int q = kDma * wave + i;
       const int r = 8 * q + (lane >> 3);
-      const uint32_t voff_a = (uint32_t)((min(r, c.rows - 1) * K + 8 * ((lane & 7) ^ (r & 7))) * 2);
+      const uint32_t voff_a = (uint32_t)((min(r, c.rows - 1) * K + 8 * ((lane & 7) ^ ((r >> 1) & 7))) * 2);
       lds_dma16(sa, voff_a, lds_a[stage] + 1024 * q);
       lds_dma16(sb, voff_b[i], lds_b[stage] + 1024 * q);
     }
   };
 
   // operand reads: block i (j) of the wave's rows (columns) is row
-  // base + lane % 32 of its tile; k step ks reads chunk 2 ks + lane / 32
+  // base + lane % 32 of its tile (base a multiple of 32, so (row / 2) % 8 is
+  // (lane / 2) % 8); k step ks reads chunk 2 ks + lane / 32
   const int arow = (wave >> 1) * 64 + (lane & 31), bcol = (wave & 1) * 64 + (lane & 31);
-  auto chunk_pos = [&](int row, int ks) { return row * 128 + (((2 * ks + (lane >> 5)) ^ (lane & 7)) << 4); };
+  auto chunk_pos = [&](int row, int ks) { return row * 128 + (((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4); };
 
   f32x16 acc[2][2];
   auto zero = [&]() {
