@@ -245,6 +245,15 @@ __device__ __forceinline__ void lds_dma16s(const char* sbase, uint32_t voff, cha
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :: "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
 }
+// 16 bytes per lane at p + OFF into v, a load the compiler does not track:
+// the kernel's own vmcnt waits make it complete before v is read.  v is an
+// in-out operand, so the load lands in the registers that hold the value it
+// replaces and the compiler has no reason to copy it while it is in flight
+// (a test checks the generated code for that).
+template <int OFF>
+__device__ __forceinline__ void load16_async(u32x4& v, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "+v"(v) : "v"(p), "n"(OFF) : "memory");
+}
 // A dword load the compiler does not track: the kernel's own vmcnt waits make
 // it complete before the value is read with take_dword (both are ordered asm).
 __device__ __forceinline__ uint32_t load_dword_async(const int32_t* ptr) {
@@ -603,25 +612,22 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   // first kQReg k-steps stay in registers (112 VGPRs) for the whole item; the
   // other 8 go to the wave's own LDS area in the same lane order (one transfer
   // per k-step, read back conflict free), which leaves the register file room
-  // for the operand pipeline.  The q loads are followed by
-  // kDmaPerWave stores of zero into unused words of the workspace header: the
-  // compiler counts those (it does not see the asm transfers), so it waits for
-  // q with vmcnt(kDmaPerWave), which leaves exactly the next tile's transfers
-  // in flight, instead of vmcnt(0).
-  u32x4 qv[kQReg];
+  // for the operand pipeline.  The register part is loaded with untracked
+  // loads (load16_async): every q load is issued before the transfers of the
+  // next tile fetch, so the vmcnt(kDmaPerWave) wait at the top of the next
+  // step covers it, and the score loop carries no wait for q.
+  u32x4 qv[kQReg] = {};
   char* qlds_w = qlds[wave];
   auto load_q = [&](int unit) {
     const size_t row = (size_t)unit * p.hq + kHW * wave + n;
     const uint16_t* qp = qg + row * kDqk + 8 * g;
-#pragma unroll
-    for (int j = 0; j < kQReg; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qp + 16 * j);
+    unroll<kQReg>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      load16_async<32 * j>(qv[j], qp);
+    });
 #pragma unroll
     for (int r = 0; r < kKSteps - kQReg; ++r)
       lds_dma16(reinterpret_cast<const char*>(qp + 16 * (kQReg + r)), qlds_w + 1024 * r);
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) err[4 * (i + 1)] = 0;  // every lane, same word: no branch
-    asm volatile("" ::: "memory");
   };
 
   // ------------------------------------------------ the block stream
@@ -814,8 +820,14 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
 
     // scores (base 2), masked past the item end; register r is token 8 (r / 4) + 4 g + r % 4
     float x[16];
+    if (nv == kBlk) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (8 * (r >> 2) + 4 * g + (r & 3) < nv) ? s[r] * scale_log2 : -INFINITY;
+      for (int r = 0; r < 16; ++r) x[r] = s[r] * scale_log2;
+    } else {
+      const int lim = nv - 4 * g;  // register r holds a valid token when 8 (r / 4) + r % 4 < lim
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (8 * (r >> 2) + (r & 3) < lim) ? s[r] * scale_log2 : -INFINITY;
+    }
     float bmax = x[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, x[r]);

@@ -8,8 +8,8 @@ would overwrite each other.  This compiles the kernel (hipcc cross-compiles
 for gfx950 without a GPU) and checks that every AGPR access in the decode
 kernels sits inside an inline-asm block, and that nothing spills to scratch.
 
-The kernels also prefetch block-table entries and row ids with dword loads
-written as inline asm, which the compiler's own wait insertion does not
+The kernels also load q and prefetch block-table entries and row ids with
+global loads written as inline asm, which the compiler's own wait insertion does not
 track: the kernel's explicit vmcnt waits cover them.  The compiler must not
 read or overwrite such a load's destination register (a copy, a spill) before
 the next vmcnt wait, or it would see the register's old contents; the last
@@ -98,8 +98,9 @@ def _vregs(code):
 
 @pytest.mark.parametrize("sparse", [False, True])
 def test_untracked_loads_untouched_until_waited(mla_asm, sparse):
-    """Between an inline-asm global_load_dword and the next vmcnt wait (in code
-    order), no instruction outside inline asm names its destination VGPR."""
+    """Between an inline-asm global load (the dword prefetches and the 16-byte
+    q loads) and the next vmcnt wait (in code order), no instruction outside
+    inline asm names its destination VGPRs."""
     body = _kernel_body(mla_asm, sparse).splitlines()
     inside, pending, found, bad = False, {}, 0, []
     for i, line in enumerate(body):
@@ -116,9 +117,10 @@ def test_untracked_loads_untouched_until_waited(mla_asm, sparse):
             pending.clear()
             continue
         if inside:
-            m = re.match(r"global_load_dword\s+v(\d+),", code)
+            m = re.match(r"global_load_dword(?:x4)?\s+(v\[\d+:\d+\]|v\d+),", code)
             if m:
-                pending[int(m.group(1))] = i
+                for r in _vregs(m.group(1)):
+                    pending[r] = i
                 found += 1
             continue
         hit = _vregs(code) & set(pending)
