@@ -907,7 +907,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       // splits 4 at a time (kPrefixMergeChunk, also in wave_finish), so the
       // bits of a unit do not depend on which workgroup completes it.
       if (PREFIX)
-        merge_units_batched<kThreads, 4, kPrefixMergeChunk>(partials, done_units, nd, p.slot_floats, G, D, out, lse);
+        merge_units_batched<kThreads, 2, kPrefixMergeChunk>(partials, done_units, nd, p.slot_floats, G, D, out, lse);
       else
         merge_units_direct<kThreads>(partials, done_units, nd, p.slot_floats, G, D, out, lse);
     }

@@ -232,39 +232,42 @@ __device__ __forceinline__ void merge_unit_direct(const float* pb, int ns, size_
   }
 }
 
-// merge_units_direct for many units at once: the (unit, element) pairs of all
-// nu units are spread over the NT threads, each thread merging UB pairs
-// together with CH splits' loads of every pair in flight, so a workgroup that
-// completes many small units (a few splits each) pays a few load round trips
-// in all rather than one or more per unit.  Splits are combined in index
-// order, as in merge_unit_direct.
+// merge_units_direct for many units at once: the (unit, column quad) pairs
+// of all nu units are spread over the NT threads, each thread merging UB
+// pairs together with CH splits' loads of every pair in flight (m, l and the
+// quad's four o values as two 8-byte loads), so a workgroup that completes
+// many small units (a few splits each) pays a few load round trips in all
+// rather than one or more per unit.  dv must be a multiple of 4 (slots and o
+// are 16-byte aligned).  Splits are combined in index order and each element
+// gets the operations of merge_unit_direct<., CH>, so both give the same bits.
 template <int NT, int UB, int CH>
 __device__ void merge_units_batched(const float* partials, const int (*units)[3], int nu, int slot_floats, int hpu,
                                     int dv, float* out, float* lse) {
   constexpr float kLn2 = 0.69314718055994531f;
-  const int E = hpu * dv;
+  const int E4 = hpu * dv / 4;  // column quads per unit
   const int o_off = partial_o_offset(hpu);
-  const int total = nu * E;
+  const int total = nu * E4;
   for (int base = threadIdx.x; base < total; base += NT * UB) {
     const float* pb[UB];
     int ns[UB], hh[UB], ee[UB], nsmax = 0;
-    float M[UB], L[UB], O[UB];
+    float M[UB], L[UB], O[UB][4];
 #pragma unroll
     for (int k = 0; k < UB; ++k) {
       const int pr = base + k * NT;
       const bool ok = pr < total;
-      const int u = ok ? pr / E : 0;
-      ee[k] = ok ? pr - u * E : 0;
+      const int u = ok ? pr / E4 : 0;
+      ee[k] = ok ? 4 * (pr - u * E4) : 0;  // first element of the quad
       hh[k] = ee[k] / dv;
       ns[k] = ok ? units[u][1] : 0;
       pb[k] = partials + (size_t)units[u][0] * slot_floats;
       nsmax = max(nsmax, ns[k]);
       M[k] = -INFINITY;
       L[k] = 0.f;
-      O[k] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) O[k][c] = 0.f;
     }
     for (int s0 = 0; s0 < nsmax; s0 += CH) {
-      float mt[UB][CH], lt[UB][CH], ot[UB][CH];
+      float mt[UB][CH], lt[UB][CH], ot[UB][CH][4];
 #pragma unroll
       for (int k = 0; k < UB; ++k) {
 #pragma unroll
@@ -273,7 +276,13 @@ __device__ void merge_units_batched(const float* partials, const int (*units)[3]
           const float* ps = pb[k] + (size_t)(ok ? s0 + i : 0) * slot_floats;
           mt[k][i] = ok ? partial_load(ps + hh[k]) : -INFINITY;
           lt[k][i] = ok ? partial_load(ps + hpu + hh[k]) : 0.f;
-          ot[k][i] = ok ? partial_load(ps + o_off + ee[k]) : 0.f;
+          const uint64_t* po = reinterpret_cast<const uint64_t*>(ps + o_off + ee[k]);
+          const uint64_t lo = __hip_atomic_load(po, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t hi = __hip_atomic_load(po + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ot[k][i][0] = ok ? __builtin_bit_cast(float, (uint32_t)lo) : 0.f;
+          ot[k][i][1] = ok ? __builtin_bit_cast(float, (uint32_t)(lo >> 32)) : 0.f;
+          ot[k][i][2] = ok ? __builtin_bit_cast(float, (uint32_t)hi) : 0.f;
+          ot[k][i][3] = ok ? __builtin_bit_cast(float, (uint32_t)(hi >> 32)) : 0.f;
         }
       }
 #pragma unroll
@@ -283,12 +292,14 @@ __device__ void merge_units_batched(const float* partials, const int (*units)[3]
         for (int i = 0; i < CH; ++i) Mc = fmaxf(Mc, mt[k][i]);
         const float a = Mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mc);
         L[k] *= a;
-        O[k] *= a;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) O[k][c] *= a;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
           const float f = __builtin_amdgcn_exp2f(mt[k][i] - Mc);
           L[k] += lt[k][i] * f;
-          O[k] += ot[k][i] * f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) O[k][c] += ot[k][i][c] * f;
         }
         M[k] = Mc;
       }
@@ -297,10 +308,11 @@ __device__ void merge_units_batched(const float* partials, const int (*units)[3]
     for (int k = 0; k < UB; ++k) {
       const int pr = base + k * NT;
       if (pr < total) {
-        const int u = pr / E;
+        const int u = pr / E4;
         const size_t row = (size_t)units[u][2] + hh[k];
         const int col = ee[k] - hh[k] * dv;
-        out[row * dv + col] = O[k] / L[k];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) out[row * dv + col + c] = O[k][c] / L[k];
         if (col == 0) lse[row] = (M[k] + __log2f(L[k])) * kLn2;
       }
     }
