@@ -94,22 +94,36 @@ __device__ __forceinline__ int acc_col(int wave, int lane, int idx) {
 
 // Sum of a split tile's partials in split order, written to Y.  A partial
 // slot holds accumulator idx of thread t at idx * kThreads + t.  Run by all
-// kThreads threads of a workgroup (one per accumulator column of the slot).
+// kThreads threads of a workgroup (one per accumulator column of the slot):
+// rounds of kIn accumulators, the loads of up to kSp splits of a round issued
+// before any is used, so a tile of a few splits takes kAcc / kIn load round
+// trips.
 __device__ __forceinline__ void merge_tile(const float* pb, int ns, int slot_floats, const int32_t* d, int N,
                                            float* __restrict__ y, int t) {
   const int wave = t >> 6, lane = t & 63;
   const int row0 = d[1], rows = d[2], col0 = d[3];
-  constexpr int kIn = 8;  // accumulators per round, every split's load in flight
+  constexpr int kIn = 16;  // accumulators per round
+  constexpr int kSp = 4;   // splits per round
   for (int i0 = 0; i0 < kAcc; i0 += kIn) {
     float s[kIn];
 #pragma unroll
     for (int q = 0; q < kIn; ++q) s[q] = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-      float v[kIn];
+    for (int s0 = 0; s0 < ns; s0 += kSp) {
+      float v[kSp][kIn];
 #pragma unroll
-      for (int q = 0; q < kIn; ++q) v[q] = partial_load(pb + (size_t)sp * slot_floats + (size_t)(i0 + q) * kThreads + t);
+      for (int sp = 0; sp < kSp; ++sp) {
+        const bool ok = s0 + sp < ns;
+        const float* ps = pb + (size_t)(ok ? s0 + sp : 0) * slot_floats + (size_t)i0 * kThreads + t;
 #pragma unroll
-      for (int q = 0; q < kIn; ++q) s[q] += v[q];
+        for (int q = 0; q < kIn; ++q) v[sp][q] = ok ? partial_load(ps + (size_t)q * kThreads) : 0.f;
+      }
+#pragma unroll
+      for (int sp = 0; sp < kSp; ++sp) {
+        if (s0 + sp < ns) {  // in split order; absent splits add nothing (not even +0)
+#pragma unroll
+          for (int q = 0; q < kIn; ++q) s[q] += v[sp][q];
+        }
+      }
     }
 #pragma unroll
     for (int q = 0; q < kIn; ++q) {
