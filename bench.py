@@ -321,7 +321,7 @@ def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
     log(args, f"workload {cfg.name}: {cfg.num_experts} experts, rows {int(wl.expert_tokens.sum())} "
               f"(max {int(wl.expert_tokens.max())}, min {int(wl.expert_tokens.min())}), K {cfg.hidden}, N {cfg.out_dim}")
     t0 = time.perf_counter()
-    workers = cus * B.MOE_WORKGROUPS_PER_CU   # two resident workgroups per compute unit: one wave
+    workers = cus * B.MOE_WORKGROUPS_PER_CU   # the resident workgroups of one wave
     for _ in range(20):
         plan = B.moe_plan(prob, wl.expert_tokens, num_cus=workers, num_xcds=xcds)
     plan_us = (time.perf_counter() - t0) / 20 * 1e6
@@ -353,7 +353,7 @@ def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
         "config": {"workload": cfg.name, "experts": cfg.num_experts, "hidden": cfg.hidden, "out_dim": cfg.out_dim,
                    "tokens": cfg.tokens, "top_k": cfg.top_k, "rows": int(wl.expert_tokens.sum()),
                    "rows_max_min": [int(wl.expert_tokens.max()), int(wl.expert_tokens.min())],
-                   "tile": [128, 128, 64], "num_cus": cus, "num_xcds": xcds, "workers": workers,
+                   "tile": [128, 256, 64], "num_cus": cus, "num_xcds": xcds, "workers": workers,
                    "plan_policy": (f"streamk_dp: whole tiles round-robin, the last partial round split in equal "
                                    f"cost chunks (1 per k tile + {int(plan.view(np.int32)[23])} per tile)")},
         "us_per_batch": st["mean_us"], "us_per_batch_median": st["median_us"],

@@ -351,15 +351,15 @@ def moe_problem(num_experts: int, hidden: int, out_dim: int) -> MoEProblem:
     return MoEProblem(num_experts, hidden, out_dim)
 
 
-MOE_WORKGROUPS_PER_CU = 2  # the MoE kernel's workgroups (64 KiB of LDS each) that fit on one compute unit
+MOE_WORKGROUPS_PER_CU = 1  # the MoE kernel's workgroups (144 KiB of LDS each) that fit on one compute unit
 
 
 def moe_plan(prob: MoEProblem, expert_tokens, num_cus=256 * MOE_WORKGROUPS_PER_CU, num_xcds=8,
              policy=POLICY_STREAMK_DP, unit_cost=None, tile_rows=MOE_TILE_ROWS, tile_k=MOE_TILE_K) -> np.ndarray:
     """MoE grouped-GEMM plan blob (uint8 array).  num_cus: the workers of the
     one wave, MOE_WORKGROUPS_PER_CU per compute unit.  The default policy
-    deals whole tiles round-robin and splits only the last partial round
-    (POLICY_STREAMK_DP); unit_cost None: one k tile per output tile."""
+    deals whole tiles round-robin and splits only the last round and the
+    remainder (POLICY_STREAMK_DP); unit_cost None: one k tile per output tile."""
     lib = load()
     opts = PlanOpts(num_cus, num_xcds, tile_k, tile_rows, policy, 1 if unit_cost is None else unit_cost)
     et = _i32(expert_tokens)

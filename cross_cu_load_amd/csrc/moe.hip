@@ -10,16 +10,20 @@
 // summed just in time by the piece that finishes last (MeldKernel summary,
 // "Core method"), in split order, so the result does not depend on timing.
 //
-// A workgroup is 4 waves, one per SIMD; wave (wm, wn) owns the 64 x 64
-// quarter (wm, wn) of the 128 x 128 output tile as 2 x 2 blocks of
+// A workgroup is 8 waves, two per SIMD; wave (wm, wn) = (w / 4, w % 4) owns
+// the 64 x 64 block (wm, wn) of the 128 x 256 output tile as 2 x 2 blocks of
 // v_mfma_f32_32x32x16_bf16 (64 fp32 accumulators per lane).  Both operands
 // are K-contiguous (X rows; W rows = output columns), so a lane's 8-element
-// MFMA operand is one 16-byte LDS read.  Each 64-wide k step of both operand
-// tiles (16 KiB each) goes HBM -> LDS with global_load_lds_dwordx4 into one
-// of two stages while the other stage computes.  In LDS, row r's 16-byte
-// chunk c sits at chunk position c ^ ((r / 2) % 8) of the row's 128 bytes:
-// a 16-byte read by 16 lanes of 16 consecutive rows' chunk c then covers the
-// 64 banks (256 bytes) once, as two rows share one 256-byte bank line.
+// MFMA operand is one 16-byte LDS read.  Each 64-wide k step of the operand
+// tiles (16 KiB of X, 32 KiB of W) goes HBM -> LDS with
+// global_load_lds_dwordx4 into a ring of three stages, two steps ahead of the
+// one being computed; one workgroup per compute unit (144 KiB of LDS).  The
+// 256-wide tile moves 48 KiB per 4.2 MFLOP, a quarter less than two 128-wide
+// tiles, and the per-CU load path (about 64 bytes a clock) is what bounds a
+// grouped GEMM with experts this small.  In LDS, row r's 16-byte chunk c
+// sits at chunk position c ^ ((r / 2) % 8) of the row's 128 bytes: a 16-byte
+// read by 16 lanes of 16 consecutive rows' chunk c then covers the 64 banks
+// (256 bytes) once, as two rows share one 256-byte bank line.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -39,14 +43,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kBM = 128, kBN = kMoeTileCols, kBK = 64;
-constexpr int kWaves = 4, kThreads = 64 * kWaves;
-constexpr int kTileBytes = kBM * kBK * 2;        // one operand tile of one stage: 16 KiB
-constexpr int kDma = kTileBytes / 1024 / kWaves;  // 1 KiB transfers per wave per operand and stage: 4
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kStages = 3;
+constexpr int kTileA = kBM * kBK * 2;            // X tile of one stage: 16 KiB
+constexpr int kTileB = kBN * kBK * 2;            // W tile of one stage: 32 KiB
+constexpr int kDmaA = kTileA / 1024 / kWaves;    // 1 KiB transfers per wave and stage: 2 of X
+constexpr int kDmaB = kTileB / 1024 / kWaves;    // and 4 of W
+constexpr int kDma = kDmaA + kDmaB;
 constexpr int kAcc = 64;                          // accumulators per lane: 2 x 2 blocks x 16
-static_assert(kBM == kBN, "both operand tiles use one geometry");
+static_assert(kBN == 2 * kBM && kWaves == 8, "waves form a 2 x 4 grid of 64 x 64 blocks");
 
-__shared__ __attribute__((aligned(16))) char lds_a[2][kTileBytes];
-__shared__ __attribute__((aligned(16))) char lds_b[2][kTileBytes];
+__shared__ __attribute__((aligned(16))) char lds_a[kStages][kTileA];
+__shared__ __attribute__((aligned(16))) char lds_b[kStages][kTileB];
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ const char* uni_ptr(const char* p) {
@@ -66,6 +74,10 @@ __device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, char
                :: "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -82,14 +94,15 @@ struct Params {
 };
 
 // Where accumulator idx = 16 (2 i + j) + r of thread (wave, lane) sits in the
-// 128 x 128 tile: block (i, j) of the wave's quarter, MFMA output register r.
+// 128 x 256 tile: block (i, j) of the wave's 64 x 64 block, MFMA output
+// register r.
 __device__ __forceinline__ int acc_row(int wave, int lane, int idx) {
   const int i = idx >> 5, r = idx & 15;
-  return (wave >> 1) * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  return (wave >> 2) * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 __device__ __forceinline__ int acc_col(int wave, int lane, int idx) {
   const int j = (idx >> 4) & 1;
-  return (wave & 1) * 64 + 32 * j + (lane & 31);
+  return (wave & 3) * 64 + 32 * j + (lane & 31);
 }
 
 // Sum of a split tile's partials in split order, written to Y.  A partial
@@ -172,32 +185,34 @@ moe_gemm_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* 
     c.col0 = uni(d[3]);
   };
 
-  // transfer i of this wave moves rows 8 q .. 8 q + 7 (q = 4 wave + i) of an
-  // operand tile: lane L takes row 8 q + L / 8, k chunk (L % 8) ^ ((row / 2) % 8);
+  // X transfer i of this wave moves rows 8 q .. 8 q + 7 (q = kDmaA wave + i)
+  // of the X tile, W transfer i rows 8 q .. (q = kDmaB wave + i) of the W
+  // tile: lane L takes row 8 q + L / 8, k chunk (L % 8) ^ ((row / 2) % 8);
   // rows of X past the tile's last row repeat it (their outputs are dropped)
-  uint32_t voff_b[kDma];
+  uint32_t voff_b[kDmaB];
 #pragma unroll
-  for (int i = 0; i < kDma; ++i) {
-    const int n = 8 * (kDma * wave + i) + (lane >> 3);
+  for (int i = 0; i < kDmaB; ++i) {
+    const int n = 8 * (kDmaB * wave + i) + (lane >> 3);
     voff_b[i] = (uint32_t)((n * K + 8 * ((lane & 7) ^ ((n >> 1) & 7))) * 2);
   }
   auto issue = [&](const Cur& c, int stage) {
     const char* sa = uni_ptr(reinterpret_cast<const char*>(x) + ((size_t)c.row0 * K + c.kb) * 2);
     const char* sb = uni_ptr(reinterpret_cast<const char*>(w) + (((size_t)c.e * N + c.col0) * K + c.kb) * 2);
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-      const int q = kDma * wave + i;
+    for (int i = 0; i < kDmaA; ++i) {
+      const int q = kDmaA * wave + i;
       const int r = 8 * q + (lane >> 3);
       const uint32_t voff_a = (uint32_t)((min(r, c.rows - 1) * K + 8 * ((lane & 7) ^ ((r >> 1) & 7))) * 2);
       lds_dma16(sa, voff_a, lds_a[stage] + 1024 * q);
-      lds_dma16(sb, voff_b[i], lds_b[stage] + 1024 * q);
     }
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) lds_dma16(sb, voff_b[i], lds_b[stage] + 1024 * (kDmaB * wave + i));
   };
 
   // operand reads: block i (j) of the wave's rows (columns) is row
   // base + lane % 32 of its tile (base a multiple of 32, so (row / 2) % 8 is
   // (lane / 2) % 8); k step ks reads chunk 2 ks + lane / 32
-  const int arow = (wave >> 1) * 64 + (lane & 31), bcol = (wave & 1) * 64 + (lane & 31);
+  const int arow = (wave >> 2) * 64 + (lane & 31), bcol = (wave & 3) * 64 + (lane & 31);
   auto chunk_pos = [&](int row, int ks) { return row * 128 + (((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4); };
 
   f32x16 acc[2][2];
@@ -222,17 +237,34 @@ moe_gemm_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* 
   };
   issue(f, 0);
   fvalid = advance(f);
+  // whether the stage after the one about to be computed is in flight
+  bool next_issued = false;
+  if (fvalid) {
+    issue(f, 1);
+    fvalid = advance(f);
+    next_issued = true;
+  }
 
   // split pieces this workgroup holds (a chunk's first and last items):
   // unit << 10 | split, -1 for none; they arrive after the stream
   int pend[2] = {-1, -1};
   int stage = 0;
+  bool stored = false;  // stores issued since the last full wait
   for (;;) {
-    wait_vmem();  // this wave's transfers of the current stage have landed
-    barrier();    // every wave's have, and every wave is done with the other stage
+    // this wave's transfers of the current stage have landed: only the next
+    // stage's kDma transfers may still be in flight (with stores issued after
+    // them, wait for everything)
+    if (next_issued && !stored)
+      wait_vmcnt<kDma>();
+    else
+      wait_vmem();
+    stored = false;
+    barrier();  // every wave's have, and every wave is done with the stage computed last
+    bool issued = false;
     if (fvalid) {
-      issue(f, stage ^ 1);
+      issue(f, stage == 0 ? 2 : stage - 1);  // (stage + 2) % 3
       fvalid = advance(f);
+      issued = true;
     }
     const char* ta = lds_a[stage];
     const char* tb = lds_b[stage];
@@ -276,9 +308,11 @@ moe_gemm_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* 
         }
       }
       zero();
+      stored = true;
     }
     if (!advance(c)) break;
-    stage ^= 1;
+    stage = stage == 2 ? 0 : stage + 1;
+    next_issued = issued;
   }
   if (tl && tid == 0) tl[1] = tl[2] = __builtin_amdgcn_s_memrealtime();
 

@@ -454,8 +454,9 @@ int build_moe(const cc_moe_problem& mp, const cc_plan_opts& o, const int32_t* ex
     chunks.resize(C);
     for (int64_t u = 0; u < U; ++u) chunks[u].push_back({u, 0, K});
   } else if (o.policy == CC_POLICY_STREAMK_DP) {
-    // whole tiles round-robin, round by round; the last U mod C tiles split
-    const int64_t full = U / C;
+    // whole tiles round-robin, round by round, for all but the last whole
+    // round; the remaining C + U mod C tiles (or all of them) are split
+    const int64_t full = std::max<int64_t>(U / C - 1, 0);
     chunks.resize(C);
     for (int64_t k = 0; k < C; ++k)
       for (int64_t r = 0; r < full; ++r) chunks[k].push_back({r * C + k, 0, K});

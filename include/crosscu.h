@@ -78,11 +78,13 @@ enum { CC_KV_NHD = 0, CC_KV_HND = 1 };
  *  PER_UNIT:  one worker per unit (query heads sharing one K/V stream), no
  *             split — the classic one-workgroup-per-(sequence, head) launch. */
 /*  STREAMK_DP: (cc_moe_plan only) the data-parallel + Stream-K form of the
- *             same equal split: the first U - U mod C units go whole, unit
- *             r C + k to chunk k in round r (so units computed at the same
- *             time are neighbours and share operand tiles in cache), and only
- *             the last U mod C units are split as STREAMK splits.  Every
- *             chunk gets the same work to within one tile.                  */
+ *             same equal split: with D = max(U div C - 1, 0) whole rounds,
+ *             the first D C units go whole, unit r C + k to chunk k in round
+ *             r (so units computed at the same time are neighbours and share
+ *             operand tiles in cache), and the remaining U - D C units are
+ *             split as STREAMK splits them; each chunk's share of those is at
+ *             least one unit, so a split unit has at most two pieces at unit
+ *             cost 0.  Every chunk gets the same work to within one tile.   */
 enum { CC_POLICY_STREAMK = 0, CC_POLICY_PER_UNIT = 1, CC_POLICY_STREAMK_DP = 2 };
 
 /* Unit costs (in tiles) measured for this library's kernels: a GQA unit's
@@ -212,7 +214,7 @@ int cc_plan_prefix(const cc_problem* prob, const cc_plan_opts* opts, const int32
  *   x  bf16 [R][hidden], w bf16 [num_experts][out_dim][hidden] (row n of
  *   expert e is its output column n), y fp32 [R][out_dim], R = sum of
  *   expert_tokens.
- * The plan cuts the output into tiles of opts.heads_per_unit rows x 128
+ * The plan cuts the output into tiles of opts.heads_per_unit rows x 256
  * columns (unit = expert, column block, row block) and each tile's hidden
  * range into k tiles of opts.tile_tokens; the (tile, k tile) work is split
  * into num_cus equal chunks as for decode (CC_POLICY_STREAMK, unit_cost) or
@@ -220,7 +222,7 @@ int cc_plan_prefix(const cc_problem* prob, const cc_plan_opts* opts, const int32
  * compute units is summed in split order by its last piece to finish
  * (cc_moe_gemm) or by a second kernel (cc_moe_gemm_variant with
  * CC_REDUCE_SPLIT_COMBINE).  cc_moe_gemm needs heads_per_unit = 128,
- * tile_tokens = 64, hidden % 64 == 0, out_dim % 128 == 0.  The plan blob has
+ * tile_tokens = 64, hidden % 64 == 0, out_dim % 256 == 0.  The plan blob has
  * the layout of a decode plan (mode CC_MODE_MOE) and works with
  * cc_workspace_size / cc_workspace_init / cc_workspace_check. */
 typedef struct cc_moe_problem {

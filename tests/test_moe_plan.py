@@ -13,7 +13,7 @@ def _case(seed):
     rng = np.random.default_rng(11000 + seed)
     E = int(rng.integers(1, 20))
     K = 64 * int(rng.integers(1, 9))
-    N = 128 * int(rng.integers(1, 5))
+    N = PL.MOE_TILE_COLS * int(rng.integers(1, 5))
     et = rng.integers(0, 600, size=E).astype(np.int32)
     et[rng.random(E) < 0.2] = 0
     if et.sum() == 0:
@@ -36,8 +36,9 @@ def test_moe_plan_bytes_and_coverage(lib, seed):
     off = np.concatenate([[0], np.cumsum(et)])
     cover = np.zeros((int(off[-1]), N), np.int32)
     for (e, r0, rows, c0) in ref["units"]:
-        assert off[e] <= r0 and r0 + rows <= off[e + 1] and 1 <= rows <= 128 and c0 % 128 == 0
-        cover[r0:r0 + rows, c0:c0 + 128] += 1
+        TC = PL.MOE_TILE_COLS
+        assert off[e] <= r0 and r0 + rows <= off[e + 1] and 1 <= rows <= 128 and c0 % TC == 0
+        cover[r0:r0 + rows, c0:c0 + TC] += 1
     assert np.all(cover == 1)
     # every tile's k range exactly once, splits in order
     got = {u: [] for u in range(ref["num_units"])}
@@ -64,7 +65,9 @@ def test_moe_plan_rejects_bad_inputs(lib):
     with pytest.raises(B.CrossCUError):
         B.moe_plan(B.moe_problem(3, 200, 256), np.array([1, 2, 3], np.int32))      # hidden % 64
     with pytest.raises(B.CrossCUError):
-        B.moe_plan(B.moe_problem(3, 256, 200), np.array([1, 2, 3], np.int32))      # out_dim % 128
+        B.moe_plan(B.moe_problem(3, 256, 200), np.array([1, 2, 3], np.int32))      # out_dim % 256
+    with pytest.raises(B.CrossCUError):
+        B.moe_plan(B.moe_problem(3, 256, 384), np.array([1, 2, 3], np.int32))      # out_dim % 256
 
 
 def test_moe_gemm_rejects_before_any_launch(lib):
@@ -83,3 +86,30 @@ def test_moe_gemm_rejects_before_any_launch(lib):
     decode_plan = B.plan(B.problem(0, 2, 1, 8, 2, 64, 64, 16, 2, 4, 0, 0.125), np.array([10, 20], np.int32), None,
                          num_cus=8, num_xcds=1)
     assert call(prob, plan=decode_plan, b=1 << 30) == B.CC_ERR_PLAN
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_streamk_dp_splits_a_tile_at_most_twice(seed):
+    """With at least two rounds of tiles, STREAMK_DP keeps all but the last
+    whole round data-parallel and splits the rest at least one tile per
+    chunk: every tile has at most two pieces, the first rounds are whole
+    tiles dealt round-robin, and the chunks' k tiles differ by at most one."""
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.integers(4, 12))
+    C = int(rng.integers(2, 12))
+    counts = rng.integers(0, 600, E)
+    counts[0] = max(counts[0], 1)
+    TC = PL.MOE_TILE_COLS
+    pl = PL.plan_moe(E, 256, 2 * TC, counts, C, 1, policy=PL.POLICY_STREAMK_DP)
+    U = pl["num_units"]
+    if U < 2 * C:
+        pytest.skip("fewer than two rounds of tiles")
+    assert max(pl["unit_nsplit"]) <= 2
+    D = U // C - 1
+    items = pl["chunk_items"]
+    for k in range(C):
+        its = items[k]
+        assert [it[0] for it in its[:D]] == [r * C + k for r in range(D)]
+        assert all(it[1] == 0 and it[2] == 256 for it in its[:D])
+    work = [sum((it[2] - it[1]) // 64 for it in items[k]) for k in range(C)]
+    assert max(work) - min(work) <= 1
