@@ -116,6 +116,52 @@ def _time_steps(torch, run, steps, warmup, flush, kernel_events):
     return np.array([a.elapsed_time(b) for a, b in ev])
 
 
+def time_interleaved(torch, runs, steps, warmup, flush, kernel_events):
+    """Kernel-timed steps of several launches in alternating rounds: round i
+    runs every launch once (the order rotated each round), each after the
+    flush, so a slow drift of the shader clock over the run (the MFMA-bound
+    kernels show one) reaches every launch alike.  runs: {name: (fn, steps)};
+    a launch with fewer steps than the others takes part in the first rounds
+    only.  Returns {name: ms array}."""
+    import gc
+    gc.collect()
+    gc.disable()
+    try:
+        stream = torch.cuda.current_stream()
+        names = list(runs)
+        for _ in range(warmup):
+            for n in names:
+                if flush:
+                    flush()
+                runs[n][0]()
+        torch.cuda.synchronize()
+        ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(runs[n][1])] for n in names}
+        for n in names:
+            for a, b in ev[n]:
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        rounds = max(runs[n][1] for n in names)
+        for i in range(rounds):
+            for j in range(len(names)):
+                n = names[(i + j) % len(names)]
+                if i >= runs[n][1]:
+                    continue
+                a, b = ev[n][i]
+                if flush:
+                    flush()
+                kernel_events(a, b)
+                runs[n][0]()
+                kernel_events(None, None)
+            if i % 16 == 15:
+                torch.cuda.synchronize()  # bounded queue of pending launches
+        torch.cuda.synchronize()
+        return {n: np.array([a.elapsed_time(b) for a, b in ev[n]]) for n in names}
+    finally:
+        gc.enable()
+
+
 def stats(ms):
     return dict(mean_us=float(ms.mean() * 1e3), median_us=float(np.median(ms) * 1e3),
                 p10_us=float(np.percentile(ms, 10) * 1e3), p90_us=float(np.percentile(ms, 90) * 1e3))
@@ -326,25 +372,26 @@ def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
         plan = B.moe_plan(prob, wl.expert_tokens, num_cus=workers, num_xcds=xcds)
     plan_us = (time.perf_counter() - t0) / 20 * 1e6
     s = B.moe_session(wl, plan)
-    ms = time_steps(torch, s.run, args.steps, args.warmup, flush, ke)
+    # the fused launch and the comparison launches in alternating rounds: this
+    # kernel is bound by on-chip work, and the shader clock drifts over a run
+    runs = {"fused": (s.run, args.steps)}
+    if not args.no_variants:
+        v1_plan = B.moe_plan(prob, wl.expert_tokens, num_cus=workers, num_xcds=xcds, policy=B.POLICY_PER_UNIT)
+        v1 = B.moe_session(wl, v1_plan)
+        v2 = B.moe_session(wl, plan)
+        runs["per_tile_workgroup"] = (v1.run, args.variant_steps)
+        runs["split_then_combine"] = (lambda: v2.run(B.REDUCE_SPLIT_COMBINE), args.variant_steps)
+    timed = time_interleaved(torch, runs, args.steps, args.warmup, flush, ke)
+    ms = timed["fused"]
     ms_markers = time_steps(torch, s.run, args.steps, args.warmup, flush)
     st = stats(ms)
     dirty, flags = B.workspace_check(plan, s.workspace)
     assert dirty == 0 and flags == 0, "workspace left dirty"
     workers = int(plan.view(np.int32)[11])
     tline = timeline_pass(torch, B, s, workers, xcds, flush)
-    variants = {}
-    if not args.no_variants:
-        v1_plan = B.moe_plan(prob, wl.expert_tokens, num_cus=workers, num_xcds=xcds, policy=B.POLICY_PER_UNIT)
-        v1 = B.moe_session(wl, v1_plan)
-        variants["per_tile_workgroup"] = stats(time_steps(torch, v1.run, args.variant_steps, 3, flush, ke))
-        del v1
-        v2 = B.moe_session(wl, plan)
-        variants["split_then_combine"] = stats(time_steps(
-            torch, lambda: v2.run(B.REDUCE_SPLIT_COMBINE), args.variant_steps, 3, flush, ke))
-        del v2
-        for v in variants.values():
-            v["tflops"] = wl.flops() / (v["mean_us"] * 1e-6) / 1e12
+    variants = {k: stats(v) for k, v in timed.items() if k != "fused"}
+    for v in variants.values():
+        v["tflops"] = wl.flops() / (v["mean_us"] * 1e-6) / 1e12
     tflops = wl.flops() / (st["mean_us"] * 1e-6) / 1e12
     result = {
         "metric": MOE_METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -358,7 +405,8 @@ def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
                                    f"cost chunks (1 per k tile + {int(plan.view(np.int32)[23])} per tile)")},
         "us_per_batch": st["mean_us"], "us_per_batch_median": st["median_us"],
         "us_p10_p90": [st["p10_us"], st["p90_us"]],
-        "timing": "kernel start to end (hipExtLaunchKernel events), cold, per step",
+        "timing": ("kernel start to end (hipExtLaunchKernel events), cold, per step; the comparison launches "
+                   "in alternating rounds with it"),
         "us_per_batch_event_markers": stats(ms_markers),
         "plan_host_us": plan_us,
         "min_bytes": wl.bytes_min(), "min_bytes_gbs": wl.bytes_min() / (st["mean_us"] * 1e-6) / 1e9,
