@@ -152,3 +152,25 @@ def test_wide_asm_stores_end_with_a_wait_state(mla_asm, sparse):
             if not nxt.startswith("s_nop"):
                 bad.append(f"line {i}: {code} followed by {nxt!r}")
     assert not bad, "; ".join(bad[:3])
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_score_chain_carries_no_vmcnt_wait(mla_asm, sparse):
+    """The score MFMAs (the chain accumulating in VGPRs) must not wait on
+    vector memory: q, page and row-id loads are covered by the wait at the top
+    of the step, and the tile's own transfers land before it.  A compiler that
+    tracked a q load again would put vmcnt(N) waits in front of them (it did,
+    with N counting down to the transfers in flight, before q was loaded
+    untracked)."""
+    lines = _kernel_body(mla_asm, sparse).splitlines()
+    chain, waited = 0, []
+    for i, line in enumerate(lines):
+        if re.search(r"v_mfma_f32_32x32x16_bf16 v\[", line):
+            chain += 1
+            for j in range(i - 1, max(0, i - 4), -1):
+                if "s_waitcnt" in lines[j]:
+                    if "vmcnt" in lines[j]:
+                        waited.append(f"line {j}: {lines[j].strip()}")
+                    break
+    assert chain >= 36, "the score chain's MFMAs were not found"
+    assert not waited, "vmcnt waits in front of score MFMAs: " + "; ".join(waited[:3])
