@@ -670,22 +670,30 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   Cursor c3{cur, i0, 0, cur_nb}, c4 = c3;
   uint32_t sid2 = 0, sid_fl = 0, spg_fl = 0;
   if constexpr (SPARSE) {
-    // tiles 0 and 1 and the state of step 0 with ordinary loads (once)
-    Cursor c = c3;
-    const uint32_t s0 = sid_check(c.I, (uint32_t)*sid_ptr(c.I, c.j));
-    const uint32_t p0 = spg_check((uint32_t)*spg_ptr(c.I, s0));
-    adv(c);
-    const uint32_t s1 = sid_check(c.I, (uint32_t)*sid_ptr(c.I, c.j));
-    const uint32_t p1 = spg_check((uint32_t)*spg_ptr(c.I, s1));
-    adv(c);
-    sid2 = sid_check(c.I, (uint32_t)*sid_ptr(c.I, c.j));
-    spg_fl = (uint32_t)*spg_ptr(c.I, sid2);
-    adv(c);
-    c3 = c;
-    sid_fl = (uint32_t)*sid_ptr(c3.I, c3.j);
-    c4 = c3;
-    adv(c4);
+    // tiles 0 and 1 and the state of step 0 with ordinary loads (once): q
+    // first (untracked, it lands behind everything below), then the row ids
+    // of tiles 0..3 in one round of loads and the block-table entries of
+    // tiles 0..2 in a second, every load of a round issued before any check
+    // (the checks' error atomics would otherwise order each load behind the
+    // previous tile's)
     load_q(cur.unit);
+    Cursor t1 = c3;
+    adv(t1);
+    Cursor t2 = t1;
+    adv(t2);
+    Cursor t3 = t2;
+    adv(t3);
+    const uint32_t r0 = (uint32_t)*sid_ptr(c3.I, c3.j), r1 = (uint32_t)*sid_ptr(t1.I, t1.j);
+    const uint32_t r2 = (uint32_t)*sid_ptr(t2.I, t2.j);
+    sid_fl = (uint32_t)*sid_ptr(t3.I, t3.j);
+    const uint32_t s0 = sid_check(c3.I, r0), s1 = sid_check(t1.I, r1);
+    sid2 = sid_check(t2.I, r2);
+    const uint32_t g0 = (uint32_t)*spg_ptr(c3.I, s0), g1 = (uint32_t)*spg_ptr(t1.I, s1);
+    spg_fl = (uint32_t)*spg_ptr(t2.I, sid2);
+    const uint32_t p0 = spg_check(g0), p1 = spg_check(g1);
+    c3 = t3;
+    c4 = t3;
+    adv(c4);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) sparse_piece(s0, p0, q, ring[0]);
 #pragma unroll
