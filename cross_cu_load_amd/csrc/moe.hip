@@ -269,22 +269,35 @@ moe_gemm_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* 
     const char* ta = lds_a[stage];
     const char* tb = lds_b[stage];
     u32x4 av[2][4], bv[2][4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    auto rd = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         av[i][ks] = *reinterpret_cast<const u32x4*>(ta + chunk_pos(arow + 32 * i, ks));
         bv[i][ks] = *reinterpret_cast<const u32x4*>(tb + chunk_pos(bcol + 32 * i, ks));
       }
-    }
+    };
+    // operand reads two k steps ahead of the products, in a fixed order
+    // (sched barriers): left to itself the scheduler reuses four operand
+    // registers and waits out an LDS round trip before every four MFMAs, and
+    // with all 16 reads in flight the wait count saturates at 15 and the
+    // first product waits for all of them
+    // the next item's scalar loads (if any) are done: with a scalar load
+    // outstanding the compiler can only wait for LDS reads with lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+    rd(0);
+    rd(1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 2 < 4) rd(ks + 2);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i][ks]),
                                                             __builtin_bit_cast(bf16x8, bv[j][ks]), acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (c.kb + kBK >= c.k1) {
       // -------- the item ends: the tile, or this piece's partial of it
       const int ns = uni(unit_nsplit[c.u]);
