@@ -50,12 +50,15 @@ def key_positions(b: int, t: int, seqlens: np.ndarray, indices: np.ndarray | Non
 
 
 def gather_rows(cache_bits: np.ndarray, block_table: np.ndarray, b: int, J: np.ndarray,
-                page_size: int) -> np.ndarray:
-    """Rows cache[block_table[b, j // P], j % P] for j in J, as float64 [|J|, H, d]."""
+                page_size: int, head: int | None = None) -> np.ndarray:
+    """Rows cache[block_table[b, j // P], j % P] for j in J, as float64 [|J|, H, d]
+    (or [|J|, d] of one head when ``head`` is given)."""
     pages = block_table[b, J // page_size]
     if np.any(pages < 0) or np.any(pages >= cache_bits.shape[0]):
         raise ValueError("block_table entry outside the cache")
-    return bf16_to_f64(cache_bits[pages, J % page_size])
+    if head is None:
+        return bf16_to_f64(cache_bits[pages, J % page_size])
+    return bf16_to_f64(cache_bits[pages, J % page_size, head])
 
 
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> tuple[np.ndarray, np.ndarray]:
@@ -131,9 +134,9 @@ def decode_attention(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray 
     units = only if only is not None else [(b, t, g) for b in range(B) for t in range(Tq) for g in range(Hkv)]
     for b, t, g in units:
         J = key_positions(b, t, seqlens, indices)
-        Krows = gather_rows(k_bits, block_table, b, J, P)[:, g, :]
+        Krows = gather_rows(k_bits, block_table, b, J, P, head=g)
         if v_bits is not None:
-            Vrows = gather_rows(v_bits, block_table, b, J, P)[:, g, :]
+            Vrows = gather_rows(v_bits, block_table, b, J, P, head=g)
         else:
             Vrows = Krows[:, :dv]
         qg = bf16_to_f64(q_bits[b, t, g * G:(g + 1) * G])
