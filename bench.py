@@ -381,6 +381,11 @@ def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
         v2 = B.moe_session(wl, plan)
         runs["per_tile_workgroup"] = (v1.run, args.variant_steps)
         runs["split_then_combine"] = (lambda: v2.run(B.REDUCE_SPLIT_COMBINE), args.variant_steps)
+        # the plain Stream-K split (contiguous equal chunks, every chunk boundary
+        # inside a tile), for what the data-parallel rounds save or cost
+        v3_plan = B.moe_plan(prob, wl.expert_tokens, num_cus=workers, num_xcds=xcds, policy=B.POLICY_STREAMK)
+        v3 = B.moe_session(wl, v3_plan)
+        runs["streamk_contiguous"] = (v3.run, args.variant_steps)
     timed = time_interleaved(torch, runs, args.steps, args.warmup, flush, ke)
     ms = timed["fused"]
     ms_markers = time_steps(torch, s.run, args.steps, args.warmup, flush)
@@ -400,9 +405,10 @@ def bench_moe(args, torch, B, W, cus, xcds, flush, ke):
         "config": {"workload": cfg.name, "experts": cfg.num_experts, "hidden": cfg.hidden, "out_dim": cfg.out_dim,
                    "tokens": cfg.tokens, "top_k": cfg.top_k, "rows": int(wl.expert_tokens.sum()),
                    "rows_max_min": [int(wl.expert_tokens.max()), int(wl.expert_tokens.min())],
-                   "tile": [128, 256, 64], "num_cus": cus, "num_xcds": xcds, "workers": workers,
-                   "plan_policy": (f"streamk_dp: whole tiles round-robin, the last partial round split in equal "
-                                   f"cost chunks (1 per k tile + {int(plan.view(np.int32)[23])} per tile)")},
+                   "tile": [256, 256, 64], "num_cus": cus, "num_xcds": xcds, "workers": workers,
+                   "plan_policy": (f"streamk_dp: whole tiles round-robin; a last round under 3/4 full split in "
+                                   f"equal cost chunks (1 per k tile + {int(plan.view(np.int32)[23])} per tile)"),
+                   "partial_slots": int(plan.view(np.int32)[18])},
         "us_per_batch": st["mean_us"], "us_per_batch_median": st["median_us"],
         "us_p10_p90": [st["p10_us"], st["p90_us"]],
         "timing": ("kernel start to end (hipExtLaunchKernel events), cold, per step; the comparison launches "

@@ -344,14 +344,14 @@ def decode(prob: Problem, plan_host: np.ndarray, plan_dev, q, k_cache, v_cache, 
 
 NOALLOC_WORKSPACE_BYTES = 64 << 20     # CC_NOALLOC_WORKSPACE_BYTES
 MODE_MOE = 3
-MOE_TILE_ROWS, MOE_TILE_K = 128, 64    # the MoE kernel's output-tile rows and k tile
+MOE_TILE_ROWS, MOE_TILE_K = 256, 64    # the MoE kernel's output-tile rows and k tile
 
 
 def moe_problem(num_experts: int, hidden: int, out_dim: int) -> MoEProblem:
     return MoEProblem(num_experts, hidden, out_dim)
 
 
-MOE_WORKGROUPS_PER_CU = 1  # the MoE kernel's workgroups (144 KiB of LDS each) that fit on one compute unit
+MOE_WORKGROUPS_PER_CU = 1  # the MoE kernel's workgroups (128 KiB of LDS each) that fit on one compute unit
 
 
 def moe_plan(prob: MoEProblem, expert_tokens, num_cus=256 * MOE_WORKGROUPS_PER_CU, num_xcds=8,

@@ -3,6 +3,7 @@
 // and touches device memory only through enqueued kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstring>
@@ -343,12 +344,12 @@ int cc_moe_gemm_variant(int reduce, const cc_moe_problem* prob, const void* plan
     cc::set_error("plan was not built for this MoE problem");
     return CC_ERR_PLAN;
   }
-  if (h[cc::H_HPU] != 128 || h[cc::H_TILE] != 64 || prob->hidden % 64 || prob->out_dim % cc::kMoeTileCols) {
-    cc::set_error("MoE kernel: 128-row tiles (heads_per_unit), 64-wide k tiles (tile_tokens), hidden %% 64 == 0, "
-                  "out_dim %% %d == 0", cc::kMoeTileCols);
+  if (h[cc::H_HPU] != cc::kMoeTileRows || h[cc::H_TILE] != 64 || prob->hidden % 64 || prob->out_dim % cc::kMoeTileCols) {
+    cc::set_error("MoE kernel: %d-row tiles (heads_per_unit), 64-wide k tiles (tile_tokens), hidden %% 64 == 0, "
+                  "out_dim %% %d == 0", cc::kMoeTileRows, cc::kMoeTileCols);
     return CC_ERR_UNSUPPORTED;
   }
-  if ((int64_t)prob->hidden * (cc::kMoeTileCols - 1) * 2 + 1024 > INT32_MAX || (int64_t)v.units() >= (1 << 21)) {
+  if ((int64_t)prob->hidden * (std::max(cc::kMoeTileRows, cc::kMoeTileCols) - 1) * 2 + 1024 > INT32_MAX || (int64_t)v.units() >= (1 << 21)) {
     cc::set_error("MoE kernel: hidden too large for 32-bit row offsets or too many tiles");
     return CC_ERR_UNSUPPORTED;
   }

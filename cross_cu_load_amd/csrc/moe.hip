@@ -11,19 +11,21 @@
 // "Core method"), in split order, so the result does not depend on timing.
 //
 // A workgroup is 8 waves, two per SIMD; wave (wm, wn) = (w / 4, w % 4) owns
-// the 64 x 64 block (wm, wn) of the 128 x 256 output tile as 2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 (64 fp32 accumulators per lane).  Both operands
+// the 128 x 64 block (wm, wn) of the 256 x 256 output tile as 4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane).  Both operands
 // are K-contiguous (X rows; W rows = output columns), so a lane's 8-element
 // MFMA operand is one 16-byte LDS read.  Each 64-wide k step of the operand
-// tiles (16 KiB of X, 32 KiB of W) goes HBM -> LDS with
-// global_load_lds_dwordx4 into a ring of three stages, two steps ahead of the
-// one being computed; one workgroup per compute unit (144 KiB of LDS).  The
-// 256-wide tile moves 48 KiB per 4.2 MFLOP, a quarter less than two 128-wide
-// tiles, and the per-CU load path (about 64 bytes a clock) is what bounds a
-// grouped GEMM with experts this small.  In LDS, row r's 16-byte chunk c
-// sits at chunk position c ^ ((r / 2) % 8) of the row's 128 bytes: a 16-byte
-// read by 16 lanes of 16 consecutive rows' chunk c then covers the 64 banks
-// (256 bytes) once, as two rows share one 256-byte bank line.
+// tiles (32 KiB of X, 32 KiB of W) goes HBM -> LDS with
+// global_load_lds_dwordx4 into one of two stages while the other computes;
+// one workgroup per compute unit (128 KiB of LDS).  A k step gives each SIMD
+// 2048 clocks of MFMA work against one barrier, one wait and 64 KiB moved per
+// CU: the fixed cost of a step (the barrier, the operand reads' first round
+// trip, the transfers' issue) is what a grouped GEMM with experts this small
+// loses most to, and the larger tile halves it per flop, outweighing the rows
+// it pads (an expert's last tile is cut to its rows).  In LDS, row r's 16-byte
+// chunk c sits at chunk position c ^ ((r / 2) % 8) of the row's 128 bytes: a
+// 16-byte read by 16 lanes of 16 consecutive rows' chunk c then covers the
+// 64 banks (256 bytes) once, as two rows share one 256-byte bank line.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -42,16 +44,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-constexpr int kBM = 128, kBN = kMoeTileCols, kBK = 64;
+constexpr int kBM = kMoeTileRows, kBN = kMoeTileCols, kBK = 64;
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
-constexpr int kStages = 3;
-constexpr int kTileA = kBM * kBK * 2;            // X tile of one stage: 16 KiB
+constexpr int kStages = 2;
+constexpr int kTileA = kBM * kBK * 2;            // X tile of one stage: 32 KiB
 constexpr int kTileB = kBN * kBK * 2;            // W tile of one stage: 32 KiB
-constexpr int kDmaA = kTileA / 1024 / kWaves;    // 1 KiB transfers per wave and stage: 2 of X
+constexpr int kDmaA = kTileA / 1024 / kWaves;    // 1 KiB transfers per wave and stage: 4 of X
 constexpr int kDmaB = kTileB / 1024 / kWaves;    // and 4 of W
-constexpr int kDma = kDmaA + kDmaB;
-constexpr int kAcc = 64;                          // accumulators per lane: 2 x 2 blocks x 16
-static_assert(kBN == 2 * kBM && kWaves == 8, "waves form a 2 x 4 grid of 64 x 64 blocks");
+constexpr int kAcc = 128;                         // accumulators per lane: 4 x 2 blocks x 16
+static_assert(kBN == kBM && kWaves == 8, "waves form a 2 x 4 grid of 128 x 64 blocks");
 
 __shared__ __attribute__((aligned(16))) char lds_a[kStages][kTileA];
 __shared__ __attribute__((aligned(16))) char lds_b[kStages][kTileB];
@@ -74,10 +75,6 @@ __device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, char
                :: "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -94,11 +91,11 @@ struct Params {
 };
 
 // Where accumulator idx = 16 (2 i + j) + r of thread (wave, lane) sits in the
-// 128 x 256 tile: block (i, j) of the wave's 64 x 64 block, MFMA output
+// 256 x 256 tile: block (i, j) of the wave's 128 x 64 block, MFMA output
 // register r.
 __device__ __forceinline__ int acc_row(int wave, int lane, int idx) {
   const int i = idx >> 5, r = idx & 15;
-  return (wave >> 2) * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  return (wave >> 2) * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 __device__ __forceinline__ int acc_col(int wave, int lane, int idx) {
   const int j = (idx >> 4) & 1;
@@ -212,13 +209,13 @@ moe_gemm_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* 
   // operand reads: block i (j) of the wave's rows (columns) is row
   // base + lane % 32 of its tile (base a multiple of 32, so (row / 2) % 8 is
   // (lane / 2) % 8); k step ks reads chunk 2 ks + lane / 32
-  const int arow = (wave >> 2) * 64 + (lane & 31), bcol = (wave & 3) * 64 + (lane & 31);
+  const int arow = (wave >> 2) * 128 + (lane & 31), bcol = (wave & 3) * 64 + (lane & 31);
   auto chunk_pos = [&](int row, int ks) { return row * 128 + (((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4); };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
   auto zero = [&]() {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   };
@@ -237,61 +234,42 @@ moe_gemm_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* 
   };
   issue(f, 0);
   fvalid = advance(f);
-  // whether the stage after the one about to be computed is in flight
-  bool next_issued = false;
-  if (fvalid) {
-    issue(f, 1);
-    fvalid = advance(f);
-    next_issued = true;
-  }
 
   // split pieces this workgroup holds (a chunk's first and last items):
   // unit << 10 | split, -1 for none; they arrive after the stream
   int pend[2] = {-1, -1};
   int stage = 0;
-  bool stored = false;  // stores issued since the last full wait
   for (;;) {
-    // this wave's transfers of the current stage have landed: only the next
-    // stage's kDma transfers may still be in flight (with stores issued after
-    // them, wait for everything)
-    if (next_issued && !stored)
-      wait_vmcnt<kDma>();
-    else
-      wait_vmem();
-    stored = false;
-    barrier();  // every wave's have, and every wave is done with the stage computed last
-    bool issued = false;
+    wait_vmem();  // this wave's transfers of the current stage (and any stores) are complete
+    barrier();    // every wave's are, and every wave is done with the other stage
     if (fvalid) {
-      issue(f, stage == 0 ? 2 : stage - 1);  // (stage + 2) % 3
+      issue(f, stage ^ 1);
       fvalid = advance(f);
-      issued = true;
     }
     const char* ta = lds_a[stage];
     const char* tb = lds_b[stage];
-    u32x4 av[2][4], bv[2][4];
+    u32x4 av[4][4], bv[2][4];
     auto rd = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        av[i][ks] = *reinterpret_cast<const u32x4*>(ta + chunk_pos(arow + 32 * i, ks));
-        bv[i][ks] = *reinterpret_cast<const u32x4*>(tb + chunk_pos(bcol + 32 * i, ks));
-      }
+      for (int i = 0; i < 4; ++i) av[i][ks] = *reinterpret_cast<const u32x4*>(ta + chunk_pos(arow + 32 * i, ks));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) bv[i][ks] = *reinterpret_cast<const u32x4*>(tb + chunk_pos(bcol + 32 * i, ks));
     };
-    // operand reads two k steps ahead of the products, in a fixed order
-    // (sched barriers): left to itself the scheduler reuses four operand
-    // registers and waits out an LDS round trip before every four MFMAs, and
-    // with all 16 reads in flight the wait count saturates at 15 and the
-    // first product waits for all of them
-    // the next item's scalar loads (if any) are done: with a scalar load
-    // outstanding the compiler can only wait for LDS reads with lgkmcnt(0)
+    // operand reads one k step ahead of the products, in a fixed order
+    // (sched barriers): left to itself the scheduler waits out an LDS round
+    // trip before every few MFMAs, and with more than 15 reads in flight the
+    // wait count saturates and the first product waits for all of them.
+    // The next item's scalar loads (if any) are done first: with a scalar
+    // load outstanding the compiler can only wait for LDS reads with
+    // lgkmcnt(0).
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
     rd(0);
-    rd(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 2 < 4) rd(ks + 2);
+      if (ks + 1 < 4) rd(ks + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i][ks]),
@@ -321,11 +299,9 @@ moe_gemm_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4* 
         }
       }
       zero();
-      stored = true;
     }
     if (!advance(c)) break;
-    stage = stage == 2 ? 0 : stage + 1;
-    next_issued = issued;
+    stage ^= 1;
   }
   if (tl && tid == 0) tl[1] = tl[2] = __builtin_amdgcn_s_memrealtime();
 

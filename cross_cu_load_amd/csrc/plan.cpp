@@ -454,12 +454,16 @@ int build_moe(const cc_moe_problem& mp, const cc_plan_opts& o, const int32_t* ex
     chunks.resize(C);
     for (int64_t u = 0; u < U; ++u) chunks[u].push_back({u, 0, K});
   } else if (o.policy == CC_POLICY_STREAMK_DP) {
-    // whole tiles round-robin, round by round, for all but the last whole
-    // round; the remaining C + U mod C tiles (or all of them) are split
-    const int64_t full = std::max<int64_t>(U / C - 1, 0);
+    // whole tiles round-robin, round by round; the remaining tiles are split
+    // (a last round at least three quarters full runs whole, a remainder of
+    // less than half a round takes the last whole round with it)
+    const int64_t rem = U % C;
+    const bool whole = rem == 0 || 4 * rem >= 3 * C;
+    const int64_t full = whole ? (U + C - 1) / C : (2 * rem >= C ? U / C : std::max<int64_t>(U / C - 1, 0));
     chunks.resize(C);
     for (int64_t k = 0; k < C; ++k)
-      for (int64_t r = 0; r < full; ++r) chunks[k].push_back({r * C + k, 0, K});
+      for (int64_t r = 0; r < full; ++r)
+        if (r * C + k < U) chunks[k].push_back({r * C + k, 0, K});
     if (U > full * C) {
       const std::vector<Work> rest(work.begin() + full * C, work.end());
       const std::vector<std::vector<Piece>> sk = split_chunks(rest, C, BK, o.unit_cost);

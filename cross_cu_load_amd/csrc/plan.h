@@ -35,6 +35,7 @@ constexpr int kItemWords = 4;
 constexpr int kPrefixWords = 20;
 constexpr int kMoeDescWords = 4;  // a MoE unit: expert, first row, rows, first column
 constexpr int kMoeTileCols = 256; // output columns of a MoE tile
+constexpr int kMoeTileRows = 256; // output rows of a MoE tile (the plan's heads_per_unit)
 constexpr int kPrefixRows = 16;  // query rows a prefix unit gathers (members x group size)
 
 enum HeaderField {

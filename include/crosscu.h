@@ -78,13 +78,17 @@ enum { CC_KV_NHD = 0, CC_KV_HND = 1 };
  *  PER_UNIT:  one worker per unit (query heads sharing one K/V stream), no
  *             split — the classic one-workgroup-per-(sequence, head) launch. */
 /*  STREAMK_DP: (cc_moe_plan only) the data-parallel + Stream-K form of the
- *             same equal split: with D = max(U div C - 1, 0) whole rounds,
- *             the first D C units go whole, unit r C + k to chunk k in round
- *             r (so units computed at the same time are neighbours and share
- *             operand tiles in cache), and the remaining U - D C units are
- *             split as STREAMK splits them; each chunk's share of those is at
- *             least one unit, so a split unit has at most two pieces at unit
- *             cost 0.  Every chunk gets the same work to within one tile.   */
+ *             same equal split: the first D C units go whole, unit r C + k to
+ *             chunk k in round r (so units computed at the same time are
+ *             neighbours and share operand tiles in cache), and the remaining
+ *             U - D C units are split as STREAMK splits them.  With
+ *             R = U mod C: R = 0 or 4 R >= 3 C runs every unit whole (the
+ *             last round's units on chunks 0 .. R - 1); 2 R >= C splits the
+ *             remainder alone (D = U div C); a smaller remainder takes the
+ *             last whole round with it (D = U div C - 1).  Each chunk's share
+ *             of a split region is at least half a unit, so a split unit has
+ *             at most three pieces at unit cost 0.  Every chunk gets the same
+ *             work to within one tile.                                     */
 enum { CC_POLICY_STREAMK = 0, CC_POLICY_PER_UNIT = 1, CC_POLICY_STREAMK_DP = 2 };
 
 /* Unit costs (in tiles) measured for this library's kernels: a GQA unit's
@@ -221,7 +225,7 @@ int cc_plan_prefix(const cc_problem* prob, const cc_plan_opts* opts, const int32
  * one worker per output tile (CC_POLICY_PER_UNIT).  A tile split across
  * compute units is summed in split order by its last piece to finish
  * (cc_moe_gemm) or by a second kernel (cc_moe_gemm_variant with
- * CC_REDUCE_SPLIT_COMBINE).  cc_moe_gemm needs heads_per_unit = 128,
+ * CC_REDUCE_SPLIT_COMBINE).  cc_moe_gemm needs heads_per_unit = 256,
  * tile_tokens = 64, hidden % 64 == 0, out_dim % 256 == 0.  The plan blob has
  * the layout of a decode plan (mode CC_MODE_MOE) and works with
  * cc_workspace_size / cc_workspace_init / cc_workspace_check. */

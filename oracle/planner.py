@@ -58,6 +58,7 @@ PREFIX_ROWS = 16                 # query rows one prefix unit gathers (members x
 MODE_GQA, MODE_MLA, MODE_MLA_SPARSE, MODE_MOE = 0, 1, 2, 3
 MOE_DESC_WORDS = 4               # a MoE unit: expert, first row, rows, first column
 MOE_TILE_COLS = 256              # output columns of a MoE unit (the C planner's fixed tile width)
+MOE_TILE_ROWS = 256              # output rows of a MoE unit (the kernel's tile height)
 POLICY_STREAMK, POLICY_PER_UNIT, POLICY_STREAMK_DP = 0, 1, 2
 
 
@@ -430,7 +431,7 @@ def plan_prefix(mode, batch, q_tokens, num_q_heads, num_kv_heads, head_dim_qk, h
                            prefix_pieces=pieces_of_prefix))
 
 
-def plan_moe(num_experts, hidden, out_dim, expert_tokens, num_cus, num_xcds, tile_rows=128, tile_cols=MOE_TILE_COLS,
+def plan_moe(num_experts, hidden, out_dim, expert_tokens, num_cus, num_xcds, tile_rows=MOE_TILE_ROWS, tile_cols=MOE_TILE_COLS,
              tile_k=64, policy=POLICY_STREAMK, unit_cost=0) -> dict:
     """A Stream-K plan for the MoE grouped GEMM Y_e = X_e W_e^T.
 
@@ -446,15 +447,21 @@ def plan_moe(num_experts, hidden, out_dim, expert_tokens, num_cus, num_xcds, til
       (unit, KV tile) work; a piece is a unit's k range within one chunk and
       its split index counts the unit's pieces in chunk order.
     * POLICY_STREAMK_DP (the data-parallel + Stream-K form of the same equal
-      split): with D = max(U div C - 1, 0) whole rounds, the first D C tiles
-      go whole, tile r C + k to chunk k in round r, so the tiles computed at
-      the same time are neighbours that share weight and row tiles in cache;
-      the remaining U - D C tiles (C + U mod C of them when U >= C) have
-      their k tiles split over the chunks as above.  Every chunk still gets
-      the same work to within one k tile, and as each chunk's share of the
-      split region is at least one tile, a tile there has at most two pieces
-      (unit cost 0): the sum of a split tile reads one other partial, not a
-      share of U mod C tiles cut C ways.
+      split): the first D C tiles go whole, tile r C + k to chunk k in round
+      r, so the tiles computed at the same time are neighbours that share
+      weight and row tiles in cache; the remaining U - D C tiles have their k
+      tiles split over the chunks as above.  With R = U mod C: R = 0 or
+      4 R >= 3 C (a last round at least three quarters full) splits nothing,
+      the last round's tiles going whole to chunks 0 .. R - 1; 2 R >= C
+      splits the remainder alone (at least half a tile per chunk); a smaller
+      remainder takes the last whole round with it (at least one tile per
+      chunk).  Every chunk gets the same work to within one tile (within one
+      k tile when something is split), and a split tile has at most three
+      pieces (unit cost 0): the sum of a split tile reads one or two other
+      partials, not a share of a small remainder cut C ways.  The three
+      quarters are this library's reading of when a split costs more than
+      the idle quarter round it saves (a split tile's partials are written
+      and read back whole).
     * the blob has ``plan``'s layout with mode 3, batch = E, head_dim_qk = K,
       head_dim_v = N, page_size = tile_cols, heads_per_unit = tile_rows,
       tile_tokens = tile_k, one page, and then MOE_DESC_WORDS per unit
@@ -488,10 +495,12 @@ def plan_moe(num_experts, hidden, out_dim, expert_tokens, num_cus, num_xcds, til
         chunk_pieces = [[(k, 0, K)] for k in range(C)]
     elif policy == POLICY_STREAMK_DP:
         # whole tiles dealt round-robin (tile r C + k to chunk k, round by
-        # round) for all but the last round, then the remaining tiles' k
-        # tiles split as in ``plan``
-        full = max(U // C - 1, 0)
-        chunk_pieces = [[(r * C + k, 0, K) for r in range(full)] for k in range(C)]
+        # round), then the remaining tiles' k tiles split as in ``plan``; a
+        # remainder of less than half a round takes the last round with it
+        rem = U % C
+        whole = rem == 0 or 4 * rem >= 3 * C
+        full = -(-U // C) if whole else (U // C if 2 * rem >= C else max(U // C - 1, 0))
+        chunk_pieces = [[(r * C + k, 0, K) for r in range(full) if r * C + k < U] for k in range(C)]
         rest = _chunks(ntiles[full * C:], lens[full * C:], C, tile_k, unit_cost) if U > full * C else [[]] * C
         for k in range(C):
             chunk_pieces[k] += [(full * C + v, a, b) for (v, a, b) in rest[k]]
