@@ -13,7 +13,7 @@
 // dense contractions on v_mfma_f32_32x32x16_bf16 tiles, one wave per SIMD with
 // the whole register file:
 //   S^T[32 tokens][32 heads] = K[32][576] . Q^T[576][32]   (36 k-steps; Q^T in
-//     112 VGPRs and 8 KiB of LDS per wave for the whole item),
+//     108 VGPRs and 9 KiB of LDS per wave for the whole item),
 //   O^T[512][32 heads]      += V^T[512][32] . P^T[32][32]  (16 column blocks of
 //     32 dv x 32 heads: 256 accumulators, held in AGPRs).
 // S^T leaves lane (n, g) with head n's scores of tokens 8j + 4g + i, which is
@@ -69,7 +69,7 @@ constexpr int kRowBytes = kDqk * 2;         // 1152
 constexpr int kBlk = 32;                    // tokens per tile
 constexpr int kKSteps = kDqk / 16;          // 36 k-steps of q.k
 constexpr int kLatentSteps = 32;            // k-steps inside the first 512 columns
-constexpr int kQReg = 28;                   // k-steps of Q^T held in registers (the rest in LDS)
+constexpr int kQReg = 27;                   // k-steps of Q^T held in registers (the rest in LDS)
 // LDS row of token t (its first 512 columns): 1088 t + 16 ((t / 4) % 4).  Row
 // starts fall on 16-byte bank slot 4 (t % 4) + (t / 4) % 4 modulo 256 bytes, so
 // 16 consecutive tokens hit 16 different slots (K operand reads) and 4
@@ -238,6 +238,13 @@ __device__ __forceinline__ void lds_dma16(const char* src, char* lds) {
   const uint32_t m0 = uni((int)(uint32_t)(uintptr_t)(lds_ptr)lds);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :: "v"(src), "s"(m0) : "memory", "m0");
+}
+// The same transfer with a scalar base and a per-lane offset, the LDS address
+// given as a number (no pointer conversion).  (An immediate offset on this
+// instruction would move the LDS destination as well as the source.)
+__device__ __forceinline__ void lds_dma16n(const char* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
 // The same transfer with a scalar base and a per-lane offset.
 __device__ __forceinline__ void lds_dma16s(const char* sbase, uint32_t voff, char* lds) {
@@ -531,11 +538,24 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   const int rt = kRowsPerWave * wave + rslot;
   const int rchunk = (lane & 7) ^ ((rt >> 1) & 7);
   // dense: a 32-token block lies inside one page (pages hold >= 32 tokens), so
-  // its rows are contiguous; rows past the item end re-read the last valid row.
+  // its rows are contiguous and all 32 of them lie inside the page.  The
+  // transfers read all 32 rows; past the item end those are whatever the page
+  // holds, so the step that uses such a tile zeroes their V columns (their
+  // scores are masked).  The address arithmetic is per step: wave w moves
+  // rows 8w .. 8w+3 from base + 9216 w (LDS row_lds(8w + q) = wb0 + 1088 q)
+  // and rows 8w+4 .. 8w+7 from 4608 bytes further (wb1 + 1088 q), row q at
+  // per-lane offset 16 lane + 1152 (q % 4), and the rope columns of its 8
+  // rows with a per-lane offset of their own.
   struct DenseFetch {
-    const char* base;
-    int nvalid;
+    const char* r0;    // row 8 wave of the block
+    const char* r4;    // row 8 wave + 4
+    const char* base;  // row 0
   };
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr)&ring[0][0];
+  const uint32_t wb0 = uni(row_lds(kRowsPerWave * wave));
+  const uint32_t wb1 = uni(row_lds(kRowsPerWave * wave + 4) - 4 * 1088);
+  const uint32_t wbr = uni(kRopeOff + 1024 * wave);
+  const uint32_t rope_voff = rt * kRowBytes + 1024 + 16 * rchunk;
   auto dense_prep = [&](const Item& I, int j, int pg) -> DenseFetch {
     const int tok0 = I.tb + j * kBlk;
     if ((unsigned)pg >= (unsigned)p.num_pages) {
@@ -544,16 +564,19 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     }
     DenseFetch F;
     F.base = reinterpret_cast<const char*>(kc) + ((long long)pg * (1 << p.log2_page) + (tok0 & page_mask)) * kRowBytes;
-    F.nvalid = min(kBlk, I.te - tok0);
+    F.r0 = F.base + kRowsPerWave * kRowBytes * wave;
+    F.r4 = F.r0 + 4 * kRowBytes;
     return F;
   };
-  auto dense_piece = [&](const DenseFetch& F, int q, char* dst) __attribute__((always_inline)) {
-    if (q < kRowsPerWave) {
-      const int t = kRowsPerWave * wave + q;
-      lds_dma16s(F.base + (size_t)min(t, F.nvalid - 1) * kRowBytes, 16 * lane, dst + row_lds(t));
-    } else {
-      lds_dma16s(F.base, min(rt, F.nvalid - 1) * kRowBytes + 1024 + 16 * rchunk, dst + kRopeOff + 1024 * wave);
-    }
+  // transfer Q of a dense block into the stage at LDS address st_lds
+  auto dense_piece = [&](const DenseFetch& F, auto qc, uint32_t st_lds) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    if constexpr (q < 4)
+      lds_dma16n(F.r0, 16 * lane + kRowBytes * q, st_lds + wb0 + 1088 * q);
+    else if constexpr (q < kRowsPerWave)
+      lds_dma16n(F.r4, 16 * lane + kRowBytes * (q - 4), st_lds + wb1 + 1088 * q);
+    else
+      lds_dma16n(F.base, rope_voff, st_lds + wbr);
   };
   // index-sparse: lane l of wave w stands for row rt = 8 w + l / 8 of a tile
   // (the row its rope transfer takes).  The row ids of a tile are loaded two
@@ -609,8 +632,8 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   const uint32_t vbase = row_lds(4 * g + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
   // Q^T operand: lane holds head 32 wave + n, dims 16 ks + 8 g .. +8.  The
-  // first kQReg k-steps stay in registers (112 VGPRs) for the whole item; the
-  // other 8 go to the wave's own LDS area in the same lane order (one transfer
+  // first kQReg k-steps stay in registers (108 VGPRs) for the whole item; the
+  // other 9 go to the wave's own LDS area in the same lane order (one transfer
   // per k-step, read back conflict free), which leaves the register file room
   // for the operand pipeline.  The register part is loaded with untracked
   // loads (load16_async): every q load is issued before the transfers of the
@@ -700,12 +723,11 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     for (int q = 0; q < kDmaPerWave; ++q) sparse_piece(s1, p1, q, ring[1]);
   } else {
     load_q(cur.unit);
-    auto fetch_now = [&](const Item& I, int j, char* dst, int pg) {
+    auto fetch_now = [&](const Item& I, int j, int sidx, int pg) {
       const DenseFetch F = dense_prep(I, j, pg);
-#pragma unroll
-      for (int q = 0; q < kDmaPerWave; ++q) dense_piece(F, q, dst);
+      unroll<kDmaPerWave>([&](auto qc) { dense_piece(F, qc, ring_lds + sidx * kStageBytes); });
     };
-    fetch_now(pI, p_j, ring[0], page_now(pI, p_j));
+    fetch_now(pI, p_j, 0, page_now(pI, p_j));
     advance(pI, p_it, p_j, p_nb);
     if (nblk > 1) {
       const int pg1 = page_now(pI, p_j);
@@ -713,13 +735,13 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       int n_it = p_it, n_j = p_j, n_nb = p_nb;
       advance(nI, n_it, n_j, n_nb);
       pg_pref = load_dword_async(nblk > 2 ? bt_entry(nI, n_j) : bt);
-      fetch_now(pI, p_j, ring[1], pg1);
+      fetch_now(pI, p_j, 1, pg1);
       pI = nI;
       p_it = n_it;
       p_j = n_j;
       p_nb = n_nb;
     } else {
-      fetch_now(cur, 0, ring[1], 0);
+      fetch_now(cur, 0, 1, 0);
     }
   }
 
@@ -745,6 +767,18 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     const char* tile = ring[st];
     const int tok0 = cur.tb + cur_j * kBlk;
     const int nv = min(kBlk, cur.te - tok0);
+    if constexpr (!SPARSE) {
+      if (nv < kBlk) {
+        // rows past the item end hold whatever the page holds there: zero
+        // their V columns (their probabilities are exactly 0, and 0 times a
+        // non-finite value would not be)
+        char* zt = ring[st];
+        for (int i = tid; i < (kBlk - nv) * 64; i += kThreads)
+          *reinterpret_cast<u32x4*>(zt + row_lds(nv + (i >> 6)) + 16 * (i & 63)) = u32x4{0u, 0u, 0u, 0u};
+        wait_lds();
+        barrier();
+      }
+    }
 
     // The fetch of the tile two blocks ahead (a filler past the end): its
     // transfers go between the score MFMAs, unless this tile ends an item and
@@ -752,7 +786,7 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     // count on that order).
     const bool item_ends = cur_j == cur_nb - 1;
     const bool q_next = item_ends && k + 1 < nblk;
-    DenseFetch F = {nullptr, 0};
+    DenseFetch F = {nullptr, nullptr, nullptr};
     uint32_t fsid = 0, fspg = 0;  // index-sparse: checked row ids and pages of the fetched tile
     if constexpr (SPARSE) {
       const uint32_t sid3 = sid_check(c3.I, take_vgpr(sid_fl));  // ids of tile k+3
@@ -780,13 +814,14 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       }
       F = dense_prep(fI, fj, fpg);
     }
-    auto piece = [&](int q, char* dst) __attribute__((always_inline)) {
-      if constexpr (SPARSE)
-        sparse_piece(fsid, fspg, q, dst);
-      else
-        dense_piece(F, q, dst);
-    };
     char* fdst = ring[st2];
+    const uint32_t fst_lds = ring_lds + st2 * kStageBytes;
+    auto piece = [&](auto qc) __attribute__((always_inline)) {
+      if constexpr (SPARSE)
+        sparse_piece(fsid, fspg, decltype(qc)::value, fdst);
+      else
+        dense_piece(F, qc, fst_lds);
+    };
 
     // S^T = K Q^T, 36 k-steps, operands read kPreS k-steps ahead
     f32x16 s;
@@ -799,8 +834,8 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       };
 #pragma unroll
       for (int ks = 0; ks < kPreS; ++ks) kload(ks);
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
+      unroll<kKSteps>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
         if (ks + kPreS < kKSteps) kload(ks + kPreS);
         if (ks == 0)
           mfma32_v_first(s, kop[0], qv[0]);
@@ -808,9 +843,8 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
           mfma32_v(s, kop[ks], qv[ks]);
         else
           mfma32_v(s, kop[ks], qop[ks]);
-        if constexpr (kInter)
-          if ((ks & 3) == 2) piece(ks >> 2, fdst);
-      }
+        if constexpr (kInter && (ks & 3) == 2) piece(std::integral_constant<int, (ks >> 2)>{});
+      });
     };
     if (!q_next)
       scores(std::true_type{});
@@ -821,10 +855,7 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       // q of the next item replaces this one as soon as the scores no longer need it
       load_q(uni(items[cur_it + 1].x));
     }
-    if (q_next) {
-#pragma unroll
-      for (int q = 0; q < kDmaPerWave; ++q) piece(q, fdst);
-    }
+    if (q_next) unroll<kDmaPerWave>([&](auto qc) { piece(qc); });
 
     // scores (base 2), masked past the item end; register r is token 8 (r / 4) + 4 g + r % 4
     float x[16];
@@ -868,8 +899,8 @@ mla_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       pb[b] = u32x4{pack_bf16(x[8 * b], x[8 * b + 1]), pack_bf16(x[8 * b + 2], x[8 * b + 3]),
                     pack_bf16(x[8 * b + 4], x[8 * b + 5]), pack_bf16(x[8 * b + 6], x[8 * b + 7])};
 
-    // O^T += V^T P^T.  Rows past the item end hold a copy of the last valid row
-    // (finite) and their probabilities are exactly 0, so they add nothing.
+    // O^T += V^T P^T.  Rows past the item end are zero (see the top of the
+    // step) and their probabilities are exactly 0, so they add nothing.
     // 32 MFMAs m = 16 b + d (k-block b, dv block d), V^T operands read kPreV ahead
     {
       u32x4 vop[32];
