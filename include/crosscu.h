@@ -111,7 +111,10 @@ enum { CC_REDUCE_FUSED = 0, CC_REDUCE_SPLIT_COMBINE = 1 };
  *                   or [num_pages][num_kv_heads][page_size][head_dim_qk] (HND)
  *   v_cache      bf16  as k_cache with head_dim_v (GQA only)
  *   block_table  int32 [batch][max_pages_per_seq]; token j of sequence b lives
- *                in page block_table[b][j / page_size], slot j % page_size
+ *                in page block_table[b][j / page_size], slot j % page_size.
+ *                The slots of a sequence's last page past its length may hold
+ *                any bits, NaN and Inf included: the kernels may read them
+ *                (whole 32-token blocks inside a page) but never use them.
  *   seqlens      int32 [batch], each >= 0 (>= topk for MLA_SPARSE); a sequence
  *                with no cached tokens gets out = 0 and lse = -inf, the
  *                neutral element of the log-sum-exp merge
