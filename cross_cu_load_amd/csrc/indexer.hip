@@ -13,8 +13,8 @@
 //
 // The top-k kernel gives each decode token one 1024-thread workgroup: the
 // scores become order-preserving unsigned keys in LDS, a radix select over
-// four 8-bit digits finds the k-th largest key T and how many keys equal to
-// T belong to the result, and a stable compaction in position order writes
+// digits of 12, 12 and 8 bits finds the k-th largest key T and how many keys
+// equal to T belong to the result, and a stable compaction in position order writes
 // every key above T plus the first such keys equal to T.  Integer work on
 // the score bits, so the result is exact and deterministic.
 #include <hip/hip_runtime.h>
@@ -104,13 +104,41 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* wsum) {
   return before + incl - x;
 }
 
+// Inclusive suffix sum over the workgroup in thread order: thread t gets the
+// sum of x over threads >= t.
+__device__ __forceinline__ uint32_t block_suffix_sum(uint32_t x, uint32_t* wtot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_down(incl, o);
+    if (lane + o < 64) incl += t;
+  }
+  __syncthreads();  // wtot free from a previous use
+  if (lane == 0) wtot[wave] = incl;
+  __syncthreads();
+  uint32_t after = 0;
+  for (int w = wave + 1; w < kTopkThreads / 64; ++w) after += wtot[w];
+  return incl + after;
+}
+
+// Radix-select passes, most significant first: key bits [20, 32), [8, 20),
+// [0, 8).  A float key's top 12 bits are its sign, exponent and 3 mantissa
+// bits, so the first pass already spreads the scores over many bins (8-bit
+// digits would put nearly all of them in a few bins, and their LDS atomics
+// would serialize).
+constexpr int kPasses = 3;
+__device__ constexpr int kPassShift[kPasses] = {20, 8, 0};
+__device__ constexpr int kPassBits[kPasses] = {12, 12, 8};
+constexpr int kBins = 1 << 12;
+
 // grid B * Tq; one workgroup per decode token
 __global__ void __launch_bounds__(kTopkThreads)
 indexer_topk_kernel(const float* __restrict__ scores, int ld, Lens lens, int tq, int topk,
                     int32_t* __restrict__ out) {
   __shared__ uint32_t keys[kMaxL];
-  __shared__ uint32_t whist[kTopkThreads / 64][256];  // one histogram per wave: fewer same-bin atomics
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t wtot[kTopkThreads / 64];
   __shared__ int wsum[kTopkThreads / 64];
   __shared__ uint32_t sh_digit, sh_above;
   const int tid = threadIdx.x;
@@ -134,58 +162,39 @@ indexer_topk_kernel(const float* __restrict__ scores, int ld, Lens lens, int tq,
       if (j < L) keys[j] = (x & 0x80000000u) ? ~x : (x | 0x80000000u);
     }
   }
-  // radix select of the topk-th largest key, most significant digit first
+  // radix select of the topk-th largest key
   uint32_t prefix = 0, mask = 0;
   uint32_t kk = (uint32_t)topk;  // rank still to place among keys matching prefix
-  uint32_t* wh = whist[tid >> 6];
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < (kTopkThreads / 64) * 256; i += kTopkThreads) whist[i >> 8][i & 255] = 0;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int shift = kPassShift[pass], nb = 1 << kPassBits[pass];
+    for (int i = tid; i < nb; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
     for (int j = tid; j < L; j += kTopkThreads) {
       const uint32_t k = keys[j];
-      if ((k & mask) == prefix) atomicAdd(&wh[(k >> shift) & 255u], 1u);
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
-    if (tid < 256) {
-      uint32_t t = 0;
-#pragma unroll
-      for (int w = 0; w < kTopkThreads / 64; ++w) t += whist[w][tid];
-      hist[tid] = t;
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l holds bins 4l .. 4l+3; the digit is where the count of larger
-      // keys first reaches kk, scanning from the top bin down
-      const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
-      const uint32_t sum = h0 + h1 + h2 + h3;
-      uint32_t incl = sum;  // sum over lanes >= tid
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_down(incl, o);
-        if (tid + o < 64) incl += t;
-      }
-      const uint32_t above = incl - sum;  // keys in bins above 4 tid + 3
-      if (above < kk && kk <= incl) {
-        uint32_t c = above;
-        uint32_t d;
-        if (c + h3 >= kk) {
-          d = 4 * tid + 3;
-        } else if (c += h3, c + h2 >= kk) {
-          d = 4 * tid + 2;
-        } else if (c += h2, c + h1 >= kk) {
-          d = 4 * tid + 1;
-        } else {
-          c += h1;
-          d = 4 * tid;
-        }
-        sh_digit = d;
-        sh_above = c;
-      }
+    // thread t owns bins [per t, per t + per); the digit is the bin where the
+    // count of larger keys first reaches kk, scanning from the top bin down
+    const int per = nb >= kTopkThreads ? nb / kTopkThreads : 1;
+    const int b0 = tid * per;
+    uint32_t own = 0;
+    for (int i = 0; i < per; ++i)
+      if (b0 + i < nb) own += hist[b0 + i];
+    const uint32_t incl = block_suffix_sum(own, wtot);  // keys in bins >= b0
+    const uint32_t above = incl - own;                  // keys in bins >= b0 + per
+    if (above < kk && kk <= incl) {
+      uint32_t c = above;
+      int d = b0 + per - 1;
+      while (c + hist[d] < kk) c += hist[d--];
+      sh_digit = (uint32_t)d;
+      sh_above = c;
     }
     __syncthreads();
     kk -= sh_above;
     prefix |= sh_digit << shift;
-    mask |= 255u << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
   }
   const uint32_t T = prefix;  // the topk-th largest key; kk keys equal to it are kept
   // stable compaction in position order; thread tid owns positions [j0, j1)
