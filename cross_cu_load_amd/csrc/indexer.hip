@@ -3,13 +3,12 @@
 // Indexer Score" ahead of TopK and sparse MLA, Summary; the Top-2048 the
 // indexer rank publishes, related-work section on TileRT).
 //
-// Two kernels.  The score kernel gives each lane one (cached token, decode
-// token) pair: the lane reads the token's 256-byte key row and the query row
-// into registers and runs one fp32 FMA chain over the 128 dimensions in index
-// order (a bf16 x bf16 product is exact in fp32, so each FMA rounds once,
-// exactly as an add of the exact product).  The lanes of one cached token
-// share its key row's loads.  It is a streaming read of the key cache, a few
-// MB.
+// Two kernels.  The score kernel gives each lane one cached token and two
+// decode tokens: the lane reads the token's 256-byte key row into registers
+// (the request's query rows sit in LDS) and runs an fp32 FMA chain over the
+// 128 dimensions in index order for each decode token (a bf16 x bf16 product
+// is exact in fp32, so each FMA rounds once, exactly as an add of the exact
+// product).  It is a streaming read of the key cache, a few MB.
 //
 // The top-k kernel gives each decode token one 1024-thread workgroup: the
 // scores become order-preserving unsigned keys in LDS, a radix select over
@@ -47,20 +46,28 @@ struct Lens {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// grid (ceil(max L * tqp / 256), B): lane = (cached token j, decode token m)
-// of request blockIdx.y, m fastest (tqp = tq rounded up to a power of two),
-// so the tqp lanes of one token read the same key row in the same load
-// instruction; each lane holds its query row and the key row in registers and
-// runs one FMA chain over the 128 dimensions in index order.
+// grid (ceil(max L * lpt / 256), B): lane = (cached token j, pair of decode
+// tokens p), p fastest (lpt = ceil(tq / 2) rounded up to a power of two, the
+// lanes of one token).  The request's query rows are staged in LDS once per
+// workgroup; each lane loads its token's key row into registers and runs two
+// independent FMA chains over the 128 dimensions in index order, one per
+// decode token (2p and 2p + 1).
 __global__ void __launch_bounds__(kScoreThreads)
 indexer_score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-                     const int32_t* __restrict__ bt, Lens lens, int tq, int log2tqp, int log2p, int max_pages,
+                     const int32_t* __restrict__ bt, Lens lens, int tq, int log2lpt, int log2p, int max_pages,
                      int num_pages, int ld, float* __restrict__ scores, int32_t* __restrict__ err) {
+  __shared__ u32x4 qs[kMaxTq][kDim / 8];
   const int b = blockIdx.y;
   const int L = lens.L[b];
+  {
+    const u32x4* qb = reinterpret_cast<const u32x4*>(q + (size_t)b * tq * kDim);
+    for (int i = threadIdx.x; i < tq * (kDim / 8); i += kScoreThreads) qs[i / (kDim / 8)][i % (kDim / 8)] = qb[i];
+  }
+  __syncthreads();
   const int t = blockIdx.x * kScoreThreads + threadIdx.x;
-  const int j = t >> log2tqp, m = t & ((1 << log2tqp) - 1);
-  if (j >= L || m >= tq) return;
+  const int j = t >> log2lpt, m0 = 2 * (t & ((1 << log2lpt) - 1));
+  if (j >= L || m0 >= tq) return;
+  const int m1 = m0 + 1 < tq ? m0 + 1 : m0;  // an odd last token: the second chain repeats the first
   int pg = bt[(size_t)b * max_pages + (j >> log2p)];
   if ((unsigned)pg >= (unsigned)num_pages) {
     if (err) atomicOr(err, kErrPage);
@@ -68,23 +75,23 @@ indexer_score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
   const u32x4* row = reinterpret_cast<const u32x4*>(
       kc + (((size_t)pg << log2p) + (size_t)(j & ((1 << log2p) - 1))) * kDim);
-  const u32x4* qrow = reinterpret_cast<const u32x4*>(q + ((size_t)b * tq + m) * kDim);
-  u32x4 r[kDim / 8], qv[kDim / 8];
+  u32x4 r[kDim / 8];
+#pragma unroll
+  for (int c = 0; c < kDim / 8; ++c) r[c] = row[c];
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int c = 0; c < kDim / 8; ++c) {
-    r[c] = row[c];
-    qv[c] = qrow[c];
-  }
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < kDim / 8; ++c) {
+    const u32x4 q0 = qs[m0][c], q1 = qs[m1][c];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      acc = __builtin_fmaf(bf16_lo(qv[c][w]), bf16_lo(r[c][w]), acc);
-      acc = __builtin_fmaf(bf16_hi(qv[c][w]), bf16_hi(r[c][w]), acc);
+      a0 = __builtin_fmaf(bf16_lo(q0[w]), bf16_lo(r[c][w]), a0);
+      a1 = __builtin_fmaf(bf16_lo(q1[w]), bf16_lo(r[c][w]), a1);
+      a0 = __builtin_fmaf(bf16_hi(q0[w]), bf16_hi(r[c][w]), a0);
+      a1 = __builtin_fmaf(bf16_hi(q1[w]), bf16_hi(r[c][w]), a1);
     }
   }
-  scores[(size_t)(b * tq + m) * ld + j] = acc;
+  scores[(size_t)(b * tq + m0) * ld + j] = a0;
+  if (m1 != m0) scores[(size_t)(b * tq + m1) * ld + j] = a1;
 }
 
 // Exclusive prefix sum over the workgroup (kTopkThreads threads), in thread order.
@@ -300,11 +307,11 @@ extern "C" int cc_indexer_topk(const cc_indexer_problem* p, const int32_t* seqle
   float* sc = static_cast<float*>(scratch);
   hipEvent_t ev0, ev1;  // debug kernel events (cc_debug_kernel_events): start of the first, end of the last
   cc::kernel_events(&ev0, &ev1);
-  const int log2tqp = ilog2(p->q_tokens);
-  const long long lanes = (long long)maxl << log2tqp;
+  const int log2lpt = ilog2((p->q_tokens + 1) / 2);
+  const long long lanes = (long long)maxl << log2lpt;
   hipExtLaunchKernelGGL(indexer_score_kernel, dim3((unsigned)((lanes + kScoreThreads - 1) / kScoreThreads), p->batch),
                         dim3(kScoreThreads), 0u, s, ev0, nullptr, 0u, static_cast<const uint16_t*>(q),
-                        static_cast<const uint16_t*>(k_cache), block_table, lens, p->q_tokens, log2tqp,
+                        static_cast<const uint16_t*>(k_cache), block_table, lens, p->q_tokens, log2lpt,
                         ilog2(p->page_size), p->max_pages_per_seq, p->num_pages, maxl, sc, err);
   hipExtLaunchKernelGGL(indexer_topk_kernel, dim3(p->batch * p->q_tokens), dim3(kTopkThreads), 0u, s, nullptr, ev1,
                         0u, static_cast<const float*>(sc), maxl, lens, p->q_tokens, p->topk, indices);
