@@ -200,3 +200,17 @@ def test_kernel_events_bracket_the_call(dev, reduce):
     # the kernel interval is not longer than the marker interval beyond noise
     assert 0 < np.median(kernel_ms) <= 1.05 * np.median(marker_ms)
     clean(s, plan)
+
+
+@pytest.mark.parametrize("reduce", [B.REDUCE_FUSED, B.REDUCE_SPLIT_COMBINE])
+@pytest.mark.parametrize("hkv,hq,d", [(8, 8, 128), (4, 8, 64), (4, 32, 128), (1, 16, 64), (2, 32, 128)])
+def test_group_sizes_and_head_dims(dev, hkv, hq, d, reduce):
+    """G = 1 (MHA), 2, 8 and 16 at head dims 64 and 128 on ragged batches, every
+    output (the workloads themselves all have G = 4)."""
+    base = W.small_variant(W.CONFIG_BY_NAME["llama3_8b_gqa"], batch=10, seqlen_hi=2500, seed_offset=hq + hkv + d)
+    cfg = dataclasses.replace(base, num_q_heads=hq, num_kv_heads=hkv, head_dim_qk=d, head_dim_v=d,
+                              softmax_scale=1 / np.sqrt(d))
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, reduce=reduce, tag=f"G={hq // hkv} d={d}")
+    compare(s, wl, label=f"gqa G={hq // hkv} d={d}")
+    clean(s, plan)
