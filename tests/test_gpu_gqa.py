@@ -214,3 +214,16 @@ def test_group_sizes_and_head_dims(dev, hkv, hq, d, reduce):
     s, plan = run(wl, *dev, reduce=reduce, tag=f"G={hq // hkv} d={d}")
     compare(s, wl, label=f"gqa G={hq // hkv} d={d}")
     clean(s, plan)
+
+
+@pytest.mark.parametrize("layout", [W.KV_NHD, W.KV_HND])
+@pytest.mark.parametrize("page", [32, 64, 256, 1024])
+def test_page_sizes(dev, page, layout):
+    """Pages of 32 to 1024 tokens (the workloads use 16 and one 512-token page):
+    32-token blocks lie inside a page or cover several, every output."""
+    cfg = dataclasses.replace(W.small_variant(W.CONFIG_BY_NAME["llama3_8b_gqa"], batch=9, seqlen_hi=3000,
+                                              seed_offset=page + layout), page_size=page, kv_layout=layout)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, tag=f"gqa page={page} layout={layout}")
+    compare(s, wl, label=f"gqa page {page} {'HND' if layout else 'NHD'}")
+    clean(s, plan)
