@@ -94,6 +94,18 @@ def test_sparse_small_all_outputs(dev, L, topk):
                     assert np.array_equal(out[b, t, h], v)
 
 
+@pytest.mark.parametrize("page", [16, 32, 128, 256])
+def test_sparse_page_sizes(dev, page):
+    """Index-sparse gathers at pages of 16 to 256 tokens (the workload uses 64),
+    every output."""
+    cfg = dataclasses.replace(W.small_variant(SPARSE, batch=2, seqlen_hi=1500, seed_offset=page),
+                              topk=200, page_size=page)
+    wl = W.make_workload(cfg)
+    s, plan = run(wl, *dev, tag=f"sparse page={page}")
+    compare(s, wl, label=f"sparse page {page}")
+    clean(s, plan)
+
+
 def test_sparse_full_size_all_outputs(dev):
     wl = full_workload("sparse_mla")
     s, plan = run(wl, *dev, tag="sparse-full")
