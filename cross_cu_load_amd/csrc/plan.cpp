@@ -22,6 +22,18 @@ thread_local std::string g_err;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Tiles of T tokens covering a length: a shift when T is a power of two (the
+// usual case), since 64-bit division dominates the planner's time otherwise.
+struct TileCount {
+  int64_t T;
+  int shift = -1;
+  explicit TileCount(int64_t t) : T(t) {
+    if ((t & (t - 1)) == 0)
+      for (shift = 0; (int64_t{1} << shift) < t; ++shift) {}
+  }
+  int64_t operator()(int64_t len) const { return shift >= 0 ? (len + T - 1) >> shift : ceil_div(len, T); }
+};
+
 struct Inputs {
   const cc_problem* p;
   const cc_plan_opts* o;
@@ -101,6 +113,8 @@ int validate(const Inputs& in) {
 }
 
 struct Built {
+  bool size_only = false;   // stop once the word count is known
+  int64_t total = 0;        // words in the blob
   std::vector<int32_t> words;
 };
 
@@ -118,41 +132,119 @@ struct Work { int64_t unit, t0, len; };
 struct Piece { int64_t w, a, e; };
 struct Item { int64_t u, t0, t1, s; };
 
+// Elements are appended field by field.  A braced temporary is built on the
+// stack with 8-byte stores and copied out with 16-byte loads, which defeats
+// store-to-load forwarding and cost ~20 cycles per element, most of the
+// planner's time.
+void add_work(std::vector<Work>& v, int64_t unit, int64_t t0, int64_t len) {
+  Work& x = v.emplace_back();
+  x.unit = unit; x.t0 = t0; x.len = len;
+}
+void add_piece(std::vector<Piece>& v, int64_t w, int64_t a, int64_t e) {
+  Piece& x = v.emplace_back();
+  x.w = w; x.a = a; x.e = e;
+}
+void add_item(std::vector<Item>& v, int64_t u, int64_t t0, int64_t t1, int64_t s) {
+  Item& x = v.emplace_back();
+  x.u = u; x.t0 = t0; x.t1 = t1; x.s = s;
+}
+
+// Pieces grouped by chunk: chunk k's pieces are pieces[off[k] .. off[k + 1]).
+// One flat list, not a list per chunk: a plan of a few hundred chunks would
+// otherwise spend most of its time allocating.
+struct Chunks {
+  std::vector<int64_t> off;
+  std::vector<Piece> pieces;
+  int64_t count() const { return (int64_t)off.size() - 1; }
+};
+
 // Pieces per chunk of the equal split of cost: one per tile plus O per
 // non-empty entry, each entry's cost first; a tile goes to the chunk whose
 // cost range holds its starting position (with O = 0, the equal tile split).
-std::vector<std::vector<Piece>> split_chunks(const std::vector<Work>& work, int64_t C, int64_t T, int64_t O) {
-  std::vector<std::vector<Piece>> chunks(C);
+Chunks split_chunks(const std::vector<Work>& work, int64_t C, int64_t T, int64_t O) {
+  const TileCount tiles(T);
   int64_t busy = 0, N = 0;
   for (const Work& x : work) {
-    const int64_t n = ceil_div(x.len, T);
+    const int64_t n = tiles(x.len);
     N += n;
     busy += n > 0;
   }
+  // Each of the C - 1 chunk boundaries cuts at most one entry in two, so
+  // busy + C - 1 pieces at most; written through a pointer, not appended.
+  Chunks ch;
+  ch.off.assign(C + 1, 0);
+  ch.pieces.resize(busy + C);
+  Piece* out = ch.pieces.data();
+  int64_t np = 0;
   const int64_t total = O * busy + N;
   const int64_t q = total / C, r = total % C;
   auto bound = [&](int64_t k) { return k * q + (k < r ? k : r); };  // chunk k: [bound(k), bound(k+1))
   int64_t cs = 0, k = 0;
   for (int64_t w = 0; w < (int64_t)work.size(); ++w) {
-    const int64_t n = ceil_div(work[w].len, T), L = work[w].len;
+    const int64_t L = work[w].len, n = tiles(L);
     if (n == 0) continue;  // an empty entry gets no piece and costs nothing
     for (int64_t i = 0; i < n;) {
       while (bound(k + 1) <= cs + O + i) ++k;
       int64_t last = bound(k + 1) - cs - O;  // tiles of w starting before chunk k ends
       if (last > n) last = n;
-      chunks[k].push_back({w, i * T, last * T < L ? last * T : L});
+      if (np == (int64_t)ch.pieces.size()) {  // not reached (the bound above); kept as a guard
+        ch.pieces.resize(2 * np + 1);
+        out = ch.pieces.data();
+      }
+      out[np].w = w;
+      out[np].a = i * T;
+      out[np].e = last * T < L ? last * T : L;
+      ++np;
+      ++ch.off[k + 1];
       i = last;
     }
     cs += O + n;
   }
-  return chunks;
+  ch.pieces.resize(np);
+  for (int64_t j = 0; j < C; ++j) ch.off[j + 1] += ch.off[j];
+  return ch;
+}
+
+// One piece per non-empty entry, chunk u holding entry u (the per-unit policy).
+Chunks whole_chunks(const std::vector<Work>& work) {
+  Chunks ch;
+  const int64_t C = (int64_t)work.size();
+  ch.off.assign(C + 1, 0);
+  ch.pieces.reserve(C);
+  for (int64_t u = 0; u < C; ++u) {
+    if (work[u].len > 0) add_piece(ch.pieces, u, 0, work[u].len);
+    ch.off[u + 1] = (int64_t)ch.pieces.size();
+  }
+  return ch;
+}
+
+// Items of pieces whose entry is the unit itself: split indices in chunk order.
+std::vector<Item> unit_items(const Chunks& ch, std::vector<int64_t>& nsplit) {
+  std::vector<Item> items(ch.pieces.size());
+  for (size_t i = 0; i < items.size(); ++i) {
+    const Piece& pc = ch.pieces[i];
+    items[i].u = pc.w;
+    items[i].t0 = pc.a;
+    items[i].t1 = pc.e;
+    items[i].s = nsplit[pc.w]++;
+  }
+  return items;
 }
 
 // The blob: header, wg_off (padded), items in worker order, unit_nsplit,
-// unit_pbase, prefix table rows.  items[k] are logical chunk k's items.
+// unit_pbase, prefix table rows.  Logical chunk k's items are
+// items[off[k] .. off[k + 1]).  With out->size_only, only the word count.
 int serialise(const cc_problem& p, const cc_plan_opts& o, const int32_t* seqlens, int64_t C, int64_t U,
-              int64_t N, int64_t hpu, const std::vector<std::vector<Item>>& items,
+              int64_t N, int64_t hpu, const std::vector<int64_t>& off, const std::vector<Item>& items,
               const std::vector<int64_t>& nsplit, const std::vector<int32_t>& prefix_rows, Built* out) {
+  const int64_t W = (int64_t)items.size();
+  const int64_t total = kHeaderWords + wg_words(C) + kItemWords * W + 2 * U + (int64_t)prefix_rows.size();
+  if (N > INT32_MAX || C > INT32_MAX || W > INT32_MAX || U > INT32_MAX || total > INT32_MAX) {
+    set_error("plan too large for int32 fields");
+    return CC_ERR_INVALID;
+  }
+  out->total = total;
+  if (out->size_only) return CC_OK;
   std::vector<int64_t> pbase(U, -1);
   int64_t S = 0, maxsplit = 0, empty = 0;
   for (int64_t u = 0; u < U; ++u) {
@@ -168,16 +260,7 @@ int serialise(const cc_problem& p, const cc_plan_opts& o, const int32_t* seqlens
     const int64_t w = spread ? (k % (C / X)) * X + k / (C / X) : k;
     chunk_of_worker[w] = k;
   }
-  int64_t W = 0;
-  for (int64_t k = 0; k < C; ++k) W += (int64_t)items[k].size();
-  const int64_t P = (int64_t)prefix_rows.size() / kPrefixWords;
-  const int64_t total = kHeaderWords + wg_words(C) + kItemWords * W + 2 * U + (int64_t)prefix_rows.size();
-  for (int64_t x : {N, C, W, U, S, total}) {
-    if (x > INT32_MAX) {
-      set_error("plan too large for int32 fields");
-      return CC_ERR_INVALID;
-    }
-  }
+  const int64_t P = (int64_t)prefix_rows.size() / kPrefixWords;  // S <= W: every slot is an item
   std::vector<int32_t>& w = out->words;
   w.assign(total, 0);
   int32_t* h = w.data();
@@ -213,7 +296,9 @@ int serialise(const cc_problem& p, const cc_plan_opts& o, const int32_t* seqlens
   int64_t n = 0;
   for (int64_t wk = 0; wk < C; ++wk) {
     wg[wk] = (int32_t)n;
-    for (const Item& x : items[chunk_of_worker[wk]]) {
+    const int64_t k = chunk_of_worker[wk];
+    for (int64_t i = off[k]; i < off[k + 1]; ++i) {
+      const Item& x = items[i];
       it[4 * n + 0] = (int32_t)x.u;
       it[4 * n + 1] = (int32_t)x.t0;
       it[4 * n + 2] = (int32_t)x.t1;
@@ -244,28 +329,21 @@ int build(const Inputs& in, Built* out) {
   const int64_t U = units_per_seq * p.batch;
   const int64_t T = o.tile_tokens;
 
-  // unit u belongs to sequence u / units_per_seq
-  std::vector<Work> work(U);
+  // units units_per_seq * b .. units_per_seq * (b + 1) - 1 belong to sequence b
+  std::vector<Work> work;
+  work.reserve(U);
+  const TileCount tiles(T);
   int64_t N = 0;
-  for (int64_t u = 0; u < U; ++u) {
-    work[u] = {u, 0, p.mode == CC_MODE_MLA_SPARSE ? p.topk : in.seqlens[u / units_per_seq]};
-    N += ceil_div(work[u].len, T);
+  for (int64_t b = 0, u = 0; b < p.batch; ++b) {
+    const int64_t L = p.mode == CC_MODE_MLA_SPARSE ? p.topk : in.seqlens[b];
+    N += tiles(L) * units_per_seq;
+    for (int64_t j = 0; j < units_per_seq; ++j, ++u) add_work(work, u, 0, L);
   }
   const int64_t C = o.policy == CC_POLICY_PER_UNIT ? U : o.num_cus;
-  std::vector<std::vector<Piece>> chunks;
-  if (o.policy == CC_POLICY_PER_UNIT) {
-    chunks.resize(C);
-    for (int64_t u = 0; u < U; ++u)
-      if (work[u].len > 0) chunks[u].push_back({u, 0, work[u].len});
-  } else {
-    chunks = split_chunks(work, C, T, o.unit_cost);
-  }
-  // split indices in chunk order
+  const Chunks ch = o.policy == CC_POLICY_PER_UNIT ? whole_chunks(work) : split_chunks(work, C, T, o.unit_cost);
   std::vector<int64_t> nsplit(U, 0);
-  std::vector<std::vector<Item>> items(C);
-  for (int64_t k = 0; k < C; ++k)
-    for (const Piece& pc : chunks[k]) items[k].push_back({pc.w, pc.a, pc.e, nsplit[pc.w]++});
-  return serialise(p, o, in.seqlens, C, U, N, o.heads_per_unit, items, nsplit, {}, out);
+  const std::vector<Item> items = unit_items(ch, nsplit);
+  return serialise(p, o, in.seqlens, C, U, N, o.heads_per_unit, ch.off, items, nsplit, {}, out);
 }
 
 // Shared-prefix inputs: group ids in range, prefixes of whole pages, members
@@ -374,34 +452,33 @@ int build_prefix(const Inputs& in, const PrefixInputs& pre, Built* out) {
   std::vector<Work> work;
   work.reserve(P + U);
   int64_t N = 0;
-  for (int64_t pu = 0; pu < P; ++pu) work.push_back({U + pu, 0, rows[pu * kPrefixWords + 2]});
+  for (int64_t pu = 0; pu < P; ++pu) add_work(work, U + pu, 0, rows[pu * kPrefixWords + 2]);
   for (int64_t b = 0; b < p.batch; ++b)
-    for (int64_t h = 0; h < Hkv; ++h) work.push_back({b * Hkv + h, lp_of[b], in.seqlens[b] - lp_of[b]});
-  for (const Work& x : work) N += ceil_div(x.len, T);
-  const std::vector<std::vector<Piece>> chunks = split_chunks(work, C, T, o.unit_cost);
+    for (int64_t h = 0; h < Hkv; ++h) add_work(work, b * Hkv + h, lp_of[b], in.seqlens[b] - lp_of[b]);
+  const TileCount tiles(T);
+  for (const Work& x : work) N += tiles(x.len);
+  const Chunks ch = split_chunks(work, C, T, o.unit_cost);
 
   std::vector<int64_t> pieces(P, 0);
-  for (const auto& ch : chunks)
-    for (const Piece& pc : ch)
-      if (work[pc.w].unit >= U) ++pieces[work[pc.w].unit - U];
+  for (const Piece& pc : ch.pieces)
+    if (work[pc.w].unit >= U) ++pieces[work[pc.w].unit - U];
   std::vector<int64_t> own(U, 0), seen(P, 0);
-  std::vector<std::vector<Item>> items(C);
-  for (int64_t k = 0; k < C; ++k) {
-    for (const Piece& pc : chunks[k]) {
-      const Work& x = work[pc.w];
-      int64_t s;
-      if (x.unit >= U) {
-        s = seen[x.unit - U]++;
-      } else {
-        s = (prefix_of[x.unit] >= 0 ? pieces[prefix_of[x.unit]] : 0) + own[x.unit]++;
-      }
-      items[k].push_back({x.unit, x.t0 + pc.a, x.t0 + pc.e, s});
+  std::vector<Item> items;
+  items.reserve(ch.pieces.size());
+  for (const Piece& pc : ch.pieces) {   // chunk order
+    const Work& x = work[pc.w];
+    int64_t s;
+    if (x.unit >= U) {
+      s = seen[x.unit - U]++;
+    } else {
+      s = (prefix_of[x.unit] >= 0 ? pieces[prefix_of[x.unit]] : 0) + own[x.unit]++;
     }
+    add_item(items, x.unit, x.t0 + pc.a, x.t0 + pc.e, s);
   }
   std::vector<int64_t> nsplit(U);
   for (int64_t u = 0; u < U; ++u) nsplit[u] = own[u] + (prefix_of[u] >= 0 ? pieces[prefix_of[u]] : 0);
   for (int64_t pu = 0; pu < P; ++pu) rows[pu * kPrefixWords + 3] = (int32_t)pieces[pu];
-  return serialise(p, o, in.seqlens, C, U, N, G, items, nsplit, rows, out);
+  return serialise(p, o, in.seqlens, C, U, N, G, ch.off, items, nsplit, rows, out);
 }
 
 // MoE grouped GEMM plan: output tiles (expert, column block, row block) of
@@ -446,13 +523,13 @@ int build_moe(const cc_moe_problem& mp, const cc_plan_opts& o, const int32_t* ex
     set_error("MoE plan: no expert has rows");
     return CC_ERR_INVALID;
   }
-  std::vector<Work> work(U);
-  for (int64_t u = 0; u < U; ++u) work[u] = {u, 0, K};
+  std::vector<Work> work;
+  work.reserve(U);
+  for (int64_t u = 0; u < U; ++u) add_work(work, u, 0, K);
   const int64_t C = o.policy == CC_POLICY_PER_UNIT ? U : o.num_cus;
-  std::vector<std::vector<Piece>> chunks;
+  Chunks ch;
   if (o.policy == CC_POLICY_PER_UNIT) {
-    chunks.resize(C);
-    for (int64_t u = 0; u < U; ++u) chunks[u].push_back({u, 0, K});
+    ch = whole_chunks(work);
   } else if (o.policy == CC_POLICY_STREAMK_DP) {
     // whole tiles round-robin, round by round; the remaining tiles are split
     // (a last round at least three quarters full runs whole, a remainder of
@@ -460,23 +537,28 @@ int build_moe(const cc_moe_problem& mp, const cc_plan_opts& o, const int32_t* ex
     const int64_t rem = U % C;
     const bool whole = rem == 0 || 4 * rem >= 3 * C;
     const int64_t full = whole ? (U + C - 1) / C : (2 * rem >= C ? U / C : std::max<int64_t>(U / C - 1, 0));
-    chunks.resize(C);
-    for (int64_t k = 0; k < C; ++k)
-      for (int64_t r = 0; r < full; ++r)
-        if (r * C + k < U) chunks[k].push_back({r * C + k, 0, K});
+    Chunks sk;
     if (U > full * C) {
       const std::vector<Work> rest(work.begin() + full * C, work.end());
-      const std::vector<std::vector<Piece>> sk = split_chunks(rest, C, BK, o.unit_cost);
-      for (int64_t k = 0; k < C; ++k)
-        for (const Piece& pc : sk[k]) chunks[k].push_back({full * C + pc.w, pc.a, pc.e});
+      sk = split_chunks(rest, C, BK, o.unit_cost);
+    }
+    ch.off.assign(C + 1, 0);
+    ch.pieces.reserve(std::min(full * C, U) + sk.pieces.size());
+    for (int64_t k = 0; k < C; ++k) {
+      for (int64_t r = 0; r < full; ++r)
+        if (r * C + k < U) add_piece(ch.pieces, r * C + k, 0, K);
+      if (!sk.off.empty())
+        for (int64_t i = sk.off[k]; i < sk.off[k + 1]; ++i) {
+          const Piece& pc = sk.pieces[i];
+          add_piece(ch.pieces, full * C + pc.w, pc.a, pc.e);
+        }
+      ch.off[k + 1] = (int64_t)ch.pieces.size();
     }
   } else {
-    chunks = split_chunks(work, C, BK, o.unit_cost);
+    ch = split_chunks(work, C, BK, o.unit_cost);
   }
   std::vector<int64_t> nsplit(U, 0);
-  std::vector<std::vector<Item>> items(C);
-  for (int64_t k = 0; k < C; ++k)
-    for (const Piece& pc : chunks[k]) items[k].push_back({pc.w, pc.a, pc.e, nsplit[pc.w]++});
+  const std::vector<Item> items = unit_items(ch, nsplit);
   // the header words of a plan, with the MoE meanings
   cc_problem p{};
   p.mode = CC_MODE_MOE;
@@ -490,9 +572,9 @@ int build_moe(const cc_moe_problem& mp, const cc_plan_opts& o, const int32_t* ex
   p.max_pages_per_seq = 1;
   p.num_pages = 1;
   const int64_t N_tiles = U * (K / BK);
-  int rc = serialise(p, o, expert_tokens, C, U, N_tiles, BM, items, nsplit, desc, out);
+  int rc = serialise(p, o, expert_tokens, C, U, N_tiles, BM, ch.off, items, nsplit, desc, out);
   if (rc) return rc;
-  out->words[H_PREFIX] = 0;  // the trailing table holds tile descriptors, not prefix units
+  if (!out->size_only) out->words[H_PREFIX] = 0;  // the trailing table holds tile descriptors, not prefix units
   return CC_OK;
 }
 
@@ -688,9 +770,10 @@ int cc_plan_size(const cc_problem* prob, const cc_plan_opts* opts, const int32_t
     return CC_ERR_INVALID;
   }
   cc::Built b;
+  b.size_only = true;
   rc = cc::build({prob, opts, seqlens, nullptr}, &b);
   if (rc) return rc;
-  *bytes = b.words.size() * sizeof(int32_t);
+  *bytes = b.total * sizeof(int32_t);
   return CC_OK;
 }
 
@@ -724,9 +807,10 @@ int cc_plan_prefix_size(const cc_problem* prob, const cc_plan_opts* opts, const 
     return CC_ERR_INVALID;
   }
   cc::Built b;
+  b.size_only = true;
   rc = cc::build_prefix({prob, opts, seqlens, nullptr}, {prefix_group, num_groups, prefix_len}, &b);
   if (rc) return rc;
-  *bytes = b.words.size() * sizeof(int32_t);
+  *bytes = b.total * sizeof(int32_t);
   return CC_OK;
 }
 
@@ -758,9 +842,10 @@ int cc_moe_plan_size(const cc_moe_problem* prob, const cc_plan_opts* opts, const
     return CC_ERR_INVALID;
   }
   cc::Built b;
+  b.size_only = true;
   const int rc = cc::build_moe(*prob, *opts, expert_tokens, &b);
   if (rc) return rc;
-  *bytes = b.words.size() * sizeof(int32_t);
+  *bytes = b.total * sizeof(int32_t);
   return CC_OK;
 }
 
