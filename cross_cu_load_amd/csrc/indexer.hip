@@ -94,21 +94,17 @@ indexer_score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   if (m1 != m0) scores[(size_t)(b * tq + m1) * ld + j] = a1;
 }
 
-// Exclusive prefix sum over the workgroup (kTopkThreads threads), in thread order.
-__device__ __forceinline__ int block_exclusive_scan(int x, int* wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int incl = x;
+constexpr int kWavesT = kTopkThreads / 64;
+
+// Sum over the first kWavesT lanes of v, for every lane of the wave: lane l
+// holds wave l's contribution (zero where it does not count), and a butterfly
+// over groups of 16 lanes adds them in four steps instead of a chain of LDS
+// reads.  Integer sums: the order does not matter.
+__device__ __forceinline__ uint32_t sum_wave_lanes(uint32_t v) {
+  static_assert(kWavesT == 16, "one butterfly group per workgroup's waves");
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  __syncthreads();  // wsum free from a previous scan
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  return before + incl - x;
+  for (int o = 1; o < kWavesT; o <<= 1) v += __shfl_xor(v, o);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 // Inclusive suffix sum over the workgroup in thread order: thread t gets the
@@ -124,8 +120,7 @@ __device__ __forceinline__ uint32_t block_suffix_sum(uint32_t x, uint32_t* wtot)
   __syncthreads();  // wtot free from a previous use
   if (lane == 0) wtot[wave] = incl;
   __syncthreads();
-  uint32_t after = 0;
-  for (int w = wave + 1; w < kTopkThreads / 64; ++w) after += wtot[w];
+  const uint32_t after = sum_wave_lanes(lane < kWavesT && lane > wave ? wtot[lane] : 0u);
   return incl + after;
 }
 
@@ -145,8 +140,8 @@ indexer_topk_kernel(const float* __restrict__ scores, int ld, Lens lens, int tq,
                     int32_t* __restrict__ out) {
   __shared__ uint32_t keys[kMaxL];
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t wtot[kTopkThreads / 64];
-  __shared__ int wsum[kTopkThreads / 64];
+  __shared__ uint32_t wtot[kWavesT];
+  __shared__ uint32_t wcount[2][kWavesT];  // per wave: keys above T, keys equal to T
   __shared__ uint32_t sh_digit, sh_above;
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
@@ -204,31 +199,46 @@ indexer_topk_kernel(const float* __restrict__ scores, int ld, Lens lens, int tq,
     mask |= (uint32_t)(nb - 1) << shift;
   }
   const uint32_t T = prefix;  // the topk-th largest key; kk keys equal to it are kept
-  // stable compaction in position order; thread tid owns positions [j0, j1)
-  const int seg = (L + kTopkThreads - 1) / kTopkThreads;
-  const int j0 = min(L, tid * seg), j1 = min(L, j0 + seg);
-  int gt = 0, eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    gt += keys[j] > T;
-    eq += keys[j] == T;
+  // Stable compaction in position order.  Wave w owns positions [w P, (w + 1) P)
+  // and walks them 64 at a time (lane = position), so key reads hit distinct
+  // LDS banks and index writes are contiguous; ballots give each lane its rank
+  // among the keys above T, and among those equal to T, before it.  The first
+  // kk keys equal to T in position order are kept.
+  const int lane = tid & 63, wave = tid >> 6;
+  const int P = (L + kWavesT * 64 - 1) / (kWavesT * 64) * 64;
+  const int jw = wave * P;
+  const unsigned long long below = (1ull << lane) - 1;
+  int gt = 0, eq = 0;  // this wave's counts (wave-uniform)
+  for (int i = 0; i < P; i += 64) {
+    const int j = jw + i + lane;
+    const bool in = j < L;
+    const uint32_t k = in ? keys[j] : 0u;
+    gt += __popcll(__ballot(in && k > T));
+    eq += __popcll(__ballot(in && k == T));
   }
-  const int eq_before = block_exclusive_scan(eq, wsum);
-  const int take_eq = max(0, min(eq, (int)kk - eq_before));
-  int pos = block_exclusive_scan(gt + take_eq, wsum);
-  int eqr = eq_before;
+  if (lane == 0) {
+    wcount[0][wave] = gt;
+    wcount[1][wave] = eq;
+  }
+  __syncthreads();
+  const bool earlier = lane < wave;  // lane l < kWavesT stands for wave l
+  const int gt_before = (int)sum_wave_lanes(earlier ? wcount[0][lane] : 0u);
+  const int eq_before = (int)sum_wave_lanes(earlier ? wcount[1][lane] : 0u);
+  int pos = gt_before + min((int)kk, eq_before);  // results before this wave's positions
+  int eqr = eq_before;                            // keys equal to T before the current 64
   int32_t* o = out + (size_t)r * topk;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t k = keys[j];
-    if (k > T) {
-      if (pos < topk) o[pos] = j;
-      ++pos;
-    } else if (k == T) {
-      if (eqr < (int)kk) {
-        if (pos < topk) o[pos] = j;
-        ++pos;
-      }
-      ++eqr;
-    }
+  for (int i = 0; i < P; i += 64) {
+    const int j = jw + i + lane;
+    const bool in = j < L;
+    const uint32_t k = in ? keys[j] : 0u;
+    const bool g = in && k > T, q = in && k == T;
+    const unsigned long long qb = __ballot(q);
+    const bool take = g || (q && eqr + __popcll(qb & below) < (int)kk);
+    const unsigned long long tb = __ballot(take);
+    const int p = pos + __popcll(tb & below);
+    if (take && p < topk) o[p] = j;
+    pos += __popcll(tb);
+    eqr += __popcll(qb);
   }
 }
 
