@@ -330,3 +330,33 @@ def test_empty_sequences_get_no_piece(policy, unit_cost):
     allempty = _plan([0, 0, 0], C=8, X=1, T=4, policy=policy, unit_cost=unit_cost)
     assert allempty["num_items"] == 0 and allempty["num_tiles"] == 0
     assert allempty["unit_nsplit"] == [0, 0, 0]
+
+
+@pytest.mark.parametrize("name", ["skewed_gqa", "llama3_8b_gqa", "tiny_gqa", "deepseek_mla", "sparse_mla"])
+def test_tail_model_on_the_workloads(name):
+    """The tail-effect example's list-scheduling model applied to each decode
+    workload's unit tile counts (32-token tiles, 256 CUs): one workgroup per
+    unit (the per-unit comparison launch) finishes with its longest unit when
+    the units fit one wave, and the Stream-K plan's busiest chunk holds
+    exactly ceil(tiles / CUs) tiles.  Their ratio is the model's predicted
+    slowdown of the per-unit launch (CSDN Q&A on waves, "Scenario examples":
+    the wave tail; "Summary": equal chunks per SM)."""
+    c = W.CONFIG_BY_NAME[name]
+    sl = W.draw_seqlens(c)
+    G = c.num_q_heads // c.num_kv_heads
+    hpu = G if c.mode == PL.MODE_GQA else c.num_q_heads
+    C, T = 256, 32
+    lens = PL.unit_lengths(c.mode, c.batch, c.q_tokens, c.num_q_heads, c.num_kv_heads, hpu, sl, c.topk)
+    nt = [-(-L // T) for L in lens]
+    N = sum(nt)
+    v1, finish, _ = PL.list_schedule(nt, C)
+    if len(nt) <= C:
+        assert v1 == max(nt)
+    assert v1 >= max(nt) and v1 >= N / C
+    maxp = max(1, int(max(-(-int(L) // c.page_size) for L in sl)))
+    p = PL.plan(c.mode, c.batch, c.q_tokens, c.num_q_heads, c.num_kv_heads, c.head_dim_qk, c.head_dim_v,
+                c.page_size, maxp, 1 << 24, c.topk, C, 8, T, hpu, sl, None, PL.POLICY_STREAMK, 0)
+    chunk_tiles = [sum(-(-(t1 - t0) // T) for (_, t0, t1, _) in its) for its in p["chunk_items"]]
+    assert sum(chunk_tiles) == N and max(chunk_tiles) == -(-N // C)
+    print(f"{name}: per-unit makespan {v1:.0f} tiles, Stream-K {max(chunk_tiles)}; predicted ratio "
+          f"{v1 / max(chunk_tiles):.1f}")
