@@ -212,6 +212,8 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   __shared__ int split_list[kArrivals][3];    // arrivals: unit, nsplit, first partial slot
   __shared__ int num_split;
   __shared__ int num_done;
+  __shared__ int slots_ready;  // waves whose slot entries are written (no shared prefixes)
+  __shared__ int waves_done;   // waves past their stream (no shared prefixes)
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63;
@@ -248,6 +250,10 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
 
   if (tid < 2 * kWaves) slot_item[tid] = -1;
   if (PREFIX && tid < kWaves) wave_narr[tid] = 0;
+  if (tid == 0) {
+    slots_ready = 0;
+    waves_done = 0;
+  }
   __syncthreads();
 
   auto load_item = [&](Cursor& c, int it) {
@@ -419,12 +425,12 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
         }
       }
     }
-    if (lane == 0) {
+    if (PREFIX && lane == 0) {  // (without shared prefixes written before the stream)
       slot_item[sl] = cu.it;
       slot_meta[sl][0] = cu.unit;
       slot_meta[sl][1] = cu.split;
       slot_meta[sl][2] = cu.nsplit;
-      slot_meta[sl][3] = PREFIX && cu.pu >= 0 ? cu.rows : cu.pbase;  // a prefix item's query rows
+      slot_meta[sl][3] = cu.pu >= 0 ? cu.rows : cu.pbase;  // a prefix item's query rows
     }
   };
 
@@ -515,6 +521,82 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     }
   };
 
+  // Wave 0's list of the items left in merge slots, in slot order: each
+  // distinct item's first slot and the slots holding it, and the split ones
+  // among them (unit, nsplit, first partial slot).
+  auto scan_slots = [&]() {
+    // one lane per merge slot, compacted with ballots so the list stays in
+    // slot order
+    const int me = lane < 2 * kWaves ? slot_item[lane] : -1;
+    unsigned mask = 0;
+    bool before = false;
+#pragma unroll
+    for (int t = 0; t < 2 * kWaves; ++t) {
+      const bool same = __builtin_amdgcn_readlane(me, t) == me;
+      mask |= (unsigned)same << t;
+      before |= same && t < lane;
+    }
+    const bool first = lane < 2 * kWaves && me >= 0 && !before;
+    const int ns = first ? slot_meta[lane][2] : 0;
+    // (a prefix item's arrivals are its members', listed below)
+    const bool split = ns > 1 && (!PREFIX || slot_meta[lane][0] < p.units);
+    const unsigned long long fb = __ballot(first), sb = __ballot(split);
+    const unsigned long long below = (1ull << lane) - 1;
+    if (first) {
+      const int n = __popcll(fb & below);
+      it_slot[n] = lane;
+      it_mask[n] = mask;
+    }
+    if (split) {
+      const int k = __popcll(sb & below);
+      split_list[k][0] = slot_meta[lane][0];
+      split_list[k][1] = ns;
+      split_list[k][2] = slot_meta[lane][3];
+    }
+    int nsp = __popcll(sb);
+    if constexpr (PREFIX) {
+      // each member with other splits arrives once for a prefix item
+      for (unsigned long long pm = __ballot(first && slot_meta[lane][0] >= p.units); pm; pm &= pm - 1) {
+        const int sl = __builtin_ctzll(pm);
+        const int nmem = uni(slot_meta[sl][3]) / G;
+        for (int j0 = 0; j0 < nmem; j0 += 64) {
+          const int j = j0 + lane;
+          int mu = 0, ns2 = 0, pb = 0;
+          if (j < nmem) {
+            mu = slot_mem[sl][j][0];
+            ns2 = slot_mem[sl][j][2];
+            pb = slot_mem[sl][j][3];
+          }
+          const bool add = j < nmem && ns2 > 1;
+          const unsigned long long ab = __ballot(add);
+          if (add) {
+            const int k = nsp + __popcll(ab & below);
+            split_list[k][0] = mu;
+            split_list[k][1] = ns2;
+            split_list[k][2] = pb;
+          }
+          nsp += __popcll(ab);
+        }
+      }
+    }
+    if constexpr (PREFIX) {
+      // the waves' put-off arrivals
+      for (int w = 0; w < kWaves; ++w) {
+        const int n = wave_narr[w];
+        for (int i = lane; i < n; i += 64) {
+          split_list[nsp + i][0] = wave_arr[w][i][0];
+          split_list[nsp + i][1] = wave_arr[w][i][1];
+          split_list[nsp + i][2] = wave_arr[w][i][2];
+        }
+        nsp += n;
+      }
+    }
+    if (lane == 0) {
+      num_items = __popcll(fb);
+      num_split = nsp;
+    }
+  };
+
   if (s < e) {
     // ------------------------------------------------ the wave's run [s, e)
     Cursor c;
@@ -566,6 +648,33 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     u32x4 qv[KS], qn[KS];
     load_q(c, qv);
     fetch(sources(c));
+    if constexpr (!PREFIX) {
+      // A wave's merge slots hold its first and last items unless it finishes
+      // an item alone (the whole item, unsplit, written out directly); its
+      // middle items are whole units.  Without shared prefixes that is known
+      // from the plan: the slot entries are written here, under the first
+      // transfers' latency, and the first wave to end its stream builds the
+      // merge list from them while the others still stream (not after the
+      // workgroup's last wave, on the critical path).
+      Cursor z = c;
+      int itz = c.it, cz = s - c.j;  // cz: the chunk block where item itz starts
+      while (cz + z.nb < e) {        // block e - 1 lies in item itz
+        cz += z.nb;
+        load_item(z, ++itz);
+      }
+      auto claim = [&](int sl, const Cursor& cu, bool whole) {
+        if (!(whole && cu.nsplit == 1) && lane == 0) {
+          slot_item[sl] = cu.it;
+          slot_meta[sl][0] = cu.unit;
+          slot_meta[sl][1] = cu.split;
+          slot_meta[sl][2] = cu.nsplit;
+          slot_meta[sl][3] = cu.pbase;
+        }
+      };
+      claim(2 * wave, c, c.j == 0 && s - c.j + c.nb <= e);
+      if (itz != c.it) claim(2 * wave + 1, z, cz + z.nb <= e);
+      if (lane == 0) __hip_atomic_fetch_add(&slots_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
 
     // the first item's state when it is neither written out nor the last item
     bool stashed = false;
@@ -705,6 +814,21 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
     if (stashed) put_slot(2 * wave, c_first, m_first, l_first, o_first);
     if (PREFIX && lane == 0) wave_narr[wave] = narr;
   }
+  if constexpr (!PREFIX) {
+    // a wave with no blocks holds no slot; the first wave past its stream
+    // builds the merge list once every wave's entries are in (each wave
+    // writes them before it streams, so the wait ends)
+    if (s >= e && lane == 0)
+      __hip_atomic_fetch_add(&slots_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    int first = 0;
+    if (lane == 0)
+      first = __hip_atomic_fetch_add(&waves_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+    if (uni(first)) {
+      while (__hip_atomic_load(&slots_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kWaves)
+        __builtin_amdgcn_s_sleep(1);
+      scan_slots();
+    }
+  }
 
   __syncthreads();
   if (tl && tid == 0) tl[1] = __builtin_amdgcn_s_memrealtime();
@@ -716,79 +840,7 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   // slots, the sum L and each slot's weight exp2(m - M); (b) after a barrier a
   // flat loop over (item, element) adds the weighted outputs in slot (token)
   // order.  Only the slots that hold an item are read.
-  if (tid < 64) {
-    // distinct items in slot order (first slot, slots holding it), and the
-    // split ones among them (unit, nsplit, first partial slot): one lane per
-    // merge slot, compacted with ballots so the list stays in slot order
-    const int me = lane < 2 * kWaves ? slot_item[lane] : -1;
-    unsigned mask = 0;
-    bool before = false;
-#pragma unroll
-    for (int t = 0; t < 2 * kWaves; ++t) {
-      const bool same = __builtin_amdgcn_readlane(me, t) == me;
-      mask |= (unsigned)same << t;
-      before |= same && t < lane;
-    }
-    const bool first = lane < 2 * kWaves && me >= 0 && !before;
-    const int ns = first ? slot_meta[lane][2] : 0;
-    // (a prefix item's arrivals are its members', listed below)
-    const bool split = ns > 1 && (!PREFIX || slot_meta[lane][0] < p.units);
-    const unsigned long long fb = __ballot(first), sb = __ballot(split);
-    const unsigned long long below = (1ull << lane) - 1;
-    if (first) {
-      const int n = __popcll(fb & below);
-      it_slot[n] = lane;
-      it_mask[n] = mask;
-    }
-    if (split) {
-      const int k = __popcll(sb & below);
-      split_list[k][0] = slot_meta[lane][0];
-      split_list[k][1] = ns;
-      split_list[k][2] = slot_meta[lane][3];
-    }
-    int nsp = __popcll(sb);
-    if constexpr (PREFIX) {
-      // each member with other splits arrives once for a prefix item
-      for (unsigned long long pm = __ballot(first && slot_meta[lane][0] >= p.units); pm; pm &= pm - 1) {
-        const int sl = __builtin_ctzll(pm);
-        const int nmem = uni(slot_meta[sl][3]) / G;
-        for (int j0 = 0; j0 < nmem; j0 += 64) {
-          const int j = j0 + lane;
-          int mu = 0, ns2 = 0, pb = 0;
-          if (j < nmem) {
-            mu = slot_mem[sl][j][0];
-            ns2 = slot_mem[sl][j][2];
-            pb = slot_mem[sl][j][3];
-          }
-          const bool add = j < nmem && ns2 > 1;
-          const unsigned long long ab = __ballot(add);
-          if (add) {
-            const int k = nsp + __popcll(ab & below);
-            split_list[k][0] = mu;
-            split_list[k][1] = ns2;
-            split_list[k][2] = pb;
-          }
-          nsp += __popcll(ab);
-        }
-      }
-    }
-    if constexpr (PREFIX) {
-      // the waves' put-off arrivals
-      for (int w = 0; w < kWaves; ++w) {
-        const int n = wave_narr[w];
-        for (int i = lane; i < n; i += 64) {
-          split_list[nsp + i][0] = wave_arr[w][i][0];
-          split_list[nsp + i][1] = wave_arr[w][i][1];
-          split_list[nsp + i][2] = wave_arr[w][i][2];
-        }
-        nsp += n;
-      }
-    }
-    if (lane == 0) {
-      num_items = __popcll(fb);
-      num_split = nsp;
-    }
-  }
+  if (PREFIX && tid < 64) scan_slots();
   __syncthreads();
   if (tl && tid == 0) tl[6] = __builtin_amdgcn_s_memrealtime();
   const int nit = uni(num_items);
