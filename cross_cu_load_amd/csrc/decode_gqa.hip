@@ -846,30 +846,32 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
   const int nit = uni(num_items);
   const int GD = G * D;
   const int SD = SR * D;  // elements of a slot's output (rows past an item's own are skipped)
-  if (tid < nit * SR) {
-    // (item, row): all slots' (m, l) loaded together (only the item's count)
-    const int ii = tid / SR, hh = tid - (tid / SR) * SR;
-    const unsigned mask = it_mask[ii];
-    float mt[2 * kWaves], lt[2 * kWaves];
+  // One lane per (item, row, merge slot), the 16 slots of a row in 16
+  // consecutive lanes: a slot's (m, l), then the row's max M and sum
+  // L = sum l exp2(m - M) by butterflies inside the 16 lanes (every lane of a
+  // group takes part: groups are all valid or all past the end).
+  static_assert(2 * kWaves == 16, "one lane per merge slot in groups of 16");
+  for (int base = 0; base < nit * SR * 16; base += kThreads) {
+    const int idx = base + tid;
+    const bool valid = idx < nit * SR * 16;
+    const int t = idx & 15, r = idx >> 4;
+    const int ii = valid ? r / SR : 0, hh = valid ? r - ii * SR : 0;
+    const bool on = valid && ((it_mask[ii] >> t) & 1);
+    const float* sb = merge_slot(t);
+    const float m = on ? sb[hh] : -INFINITY;
+    const float l = on ? sb[SR + hh] : 0.f;
+    float M = m;
 #pragma unroll
-    for (int t = 0; t < 2 * kWaves; ++t) {
-      const bool on = (mask >> t) & 1;
-      const float* sb = merge_slot(t);
-      mt[t] = on ? sb[hh] : -INFINITY;
-      lt[t] = on ? sb[SR + hh] : 0.f;
+    for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
+    const float f = fast_exp2(m - M);  // 0 for slots of other items
+    float L = l * f;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) L += __shfl_xor(L, o, 16);
+    if (on) slot_w[t][hh] = f;
+    if (valid && t == 0) {
+      item_M[ii][hh] = M;
+      item_L[ii][hh] = L;
     }
-    float M = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2 * kWaves; ++t) M = fmaxf(M, mt[t]);
-    float L = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2 * kWaves; ++t) {  // slot (= token) order
-      const float f = fast_exp2(mt[t] - M);  // 0 for slots of other items
-      L += lt[t] * f;
-      if ((mask >> t) & 1) slot_w[t][hh] = f;
-    }
-    item_M[ii][hh] = M;
-    item_L[ii][hh] = L;
   }
   __syncthreads();
   if (tl && tid == 0) tl[7] = __builtin_amdgcn_s_memrealtime();
