@@ -95,6 +95,12 @@ int decode_impl(int reduce, const cc_problem* prob, const void* plan_host, const
     cc::set_error("null argument");
     return CC_ERR_INVALID;
   }
+  // the kernels move q, K, V, out and partials in 16-byte accesses
+  auto misaligned = [](const void* ptr) { return ptr && (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
+  if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(out) || misaligned(workspace)) {
+    cc::set_error("q, k_cache, v_cache, out and workspace must be 16-byte aligned");
+    return CC_ERR_INVALID;
+  }
   if (reduce != CC_REDUCE_FUSED && reduce != CC_REDUCE_SPLIT_COMBINE) {
     cc::set_error("unknown reduction %d", reduce);
     return CC_ERR_INVALID;

@@ -286,7 +286,9 @@ int cc_workspace_check(const void* plan_host, const void* workspace, void* strea
  * plan_host: the blob from cc_plan (host); plan_dev: the same bytes in device
  * memory.  q, k_cache, v_cache (NULL for MLA modes), block_table, seqlens,
  * indices (MLA_SPARSE, else NULL): device, layouts as in cc_problem.
- * out, lse: device outputs.  workspace: device, >= cc_workspace_size bytes,
+ * out, lse: device outputs.  q, k_cache, v_cache, out and the workspace must
+ * be 16-byte aligned (CC_ERR_INVALID otherwise; every torch allocation is).
+ * workspace: device, >= cc_workspace_size bytes,
  * initialised once with cc_workspace_init.  Asynchronous on `stream`.  When
  * the plan holds empty sequences, a first small kernel writes their out (0)
  * and lse (-inf).

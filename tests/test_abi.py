@@ -248,6 +248,12 @@ def test_decode_rejects_before_any_launch(lib):
     assert call(prob, plan=junk.ctypes.data_as(ctypes.c_void_p)) == B.CC_ERR_PLAN
     bad_scale = B.problem(**{**kw, "softmax_scale": 0.0})
     assert call(bad_scale) == B.CC_ERR_INVALID
+    # 16-byte accesses: a misaligned out or q is refused
+    odd_ptr = ctypes.c_void_p(0x1004)
+    assert lib.cc_decode_variant(0, ctypes.byref(prob), hp, fake, fake, fake, fake, fake, fake, None, odd_ptr,
+                                 fake, fake, ws_need, None) == B.CC_ERR_INVALID
+    assert lib.cc_decode_variant(0, ctypes.byref(prob), hp, fake, odd_ptr, fake, fake, fake, fake, None, fake,
+                                 fake, fake, ws_need, None) == B.CC_ERR_INVALID
     # unsupported shapes (head dim 96) are refused before launch
     odd = B.problem(**{**kw, "head_dim_qk": 96, "head_dim_v": 96})
     blob2 = B.plan(odd, sl, None, num_cus=8, num_xcds=1, tile_tokens=32, heads_per_unit=4)
