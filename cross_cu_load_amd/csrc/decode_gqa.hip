@@ -963,7 +963,8 @@ gqa_decode_kernel(const Params p, const int32_t* __restrict__ wg_off, const int4
       if (PREFIX)
         merge_units_batched<kThreads, 2, kPrefixMergeChunk>(partials, done_units, nd, p.slot_floats, G, D, out, lse);
       else
-        merge_units_direct<kThreads>(partials, done_units, nd, p.slot_floats, G, D, out, lse);
+        merge_units_grouped<kThreads>(partials, done_units, nd, p.slot_floats, G, D, out, lse,
+                                      reinterpret_cast<float*>(smem));
     }
   }
   if (tl && tid == 0) {

@@ -180,16 +180,13 @@ __device__ void merge_splits(const float* pb, int ns, int slot_floats, int hpu, 
   }
 }
 
-// Single-round merge for units whose output fits the workgroup (hpu * dv <=
-// NT elements per unit, nu units at once): thread e owns output element e of
-// every unit it covers and issues the loads of m, l and o of 32 splits at a
-// time before using any of them, combining the chunks online (in split order,
-// so the result does not depend on which piece arrived last).  On the tail of
-// a decode this halves the memory round trips of merge_splits' two-phase form.
-// units[i] = {partial base slot, nsplit, output row}; out/lse rows are
-// dv / 1 floats apart.
+// Single-round merge of one unit: thread e owns output element e and issues
+// the loads of m, l and o of CH splits at a time before using any of them,
+// combining the chunks online in split order (so the result does not depend
+// on which piece arrived last).  The shared-prefix kernel's waves use it with
+// CH = 4, the same chunking as merge_units_batched, so both give the same bits.
 constexpr int kDirectChunk = 32;
-// One unit of merge_units_direct: ns splits from partial slot pb on, output
+// ns splits from partial slot pb on, output
 // rows row0 .. row0 + hpu - 1; thread t of NT; CH splits' loads in flight.
 template <int NT, int CH = kDirectChunk>
 __device__ __forceinline__ void merge_unit_direct(const float* pb, int ns, size_t row0, int slot_floats, int hpu,
@@ -232,7 +229,7 @@ __device__ __forceinline__ void merge_unit_direct(const float* pb, int ns, size_
   }
 }
 
-// merge_units_direct for many units at once: the (unit, column quad) pairs
+// merge_unit_direct for many units at once: the (unit, column quad) pairs
 // of all nu units are spread over the NT threads, each thread merging UB
 // pairs together with CH splits' loads of every pair in flight (m, l and the
 // quad's four o values as two 8-byte loads), so a workgroup that completes
@@ -319,15 +316,102 @@ __device__ void merge_units_batched(const float* partials, const int (*units)[3]
   }
 }
 
+
+// The units a workgroup completed, one after another, each in one round of
+// loads with the splits spread over thread groups.  Thread t takes column quad
+// q = t mod E4 (E4 = hpu dv / 4 quads) for group g = t / E4, and group g the
+// splits g, g + TG, g + 2 TG, ... (TG = min(8, NT / E4) groups), merged online
+// in that order with kGroupChunk splits' loads in flight; the groups' (M, L, O)
+// then meet in LDS and group 0 combines them in group order.  A split costs a
+// thread four loads (m, l and its o quad as two 8-byte halves) for four output
+// elements, against three per element in merge_unit_direct.  The grouping is
+// fixed, so the bits do not depend on which piece arrived last.  lds: at least
+// 24 NT bytes; dv a multiple of 4; out rows 16-byte aligned.
+constexpr int kGroupChunk = 8;
 template <int NT>
-__device__ __forceinline__ void merge_units_direct(const float* partials, const int (*units)[3], int nu, int slot_floats, int hpu,
-                                   int dv, float* out, float* lse) {
+__device__ void merge_units_grouped(const float* partials, const int (*units)[3], int nu, int slot_floats,
+                                    int hpu, int dv, float* out, float* lse, float* lds) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  constexpr float kLn2 = 0.69314718055994531f;
+  const int tid = threadIdx.x;
+  const int E4 = hpu * dv / 4;
+  int TG = NT / E4;
+  TG = TG < 1 ? 1 : (TG > 8 ? 8 : TG);
+  const int g = TG > 1 ? tid / E4 : 0;
+  const int o_off = partial_o_offset(hpu);
+  f4* lo = reinterpret_cast<f4*>(lds);  // [TG][E4] group outputs, then M and L
+  float* lm = lds + 4 * NT;
+  float* ll = lm + NT;
   for (int u = 0; u < nu; ++u) {
-    // unit fields are the same for every thread: split bases stay scalar
     const int ns = __builtin_amdgcn_readfirstlane(units[u][1]);
     const float* pb = partials + (size_t)__builtin_amdgcn_readfirstlane(units[u][0]) * slot_floats;
     const size_t row0 = (size_t)__builtin_amdgcn_readfirstlane(units[u][2]);
-    merge_unit_direct<NT>(pb, ns, row0, slot_floats, hpu, dv, out, lse, threadIdx.x);
+    for (int q0 = 0; q0 < E4; q0 += NT) {  // one pass unless E4 > NT (then TG = 1)
+      const int q = q0 + (TG > 1 ? tid - g * E4 : tid);
+      const bool on = g < TG && q < E4;
+      const int hh = on ? (4 * q) / dv : 0;
+      float M = -INFINITY, L = 0.f;
+      f4 O = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = g; on && s0 < ns; s0 += TG * kGroupChunk) {
+        float mt[kGroupChunk], lt[kGroupChunk];
+        f4 ot[kGroupChunk];
+#pragma unroll
+        for (int i = 0; i < kGroupChunk; ++i) {
+          const int sp = s0 + i * TG;
+          const bool ok = sp < ns;
+          const float* ps = pb + (size_t)(ok ? sp : 0) * slot_floats;
+          const float m = partial_load(ps + hh), l = partial_load(ps + hpu + hh);
+          const uint64_t* po = reinterpret_cast<const uint64_t*>(ps + o_off + 4 * q);
+          const uint64_t lo8 = __hip_atomic_load(po, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t hi8 = __hip_atomic_load(po + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          mt[i] = ok ? m : -INFINITY;
+          lt[i] = ok ? l : 0.f;
+          ot[i] = ok ? f4{__builtin_bit_cast(float, (uint32_t)lo8), __builtin_bit_cast(float, (uint32_t)(lo8 >> 32)),
+                          __builtin_bit_cast(float, (uint32_t)hi8), __builtin_bit_cast(float, (uint32_t)(hi8 >> 32))}
+                     : f4{0.f, 0.f, 0.f, 0.f};
+        }
+        float Mc = M;
+#pragma unroll
+        for (int i = 0; i < kGroupChunk; ++i) Mc = fmaxf(Mc, mt[i]);
+        const float a = Mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
+        L *= a;
+        O *= a;
+#pragma unroll
+        for (int i = 0; i < kGroupChunk; ++i) {
+          const float f = __builtin_amdgcn_exp2f(mt[i] - Mc);
+          L += lt[i] * f;
+          O += ot[i] * f;
+        }
+        M = Mc;
+      }
+      if (TG > 1) {
+        if (on) {
+          lo[g * E4 + q] = O;
+          lm[g * E4 + q] = M;
+          ll[g * E4 + q] = L;
+        }
+        __syncthreads();
+        if (on && g == 0) {
+          for (int gg = 1; gg < TG; ++gg) {  // group order
+            const float Mg = lm[gg * E4 + q], Lg = ll[gg * E4 + q];
+            const f4 Og = lo[gg * E4 + q];
+            const float Mc = fmaxf(M, Mg);
+            const float a = Mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
+            const float b = Mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mg - Mc);
+            L = L * a + Lg * b;
+            O = O * a + Og * b;
+            M = Mc;
+          }
+        }
+        __syncthreads();  // the LDS is free for the next unit
+      }
+      if (on && g == 0) {
+        const int col = 4 * q - hh * dv;
+        const size_t row = row0 + hh;
+        *reinterpret_cast<f4*>(out + row * dv + col) = O / L;
+        if (col == 0) lse[row] = (M + __log2f(L)) * kLn2;
+      }
+    }
   }
 }
 
